@@ -1,0 +1,393 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test would fail for a plausible slip in the oracle: a dropped factor 2,
+a wrong sign of the compensation, a transposed or lower/upper-swapped U, a
+row of U read at the wrong index, the lazy update applied to the wrong
+columns, a grid off by one level, a wrong rounding mode.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+from oracle import gptq as og
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F32 = np.float32
+
+
+def _spd_problem(d_out, d_in, n, seed, dead=()):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((d_in, n)) + 0.5 * rng.standard_normal((d_in, 3)) @ rng.standard_normal((3, n))
+    for d in dead:
+        X[d] = 0.0
+    W = rng.standard_normal((d_out, d_in)) * 0.02
+    return W, X
+
+
+# ---------------------------------------------------------------------------
+# P1: the worked two-weight example (aicassindra "A worked two-weight example")
+# ---------------------------------------------------------------------------
+def test_worked_example_golden():
+    g = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    H = np.array(g["H"])
+    w = np.array([g["w"]])
+    U, dead, lam = oracle.prepare(H, lam=0.0)
+    assert lam == 0.0 and not dead.any()
+    step = g["grid_step"]
+    trace = []
+    r = oracle.quantize(w, U, bits=8, group_size=0, block_size=128,
+                        fixed_grid=(np.array([step]), np.array([0.0])), trace=trace)
+    # q1 = 0.5 on a grid of step 0.5
+    assert r.w_hat[0, 0] == pytest.approx(g["q1"], abs=0)
+    # delta1 = q1 - w1
+    assert r.w_hat[0, 0] - w[0, 0] == pytest.approx(g["delta1"], abs=1e-15)
+    # compensation moves w2 from 0.30 to 0.38 (delta2 = +0.08)
+    assert trace[1][0] == pytest.approx(g["w2_after"], abs=1e-14)
+    assert trace[1][0] - w[0, 1] == pytest.approx(g["delta2"], abs=1e-14)
+    # output error delta H delta^T: 0.0576 without compensation ...
+    d_nocomp = np.array([g["delta1"], 0.0])
+    assert d_nocomp @ H @ d_nocomp == pytest.approx(g["error_no_compensation"], abs=1e-14)
+    # ... 0.0384 with it; this equals the first scaled error E_1^2 = e_1^2/[H^-1]_11
+    d_comp = np.array([g["delta1"], trace[1][0] - w[0, 1]])
+    assert d_comp @ H @ d_comp == pytest.approx(g["error_with_compensation"], abs=1e-14)
+    assert r.E[0, 0] ** 2 == pytest.approx(g["error_with_compensation"], abs=1e-14)
+    red = 1 - g["error_with_compensation"] / g["error_no_compensation"]
+    assert red == pytest.approx(g["reduction_fraction"], abs=0.005)
+
+
+def test_two_by_two_factor_closed_form():
+    # Cholesky of H^-1 for H = [[a, b], [b, c]] in closed form
+    a, b, c = 4.0, 2.0, 3.0
+    det = a * c - b * b
+    hinv = np.array([[c, -b], [-b, a]]) / det
+    u00 = np.sqrt(hinv[0, 0])
+    u01 = hinv[0, 1] / u00
+    u11 = np.sqrt(hinv[1, 1] - u01 ** 2)
+    U = oracle.hinv_cholesky_upper(np.array([[a, b], [b, c]]))
+    np.testing.assert_allclose(U, [[u00, u01], [0.0, u11]], rtol=1e-15, atol=1e-16)
+    np.testing.assert_allclose(U, [[0.6123724356957945, -0.408248290463863], [0, 0.5773502691896258]], rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Hessian: the Kronecker structure (math4ai "GPTQ Hessian"), factor 2, layout
+# ---------------------------------------------------------------------------
+def test_kronecker_bruteforce_pins_factor_two_and_layout():
+    rng = np.random.default_rng(3)
+    d_out, d_in, n = 2, 3, 5
+    X = rng.standard_normal((d_in, n))
+    W = rng.standard_normal((d_out, d_in))
+
+    def f(v):
+        What = v.reshape(d_out, d_in)  # rows stacked one under another
+        R = W @ X - What @ X
+        return float(np.sum(R * R))
+
+    m = d_out * d_in
+    x0 = rng.standard_normal(m)
+    h = 0.5
+    Hb = np.zeros((m, m))
+    for a in range(m):
+        for b in range(m):
+            ea = np.zeros(m); ea[a] = h
+            eb = np.zeros(m); eb[b] = h
+            Hb[a, b] = (f(x0 + ea + eb) - f(x0 + ea) - f(x0 + eb) + f(x0)) / (h * h)
+    H = oracle.hessian([X])
+    np.testing.assert_allclose(Hb, np.kron(np.eye(d_out), H), rtol=1e-9, atol=1e-9)
+
+
+def test_hessian_chunks_and_one_hot():
+    X = np.zeros((3, 4))
+    X[1, 2] = 1.0
+    H = oracle.hessian([X[:, :1], X[:, 1:]])
+    expect = np.zeros((3, 3)); expect[1, 1] = 2.0
+    np.testing.assert_array_equal(H, expect)
+    assert np.all(oracle.hessian([], d_in=5) == 0)
+
+
+# ---------------------------------------------------------------------------
+# damping and dead channels (aicassindra "The Cholesky trick")
+# ---------------------------------------------------------------------------
+def test_damp_closed_form():
+    H = np.diag([1.0, 2.0, 3.0, 0.0])
+    H[0, 1] = H[1, 0] = 0.5
+    Hd, dead, lam = oracle.damp(H, 0.01)
+    assert lam == pytest.approx(0.01 * 6.0 / 4)
+    assert dead.tolist() == [False, False, False, True]
+    np.testing.assert_allclose(np.diag(Hd), [1.015, 2.015, 3.015, 1.015])
+    assert Hd[0, 1] == 0.5 and Hd[1, 0] == 0.5
+
+
+def test_non_pd_detection():
+    rng = np.random.default_rng(1)
+    X = rng.standard_normal((12, 5))  # N < d_in: rank 5
+    H = oracle.hessian([X])
+    with pytest.raises(oracle.NotPositiveDefinite):
+        oracle.prepare(H, lam=0.0)
+    U, _, _ = oracle.prepare(H, 0.01)  # damping makes it well-posed
+    assert np.all(np.isfinite(U))
+
+
+def test_factor_properties_and_reverse_route():
+    W, X = _spd_problem(4, 20, 60, 5)
+    Hd, _, _ = oracle.damp(oracle.hessian([X]))
+    U = oracle.hinv_cholesky_upper(Hd)
+    assert np.all(np.tril(U, -1) == 0) and np.all(np.diag(U) > 0)
+    np.testing.assert_allclose(U.T @ U @ Hd, np.eye(20), atol=1e-10)
+    # the device route: reverse-order Cholesky H = R R^T (R upper), U = R^-1
+    J = np.eye(20)[::-1]
+    Lt = np.linalg.cholesky(J @ Hd @ J)
+    R = J @ Lt @ J
+    np.testing.assert_allclose(R @ R.T, Hd, rtol=1e-12, atol=1e-9)
+    np.testing.assert_allclose(np.linalg.inv(R), U, rtol=1e-9, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# grid and rounding (readings; hand-computed values)
+# ---------------------------------------------------------------------------
+def test_grid_hand_values():
+    s, z = oracle.grid(F32(-0.3), F32(0.45), 4)
+    assert s == F32(F32(F32(0.45) - F32(-0.3)) / F32(15))
+    assert float(s) == pytest.approx(0.05, rel=1e-6)
+    assert z == 6.0
+    # all-zero range -> [-1, 1]: s = fl32(2/15) = 0.13333334 rounds up, so
+    # fl32(1/s) = 7.4999995 and z = 7 (not 8)
+    s, z = oracle.grid(F32(0), F32(0), 4)
+    assert s == F32(F32(2) / F32(15)) and F32(F32(1) / s) == F32(7.4999995) and z == 7.0
+    # positive-only: zero is the lower end
+    s, z = oracle.grid(F32(0.2), F32(0.5), 4)
+    assert z == 0.0 and s == F32(F32(0.5) / F32(15))
+    # negative-only: zero is the upper end
+    s, z = oracle.grid(F32(-0.6), F32(-0.1), 3)
+    assert z == 7.0 and s == F32(F32(0.6) / F32(7))
+
+
+def test_grid_covers_range_and_represents_zero():
+    rng = np.random.default_rng(9)
+    mn = -np.abs(rng.standard_normal(1000)).astype(F32)
+    mx = np.abs(rng.standard_normal(1000)).astype(F32)
+    for bits in (2, 3, 4, 8):
+        s, z = oracle.grid(mn, mx, bits)
+        maxq = 2 ** bits - 1
+        lo = s.astype(np.float64) * (0 - z)
+        hi = s.astype(np.float64) * (maxq - z)
+        assert np.all(np.abs(lo - mn) <= s * 0.5 + 1e-7)
+        assert np.all(np.abs(hi - mx) <= s * 0.5 + 1e-7)
+        q, _ = oracle.quantize_values(np.zeros(1000), s, z, bits)
+        assert np.all(q == z)
+
+
+def test_rounding_half_to_even_and_clamp():
+    s = np.array([1.0, 1.0, 1.0, 1.0, 0.5], F32)
+    z = np.array([0.0, 0.0, 0.0, 0.0, 3.0], F32)
+    q, v = oracle.quantize_values(np.array([2.5, 3.5, -4.0, 99.0, 0.25]), s, z, 4)
+    assert q.tolist() == [2.0, 4.0, 0.0, 15.0, 4.0]
+    assert v[-1] == F32(3.5)
+
+
+# ---------------------------------------------------------------------------
+# P2: the Cholesky-row update equals the explicit OBS update by re-inversion
+# (aicassindra "Greedy quantization..."; mbrenndoerfer Schur complement)
+# ---------------------------------------------------------------------------
+def test_schur_complement_formula():
+    W, X = _spd_problem(1, 9, 30, 2)
+    Hd, _, _ = oracle.damp(oracle.hessian([X]))
+    Hinv = np.linalg.inv(Hd)
+    q = 0
+    down = Hinv[1:, 1:] - np.outer(Hinv[1:, q], Hinv[q, 1:]) / Hinv[q, q]
+    np.testing.assert_allclose(down, np.linalg.inv(Hd[1:, 1:]), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("d_in,block", [(9, 1), (16, 4), (13, 16)])
+def test_sweep_matches_explicit_obs_reinversion(d_in, block):
+    W, X = _spd_problem(5, d_in, 40, 11 + d_in)
+    Hd, _, _ = oracle.damp(oracle.hessian([X]))
+    U = oracle.hinv_cholesky_upper(Hd)
+    bits = 3
+    r = oracle.quantize(W, U, bits, 0, block)
+    s = r.scales[:, 0]
+    z = r.zeros[:, 0].astype(F32)
+    for row in range(W.shape[0]):
+        w = W[row].astype(np.float64).copy()
+        for q in range(d_in):
+            Finv = np.linalg.inv(Hd[q:, q:])
+            qv, _ = oracle.quantize_values(w[q:q + 1], s[row:row + 1], z[row:row + 1], bits)
+            wq = float(s[row]) * (float(qv[0]) - float(z[row]))
+            e = w[q] - wq
+            # OBS: delta = -(e / [Hf^-1]_qq) [Hf^-1]_{:,q}
+            w[q:] += -(e / Finv[0, 0]) * Finv[:, 0]
+            assert w[q] == pytest.approx(wq, abs=1e-13)
+            assert r.codes[row, q] == int(qv[0])
+            assert r.E[row, q] == pytest.approx(e / np.sqrt(Finv[0, 0]), rel=1e-9, abs=1e-14)
+        np.testing.assert_allclose(r.w_hat[row], w, rtol=1e-10, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# P3: lazy batches are exact (aicassindra "GPTQ's speedups": same math)
+# ---------------------------------------------------------------------------
+def test_lazy_batch_invariance():
+    W, X = _spd_problem(24, 200, 400, 21)
+    U, dead, _ = oracle.prepare(oracle.hessian([X]))
+    ref = oracle.quantize(W, U, 4, 0, 1)
+    for B in (3, 32, 128, 200, 1000):
+        r = oracle.quantize(W, U, 4, 0, B)
+        np.testing.assert_array_equal(r.codes, ref.codes)
+        np.testing.assert_allclose(r.w_hat, ref.w_hat, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(r.E, ref.E, rtol=1e-10, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# P4: rows decouple (aicassindra objective; math4ai row split)
+# ---------------------------------------------------------------------------
+def test_row_decoupling_and_permutation():
+    W, X = _spd_problem(40, 64, 200, 31)
+    U, dead, _ = oracle.prepare(oracle.hessian([X]))
+    for g in (0, 16):
+        full = oracle.quantize(W, U, 4, g, 16)
+        perm = np.random.default_rng(0).permutation(40)
+        sub = perm[:7]
+        r = oracle.quantize(W[sub], U, 4, g, 16)
+        np.testing.assert_array_equal(r.codes, full.codes[sub])
+        np.testing.assert_array_equal(r.scales, full.scales[sub])
+        np.testing.assert_allclose(r.E, full.E[sub], rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# P6: diagonal H -> no compensation -> plain round-to-nearest
+# ---------------------------------------------------------------------------
+def test_diagonal_hessian_reduces_to_rtn():
+    rng = np.random.default_rng(4)
+    d_in, n = 32, 64
+    Q, _ = np.linalg.qr(rng.standard_normal((n, n)))
+    X = (np.diag(rng.uniform(0.5, 2.0, d_in)) @ Q[:d_in])  # orthogonal rows
+    H = oracle.hessian([X])
+    assert np.max(np.abs(H - np.diag(np.diag(H)))) < 1e-12
+    U, _, _ = oracle.prepare(H)
+    W = rng.standard_normal((10, d_in)) * 0.02
+    r = oracle.quantize(W, U, 4, 0, 8)
+    # textbook RTN with the same grid: nearest of the 16 levels s (k - z)
+    s = r.scales[:, :1].astype(np.float64)
+    z = r.zeros[:, :1].astype(np.float64)
+    levels = s * (np.arange(16)[None, :] - z)
+    nearest = np.argmin(np.abs(W[:, :, None] - levels[:, None, :]), axis=2)
+    np.testing.assert_array_equal(r.codes, nearest)
+
+
+# ---------------------------------------------------------------------------
+# P8: sum of squared scaled errors = tr(dW H dW^T), for any code choice
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("g,dead", [(0, ()), (16, ()), (0, (3, 17)), (8, (0, 40))])
+def test_loss_identity(g, dead):
+    W, X = _spd_problem(12, 48, 150, 41, dead=dead)
+    H = oracle.hessian([X])
+    Hd, dmask, lam = oracle.damp(H)
+    U = oracle.hinv_cholesky_upper(Hd)
+    r = oracle.quantize(W, U, 3, g, 16, dead=dmask)
+    W0 = W.copy(); W0[:, dmask] = 0.0
+    D = W0 - r.w_hat
+    np.testing.assert_allclose(r.err_sq, np.einsum("ij,jk,ik->i", D, Hd, D), rtol=1e-9)
+    # and in terms of the objective: sum E^2 = 2 ||dW X||^2 + lam ||dW||^2 (live part)
+    out = oracle.output_error(W0, r.w_hat, [X])
+    assert r.err_sq.sum() == pytest.approx(2 * out + lam * np.sum(D * D), rel=1e-9)
+    # any code choice: replay on random neighbouring codes
+    rng = np.random.default_rng(7)
+    hint = np.clip(r.codes.astype(int) + rng.integers(-1, 2, r.codes.shape), 0, 7)
+    r2 = oracle.quantize(W, U, 3, g, 16, dead=dmask, hint=hint)
+    D2 = W0 - r2.w_hat
+    np.testing.assert_allclose(r2.err_sq, np.einsum("ij,jk,ik->i", D2, Hd, D2), rtol=1e-9)
+
+
+# ---------------------------------------------------------------------------
+# P9: after each step the free weights are the constrained optimum
+# ---------------------------------------------------------------------------
+def test_per_step_optimality():
+    W, X = _spd_problem(3, 20, 80, 51)
+    Hd, _, _ = oracle.damp(oracle.hessian([X]))
+    U = oracle.hinv_cholesky_upper(Hd)
+    for B in (1, 6, 20):
+        trace = []
+        r = oracle.quantize(W, U, 3, 0, B, trace=trace)
+        T = np.stack(trace, axis=1)  # [d_out, d_in] value of column j just before rounding
+        for q in range(1, 20):
+            Qi = np.arange(q)
+            Fi = np.arange(q, 20)
+            # argmin over w_F of (w - w0) H (w - w0)^T with w_Q fixed at What_Q
+            dQ = r.w_hat[:, Qi] - W[:, Qi]
+            wF = W[:, Fi] - np.linalg.solve(Hd[np.ix_(Fi, Fi)], Hd[np.ix_(Fi, Qi)] @ dQ.T).T
+            np.testing.assert_allclose(T[:, q], wF[:, 0], rtol=1e-9, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# P10: dead channels are decoupled (aicassindra "simply skipped")
+# ---------------------------------------------------------------------------
+def test_dead_channel_removal_equivalence():
+    dead_idx = (2, 9, 10)
+    W, X = _spd_problem(8, 24, 100, 61, dead=dead_idx)
+    W[:, list(dead_idx)] = 0.0  # keep the per-row grid identical in both problems
+    H = oracle.hessian([X])
+    Hd, dmask, lam = oracle.damp(H)
+    assert set(np.nonzero(dmask)[0]) == set(dead_idx)
+    r = oracle.quantize(W, oracle.hinv_cholesky_upper(Hd), 4, 0, 5, dead=dmask)
+    live = np.setdiff1d(np.arange(24), dead_idx)
+    Ur, _, _ = oracle.prepare(oracle.hessian([X[live]]), lam=lam)
+    rr = oracle.quantize(W[:, live], Ur, 4, 0, 5)
+    np.testing.assert_array_equal(r.codes[:, live], rr.codes)
+    np.testing.assert_allclose(r.E[:, live], rr.E, rtol=1e-9, atol=1e-14)
+    assert np.all(r.E[:, list(dead_idx)] == 0)
+    assert np.all(r.codes[:, list(dead_idx)] == r.zeros[:, :1])
+
+
+# ---------------------------------------------------------------------------
+# group grids: rebuilt from the current weights at each group start
+# ---------------------------------------------------------------------------
+def test_group_grid_from_current_weights():
+    W, X = _spd_problem(6, 32, 90, 71)
+    U, _, _ = oracle.prepare(oracle.hessian([X]))
+    trace = []
+    r = oracle.quantize(W, U, 4, 8, 16, trace=trace)
+    T = np.stack(trace, axis=1)
+    for g in range(4):
+        j = 8 * g
+        # at the group start, columns j..j+7 as stored; column j is current
+        # (the in-block and deferred updates before j are applied)
+        mn = np.minimum(T[:, j], 0)
+        assert np.all(r.minmax[:, g, 0] <= mn.astype(F32) + 1e-7)
+    # a single group spanning the row equals the per-row grid
+    r1 = oracle.quantize(W, U, 4, 32, 16)
+    r0 = oracle.quantize(W, U, 4, 0, 16)
+    np.testing.assert_array_equal(r1.scales, r0.scales)
+    np.testing.assert_array_equal(r1.codes, r0.codes)
+
+
+def test_dequantize_matches_sweep():
+    W, X = _spd_problem(6, 32, 90, 81)
+    U, _, _ = oracle.prepare(oracle.hessian([X]))
+    for g in (0, 8):
+        r = oracle.quantize(W, U, 4, g, 16)
+        np.testing.assert_array_equal(oracle.dequantize(r.codes, r.scales, r.zeros, g), r.w_hat)
+
+
+# ---------------------------------------------------------------------------
+# tie-aware replay classifies an injected tie and an injected real flip
+# ---------------------------------------------------------------------------
+def test_tie_aware_replay():
+    W, X = _spd_problem(64, 64, 200, 91)
+    U, _, _ = oracle.prepare(oracle.hessian([X]))
+    r = oracle.quantize(W, U, 4, 0, 16)
+    same = oracle.quantize(W, U, 4, 0, 16, hint=r.codes)
+    assert same.ties == 0 and same.hard == 0
+    frac = np.abs(r.V - np.floor(r.V) - 0.5)  # distance to the nearest midpoint
+    i, j = np.unravel_index(np.argmin(frac), frac.shape)
+    hint = r.codes.copy()
+    other = np.floor(r.V[i, j]) if r.codes[i, j] == np.floor(r.V[i, j]) + 1 else np.floor(r.V[i, j]) + 1
+    hint[i, j] = int(other)
+    t = oracle.quantize(W, U, 4, 0, 16, hint=hint, tie_tol=float(frac[i, j]) + 1e-9)
+    assert t.ties == 1 and t.hard == 0
+    i2, j2 = np.unravel_index(np.argmax(frac > 0.3), frac.shape)  # far from any midpoint
+    hint2 = r.codes.copy()
+    hint2[i2, j2] = (int(hint2[i2, j2]) + 1) % 16
+    h = oracle.quantize(W, U, 4, 0, 16, hint=hint2)
+    assert h.hard >= 1
