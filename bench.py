@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of the GPTQ per-layer path on one MI355X.
+
+A step is one pass of the whole path over one layer: zero H, accumulate
+H = 2 X X^T over the token chunks, damp + factor U, and the blocked sweep.
+Inputs are seeded synthetic tensors already resident in HBM.  Prints one
+JSON line with ms per layer, per-stage and per-kernel times, the roofline
+of the dominant kernel (its time measured with HIP events on the stream it
+runs on) and the oracle's time on the host cores as a baseline.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload attn_proj]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ms per 4096×4096 4-bit GPTQ layer (XXᵀ+Cholesky+sweep); % MFMA/HBM peak"
+PEAK_TFLOPS = {"f16": 2500.0, "f32": 157.3, "f64": 78.6}
+PEAK_HBM_GBS = 8000.0
+NB = 64  # panel width of the blocked factorization (kCholNB in the library)
+
+# kernel -> (dtype class of its arithmetic, bound)
+KERNEL_CLASS = {
+    "hessian_f16": ("f16", "mfma"),
+    "hessian_f32": ("f32", "mfma"),
+    "chol_panel": ("f64", "mfma"),
+    "chol_trail": ("f64", "mfma"),
+    "q_trail": ("f32", "mfma"),
+}
+
+
+def algorithmic_flops(name: str, d_out: int, d_in: int, n_tok: int, block: int) -> float:
+    """Flops the method needs in the work a kernel class does in one layer."""
+    n = d_in
+    if name.startswith("hessian"):
+        return float(n) * (n + 1) * n_tok
+    if name == "chol_trail":
+        tot = 0.0
+        T = (n + NB - 1) // NB
+        for k in range(T):
+            m = max(0, n - (k + 1) * NB)
+            tot += m * (m + 1) * NB + 2.0 * m * min(n, (k + 1) * NB) * NB
+        return tot
+    if name == "chol_panel":
+        tot = 0.0
+        T = (n + NB - 1) // NB
+        for k in range(T):
+            m = max(0, n - (k + 1) * NB)
+            tot += 2.0 * m * NB * NB + 2.0 * NB * NB * min(n, k * NB)
+        return tot
+    if name == "q_trail":
+        tot = 0.0
+        for b0 in range(0, n, block):
+            b1 = min(b0 + block, n)
+            tot += 2.0 * d_out * (b1 - b0) * (n - b1)
+        return tot
+    return 0.0
+
+
+def cpu_baseline(W, X_chunks, bits, group, block, damp, rows: int):
+    import numpy as np
+
+    import oracle
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        threads = 1
+    d_out = W.shape[0]
+    rows = min(rows, d_out)
+    t0 = time.perf_counter()
+    H = oracle.hessian(X_chunks)
+    t1 = time.perf_counter()
+    U, dead, _ = oracle.prepare(H, damp)
+    t2 = time.perf_counter()
+    oracle.quantize(W[:rows].astype(np.float64), U, bits, group, block, dead=dead)
+    t3 = time.perf_counter()
+    scale = d_out / rows
+    ms = ((t1 - t0) + (t2 - t1) + (t3 - t2) * scale) * 1e3
+    return {
+        "value": round(ms, 1),
+        "unit": "ms",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"full H and U; sweep on {rows} of {d_out} rows scaled x{scale:g} (rows decouple); "
+                   f"stage s: H {t1 - t0:.2f}, U {t2 - t1:.2f}, sweep sample {t3 - t2:.2f}"),
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="attn_proj")
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-breakdown", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the path is a single-GPU kernel sequence); got --gpus {args.gpus}",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import workloads as wlm
+    from post_weight_quantization_04_amd import _lib, layer
+
+    if not os.path.exists(_lib.LIB_PATH):
+        from post_weight_quantization_04_amd import build
+        build.build()
+    _lib.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 2
+
+    wl = wlm.get(args.workload)
+    if len(wl.layers) != 1:
+        print("bench.py times single-layer workloads", file=sys.stderr)
+        return 2
+    spec = wl.layers[0]
+    xs = wl.x(spec.x_key)
+    d_out, d_in, n_tok = spec.d_out, spec.d_in, xs.n_tokens
+    print(f"[bench] workload {wl.name}: W {d_out}x{d_in} {spec.dtype}, X {d_in}x{n_tok} {xs.dtype}, "
+          f"{wl.bits}-bit g{wl.group_size} B{wl.block_size}", file=sys.stderr, flush=True)
+    W = wlm.make_weight(wl)
+    X = wlm.x_full(wl, spec.x_key)
+    dev = torch.device("cuda:0")
+    Wd = torch.from_numpy(W).to(dev)
+    Xd = torch.from_numpy(X).to(dev)
+    H = torch.zeros((d_in, d_in), dtype=torch.float32, device=dev)
+    ws1, ws2 = layer.Workspace(dev), layer.Workspace(dev)
+    fac = layer.prepare(H.fill_(0).fill_diagonal_(1.0), wl.damp, ws=ws1)
+    qout = layer.quantize(Wd, fac, wl.bits, wl.group_size, wl.block_size, ws=ws2)
+    chunk = xs.chunk
+    stream = torch.cuda.current_stream()
+
+    def stage_h():
+        H.zero_()
+        for t0 in range(0, n_tok, chunk):
+            _lib.hessian_accumulate(H, Xd[:, t0:t0 + chunk])
+
+    def stage_u():
+        layer.prepare(H, wl.damp, ws=ws1, out=fac)
+
+    def stage_q():
+        layer.quantize(Wd, fac, wl.bits, wl.group_size, wl.block_size, ws=ws2, out=qout)
+
+    def step():
+        stage_h()
+        stage_u()
+        stage_q()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(fac.info.cpu()[0]) != 0:
+        print(f"factorization failed: info={int(fac.info.cpu()[0])}", file=sys.stderr)
+        return 1
+
+    # per-stage times (torch events on the current stream, which the library uses)
+    stages = {"hessian": stage_h, "prepare_hinv": stage_u, "quantize_layer": stage_q}
+    stage_ms = {}
+    reps = max(3, min(args.steps, 10))
+    for name, fn in stages.items():
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        step()
+        torch.cuda.synchronize()
+        tot = 0.0
+        for _ in range(reps):
+            if name != "hessian":
+                stage_h()
+            if name == "quantize_layer":
+                stage_u()
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            tot += a.elapsed_time(b)
+        stage_ms[name] = tot / reps
+
+    # per-kernel times (library-recorded HIP events around each launch)
+    kernel_ms = {}
+    kernel_launches = {}
+    if not args.no_kernel_breakdown:
+        for name in _lib.kernel_names():
+            _lib.timing_enable(name)
+            step()
+            torch.cuda.synchronize()
+            ms, cnt = _lib.timing_read()
+            _lib.timing_enable(None)
+            if cnt:
+                kernel_ms[name] = ms
+                kernel_launches[name] = cnt
+    dominant = max((k for k in kernel_ms if k in KERNEL_CLASS), key=lambda k: kernel_ms[k], default="chol_trail")
+
+    # timed region: K steps, with the dominant kernel's launches bracketed by events
+    _lib.timing_enable(dominant)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    dom_ms, dom_launches = _lib.timing_read()
+    _lib.timing_enable(None)
+    if int(fac.info.cpu()[0]) != 0:
+        print("factorization failed in the timed region", file=sys.stderr)
+        return 1
+
+    dclass, bound = KERNEL_CLASS.get(dominant, ("f32", "alu"))
+    flops_step = algorithmic_flops(dominant, d_out, d_in, n_tok, wl.block_size)
+    dom_ms_step = dom_ms / max(args.steps, 1)
+    achieved = flops_step / (dom_ms_step * 1e-3) / 1e12 if dom_ms_step > 0 else 0.0
+    peak = PEAK_TFLOPS[dclass]
+    roofline = {
+        "bound": bound,
+        "kernel": dominant,
+        "achieved": round(achieved, 2),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": None,
+        "avg_launch_ms": round(dom_ms / max(dom_launches, 1), 5),
+        "launches_per_step": dom_launches // max(args.steps, 1),
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host ...", file=sys.stderr, flush=True)
+        chunks = [X[:, t:t + chunk] for t in range(0, n_tok, chunk)]
+        cpu = cpu_baseline(W, chunks, wl.bits, wl.group_size, wl.block_size, wl.damp, args.cpu_rows)
+
+    out = {
+        "metric": METRIC,
+        "value": round(ms_per_step, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16-mfma H / f64-mfma U / f32 sweep",
+        "data": "synthetic (seeded; see workloads/)",
+        "config": {"workload": wl.name, "d_out": d_out, "d_in": d_in, "n_tokens": n_tok, "bits": wl.bits,
+                   "group_size": wl.group_size, "block_size": wl.block_size, "damp": wl.damp,
+                   "w_dtype": spec.dtype, "x_dtype": xs.dtype, "token_chunk": chunk},
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "kernels_ms_per_step": {k: round(v, 4) for k, v in sorted(kernel_ms.items(), key=lambda kv: -kv[1])},
+        "kernel_launches_per_step": kernel_launches,
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

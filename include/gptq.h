@@ -1,0 +1,183 @@
+/*
+ * gptq.h -- C ABI of the GPTQ per-layer quantization path for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The path quantizes one linear layer W [d_out, d_in] against calibration
+ * inputs X [d_in, N] in four stages:
+ *   1. H = 2 X X^T                                (gptq_hessian_accumulate)
+ *   2. H <- H + lambda I, dead channels skipped   (gptq_prepare_hinv)
+ *   3. U upper with H^-1 = U^T U                  (gptq_prepare_hinv)
+ *   4. fixed-order, block-lazy quantize-and-compensate sweep
+ *                                                 (gptq_quantize_layer)
+ *
+ * Conventions shared by every entry point
+ *   - Tensor arguments are DEVICE pointers allocated and owned by the caller;
+ *     the library never allocates, frees or keeps caller memory.  Scratch
+ *     memory is a caller-provided device workspace whose minimum size the
+ *     *_workspace() queries return.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *     default stream) and returns; results are valid once the stream has
+ *     reached that point.  Calls on one stream run in order.
+ *   - Matrices are row-major with the leading dimension stated per argument.
+ *   - The return value reports argument and launch errors only
+ *     (gptq_status).  Argument checks happen before any HIP call, so an
+ *     invalid call touches no device state.  Numerical failure (a Hessian
+ *     that is not positive definite) is reported through the device word
+ *     `info` of gptq_prepare_hinv.
+ *   - A size of 0 (d_out, d_in or n_tokens) is a valid empty problem: the
+ *     call checks the other arguments and enqueues nothing.
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GPTQ_OK = 0,
+    GPTQ_EINVAL = 1,       /* invalid argument (null pointer, negative size, bits out of [2,8], ...) */
+    GPTQ_EUNSUPPORTED = 2, /* valid request these kernels do not handle (documented per call) */
+    GPTQ_EHIP = 3,         /* a HIP runtime call or kernel launch failed */
+    GPTQ_EWORKSPACE = 4    /* workspace pointer null or smaller than the *_workspace() size */
+} gptq_status;
+
+typedef enum {
+    GPTQ_F16 = 0, /* IEEE binary16 */
+    GPTQ_F32 = 1  /* IEEE binary32 */
+} gptq_dtype;
+
+/*
+ * Stage 1 -- Hessian accumulation.
+ * Operation (aicassindra.com "tm_gptq_math", section "Why it is
+ * second-order: the Hessian"; math4ai "GPTQ Hessian", damping sentence):
+ *     H += 2 * X * X^T
+ * over the n_tokens columns of X; calling it once per token chunk streams a
+ * long calibration set into one H (X X^T is a sum over tokens).  There is no
+ * 1/N normalisation.
+ *
+ *   H        [d_in, d_in] float32, leading dimension d_in.  Only the lower
+ *            triangle including the diagonal (row >= col) is read and
+ *            written; the strictly upper triangle is left untouched.  The
+ *            caller zeroes H before the first chunk.
+ *   X        [d_in, n_tokens] of x_dtype, row stride ldx elements (>= n_tokens):
+ *            row i holds channel i's value for each token, so a token chunk
+ *            of a larger X is the pointer X + t0 with the same ldx.
+ *   Products of float16 inputs are exact in float32; accumulation is float32
+ *   (MFMA), with one float32 add into H per call.
+ * Errors: GPTQ_EINVAL for H or X null (when the problem is not empty),
+ * d_in < 0, n_tokens < 0, ldx < n_tokens, unknown x_dtype.
+ */
+int gptq_hessian_accumulate(float* H, int64_t d_in, const void* X, int x_dtype,
+                            int64_t n_tokens, int64_t ldx, void* stream);
+
+/*
+ * Stages 2 and 3 -- damping, dead channels and the factor U.
+ * Operation (aicassindra "The Cholesky trick for the inverse Hessian";
+ * math4ai "GPTQ Hessian", damping sentence and column-sweep paragraph;
+ * mbrenndoerfer "GPTQ > Mathematical Details of the Update", Cholesky
+ * paragraph):
+ *     dead_i  = (H_ii == 0)                 channels the data never excited
+ *     lambda  = damp_frac * mean_i H_ii      over all d_in entries (dead = 0)
+ *     H_dd    = 1 for dead d, then H_ii += lambda for every i
+ *     U       upper triangular, U_ii > 0, with H^-1 = U^T U
+ * U is computed as the inverse of the reverse-order Cholesky factor
+ * (H = R R^T, R upper, U = R^-1), which equals the Cholesky factor of H^-1
+ * by uniqueness, in float64 (MFMA f64), and is rounded to float32 once.
+ *
+ *   H          [d_in, d_in] float32, lower triangle read (as written by
+ *              gptq_hessian_accumulate); not modified.
+ *   damp_frac  lambda as a fraction of the mean diagonal (0.01 = 1%); >= 0.
+ *   U          [d_in, d_in] float32 output, leading dimension d_in; the
+ *              strictly lower triangle is written as 0.
+ *   dead       [d_in] uint8 output (1 = dead channel), may be NULL.
+ *   info       device int32 output: 0 on success; k > 0 if the damped
+ *              Hessian is not positive definite, where k is the order of the
+ *              smallest trailing principal submatrix H[d_in-k:, d_in-k:]
+ *              found not positive definite (U is then undefined).
+ *   lambda_out device double output (lambda used), may be NULL.
+ *   workspace  device memory of at least gptq_prepare_hinv_workspace(d_in)
+ *              bytes, 256-byte aligned; clobbered.
+ * Errors: GPTQ_EINVAL (null H, U or info when d_in > 0; d_in < 0;
+ * damp_frac < 0 or not finite), GPTQ_EWORKSPACE.
+ */
+size_t gptq_prepare_hinv_workspace(int64_t d_in);
+int gptq_prepare_hinv(const float* H, int64_t d_in, float damp_frac, float* U, uint8_t* dead,
+                      int32_t* info, double* lambda_out, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * Stage 4 -- the quantize-and-compensate sweep.
+ * Operation (aicassindra "Greedy quantization with error compensation" and
+ * "GPTQ's speedups: fixed order and lazy batches"; math4ai "GPTQ Hessian",
+ * column-sweep paragraph): columns j = 0 .. d_in-1 in order, all rows in
+ * lockstep, in blocks of block_size columns.  For each column j:
+ *     v       = fl32(fl32(w_j / s) + z)           position on the grid
+ *     q       = clamp(rint(v), 0, 2^bits - 1)     the code (round half to even)
+ *     e       = (w_j - s (q - z)) / U_jj           scaled error
+ *     w_k    -= e U_jk   for later columns k of the same block (at once)
+ * and after each block [b0, b1):
+ *     W[:, b1:] -= E[:, b0:b1] U[b0:b1, b1:]      (lazy batched update)
+ * Grid: asymmetric min-max over [min(0, min w), max(0, max w)] (an all-zero
+ * range becomes [-1, 1]), s = fl32(fl32(mx - mn) / maxq),
+ * z = clamp(rint(fl32(-mn / s)), 0, maxq), all IEEE float32.
+ * group_size == 0: one grid per row from the input W.  group_size > 0: a new
+ * grid at every column j with j % group_size == 0, from the current
+ * (partially compensated) W[:, j : j + group_size].
+ * Dead channels: W[:, dead] is set to 0 after the per-row grid, so their code
+ * is z and they move nothing.
+ *
+ *   W           [d_out, d_in] of w_dtype, leading dimension d_in; not modified.
+ *   U           [d_in, d_in] float32 upper factor (gptq_prepare_hinv output).
+ *   dead        [d_in] uint8 or NULL (no dead channels).
+ *   bits        2..8.
+ *   group_size  0, or a multiple of 16 that divides d_in and either divides
+ *               block_size or is a multiple of it (GPTQ_EUNSUPPORTED
+ *               otherwise).
+ *   block_size  1..256 columns per lazy block.
+ *   codes       [d_out, d_in] uint8 output (one code per byte).
+ *   scales      [d_out, n_groups] float32 output, n_groups = 1 if group_size
+ *               == 0 else d_in / group_size.
+ *   zeros       [d_out, n_groups] int32 output.
+ *   err_row     [d_out] float32 output or NULL: sum over j of e_j^2 per row
+ *               (the layer loss in the metric of the damped H).
+ *   minmax      [d_out, n_groups, 2] float32 output or NULL: the range
+ *               (min(0, min w), max(0, max w)) each grid was built from.
+ *   workspace   at least gptq_quantize_layer_workspace(d_out, d_in,
+ *               block_size) bytes of device memory, 256-byte aligned.
+ * Errors: GPTQ_EINVAL (null required pointer, negative sizes, bits outside
+ * [2, 8], block_size outside [1, 256], negative group_size, group_size not
+ * dividing d_in, unknown w_dtype), GPTQ_EUNSUPPORTED (group_size not a
+ * multiple of 16, or neither dividing nor a multiple of block_size),
+ * GPTQ_EWORKSPACE.
+ */
+size_t gptq_quantize_layer_workspace(int64_t d_out, int64_t d_in, int64_t block_size);
+int gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in, const float* U,
+                        const uint8_t* dead, int bits, int64_t group_size, int64_t block_size,
+                        uint8_t* codes, float* scales, int32_t* zeros, float* err_row,
+                        float* minmax, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a gptq_status value (static string). */
+const char* gptq_status_string(int status);
+
+/*
+ * Kernel timing (measurement aid, not part of the method).
+ * gptq_timing_enable(id) makes every later launch of kernel `id` (see
+ * gptq_kernel_name) record a HIP event pair on its stream; id < 0 turns
+ * timing off.  gptq_timing_read waits for the recorded events, returns the
+ * summed duration in milliseconds and the launch count since the last read,
+ * and resets them.  Host-side state, not thread-safe.
+ */
+int gptq_kernel_count(void);
+const char* gptq_kernel_name(int id);
+int gptq_timing_enable(int id);
+int gptq_timing_read(double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_MI355X_H */

@@ -1,0 +1,173 @@
+"""ctypes binding of ``libgptq_mi355x.so`` (the C ABI in ``include/gptq.h``).
+
+Argument marshalling only: torch tensors are turned into device pointers and
+the current HIP stream; every computation happens in the library's kernels.
+There is no fallback: if the library is missing or fails to load, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgptq_mi355x.so")
+
+GPTQ_OK, GPTQ_EINVAL, GPTQ_EUNSUPPORTED, GPTQ_EHIP, GPTQ_EWORKSPACE = 0, 1, 2, 3, 4
+GPTQ_F16, GPTQ_F32 = 0, 1
+
+EXPORTS = (
+    "gptq_hessian_accumulate",
+    "gptq_prepare_hinv_workspace",
+    "gptq_prepare_hinv",
+    "gptq_quantize_layer_workspace",
+    "gptq_quantize_layer",
+    "gptq_status_string",
+    "gptq_kernel_count",
+    "gptq_kernel_name",
+    "gptq_timing_enable",
+    "gptq_timing_read",
+)
+
+
+class GptqError(RuntimeError):
+    def __init__(self, fn: str, rc: int, msg: str):
+        super().__init__(f"{fn} -> {rc} ({msg})")
+        self.rc = rc
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library once and declare every signature of ``include/gptq.h``."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is missing: build it with `python -m post_weight_quantization_04_amd.build`")
+    lib = ctypes.CDLL(path)
+    sig = {
+        "gptq_hessian_accumulate": (_i32, [_vp, _i64, _vp, _i32, _i64, _i64, _vp]),
+        "gptq_prepare_hinv_workspace": (_sz, [_i64]),
+        "gptq_prepare_hinv": (_i32, [_vp, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "gptq_quantize_layer_workspace": (_sz, [_i64, _i64, _i64]),
+        "gptq_quantize_layer": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
+                                       _vp, _sz, _vp]),
+        "gptq_status_string": (ctypes.c_char_p, [_i32]),
+        "gptq_kernel_count": (_i32, []),
+        "gptq_kernel_name": (ctypes.c_char_p, [_i32]),
+        "gptq_timing_enable": (_i32, [_i32]),
+        "gptq_timing_read": (_i32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(rc: int) -> str:
+    return load().gptq_status_string(rc).decode()
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != GPTQ_OK:
+        raise GptqError(fn, rc, status_string(rc))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("device tensor expected")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensor expected")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return GPTQ_F16
+    if t.dtype == torch.float32:
+        return GPTQ_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+# ---------------------------------------------------------------------------
+# the three entry points
+# ---------------------------------------------------------------------------
+def hessian_accumulate(H, X, stream=None) -> None:
+    """``H[lower] += 2 X X^T`` for ``X: [d_in, n]`` (a 2-D view with unit
+    column stride; row stride = ``X.stride(0)``)."""
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be 2-D with unit column stride")
+    d_in, n = X.shape
+    if H.shape != (d_in, d_in):
+        raise ValueError("H shape")
+    if not X.is_cuda:
+        raise ValueError("device tensor expected")
+    rc = load().gptq_hessian_accumulate(_ptr(H), d_in, X.data_ptr(), _dtype_code(X), n, X.stride(0),
+                                        _stream(stream))
+    _check("gptq_hessian_accumulate", rc)
+
+
+def prepare_hinv_workspace(d_in: int) -> int:
+    return int(load().gptq_prepare_hinv_workspace(d_in))
+
+
+def prepare_hinv(H, damp_frac: float, U, dead=None, info=None, lambda_out=None, workspace=None,
+                 stream=None) -> None:
+    d_in = H.shape[0]
+    rc = load().gptq_prepare_hinv(_ptr(H), d_in, float(damp_frac), _ptr(U), _ptr(dead), _ptr(info),
+                                  _ptr(lambda_out), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                  _stream(stream))
+    _check("gptq_prepare_hinv", rc)
+
+
+def quantize_layer_workspace(d_out: int, d_in: int, block_size: int) -> int:
+    return int(load().gptq_quantize_layer_workspace(d_out, d_in, block_size))
+
+
+def quantize_layer(W, U, dead, bits: int, group_size: int, block_size: int, codes, scales, zeros,
+                   err_row=None, minmax=None, workspace=None, stream=None) -> None:
+    d_out, d_in = W.shape
+    rc = load().gptq_quantize_layer(_ptr(W), _dtype_code(W), d_out, d_in, _ptr(U), _ptr(dead), int(bits),
+                                    int(group_size), int(block_size), _ptr(codes), _ptr(scales), _ptr(zeros),
+                                    _ptr(err_row), _ptr(minmax), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                    _stream(stream))
+    _check("gptq_quantize_layer", rc)
+
+
+# ---------------------------------------------------------------------------
+# kernel timing
+# ---------------------------------------------------------------------------
+def kernel_names() -> Tuple[str, ...]:
+    lib = load()
+    return tuple(lib.gptq_kernel_name(i).decode() for i in range(lib.gptq_kernel_count()))
+
+
+def timing_enable(name: Optional[str]) -> None:
+    idx = -1 if name is None else kernel_names().index(name)
+    _check("gptq_timing_enable", load().gptq_timing_enable(idx))
+
+
+def timing_read() -> Tuple[float, int]:
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check("gptq_timing_read", load().gptq_timing_read(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

@@ -1,0 +1,167 @@
+// C ABI entry points: argument validation (before any HIP call), workspace
+// checks, launch sequencing on the caller's stream, and kernel timing.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/gptq.h"
+#include "kernels.hpp"
+
+namespace gptq {
+
+// ---------------------------------------------------------------------------
+// Kernel timing: host-side list of event pairs for the selected kernel id.
+// ---------------------------------------------------------------------------
+namespace {
+const char* const kNames[K_COUNT] = {
+    "hessian_f16", "hessian_f32", "hinv_diag_stats", "hinv_load_reversed", "chol_diag", "chol_panel",
+    "chol_trail",  "hinv_store_u", "q_row_grid",     "q_convert",          "q_rdiag",   "q_group_grid",
+    "q_sweep",     "q_trail",
+};
+int g_timed = -1;
+struct EventPair {
+    hipEvent_t a, b;
+};
+std::vector<EventPair> g_pending;
+std::vector<EventPair> g_free;
+}  // namespace
+
+TimedLaunch::TimedLaunch(int id, hipStream_t s) : slot(-1), stream(s) {
+    if (id != g_timed) return;
+    EventPair ep;
+    if (!g_free.empty()) {
+        ep = g_free.back();
+        g_free.pop_back();
+    } else {
+        if (hipEventCreate(&ep.a) != hipSuccess) return;
+        if (hipEventCreate(&ep.b) != hipSuccess) {
+            (void)hipEventDestroy(ep.a);
+            return;
+        }
+    }
+    if (hipEventRecord(ep.a, s) != hipSuccess) {
+        g_free.push_back(ep);
+        return;
+    }
+    g_pending.push_back(ep);
+    slot = (int)g_pending.size() - 1;
+}
+
+TimedLaunch::~TimedLaunch() {
+    if (slot >= 0) (void)hipEventRecord(g_pending[slot].b, stream);
+}
+
+}  // namespace gptq
+
+using namespace gptq;
+
+namespace {
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline int hip_status(hipError_t e) { return e == hipSuccess ? GPTQ_OK : GPTQ_EHIP; }
+}  // namespace
+
+extern "C" {
+
+const char* gptq_status_string(int status) {
+    switch (status) {
+        case GPTQ_OK: return "GPTQ_OK";
+        case GPTQ_EINVAL: return "GPTQ_EINVAL: invalid argument";
+        case GPTQ_EUNSUPPORTED: return "GPTQ_EUNSUPPORTED: valid request not handled by these kernels";
+        case GPTQ_EHIP: return "GPTQ_EHIP: HIP runtime or launch failure";
+        case GPTQ_EWORKSPACE: return "GPTQ_EWORKSPACE: workspace missing or too small";
+        default: return "GPTQ: unknown status";
+    }
+}
+
+int gptq_kernel_count(void) { return K_COUNT; }
+
+const char* gptq_kernel_name(int id) { return (id >= 0 && id < K_COUNT) ? kNames[id] : nullptr; }
+
+int gptq_timing_enable(int id) {
+    if (id >= K_COUNT) return GPTQ_EINVAL;
+    g_timed = id < 0 ? -1 : id;
+    return GPTQ_OK;
+}
+
+int gptq_timing_read(double* total_ms, int64_t* launches) {
+    if (!total_ms || !launches) return GPTQ_EINVAL;
+    double tot = 0.0;
+    int64_t cnt = 0;
+    int rc = GPTQ_OK;
+    for (auto& ep : g_pending) {
+        if (hipEventSynchronize(ep.b) != hipSuccess) {
+            rc = GPTQ_EHIP;
+            continue;
+        }
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, ep.a, ep.b) != hipSuccess) {
+            rc = GPTQ_EHIP;
+            continue;
+        }
+        tot += ms;
+        ++cnt;
+    }
+    for (auto& ep : g_pending) g_free.push_back(ep);
+    g_pending.clear();
+    *total_ms = tot;
+    *launches = cnt;
+    return rc;
+}
+
+int gptq_hessian_accumulate(float* H, int64_t d_in, const void* X, int x_dtype, int64_t n_tokens, int64_t ldx,
+                            void* stream) {
+    if (d_in < 0 || n_tokens < 0 || ldx < n_tokens) return GPTQ_EINVAL;
+    if (x_dtype != GPTQ_F16 && x_dtype != GPTQ_F32) return GPTQ_EINVAL;
+    if (d_in == 0 || n_tokens == 0) return GPTQ_OK;
+    if (!H || !X) return GPTQ_EINVAL;
+    if (d_in > (int64_t)1 << 20) return GPTQ_EUNSUPPORTED;
+    return hip_status(launch_hessian(H, d_in, X, x_dtype == GPTQ_F16, n_tokens, ldx, as_stream(stream)));
+}
+
+size_t gptq_prepare_hinv_workspace(int64_t d_in) { return d_in > 0 ? hinv_workspace_bytes(d_in) : 0; }
+
+int gptq_prepare_hinv(const float* H, int64_t d_in, float damp_frac, float* U, uint8_t* dead, int32_t* info,
+                      double* lambda_out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (d_in < 0 || !(damp_frac >= 0.0f) || !isfinite(damp_frac)) return GPTQ_EINVAL;
+    if (d_in == 0) return GPTQ_OK;
+    if (!H || !U || !info) return GPTQ_EINVAL;
+    if (d_in > (int64_t)1 << 17) return GPTQ_EUNSUPPORTED;
+    if (!workspace || workspace_bytes < hinv_workspace_bytes(d_in) ||
+        reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return GPTQ_EWORKSPACE;
+    return hip_status(
+        launch_prepare_hinv(H, d_in, (double)damp_frac, U, dead, info, lambda_out, workspace, as_stream(stream)));
+}
+
+size_t gptq_quantize_layer_workspace(int64_t d_out, int64_t d_in, int64_t block_size) {
+    if (d_out <= 0 || d_in <= 0 || block_size <= 0) return 0;
+    return quant_workspace_bytes(d_out, d_in, block_size);
+}
+
+int gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in, const float* U,
+                        const uint8_t* dead, int bits, int64_t group_size, int64_t block_size, uint8_t* codes,
+                        float* scales, int32_t* zeros, float* err_row, float* minmax, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    if (d_out < 0 || d_in < 0) return GPTQ_EINVAL;
+    if (w_dtype != GPTQ_F16 && w_dtype != GPTQ_F32) return GPTQ_EINVAL;
+    if (bits < 2 || bits > 8) return GPTQ_EINVAL;
+    if (block_size < 1 || block_size > 256) return GPTQ_EINVAL;
+    if (group_size < 0) return GPTQ_EINVAL;
+    if (group_size > 0 && d_in > 0 && d_in % group_size != 0) return GPTQ_EINVAL;
+    if (group_size > 0) {
+        if (group_size % 16 != 0) return GPTQ_EUNSUPPORTED;
+        if (block_size % group_size != 0 && group_size % block_size != 0) return GPTQ_EUNSUPPORTED;
+    }
+    if (d_out == 0 || d_in == 0) return GPTQ_OK;
+    if (!W || !U || !codes || !scales || !zeros) return GPTQ_EINVAL;
+    if (d_out > ((int64_t)1 << 24) || d_in > ((int64_t)1 << 20)) return GPTQ_EUNSUPPORTED;
+    if (!workspace || workspace_bytes < quant_workspace_bytes(d_out, d_in, block_size) ||
+        reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return GPTQ_EWORKSPACE;
+    return hip_status(launch_quantize(W, w_dtype == GPTQ_F16, d_out, d_in, U, dead, bits, group_size, block_size,
+                                      codes, scales, zeros, err_row, minmax, workspace, as_stream(stream)));
+}
+
+}  // extern "C"

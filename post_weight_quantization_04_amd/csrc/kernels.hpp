@@ -1,0 +1,55 @@
+// Host-side launchers of the gfx950 kernels (one translation unit per stage)
+// and the kernel-timing hook shared by them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gptq {
+
+enum KernelId {
+    K_HESS_F16 = 0,
+    K_HESS_F32,
+    K_HINV_DIAGSUM,
+    K_HINV_LOAD,
+    K_CHOL_DIAG,
+    K_CHOL_PANEL,
+    K_CHOL_TRAIL,
+    K_HINV_STORE,
+    K_Q_ROWGRID,
+    K_Q_CONVERT,
+    K_Q_RDIAG,
+    K_Q_GROUPGRID,
+    K_Q_SWEEP,
+    K_Q_TRAIL,
+    K_COUNT
+};
+
+// Records a HIP event pair around the launches made while it is alive when
+// timing is enabled for `id` (see gptq_timing_enable); a no-op otherwise.
+struct TimedLaunch {
+    TimedLaunch(int id, hipStream_t s);
+    ~TimedLaunch();
+    int slot;
+    hipStream_t stream;
+};
+
+// ---- stage 1 ---------------------------------------------------------------
+hipError_t launch_hessian(float* H, int64_t n, const void* X, int x_is_f16, int64_t ntok,
+                          int64_t ldx, hipStream_t s);
+
+// ---- stages 2 + 3 ----------------------------------------------------------
+constexpr int kCholNB = 64;  // panel width of the blocked factorization
+size_t hinv_workspace_bytes(int64_t n);
+hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, float* U, uint8_t* dead,
+                               int32_t* info, double* lambda_out, void* ws, hipStream_t s);
+
+// ---- stage 4 ---------------------------------------------------------------
+size_t quant_workspace_bytes(int64_t d_out, int64_t d_in, int64_t block);
+hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d_in, const float* U,
+                           const uint8_t* dead, int bits, int64_t group, int64_t block,
+                           uint8_t* codes, float* scales, int32_t* zeros, float* err_row,
+                           float* minmax, void* ws, hipStream_t s);
+
+}  // namespace gptq

@@ -1,0 +1,449 @@
+// Stage 4: the fixed-order, block-lazy quantize-and-compensate sweep
+// (aicassindra.com "tm_gptq_math", "Greedy quantization with error
+// compensation" and "GPTQ's speedups: fixed order and lazy batches"; math4ai
+// "GPTQ Hessian", column-sweep paragraph).
+//
+// Per lazy block [b0, b1):
+//   sweep_kernel   one workgroup per 64 rows (lane = row); wave q owns the 16
+//                  block columns b0+16q.. in registers.  In phase p wave p
+//                  rounds its columns one by one and compensates the rest of
+//                  its sub-block at once; its scaled errors go to LDS and the
+//                  waves owning later columns fold them in at the start of
+//                  phase p+1 (the same OBS updates, grouped by sub-block).
+//                  U entries are uniform across the wave and come in through
+//                  scalar loads.
+//   trail_kernel   W[:, b1:] -= E U[b0:b1, b1:], 128x128 tiles on MFMA
+//                  32x32x2 f32 with fp32 accumulation.
+#include <math.h>
+
+#include <algorithm>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace gptq {
+
+namespace {
+
+constexpr int kSub = 16;      // columns per wave in the sweep
+constexpr int kRowsPerWg = 64;
+constexpr int kMaxBlock = 256;
+constexpr int kEld = 65;      // padded LDS row of the scaled-error exchange
+
+__host__ __device__ inline int64_t rup(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+struct QuantWs {
+    float* Wk;     // [d_out, d_in] working weights
+    float* E;      // [d_out, block] scaled errors of the current block
+    float* rdiag;  // [d_in] 1 / U_jj
+};
+
+QuantWs carve(void* ws, int64_t d_out, int64_t d_in, int64_t block) {
+    char* p = static_cast<char*>(ws);
+    QuantWs w;
+    w.Wk = reinterpret_cast<float*>(p);
+    p += rup(d_out * d_in * 4, 256);
+    w.E = reinterpret_cast<float*>(p);
+    p += rup(d_out * block * 4, 256);
+    w.rdiag = reinterpret_cast<float*>(p);
+    return w;
+}
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T v) {
+    return (float)v;
+}
+
+// ---------------------------------------------------------------------------
+// Per-row grid from the input W (group_size == 0): one wave per row,
+// min/max by butterfly shuffles.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void row_grid_kernel(const T* __restrict__ W, int64_t d_out, int64_t d_in,
+                                                       float maxq, float* __restrict__ scales,
+                                                       int32_t* __restrict__ zeros, float* __restrict__ minmax) {
+    const int64_t R = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (R >= d_out) return;
+    float lo = INFINITY, hi = -INFINITY;
+    const T* row = W + R * d_in;
+    for (int64_t c = lane; c < d_in; c += 64) {
+        float x = to_f32(row[c]);
+        lo = fminf(lo, x);
+        hi = fmaxf(hi, x);
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if (lane == 0) {
+        lo = fminf(lo, 0.0f);
+        hi = fmaxf(hi, 0.0f);
+        Grid g = make_grid(lo, hi, maxq);
+        scales[R] = g.s;
+        zeros[R] = (int32_t)g.z;
+        if (minmax) {
+            minmax[2 * R] = lo;
+            minmax[2 * R + 1] = hi;
+        }
+    }
+}
+
+// Group grid from the current working weights W[:, c0 : c0+g) (g > block).
+__global__ __launch_bounds__(256) void group_grid_kernel(const float* __restrict__ Wk, int64_t d_out, int64_t d_in,
+                                                         int64_t c0, int64_t g, int64_t gi, int64_t ng, float maxq,
+                                                         float* __restrict__ scales, int32_t* __restrict__ zeros,
+                                                         float* __restrict__ minmax) {
+    const int64_t R = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (R >= d_out) return;
+    float lo = INFINITY, hi = -INFINITY;
+    const float* row = Wk + R * d_in + c0;
+    for (int64_t c = lane; c < g; c += 64) {
+        float x = row[c];
+        lo = fminf(lo, x);
+        hi = fmaxf(hi, x);
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if (lane == 0) {
+        lo = fminf(lo, 0.0f);
+        hi = fmaxf(hi, 0.0f);
+        Grid gr = make_grid(lo, hi, maxq);
+        scales[R * ng + gi] = gr.s;
+        zeros[R * ng + gi] = (int32_t)gr.z;
+        if (minmax) {
+            minmax[2 * (R * ng + gi)] = lo;
+            minmax[2 * (R * ng + gi) + 1] = hi;
+        }
+    }
+}
+
+// Working copy in fp32 (exact for f16 inputs, subnormals included); dead
+// columns are zeroed.
+template <typename T>
+__global__ __launch_bounds__(256) void convert_kernel(const T* __restrict__ W, float* __restrict__ Wk, int64_t total,
+                                                      int64_t d_in, const uint8_t* __restrict__ dead) {
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+        float x = to_f32(W[e]);
+        if (dead && dead[e % d_in]) x = 0.0f;
+        Wk[e] = x;
+    }
+}
+
+__global__ __launch_bounds__(256) void rdiag_kernel(const float* __restrict__ U, int64_t n, float* __restrict__ rdiag) {
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j < n) rdiag[j] = 1.0f / U[j * n + j];
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j < n) p[j] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// In-block sweep.  Dynamic LDS: Ebuf [nw][16][kEld] f32, codes [64][nw*16] u8,
+// red [nw][64][2] f32, errs [nw][64] f32.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void sweep_kernel(const float* __restrict__ Wk, int64_t d_out, int64_t d_in,
+                                                     const float* __restrict__ U, const float* __restrict__ rdiag,
+                                                     int64_t b0, int64_t b1, int bits, int64_t group, int64_t ng,
+                                                     float* __restrict__ scales, int32_t* __restrict__ zeros,
+                                                     float* __restrict__ minmax, uint8_t* __restrict__ codes,
+                                                     float* __restrict__ E, int64_t ldE, float* __restrict__ err_row) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int bw = (int)(b1 - b0);
+    const int nw = (bw + kSub - 1) / kSub;
+    float* Ebuf = reinterpret_cast<float*>(smem);                       // nw*16*kEld
+    float* red = Ebuf + nw * kSub * kEld;                                 // nw*64*2
+    float* errs = red + nw * 64 * 2;                                      // nw*64
+    uint8_t* cbuf = reinterpret_cast<uint8_t*>(errs + nw * 64);           // 64 * nw*16
+
+    const int lane = threadIdx.x & 63;
+    const int q = wave_id();
+    const int64_t R = (int64_t)blockIdx.x * kRowsPerWg + lane;
+    const bool rowok = R < d_out;
+    const int cq = min(kSub, bw - kSub * q);  // >= 1
+    const int64_t c0q = b0 + kSub * q;
+    const float maxq = (float)((1 << bits) - 1);
+
+    float wv[kSub];
+#pragma unroll
+    for (int t = 0; t < kSub; ++t) wv[t] = (rowok && t < cq) ? Wk[R * d_in + c0q + t] : 0.0f;
+
+    float s = 1.0f, zf = 0.0f;
+    if (group == 0) {
+        if (rowok) {
+            s = scales[R];
+            zf = (float)zeros[R];
+        }
+    } else if (group > bw) {
+        // group wider than the block (a multiple of it): grid prepared at the
+        // group start by group_grid_kernel
+        const int64_t gi = b0 / group;
+        if (rowok) {
+            s = scales[R * ng + gi];
+            zf = (float)zeros[R * ng + gi];
+        }
+    }
+    float errsq = 0.0f;
+
+    for (int p = 0; p < nw; ++p) {
+        if (p > 0 && q >= p) {
+            // fold in the scaled errors of sub-block p-1 (16 full columns)
+            const float* ebp = Ebuf + (p - 1) * kSub * kEld;
+#pragma unroll
+            for (int t = 0; t < kSub; ++t) {
+                const float e = ebp[t * kEld + lane];
+                const float* urow = U + (b0 + kSub * (p - 1) + t) * d_in + c0q;
+                if (cq == kSub) {
+#pragma unroll
+                    for (int c = 0; c < kSub; ++c) wv[c] -= e * urow[c];
+                } else {
+#pragma unroll
+                    for (int c = 0; c < kSub; ++c)
+                        if (c < cq) wv[c] -= e * urow[c];
+                }
+            }
+        }
+        if (group > 0 && group <= bw && ((int64_t)kSub * p) % group == 0) {
+            // group start at column b0 + 16p: grid from the current weights
+            const int gwaves = (int)(group / kSub);
+            if (q >= p && q < p + gwaves) {
+                float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+                for (int c = 0; c < kSub; ++c)
+                    if (c < cq) {
+                        lo = fminf(lo, wv[c]);
+                        hi = fmaxf(hi, wv[c]);
+                    }
+                red[(q * 64 + lane) * 2] = lo;
+                red[(q * 64 + lane) * 2 + 1] = hi;
+            }
+            __syncthreads();
+            float lo = INFINITY, hi = -INFINITY;
+            for (int qq = p; qq < p + gwaves; ++qq) {
+                lo = fminf(lo, red[(qq * 64 + lane) * 2]);
+                hi = fmaxf(hi, red[(qq * 64 + lane) * 2 + 1]);
+            }
+            lo = fminf(lo, 0.0f);
+            hi = fmaxf(hi, 0.0f);
+            Grid g = make_grid(lo, hi, maxq);
+            s = g.s;
+            zf = g.z;
+            if (q == p && rowok) {
+                const int64_t gi = (b0 + kSub * p) / group;
+                scales[R * ng + gi] = g.s;
+                zeros[R * ng + gi] = (int32_t)g.z;
+                if (minmax) {
+                    minmax[2 * (R * ng + gi)] = lo;
+                    minmax[2 * (R * ng + gi) + 1] = hi;
+                }
+            }
+        }
+        if (q == p) {
+            float* ebq = Ebuf + p * kSub * kEld;
+#pragma unroll
+            for (int t = 0; t < kSub; ++t) {
+                if (t < cq) {
+                    const int64_t j = c0q + t;
+                    const float w = wv[t];
+                    const float x = w / s;
+                    const float v = x + zf;
+                    float qf = __builtin_rintf(v);
+                    qf = fminf(fmaxf(qf, 0.0f), maxq);
+                    const float what = (qf - zf) * s;
+                    const float e = (w - what) * rdiag[j];
+                    cbuf[lane * (nw * kSub) + kSub * p + t] = (uint8_t)qf;
+                    ebq[t * kEld + lane] = e;
+                    errsq += e * e;
+                    const float* urow = U + j * d_in + c0q;
+#pragma unroll
+                    for (int t2 = t + 1; t2 < kSub; ++t2)
+                        if (t2 < cq) wv[t2] -= e * urow[t2];
+                }
+            }
+        }
+        __syncthreads();
+    }
+    errs[q * 64 + lane] = errsq;
+    __syncthreads();
+
+    // write codes and scaled errors of the block, row-contiguous
+    const int nthreads = blockDim.x;
+    const int64_t rows_here = min((int64_t)kRowsPerWg, d_out - (int64_t)blockIdx.x * kRowsPerWg);
+    for (int e = threadIdx.x; e < rows_here * bw; e += nthreads) {
+        const int r = e / bw, c = e % bw;
+        const int64_t RR = (int64_t)blockIdx.x * kRowsPerWg + r;
+        codes[RR * d_in + b0 + c] = cbuf[r * (nw * kSub) + c];
+        E[RR * ldE + c] = Ebuf[(c / kSub) * kSub * kEld + (c % kSub) * kEld + r];
+    }
+    if (err_row && q == 0 && rowok) {
+        float acc = err_row[R];
+        for (int qq = 0; qq < nw; ++qq) acc += errs[qq * 64 + lane];
+        err_row[R] = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Lazy trailing update W[:, b1:] -= E[:, :K] U[b0:b1, b1:], K = b1 - b0.
+// 128x128 tile per workgroup; 4 waves in 2x2, each 64x64 = 2x2 MFMA 32x32.
+// ---------------------------------------------------------------------------
+constexpr int kTT = 128;
+constexpr int kTK = 32;
+constexpr int kTld = kTT + 4;
+
+template <bool kVec>
+__global__ __launch_bounds__(256) void trail_kernel(float* __restrict__ Wk, int64_t d_out, int64_t d_in,
+                                                    const float* __restrict__ E, int64_t ldE,
+                                                    const float* __restrict__ U, int64_t b0, int64_t b1) {
+    __shared__ float As[kTK][kTld];
+    __shared__ float Bs[kTK][kTld];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wi = w >> 1, wj = w & 1;
+    const int64_t r0 = (int64_t)blockIdx.y * kTT;
+    const int64_t c0 = b1 + (int64_t)blockIdx.x * kTT;
+    const int K = (int)(b1 - b0);
+
+    float16v acc[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) acc[m][q] = (float16v){};
+
+    for (int kc = 0; kc < K; kc += kTK) {
+        {  // E chunk, transposed into As[k][row]
+            const int row = tid >> 1, kh = (tid & 1) * 16;
+            const int64_t R = r0 + row;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int k = kc + kh + e;
+                As[kh + e][row] = (R < d_out && k < K) ? E[R * ldE + k] : 0.0f;
+            }
+        }
+        {  // U chunk, rows b0+kc.., direct
+            const int kk = tid >> 3, cc = (tid & 7) * 16;
+            const int k = kc + kk;
+            const int64_t col = c0 + cc;
+            const float* src = U + (b0 + k) * d_in + col;
+            if (kVec && k < K && col + 16 <= d_in) {
+#pragma unroll
+                for (int e = 0; e < 16; e += 4) *reinterpret_cast<float4v*>(&Bs[kk][cc + e]) = *reinterpret_cast<const float4v*>(src + e);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) Bs[kk][cc + e] = (k < K && col + e < d_in) ? src[e] : 0.0f;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < kTK; ks += 2) {
+            float a[2], b[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) a[m] = As[ks + (lane >> 5)][wi * 64 + 32 * m + (lane & 31)];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) b[q] = Bs[ks + (lane >> 5)][wj * 64 + 32 * q + (lane & 31)];
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) acc[m][q] = mfma32x32x2_f32(a[m], b[q], acc[m][q]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = r0 + wi * 64 + 32 * m + acc32_row(v, lane);
+                const int64_t col = c0 + wj * 64 + 32 * q + (lane & 31);
+                if (row < d_out && col < d_in) {
+                    float* p = Wk + row * d_in + col;
+                    *p = *p - acc[m][q][v];
+                }
+            }
+}
+
+}  // namespace
+
+size_t quant_workspace_bytes(int64_t d_out, int64_t d_in, int64_t block) {
+    return (size_t)(rup(d_out * d_in * 4, 256) + rup(d_out * block * 4, 256) + rup(d_in * 4, 256));
+}
+
+hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d_in, const float* U,
+                           const uint8_t* dead, int bits, int64_t group, int64_t block, uint8_t* codes,
+                           float* scales, int32_t* zeros, float* err_row, float* minmax, void* ws, hipStream_t s) {
+    if (d_out == 0 || d_in == 0) return hipSuccess;
+    QuantWs w = carve(ws, d_out, d_in, block);
+    const int64_t ng = group ? d_in / group : 1;
+    const float maxq = (float)((1 << bits) - 1);
+    const unsigned rows4 = (unsigned)((d_out + 3) / 4);
+    if (group == 0) {
+        TimedLaunch t(K_Q_ROWGRID, s);
+        if (w_is_f16)
+            hipLaunchKernelGGL(row_grid_kernel<half_t>, dim3(rows4), dim3(256), 0, s, static_cast<const half_t*>(W),
+                               d_out, d_in, maxq, scales, zeros, minmax);
+        else
+            hipLaunchKernelGGL(row_grid_kernel<float>, dim3(rows4), dim3(256), 0, s, static_cast<const float*>(W),
+                               d_out, d_in, maxq, scales, zeros, minmax);
+    }
+    {
+        TimedLaunch t(K_Q_CONVERT, s);
+        const int64_t total = d_out * d_in;
+        const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
+        if (w_is_f16)
+            hipLaunchKernelGGL(convert_kernel<half_t>, dim3(blocks), dim3(256), 0, s, static_cast<const half_t*>(W),
+                               w.Wk, total, d_in, dead);
+        else
+            hipLaunchKernelGGL(convert_kernel<float>, dim3(blocks), dim3(256), 0, s, static_cast<const float*>(W),
+                               w.Wk, total, d_in, dead);
+    }
+    {
+        TimedLaunch t(K_Q_RDIAG, s);
+        hipLaunchKernelGGL(rdiag_kernel, dim3((unsigned)((d_in + 255) / 256)), dim3(256), 0, s, U, d_in, w.rdiag);
+    }
+    if (err_row)
+        hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((d_out + 255) / 256)), dim3(256), 0, s, err_row, d_out);
+    const bool vec = (reinterpret_cast<uintptr_t>(U) % 16 == 0) && (d_in % 4 == 0) && (block % 4 == 0);
+    {
+        // the widest block (256 columns) needs 93 KiB of LDS per workgroup
+        const int nwmax = (int)((std::min(block, d_in) + kSub - 1) / kSub);
+        const size_t ldsmax = (size_t)nwmax * kSub * kEld * 4 + (size_t)nwmax * 64 * 2 * 4 + (size_t)nwmax * 64 * 4 +
+                              (size_t)64 * nwmax * kSub;
+        if (ldsmax > 64 * 1024) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_kernel),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsmax);
+            if (e != hipSuccess) return e;
+        }
+    }
+    const unsigned row_tiles = (unsigned)((d_out + kRowsPerWg - 1) / kRowsPerWg);
+    for (int64_t b0 = 0; b0 < d_in; b0 += block) {
+        const int64_t b1 = std::min(b0 + block, d_in);
+        const int bw = (int)(b1 - b0);
+        const int nw = (bw + kSub - 1) / kSub;
+        if (group > block && b0 % group == 0) {
+            TimedLaunch t(K_Q_GROUPGRID, s);
+            hipLaunchKernelGGL(group_grid_kernel, dim3(rows4), dim3(256), 0, s, (const float*)w.Wk, d_out, d_in, b0,
+                               group, b0 / group, ng, maxq, scales, zeros, minmax);
+        }
+        {
+            TimedLaunch t(K_Q_SWEEP, s);
+            const size_t lds = (size_t)nw * kSub * kEld * 4 + (size_t)nw * 64 * 2 * 4 + (size_t)nw * 64 * 4 +
+                               (size_t)64 * nw * kSub;
+            hipLaunchKernelGGL(sweep_kernel, dim3(row_tiles), dim3(64 * nw), lds, s, (const float*)w.Wk, d_out, d_in, U,
+                               (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes, w.E,
+                               block, err_row);
+        }
+        if (b1 < d_in) {
+            TimedLaunch t(K_Q_TRAIL, s);
+            dim3 grid((unsigned)((d_in - b1 + kTT - 1) / kTT), (unsigned)((d_out + kTT - 1) / kTT));
+            if (vec)
+                hipLaunchKernelGGL(trail_kernel<true>, grid, dim3(256), 0, s, w.Wk, d_out, d_in, (const float*)w.E,
+                                   block, U, b0, b1);
+            else
+                hipLaunchKernelGGL(trail_kernel<false>, grid, dim3(256), 0, s, w.Wk, d_out, d_in, (const float*)w.E,
+                                   block, U, b0, b1);
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gptq

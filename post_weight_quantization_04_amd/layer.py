@@ -1,0 +1,101 @@
+"""Per-layer driver over the three C-ABI entry points.
+
+Allocates device buffers with torch (memory and streams only) and enqueues
+the library calls; it performs no arithmetic of its own.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Iterable, Optional
+
+from . import _lib
+
+
+@dataclasses.dataclass
+class Factor:
+    U: "torch.Tensor"        # [d_in, d_in] float32, upper
+    dead: "torch.Tensor"     # [d_in] uint8
+    info: "torch.Tensor"     # [1] int32 (0 = ok)
+    lam: "torch.Tensor"      # [1] float64
+
+
+@dataclasses.dataclass
+class Quantized:
+    codes: "torch.Tensor"    # [d_out, d_in] uint8
+    scales: "torch.Tensor"   # [d_out, n_groups] float32
+    zeros: "torch.Tensor"    # [d_out, n_groups] int32
+    err_row: "torch.Tensor"  # [d_out] float32
+    minmax: "torch.Tensor"   # [d_out, n_groups, 2] float32
+
+
+class Workspace:
+    """Grow-only device scratch buffer shared by the calls of one stream."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int):
+        import torch
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+def hessian(X, chunk: Optional[int] = None, H=None, stream=None):
+    """``H = 2 X X^T`` (lower triangle) from a device ``X [d_in, N]``,
+    streamed in token chunks of ``chunk`` (whole X if None)."""
+    import torch
+    d_in, n = X.shape
+    if H is None:
+        H = torch.zeros((d_in, d_in), dtype=torch.float32, device=X.device)
+    else:
+        H.zero_()
+    step = chunk or max(n, 1)
+    for t0 in range(0, n, step):
+        _lib.hessian_accumulate(H, X[:, t0:t0 + step], stream=stream)
+    return H
+
+
+def hessian_chunks(chunks: Iterable, d_in: int, device="cuda", H=None, stream=None):
+    import torch
+    if H is None:
+        H = torch.zeros((d_in, d_in), dtype=torch.float32, device=device)
+    for xc in chunks:
+        _lib.hessian_accumulate(H, xc, stream=stream)
+    return H
+
+
+def prepare(H, damp_frac: float = 0.01, ws: Optional[Workspace] = None, out: Optional[Factor] = None,
+            stream=None) -> Factor:
+    import torch
+    d_in = H.shape[0]
+    dev = H.device
+    if out is None:
+        out = Factor(torch.empty((d_in, d_in), dtype=torch.float32, device=dev),
+                     torch.empty((d_in,), dtype=torch.uint8, device=dev),
+                     torch.empty((1,), dtype=torch.int32, device=dev),
+                     torch.empty((1,), dtype=torch.float64, device=dev))
+    ws = ws or Workspace(dev)
+    buf = ws.get(_lib.prepare_hinv_workspace(d_in))
+    _lib.prepare_hinv(H, damp_frac, out.U, out.dead, out.info, out.lam, buf, stream=stream)
+    return out
+
+
+def quantize(W, factor: Factor, bits: int, group_size: int, block_size: int, ws: Optional[Workspace] = None,
+             out: Optional[Quantized] = None, use_dead: bool = True, stream=None) -> Quantized:
+    import torch
+    d_out, d_in = W.shape
+    dev = W.device
+    ng = 1 if group_size == 0 else d_in // group_size
+    if out is None:
+        out = Quantized(torch.empty((d_out, d_in), dtype=torch.uint8, device=dev),
+                        torch.empty((d_out, ng), dtype=torch.float32, device=dev),
+                        torch.empty((d_out, ng), dtype=torch.int32, device=dev),
+                        torch.empty((d_out,), dtype=torch.float32, device=dev),
+                        torch.empty((d_out, ng, 2), dtype=torch.float32, device=dev))
+    ws = ws or Workspace(dev)
+    buf = ws.get(_lib.quantize_layer_workspace(d_out, d_in, block_size))
+    _lib.quantize_layer(W, factor.U, factor.dead if use_dead else None, bits, group_size, block_size, out.codes,
+                        out.scales, out.zeros, out.err_row, out.minmax, buf, stream=stream)
+    return out
