@@ -105,7 +105,7 @@ int gptq_hessian_accumulate(float* H, int64_t d_in, const void* X, int x_dtype,
  * damp_frac < 0 or not finite), GPTQ_EWORKSPACE.
  */
 size_t gptq_prepare_hinv_workspace(int64_t d_in);
-int gptq_prepare_hinv(const float* H, int64_t d_in, float damp_frac, float* U, uint8_t* dead,
+int gptq_prepare_hinv(const float* H, int64_t d_in, double damp_frac, float* U, uint8_t* dead,
                       int32_t* info, double* lambda_out, void* workspace, size_t workspace_bytes,
                       void* stream);
 

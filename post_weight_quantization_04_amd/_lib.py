@@ -54,7 +54,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "gptq_hessian_accumulate": (_i32, [_vp, _i64, _vp, _i32, _i64, _i64, _vp]),
         "gptq_prepare_hinv_workspace": (_sz, [_i64]),
-        "gptq_prepare_hinv": (_i32, [_vp, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "gptq_prepare_hinv": (_i32, [_vp, _i64, ctypes.c_double, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
         "gptq_quantize_layer_workspace": (_sz, [_i64, _i64, _i64]),
         "gptq_quantize_layer": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _sz, _vp]),

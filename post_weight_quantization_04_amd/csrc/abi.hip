@@ -122,9 +122,9 @@ int gptq_hessian_accumulate(float* H, int64_t d_in, const void* X, int x_dtype, 
 
 size_t gptq_prepare_hinv_workspace(int64_t d_in) { return d_in > 0 ? hinv_workspace_bytes(d_in) : 0; }
 
-int gptq_prepare_hinv(const float* H, int64_t d_in, float damp_frac, float* U, uint8_t* dead, int32_t* info,
+int gptq_prepare_hinv(const float* H, int64_t d_in, double damp_frac, float* U, uint8_t* dead, int32_t* info,
                       double* lambda_out, void* workspace, size_t workspace_bytes, void* stream) {
-    if (d_in < 0 || !(damp_frac >= 0.0f) || !isfinite(damp_frac)) return GPTQ_EINVAL;
+    if (d_in < 0 || !(damp_frac >= 0.0) || !isfinite(damp_frac)) return GPTQ_EINVAL;
     if (d_in == 0) return GPTQ_OK;
     if (!H || !U || !info) return GPTQ_EINVAL;
     if (d_in > (int64_t)1 << 17) return GPTQ_EUNSUPPORTED;
@@ -132,7 +132,7 @@ int gptq_prepare_hinv(const float* H, int64_t d_in, float damp_frac, float* U, u
         reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
         return GPTQ_EWORKSPACE;
     return hip_status(
-        launch_prepare_hinv(H, d_in, (double)damp_frac, U, dead, info, lambda_out, workspace, as_stream(stream)));
+        launch_prepare_hinv(H, d_in, damp_frac, U, dead, info, lambda_out, workspace, as_stream(stream)));
 }
 
 size_t gptq_quantize_layer_workspace(int64_t d_out, int64_t d_in, int64_t block_size) {

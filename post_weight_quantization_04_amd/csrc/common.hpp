@@ -21,7 +21,8 @@ constexpr int kWave = 64;
 //     lane j + 32*kg, with kg = l / 32 selecting the k group; result lane l
 //     holds C[8*(v/4) + 4*(l/32) + (v%4)][l % 32] for v = 0..15.
 //   16x16x4 f64: A[i][k] from lane i + 16*k, B[k][j] from lane j + 16*k;
-//     result lane l holds C[4*(l/16) + v][l % 16] for v = 0..3.
+//     result lane l holds C[4*v + l/16][l % 16] for v = 0..3 (measured on
+//     gfx950; rows interleave across the four lane groups).
 // The k order inside a group is the hardware's; a product A B^T of two
 // operands loaded with the same lane->k map is independent of it.
 // ---------------------------------------------------------------------------

@@ -288,7 +288,7 @@ __device__ __forceinline__ void tile_store_f64(double* __restrict__ C, int64_t l
         for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int row = wi * 32 + 16 * m + 4 * (lane >> 4) + v;
+                const int row = wi * 32 + 16 * m + 4 * v + (lane >> 4);
                 const int col = wj * 32 + 16 * q + (lane & 15);
                 double* p = C + (int64_t)row * ldc + col;
                 if (kMode == 0) *p = acc[m][q][v];
