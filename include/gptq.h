@@ -137,7 +137,8 @@ int gptq_prepare_hinv(const float* H, int64_t d_in, double damp_frac, float* U, 
  *   group_size  0, or a multiple of 16 that divides d_in and either divides
  *               block_size or is a multiple of it (GPTQ_EUNSUPPORTED
  *               otherwise).
- *   block_size  1..256 columns per lazy block.
+ *   block_size  1..128 columns per lazy block (the U block of the current
+ *               lazy block is staged in LDS).
  *   codes       [d_out, d_in] uint8 output (one code per byte).
  *   scales      [d_out, n_groups] float32 output, n_groups = 1 if group_size
  *               == 0 else d_in / group_size.
@@ -149,7 +150,7 @@ int gptq_prepare_hinv(const float* H, int64_t d_in, double damp_frac, float* U, 
  *   workspace   at least gptq_quantize_layer_workspace(d_out, d_in,
  *               block_size) bytes of device memory, 256-byte aligned.
  * Errors: GPTQ_EINVAL (null required pointer, negative sizes, bits outside
- * [2, 8], block_size outside [1, 256], negative group_size, group_size not
+ * [2, 8], block_size outside [1, 128], negative group_size, group_size not
  * dividing d_in, unknown w_dtype), GPTQ_EUNSUPPORTED (group_size not a
  * multiple of 16, or neither dividing nor a multiple of block_size),
  * GPTQ_EWORKSPACE.

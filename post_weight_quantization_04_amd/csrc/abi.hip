@@ -147,7 +147,7 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in,
     if (d_out < 0 || d_in < 0) return GPTQ_EINVAL;
     if (w_dtype != GPTQ_F16 && w_dtype != GPTQ_F32) return GPTQ_EINVAL;
     if (bits < 2 || bits > 8) return GPTQ_EINVAL;
-    if (block_size < 1 || block_size > 256) return GPTQ_EINVAL;
+    if (block_size < 1 || block_size > 128) return GPTQ_EINVAL;
     if (group_size < 0) return GPTQ_EINVAL;
     if (group_size > 0 && d_in > 0 && d_in % group_size != 0) return GPTQ_EINVAL;
     if (group_size > 0) {

@@ -48,40 +48,45 @@ __device__ __forceinline__ void store_quarter(float* __restrict__ H, int64_t n, 
 constexpr int kK16 = 64;       // tokens per LDS stage
 constexpr int kLd16 = kK16 + 8;  // padded LDS row (halves)
 
+// Each thread moves 4 rows x 8 halves of a 128 x 64 slab: row (tid>>3) + 32 i,
+// halves (tid&7)*8 .. +8.
 template <bool kVec>
-__device__ __forceinline__ void load_slab_f16(half_t (*S)[kLd16], const half_t* __restrict__ X, int64_t n,
-                                              int64_t ldx, int64_t ntok, int r0, int64_t k0, int tid) {
+__device__ __forceinline__ void fetch_slab_f16(half8 (&v)[4], const half_t* __restrict__ X, int64_t n, int64_t ldx,
+                                               int64_t ntok, int r0, int64_t k0, int tid) {
     const int kk = (tid & 7) * 8;
 #pragma unroll
-    for (int rr = 0; rr < kTile; rr += kThreads / 8) {
-        int r = rr + (tid >> 3);
-        int64_t row = r0 + r;
-        int64_t k = k0 + kk;
-        half8 v;
+    for (int i = 0; i < 4; ++i) {
+        const int64_t row = r0 + (tid >> 3) + 32 * i;
+        const int64_t k = k0 + kk;
         if (kVec && row < n && k + 8 <= ntok) {
-            v = *reinterpret_cast<const half8*>(X + row * ldx + k);
+            v[i] = *reinterpret_cast<const half8*>(X + row * ldx + k);
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                v[e] = (row < n && k + e < ntok) ? X[row * ldx + k + e] : (half_t)0;
+            for (int e = 0; e < 8; ++e) v[i][e] = (row < n && k + e < ntok) ? X[row * ldx + k + e] : (half_t)0;
         }
-        *reinterpret_cast<half8*>(&S[r][kk]) = v;
     }
 }
 
+__device__ __forceinline__ void stash_slab_f16(const half8 (&v)[4], half_t (*S)[kLd16], int tid) {
+    const int kk = (tid & 7) * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<half8*>(&S[(tid >> 3) + 32 * i][kk]) = v[i];
+}
+
+// Token slab k+1 is fetched into registers while the MFMAs consume slab k
+// from one of two LDS buffers (one barrier per slab).
 template <bool kVec>
 __global__ __launch_bounds__(kThreads) void hessian_f16_kernel(float* __restrict__ H, int64_t n,
                                                               const half_t* __restrict__ X, int64_t ldx,
                                                               int64_t ntok) {
-    __shared__ half_t As[kTile][kLd16];
-    __shared__ half_t Bs[kTile][kLd16];
+    __shared__ half_t As[2][kTile][kLd16];
+    __shared__ half_t Bs[2][kTile][kLd16];
     int I, J;
     tile_of(blockIdx.x, I, J);
     const bool diag = (I == J);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wi = w >> 1, wj = w & 1;
     const bool active = !(diag && wi < wj);  // upper quarter of a diagonal tile
-    half_t(*Bp)[kLd16] = diag ? As : Bs;
 
     float16v acc[2][2];
 #pragma unroll
@@ -89,17 +94,28 @@ __global__ __launch_bounds__(kThreads) void hessian_f16_kernel(float* __restrict
 #pragma unroll
         for (int q = 0; q < 2; ++q) acc[m][q] = (float16v){};
 
-    for (int64_t k0 = 0; k0 < ntok; k0 += kK16) {
-        load_slab_f16<kVec>(As, X, n, ldx, ntok, I * kTile, k0, tid);
-        if (!diag) load_slab_f16<kVec>(Bs, X, n, ldx, ntok, J * kTile, k0, tid);
+    half8 ra[4], rb[4];
+    fetch_slab_f16<kVec>(ra, X, n, ldx, ntok, I * kTile, 0, tid);
+    if (!diag) fetch_slab_f16<kVec>(rb, X, n, ldx, ntok, J * kTile, 0, tid);
+    const int64_t nslab = (ntok + kK16 - 1) / kK16;
+    for (int64_t sl = 0; sl < nslab; ++sl) {
+        const int buf = (int)(sl & 1);
+        stash_slab_f16(ra, As[buf], tid);
+        if (!diag) stash_slab_f16(rb, Bs[buf], tid);
         __syncthreads();
+        if (sl + 1 < nslab) {
+            fetch_slab_f16<kVec>(ra, X, n, ldx, ntok, I * kTile, (sl + 1) * kK16, tid);
+            if (!diag) fetch_slab_f16<kVec>(rb, X, n, ldx, ntok, J * kTile, (sl + 1) * kK16, tid);
+        }
+        half_t(*Ap)[kLd16] = As[buf];
+        half_t(*Bp)[kLd16] = diag ? As[buf] : Bs[buf];
         if (active) {
 #pragma unroll
             for (int ks = 0; ks < kK16; ks += 16) {
                 half8 a[2], b[2];
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
-                    a[m] = *reinterpret_cast<const half8*>(&As[wi * 64 + 32 * m + (lane & 31)][ks + 8 * (lane >> 5)]);
+                    a[m] = *reinterpret_cast<const half8*>(&Ap[wi * 64 + 32 * m + (lane & 31)][ks + 8 * (lane >> 5)]);
 #pragma unroll
                 for (int q = 0; q < 2; ++q)
                     b[q] = *reinterpret_cast<const half8*>(&Bp[wj * 64 + 32 * q + (lane & 31)][ks + 8 * (lane >> 5)]);
@@ -109,7 +125,6 @@ __global__ __launch_bounds__(kThreads) void hessian_f16_kernel(float* __restrict
                     for (int q = 0; q < 2; ++q) acc[m][q] = mfma32x32x16_f16(a[m], b[q], acc[m][q]);
             }
         }
-        __syncthreads();
     }
     if (active) store_quarter(H, n, I * kTile + wi * 64, J * kTile + wj * 64, acc, lane);
 }

@@ -28,7 +28,7 @@ namespace {
 constexpr int NB = kCholNB;  // 64
 constexpr int kGemmThreads = 256;
 constexpr int kKc = 32;        // k per LDS stage of the tile GEMM
-constexpr int kLdsLd = NB + 16;  // padded LDS row (doubles)
+constexpr int kLdsLd = NB + 8;   // padded LDS row (doubles)
 
 struct HinvWs {
     double* G;      // [n_pad, n_pad]
@@ -130,111 +130,171 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(const float* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Diagonal block k: in-place Cholesky with simultaneous inversion.
-// Pivot c: d = sqrt(G_cc); row c becomes the scaled inverse row, column c
-// below the pivot becomes l = G_ic / d, and every later row is updated:
-//   j < c: G_ij -= l_i M_cj ; j == c: G_ic = -l_i / d ; j > c: G_ij -= l_i l_j.
-// Thread t owns the 4x4 sub-block (t/16, t%16) in registers.
+// Diagonal block k: Cholesky factor L_kk and its inverse M = L_kk^-1 in one
+// workgroup, as Gauss-Jordan elimination of [A | I] with symmetric pivots.
+// Pivot c (d = sqrt(A_cc)): the step publishes
+//     vL_i = A_ic / d for i > c, 0 otherwise     (column c of L)
+//     vM_j = B_cj / d for j <= c, 0 otherwise    (row c of M)
+// and every thread updates its own entries with no case split:
+//     A_ij -= vL_i vL_j        B_ij -= vL_i vM_j
+// (the zeros leave finished rows and unreached columns untouched); the
+// owners of column c and row c store vL / vM into their entries.
+// 512 threads; thread t owns rows 2(t/16)..+1, columns 4(t%16)..+3 of both
+// A and B in registers.  Two barriers per pivot; the owner of the next
+// pivot forwards its updated value through LDS.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void chol_diag_kernel(double* __restrict__ G, int64_t np, int k,
-                                                        int32_t* __restrict__ info, int* __restrict__ fail) {
-    __shared__ double s_piv;
-    __shared__ double prow[2][NB];
-    __shared__ double lcol[2][NB];
-    if (*fail) return;
-    const int tid = threadIdx.x;
-    const int a = tid >> 4, b = tid & 15;
-    const bool active = (b <= a);
-    double* blk = G + (int64_t)k * NB * np + (int64_t)k * NB;
-    double g[4][4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) g[r][c] = active ? blk[(int64_t)(4 * a + r) * np + 4 * b + c] : 0.0;
+__device__ __forceinline__ double rsqrt_f64(double x) {
+    double y = __builtin_amdgcn_rsq(x);
+    const double h = 0.5 * x * y;
+    y = fma(y, fma(-h, y, 0.5), y);
+    return y;
+}
 
-    for (int c = 0; c < NB; ++c) {
-        const int buf = c & 1, ca = c >> 2, cr = c & 3;
-        if (a == ca && b == ca) {
+// One pivot step; CC = c % 4 is a compile-time constant so that every
+// register pick below is static.
+template <int CC>
+__device__ __forceinline__ bool diag_pivot(int c, int a, int b, double (&g)[2][4], double (&m)[2][4],
+                                           double* vL, double* vM, double* s_piv) {
+    constexpr int CR = CC & 1;
+    __syncthreads();
+    const double pv = *s_piv;
+    if (!(pv > 0.0)) return false;  // uniform: every thread reads the same value
+    const int cb = c >> 2;
+    const int ca = c >> 1;
+    if (b == cb || a == ca) {
+        const double rd = rsqrt_f64(pv);
+        if (b == cb) {  // column c of A (rows 2a, 2a+1)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (r == cr) s_piv = g[r][r];
-        }
-        __syncthreads();
-        const double pv = s_piv;
-        if (!(pv > 0.0)) {  // uniform: every thread reads the same value
-            if (tid == 0) {
-                *info = k * NB + c + 1;
-                *fail = 1;
-            }
-            return;
-        }
-        const double rd = 1.0 / sqrt(pv);
-        if (active && a == ca) {
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                int j = 4 * b + cc;
-                if (j < c) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (r == cr) prow[buf][j] = g[r][cc] * rd;
-                }
+            for (int r = 0; r < 2; ++r) {
+                const int i = 2 * a + r;
+                const double l = (i > c) ? g[r][CC] * rd : 0.0;
+                vL[i] = l;
+                g[r][CC] = (i > c) ? l : ((i == c) ? pv * rd : g[r][CC]);
             }
         }
-        if (active && b == ca) {
+        if (a == ca) {  // row c of B (columns 4b .. 4b+3)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                int i = 4 * a + rr;
-                if (i > c) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (q == cr) lcol[buf][i] = g[rr][q] * rd;
-                }
-            }
-        }
-        __syncthreads();
-        if (active && 4 * a + 3 >= c) {
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int i = 4 * a + rr;
-                if (i < c) continue;
-                const double li = (i > c) ? lcol[buf][i] : 0.0;
-#pragma unroll
-                for (int cc = 0; cc < 4; ++cc) {
-                    const int j = 4 * b + cc;
-                    if (j > i) continue;
-                    if (i == c) {
-                        g[rr][cc] = (j < c) ? g[rr][cc] * rd : rd;
-                    } else if (j < c) {
-                        g[rr][cc] -= li * prow[buf][j];
-                    } else if (j == c) {
-                        g[rr][cc] = -li * rd;
-                    } else {
-                        g[rr][cc] -= li * lcol[buf][j];
-                    }
-                }
+            for (int q = 0; q < 4; ++q) {
+                const int j = 4 * b + q;
+                const double v = (j <= c) ? m[CR][q] * rd : 0.0;
+                vM[j] = v;
+                m[CR][q] = v;
             }
         }
     }
-    // write back L^-1 of the block with an explicit zero upper triangle
+    __syncthreads();
+    double li[2], lj[4], mj[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 2; ++r) li[r] = vL[2 * a + r];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        lj[q] = vL[4 * b + q];
+        mj[q] = vM[4 * b + q];
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            g[r][q] = fma(-li[r], lj[q], g[r][q]);
+            m[r][q] = fma(-li[r], mj[q], m[r][q]);
+        }
+    // forward the next pivot: (c+1, c+1) sits at row (CC+1)&1, column (CC+1)&3
+    constexpr int NR = (CC + 1) & 1, NQ = (CC + 1) & 3;
+    const int c1 = c + 1;
+    if (c1 < NB && a == (c1 >> 1) && b == (c1 >> 2)) *s_piv = g[NR][NQ];
+    return true;
+}
+
+__global__ __launch_bounds__(512) void chol_diag_kernel(double* __restrict__ G, int64_t np, int k,
+                                                        int32_t* __restrict__ info, int* __restrict__ fail) {
+    __shared__ __align__(16) double vL[NB];
+    __shared__ __align__(16) double vM[NB];
+    __shared__ double s_piv;
+    if (*fail) return;
+    const int tid = threadIdx.x;
+    const int a = tid >> 4, b = tid & 15;  // rows 2a, 2a+1; columns 4b .. 4b+3
+    double* blk = G + (int64_t)k * NB * np + (int64_t)k * NB;
+    double g[2][4], m[2][4];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            int i = 4 * a + r, j = 4 * b + c;
-            blk[(int64_t)i * np + j] = (j <= i) ? g[r][c] : 0.0;
+            g[r][c] = blk[(int64_t)(2 * a + r) * np + 4 * b + c];
+            m[r][c] = (2 * a + r == 4 * b + c) ? 1.0 : 0.0;
         }
+    if (tid == 0) s_piv = g[0][0];
+
+    int failed_at = -1;
+    for (int c0 = 0; c0 < NB; c0 += 4) {
+        if (!diag_pivot<0>(c0 + 0, a, b, g, m, vL, vM, &s_piv)) { failed_at = c0 + 0; break; }
+        if (!diag_pivot<1>(c0 + 1, a, b, g, m, vL, vM, &s_piv)) { failed_at = c0 + 1; break; }
+        if (!diag_pivot<2>(c0 + 2, a, b, g, m, vL, vM, &s_piv)) { failed_at = c0 + 2; break; }
+        if (!diag_pivot<3>(c0 + 3, a, b, g, m, vL, vM, &s_piv)) { failed_at = c0 + 3; break; }
+    }
+    if (failed_at >= 0) {
+        if (tid == 0) {
+            *info = k * NB + failed_at + 1;
+            *fail = 1;
+        }
+        return;
+    }
+    // write back M = L^-1 (exactly zero above the diagonal)
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) blk[(int64_t)(2 * a + r) * np + 4 * b + q] = m[r][q];
 }
 
 // ---------------------------------------------------------------------------
 // 64x64x64 float64 tile product on MFMA 16x16x4 f64:  acc += A B.
 // A is given row-major [64 rows][64 k] (lda); B is row-major [64 k][64 cols]
 // (ldb) or, with kBT, its transpose given row-major [64 cols][64 k].
-// Four waves in a 2x2 grid, each 32x32 as 2x2 MFMA tiles.
+// Four waves in a 2x2 grid, each 32x32 as 2x2 MFMA tiles.  K runs in two
+// chunks of 32: chunk 1 is fetched into registers while the MFMAs consume
+// chunk 0 (two LDS buffers, one barrier per chunk).
 // ---------------------------------------------------------------------------
 struct GemmLds {
-    double A[kKc][kLdsLd];
-    double B[kKc][kLdsLd];
+    double A[2][kKc][kLdsLd];
+    double B[2][kKc][kLdsLd];
 };
+
+template <bool kBT>
+struct GemmRegs {
+    double a[8];
+    double b[8];
+};
+
+// thread -> A^T: row tid&63, k run (tid>>6)*8 ; B direct: k row tid>>3, cols (tid&7)*8 ;
+// B^T: col tid&63, k run (tid>>6)*8
+template <bool kBT>
+__device__ __forceinline__ void gemm_fetch(GemmRegs<kBT>& r, const double* __restrict__ A, int64_t lda,
+                                           const double* __restrict__ B, int64_t ldb, int k0, int tid) {
+    const double* sa = A + (int64_t)(tid & 63) * lda + k0 + (tid >> 6) * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r.a[e] = sa[e];
+    if (kBT) {
+        const double* sb = B + (int64_t)(tid & 63) * ldb + k0 + (tid >> 6) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r.b[e] = sb[e];
+    } else {
+        const double* sb = B + (int64_t)(k0 + (tid >> 3)) * ldb + (tid & 7) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r.b[e] = sb[e];
+    }
+}
+
+template <bool kBT>
+__device__ __forceinline__ void gemm_stash(const GemmRegs<kBT>& r, GemmLds& s, int buf, int tid) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s.A[buf][(tid >> 6) * 8 + e][tid & 63] = r.a[e];
+    if (kBT) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s.B[buf][(tid >> 6) * 8 + e][tid & 63] = r.b[e];
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s.B[buf][tid >> 3][(tid & 7) * 8 + e] = r.b[e];
+    }
+}
 
 template <bool kBT>
 __device__ __forceinline__ void tile_gemm_f64(const double* __restrict__ A, int64_t lda,
@@ -242,38 +302,27 @@ __device__ __forceinline__ void tile_gemm_f64(const double* __restrict__ A, int6
                                               double4v (&acc)[2][2]) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wi = w >> 1, wj = w & 1;
-    for (int k0 = 0; k0 < NB; k0 += kKc) {
-        {  // A^T into LDS: thread -> (row = tid & 63, k run of 8)
-            const int row = tid & 63, kc = (tid >> 6) * 8;
-            const double* src = A + (int64_t)row * lda + k0 + kc;
+    GemmRegs<kBT> regs;
+    gemm_fetch<kBT>(regs, A, lda, B, ldb, 0, tid);
+    constexpr int nch = NB / kKc;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s.A[kc + e][row] = src[e];
-        }
-        if (kBT) {
-            const int col = tid & 63, kc = (tid >> 6) * 8;
-            const double* src = B + (int64_t)col * ldb + k0 + kc;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s.B[kc + e][col] = src[e];
-        } else {
-            const int kk = tid >> 3, cc = (tid & 7) * 8;
-            const double* src = B + (int64_t)(k0 + kk) * ldb + cc;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s.B[kk][cc + e] = src[e];
-        }
+    for (int c = 0; c < nch; ++c) {
+        const int buf = c & 1;
+        gemm_stash<kBT>(regs, s, buf, tid);
         __syncthreads();
+        if (c + 1 < nch) gemm_fetch<kBT>(regs, A, lda, B, ldb, (c + 1) * kKc, tid);
 #pragma unroll
         for (int ks = 0; ks < kKc; ks += 4) {
             double av[2], bv[2];
 #pragma unroll
-            for (int m = 0; m < 2; ++m) av[m] = s.A[ks + (lane >> 4)][wi * 32 + 16 * m + (lane & 15)];
+            for (int m = 0; m < 2; ++m) av[m] = s.A[buf][ks + (lane >> 4)][wi * 32 + 16 * m + (lane & 15)];
 #pragma unroll
-            for (int q = 0; q < 2; ++q) bv[q] = s.B[ks + (lane >> 4)][wj * 32 + 16 * q + (lane & 15)];
+            for (int q = 0; q < 2; ++q) bv[q] = s.B[buf][ks + (lane >> 4)][wj * 32 + 16 * q + (lane & 15)];
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
                 for (int q = 0; q < 2; ++q) acc[m][q] = mfma16x16x4_f64(av[m], bv[q], acc[m][q]);
         }
-        __syncthreads();
     }
 }
 
@@ -388,7 +437,7 @@ hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, floa
     for (int k = 0; k < T; ++k) {
         {
             TimedLaunch t(K_CHOL_DIAG, s);
-            hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, s, w.G, np, k, info, w.fail);
+            hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(512), 0, s, w.G, np, k, info, w.fail);
         }
         if (T > 1) {
             TimedLaunch t(K_CHOL_PANEL, s);

@@ -27,7 +27,7 @@ namespace {
 
 constexpr int kSub = 16;      // columns per wave in the sweep
 constexpr int kRowsPerWg = 64;
-constexpr int kMaxBlock = 256;
+constexpr int kMaxBlock = 128;
 constexpr int kEld = 65;      // padded LDS row of the scaled-error exchange
 
 __host__ __device__ inline int64_t rup(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
@@ -140,19 +140,84 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, i
 }
 
 // ---------------------------------------------------------------------------
-// In-block sweep.  Dynamic LDS: Ebuf [nw][16][kEld] f32, codes [64][nw*16] u8,
-// red [nw][64][2] f32, errs [nw][64] f32.
+// In-block sweep.  Dynamic LDS: Us [bw][bw+4] f32 (the U block, staged once),
+// rdg [bw] f32 (1 / U_jj), Ebuf [nw][16][kEld] f32, red [nw][64][2] f32,
+// errs [nw][64] f32, codes [64][nw*16] u8.  U entries are read with
+// wave-uniform addresses (LDS broadcast).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void sweep_kernel(const float* __restrict__ Wk, int64_t d_out, int64_t d_in,
-                                                     const float* __restrict__ U, const float* __restrict__ rdiag,
-                                                     int64_t b0, int64_t b1, int bits, int64_t group, int64_t ng,
-                                                     float* __restrict__ scales, int32_t* __restrict__ zeros,
-                                                     float* __restrict__ minmax, uint8_t* __restrict__ codes,
-                                                     float* __restrict__ E, int64_t ldE, float* __restrict__ err_row) {
+__host__ __device__ inline size_t sweep_lds_bytes(int bw) {
+    const int nw = (bw + kSub - 1) / kSub;
+    return (size_t)bw * (bw + 4) * 4 + (size_t)bw * 4 + (size_t)nw * kSub * kEld * 4 + (size_t)nw * 64 * 2 * 4 +
+           (size_t)nw * 64 * 4 + (size_t)64 * nw * kSub;
+}
+
+// Folds the 16 scaled errors of an earlier sub-block into this wave's
+// columns: w_c -= sum_t e_t U[t][c].  kFull: all 16 columns present (no
+// guards, so every LDS read can be issued ahead of the FMAs).
+template <bool kFull>
+__device__ __forceinline__ void fold_in(float (&wv)[kSub], const float* __restrict__ ebp,
+                                        const float* __restrict__ ublk, int uld, int lane, int cq) {
+    float e[kSub];
+#pragma unroll
+    for (int t = 0; t < kSub; ++t) e[t] = ebp[t * kEld + lane];
+#pragma unroll
+    for (int t = 0; t < kSub; ++t) {
+        float u[kSub];
+#pragma unroll
+        for (int c = 0; c < kSub; ++c) u[c] = ublk[t * uld + c];
+#pragma unroll
+        for (int c = 0; c < kSub; ++c)
+            if (kFull || c < cq) wv[c] -= e[t] * u[c];
+    }
+}
+
+// Rounds this wave's columns in order, compensating the later columns of
+// the sub-block at once.  U rows of the sub-block and 1/U_jj are read into
+// registers before the dependent chain starts.
+template <bool kFull>
+__device__ __forceinline__ void sweep_sub(float (&wv)[kSub], float s, float zf, float maxq,
+                                          const float* __restrict__ ublk, int uld, const float* __restrict__ rd,
+                                          float* __restrict__ ebq, uint8_t* __restrict__ crow, int lane, int cq,
+                                          float& errsq) {
+    float r[kSub];
+#pragma unroll
+    for (int t = 0; t < kSub; ++t) r[t] = rd[t];
+#pragma unroll
+    for (int t = 0; t < kSub; ++t) {
+        if (kFull || t < cq) {
+            float u[kSub];
+#pragma unroll
+            for (int t2 = t + 1; t2 < kSub; ++t2) u[t2] = ublk[t * uld + t2];
+            const float w = wv[t];
+            const float x = w / s;
+            const float v = x + zf;
+            float qf = __builtin_rintf(v);
+            qf = fminf(fmaxf(qf, 0.0f), maxq);
+            const float what = (qf - zf) * s;
+            const float e = (w - what) * r[t];
+            crow[t] = (uint8_t)qf;
+            ebq[t * kEld + lane] = e;
+            errsq += e * e;
+#pragma unroll
+            for (int t2 = t + 1; t2 < kSub; ++t2)
+                if (kFull || t2 < cq) wv[t2] -= e * u[t2];
+        }
+    }
+}
+
+__global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk, int64_t d_out, int64_t d_in,
+                                                    const float* __restrict__ U, const float* __restrict__ rdiag,
+                                                    int64_t b0, int64_t b1, int bits, int64_t group, int64_t ng,
+                                                    float* __restrict__ scales, int32_t* __restrict__ zeros,
+                                                    float* __restrict__ minmax, uint8_t* __restrict__ codes,
+                                                    float* __restrict__ E, int64_t ldE, float* __restrict__ err_row) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int bw = (int)(b1 - b0);
     const int nw = (bw + kSub - 1) / kSub;
-    float* Ebuf = reinterpret_cast<float*>(smem);                       // nw*16*kEld
+    const int uld = bw + 4;
+    float* Us = reinterpret_cast<float*>(smem);                         // bw*uld
+    float* rdg = Us + bw * uld;                                           // bw
+    float* Ebuf = rdg + bw;                                               // nw*16*kEld
     float* red = Ebuf + nw * kSub * kEld;                                 // nw*64*2
     float* errs = red + nw * 64 * 2;                                      // nw*64
     uint8_t* cbuf = reinterpret_cast<uint8_t*>(errs + nw * 64);           // 64 * nw*16
@@ -164,6 +229,26 @@ __global__ __launch_bounds__(1024) void sweep_kernel(const float* __restrict__ W
     const int cq = min(kSub, bw - kSub * q);  // >= 1
     const int64_t c0q = b0 + kSub * q;
     const float maxq = (float)((1 << bits) - 1);
+
+    // stage the U block (upper part; the rest is never read) and 1/U_jj,
+    // with every thread's loads in flight before its LDS stores
+    {
+        constexpr int kPer = (kMaxBlock * kMaxBlock + 511) / 512;  // elements per thread at 512 threads
+        float t[kPer];
+        const int nth = blockDim.x;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = threadIdx.x + i * nth;
+            const int r = e / bw, c = e % bw;
+            t[i] = (e < bw * bw && c >= r) ? U[(b0 + r) * d_in + b0 + c] : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = threadIdx.x + i * nth;
+            if (e < bw * bw) Us[(e / bw) * uld + e % bw] = t[i];
+        }
+        for (int e = threadIdx.x; e < bw; e += nth) rdg[e] = rdiag[b0 + e];
+    }
 
     float wv[kSub];
 #pragma unroll
@@ -185,24 +270,17 @@ __global__ __launch_bounds__(1024) void sweep_kernel(const float* __restrict__ W
         }
     }
     float errsq = 0.0f;
+    __syncthreads();
 
     for (int p = 0; p < nw; ++p) {
         if (p > 0 && q >= p) {
             // fold in the scaled errors of sub-block p-1 (16 full columns)
             const float* ebp = Ebuf + (p - 1) * kSub * kEld;
-#pragma unroll
-            for (int t = 0; t < kSub; ++t) {
-                const float e = ebp[t * kEld + lane];
-                const float* urow = U + (b0 + kSub * (p - 1) + t) * d_in + c0q;
-                if (cq == kSub) {
-#pragma unroll
-                    for (int c = 0; c < kSub; ++c) wv[c] -= e * urow[c];
-                } else {
-#pragma unroll
-                    for (int c = 0; c < kSub; ++c)
-                        if (c < cq) wv[c] -= e * urow[c];
-                }
-            }
+            const float* ublk = Us + (kSub * (p - 1)) * uld + kSub * q;
+            if (cq == kSub)
+                fold_in<true>(wv, ebp, ublk, uld, lane, cq);
+            else
+                fold_in<false>(wv, ebp, ublk, uld, lane, cq);
         }
         if (group > 0 && group <= bw && ((int64_t)kSub * p) % group == 0) {
             // group start at column b0 + 16p: grid from the current weights
@@ -241,26 +319,13 @@ __global__ __launch_bounds__(1024) void sweep_kernel(const float* __restrict__ W
         }
         if (q == p) {
             float* ebq = Ebuf + p * kSub * kEld;
-#pragma unroll
-            for (int t = 0; t < kSub; ++t) {
-                if (t < cq) {
-                    const int64_t j = c0q + t;
-                    const float w = wv[t];
-                    const float x = w / s;
-                    const float v = x + zf;
-                    float qf = __builtin_rintf(v);
-                    qf = fminf(fmaxf(qf, 0.0f), maxq);
-                    const float what = (qf - zf) * s;
-                    const float e = (w - what) * rdiag[j];
-                    cbuf[lane * (nw * kSub) + kSub * p + t] = (uint8_t)qf;
-                    ebq[t * kEld + lane] = e;
-                    errsq += e * e;
-                    const float* urow = U + j * d_in + c0q;
-#pragma unroll
-                    for (int t2 = t + 1; t2 < kSub; ++t2)
-                        if (t2 < cq) wv[t2] -= e * urow[t2];
-                }
-            }
+            uint8_t* crow = cbuf + lane * (nw * kSub) + kSub * p;
+            const float* ublk = Us + (kSub * p) * uld + kSub * p;
+            const float* rd = rdg + kSub * p;
+            if (cq == kSub)
+                sweep_sub<true>(wv, s, zf, maxq, ublk, uld, rd, ebq, crow, lane, cq, errsq);
+            else
+                sweep_sub<false>(wv, s, zf, maxq, ublk, uld, rd, ebq, crow, lane, cq, errsq);
         }
         __syncthreads();
     }
@@ -286,22 +351,79 @@ __global__ __launch_bounds__(1024) void sweep_kernel(const float* __restrict__ W
 // ---------------------------------------------------------------------------
 // Lazy trailing update W[:, b1:] -= E[:, :K] U[b0:b1, b1:], K = b1 - b0.
 // 128x128 tile per workgroup; 4 waves in 2x2, each 64x64 = 2x2 MFMA 32x32.
+// K runs in chunks of 32: chunk c+1 is fetched into registers while the
+// MFMAs consume chunk c from one of two LDS buffers (one barrier per chunk).
+// E is staged row-major with an odd row stride, so the A-operand reads
+// (32 rows, one k) hit distinct banks.
 // ---------------------------------------------------------------------------
 constexpr int kTT = 128;
 constexpr int kTK = 32;
-constexpr int kTld = kTT + 4;
+constexpr int kEs = kTK + 1;   // E stage row stride (odd)
+constexpr int kUs = kTT + 4;   // U stage row stride
+
+struct TrailLds {
+    float E[2][kTT * kEs];
+    float U[2][kTK * kUs];
+};
+
+template <bool kVec>
+struct TrailRegs {
+    float e[16];
+    float u[16];
+};
+
+// thread -> E: row tid/2, k run (tid&1)*16 .. +16 ; U: k row tid/8, cols (tid&7)*16 .. +16
+template <bool kVec>
+__device__ __forceinline__ void trail_fetch(TrailRegs<kVec>& r, const float* __restrict__ E, int64_t ldE,
+                                            const float* __restrict__ U, int64_t d_out, int64_t d_in, int64_t r0,
+                                            int64_t c0, int64_t b0, int K, int kc, int tid) {
+    {
+        const int64_t R = r0 + (tid >> 1);
+        const int k = kc + (tid & 1) * 16;
+        const float* src = E + R * ldE + k;
+        if (kVec && R < d_out && k + 16 <= K) {
+#pragma unroll
+            for (int e = 0; e < 16; e += 4) *reinterpret_cast<float4v*>(&r.e[e]) = *reinterpret_cast<const float4v*>(src + e);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) r.e[e] = (R < d_out && k + e < K) ? src[e] : 0.0f;
+        }
+    }
+    {
+        const int k = kc + (tid >> 3);
+        const int64_t col = c0 + (tid & 7) * 16;
+        const float* src = U + (b0 + k) * d_in + col;
+        if (kVec && k < K && col + 16 <= d_in) {
+#pragma unroll
+            for (int e = 0; e < 16; e += 4) *reinterpret_cast<float4v*>(&r.u[e]) = *reinterpret_cast<const float4v*>(src + e);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) r.u[e] = (k < K && col + e < d_in) ? src[e] : 0.0f;
+        }
+    }
+}
+
+template <bool kVec>
+__device__ __forceinline__ void trail_stash(const TrailRegs<kVec>& r, TrailLds& s, int buf, int tid) {
+    float* Es = s.E[buf] + (tid >> 1) * kEs + (tid & 1) * 16;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) Es[e] = r.e[e];
+    float* Us = s.U[buf] + (tid >> 3) * kUs + (tid & 7) * 16;
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) *reinterpret_cast<float4v*>(&Us[e]) = *reinterpret_cast<const float4v*>(&r.u[e]);
+}
 
 template <bool kVec>
 __global__ __launch_bounds__(256) void trail_kernel(float* __restrict__ Wk, int64_t d_out, int64_t d_in,
                                                     const float* __restrict__ E, int64_t ldE,
                                                     const float* __restrict__ U, int64_t b0, int64_t b1) {
-    __shared__ float As[kTK][kTld];
-    __shared__ float Bs[kTK][kTld];
+    __shared__ TrailLds s;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wi = w >> 1, wj = w & 1;
     const int64_t r0 = (int64_t)blockIdx.y * kTT;
     const int64_t c0 = b1 + (int64_t)blockIdx.x * kTT;
     const int K = (int)(b1 - b0);
+    const int nchunks = (K + kTK - 1) / kTK;
 
     float16v acc[2][2];
 #pragma unroll
@@ -309,43 +431,27 @@ __global__ __launch_bounds__(256) void trail_kernel(float* __restrict__ Wk, int6
 #pragma unroll
         for (int q = 0; q < 2; ++q) acc[m][q] = (float16v){};
 
-    for (int kc = 0; kc < K; kc += kTK) {
-        {  // E chunk, transposed into As[k][row]
-            const int row = tid >> 1, kh = (tid & 1) * 16;
-            const int64_t R = r0 + row;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int k = kc + kh + e;
-                As[kh + e][row] = (R < d_out && k < K) ? E[R * ldE + k] : 0.0f;
-            }
-        }
-        {  // U chunk, rows b0+kc.., direct
-            const int kk = tid >> 3, cc = (tid & 7) * 16;
-            const int k = kc + kk;
-            const int64_t col = c0 + cc;
-            const float* src = U + (b0 + k) * d_in + col;
-            if (kVec && k < K && col + 16 <= d_in) {
-#pragma unroll
-                for (int e = 0; e < 16; e += 4) *reinterpret_cast<float4v*>(&Bs[kk][cc + e]) = *reinterpret_cast<const float4v*>(src + e);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) Bs[kk][cc + e] = (k < K && col + e < d_in) ? src[e] : 0.0f;
-            }
-        }
+    TrailRegs<kVec> regs;
+    trail_fetch<kVec>(regs, E, ldE, U, d_out, d_in, r0, c0, b0, K, 0, tid);
+    for (int c = 0; c < nchunks; ++c) {
+        const int buf = c & 1;
+        trail_stash<kVec>(regs, s, buf, tid);
         __syncthreads();
+        if (c + 1 < nchunks) trail_fetch<kVec>(regs, E, ldE, U, d_out, d_in, r0, c0, b0, K, (c + 1) * kTK, tid);
+        const float* Es = s.E[buf];
+        const float* Us = s.U[buf];
 #pragma unroll
         for (int ks = 0; ks < kTK; ks += 2) {
             float a[2], b[2];
 #pragma unroll
-            for (int m = 0; m < 2; ++m) a[m] = As[ks + (lane >> 5)][wi * 64 + 32 * m + (lane & 31)];
+            for (int m = 0; m < 2; ++m) a[m] = Es[(wi * 64 + 32 * m + (lane & 31)) * kEs + ks + (lane >> 5)];
 #pragma unroll
-            for (int q = 0; q < 2; ++q) b[q] = Bs[ks + (lane >> 5)][wj * 64 + 32 * q + (lane & 31)];
+            for (int q = 0; q < 2; ++q) b[q] = Us[(ks + (lane >> 5)) * kUs + wj * 64 + 32 * q + (lane & 31)];
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
                 for (int q = 0; q < 2; ++q) acc[m][q] = mfma32x32x2_f32(a[m], b[q], acc[m][q]);
         }
-        __syncthreads();
     }
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -402,12 +508,9 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
     }
     if (err_row)
         hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((d_out + 255) / 256)), dim3(256), 0, s, err_row, d_out);
-    const bool vec = (reinterpret_cast<uintptr_t>(U) % 16 == 0) && (d_in % 4 == 0) && (block % 4 == 0);
+    const bool vec = (reinterpret_cast<uintptr_t>(U) % 16 == 0) && (d_in % 4 == 0) && (block % 4 == 0);  // E rows are 16-byte aligned when block % 4 == 0
     {
-        // the widest block (256 columns) needs 93 KiB of LDS per workgroup
-        const int nwmax = (int)((std::min(block, d_in) + kSub - 1) / kSub);
-        const size_t ldsmax = (size_t)nwmax * kSub * kEld * 4 + (size_t)nwmax * 64 * 2 * 4 + (size_t)nwmax * 64 * 4 +
-                              (size_t)64 * nwmax * kSub;
+        const size_t ldsmax = sweep_lds_bytes((int)std::min(block, d_in));
         if (ldsmax > 64 * 1024) {
             hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_kernel),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsmax);
@@ -426,8 +529,7 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
         }
         {
             TimedLaunch t(K_Q_SWEEP, s);
-            const size_t lds = (size_t)nw * kSub * kEld * 4 + (size_t)nw * 64 * 2 * 4 + (size_t)nw * 64 * 4 +
-                               (size_t)64 * nw * kSub;
+            const size_t lds = sweep_lds_bytes(bw);
             hipLaunchKernelGGL(sweep_kernel, dim3(row_tiles), dim3(64 * nw), lds, s, (const float*)w.Wk, d_out, d_in, U,
                                (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes, w.E,
                                block, err_row);

@@ -93,7 +93,7 @@ def test_quantize_argument_errors(clib):
         return f(W, dtype, d_out, d_in, U, None, bits, group, block, p, p, p, None, None, ws, wsb, None)
 
     assert call(bits=1) == 1 and call(bits=9) == 1
-    assert call(block=0) == 1 and call(block=257) == 1
+    assert call(block=0) == 1 and call(block=129) == 1
     assert call(group=-16) == 1
     assert call(group=48) == 1                 # does not divide d_in
     assert call(d_in=48, group=24) == 2        # not a multiple of 16
