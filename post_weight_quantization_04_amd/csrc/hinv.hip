@@ -132,16 +132,18 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(const float* __restr
 // ---------------------------------------------------------------------------
 // Diagonal block k: Cholesky factor L_kk and its inverse M = L_kk^-1 in one
 // workgroup, as Gauss-Jordan elimination of [A | I] with symmetric pivots.
-// Pivot c (d = sqrt(A_cc)): the step publishes
-//     vL_i = A_ic / d for i > c, 0 otherwise     (column c of L)
-//     vM_j = B_cj / d for j <= c, 0 otherwise    (row c of M)
+// Pivot c with p = A_cc uses the raw vectors
+//     a_i = A_ic for i > c, 0 otherwise          (column c of A)
+//     b_j = B_cj for j <= c, 0 otherwise         (row c of B)
 // and every thread updates its own entries with no case split:
-//     A_ij -= vL_i vL_j        B_ij -= vL_i vM_j
-// (the zeros leave finished rows and unreached columns untouched); the
-// owners of column c and row c store vL / vM into their entries.
+//     A_ij -= (a_i / p) a_j        B_ij -= (a_i / p) b_j
+// (the zeros leave finished rows and unreached columns untouched); then the
+// owners of column c store L_ic = a_i / sqrt(p), L_cc = sqrt(p), and the
+// owners of row c store M_cj = b_j / sqrt(p).  The owners of column c+1 and
+// row c+1 publish the next raw vectors and pivot into the other LDS buffer
+// right after their update, so one barrier per pivot suffices.
 // 512 threads; thread t owns rows 2(t/16)..+1, columns 4(t%16)..+3 of both
-// A and B in registers.  Two barriers per pivot; the owner of the next
-// pivot forwards its updated value through LDS.
+// A and B in registers.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ double rsqrt_f64(double x) {
     double y = __builtin_amdgcn_rsq(x);
@@ -150,66 +152,77 @@ __device__ __forceinline__ double rsqrt_f64(double x) {
     return y;
 }
 
-// One pivot step; CC = c % 4 is a compile-time constant so that every
-// register pick below is static.
+struct DiagVec {
+    double a[2][NB];
+    double b[2][NB];
+    double piv[2];
+};
+
+// publish the raw vectors of pivot c (into buffer c & 1) from registers
 template <int CC>
-__device__ __forceinline__ bool diag_pivot(int c, int a, int b, double (&g)[2][4], double (&m)[2][4],
-                                           double* vL, double* vM, double* s_piv) {
+__device__ __forceinline__ void diag_publish(int c, int a, int b, const double (&g)[2][4], const double (&m)[2][4],
+                                             DiagVec& v) {
     constexpr int CR = CC & 1;
-    __syncthreads();
-    const double pv = *s_piv;
-    if (!(pv > 0.0)) return false;  // uniform: every thread reads the same value
-    const int cb = c >> 2;
-    const int ca = c >> 1;
-    if (b == cb || a == ca) {
-        const double rd = rsqrt_f64(pv);
-        if (b == cb) {  // column c of A (rows 2a, 2a+1)
+    const int buf = c & 1;
+    if (b == (c >> 2)) {
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int i = 2 * a + r;
-                const double l = (i > c) ? g[r][CC] * rd : 0.0;
-                vL[i] = l;
-                g[r][CC] = (i > c) ? l : ((i == c) ? pv * rd : g[r][CC]);
-            }
-        }
-        if (a == ca) {  // row c of B (columns 4b .. 4b+3)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int j = 4 * b + q;
-                const double v = (j <= c) ? m[CR][q] * rd : 0.0;
-                vM[j] = v;
-                m[CR][q] = v;
-            }
+        for (int r = 0; r < 2; ++r) {
+            const int i = 2 * a + r;
+            v.a[buf][i] = (i > c) ? g[r][CC] : 0.0;
+            if (i == c) v.piv[buf] = g[r][CC];
         }
     }
-    __syncthreads();
-    double li[2], lj[4], mj[4];
+    if (a == (c >> 1)) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) li[r] = vL[2 * a + r];
+        for (int q = 0; q < 4; ++q) {
+            const int j = 4 * b + q;
+            v.b[buf][j] = (j <= c) ? m[CR][q] : 0.0;
+        }
+    }
+}
+
+template <int CC>
+__device__ __forceinline__ bool diag_pivot(int c, int a, int b, double (&g)[2][4], double (&m)[2][4], DiagVec& v) {
+    constexpr int CR = CC & 1;
+    const int buf = c & 1;
+    const double pv = v.piv[buf];
+    if (!(pv > 0.0)) return false;  // uniform: every thread reads the same value
+    const double rs = rsqrt_f64(pv);
+    const double inv = rs * rs;
+    double ti[2], aj[4], bj[4];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) ti[r] = v.a[buf][2 * a + r] * inv;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        lj[q] = vL[4 * b + q];
-        mj[q] = vM[4 * b + q];
+        aj[q] = v.a[buf][4 * b + q];
+        bj[q] = v.b[buf][4 * b + q];
     }
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            g[r][q] = fma(-li[r], lj[q], g[r][q]);
-            m[r][q] = fma(-li[r], mj[q], m[r][q]);
+            g[r][q] = fma(-ti[r], aj[q], g[r][q]);
+            m[r][q] = fma(-ti[r], bj[q], m[r][q]);
         }
-    // forward the next pivot: (c+1, c+1) sits at row (CC+1)&1, column (CC+1)&3
-    constexpr int NR = (CC + 1) & 1, NQ = (CC + 1) & 3;
-    const int c1 = c + 1;
-    if (c1 < NB && a == (c1 >> 1) && b == (c1 >> 2)) *s_piv = g[NR][NQ];
+    if (b == (c >> 2)) {  // column c of L
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int i = 2 * a + r;
+            g[r][CC] = (i > c) ? g[r][CC] * rs : ((i == c) ? pv * rs : g[r][CC]);
+        }
+    }
+    if (a == (c >> 1)) {  // row c of M
+#pragma unroll
+        for (int q = 0; q < 4; ++q) m[CR][q] *= rs;
+    }
+    if (c + 1 < NB) diag_publish<(CC + 1) & 3>(c + 1, a, b, g, m, v);
+    __syncthreads();
     return true;
 }
 
 __global__ __launch_bounds__(512) void chol_diag_kernel(double* __restrict__ G, int64_t np, int k,
                                                         int32_t* __restrict__ info, int* __restrict__ fail) {
-    __shared__ __align__(16) double vL[NB];
-    __shared__ __align__(16) double vM[NB];
-    __shared__ double s_piv;
+    __shared__ __align__(16) DiagVec v;
     if (*fail) return;
     const int tid = threadIdx.x;
     const int a = tid >> 4, b = tid & 15;  // rows 2a, 2a+1; columns 4b .. 4b+3
@@ -222,14 +235,15 @@ __global__ __launch_bounds__(512) void chol_diag_kernel(double* __restrict__ G, 
             g[r][c] = blk[(int64_t)(2 * a + r) * np + 4 * b + c];
             m[r][c] = (2 * a + r == 4 * b + c) ? 1.0 : 0.0;
         }
-    if (tid == 0) s_piv = g[0][0];
+    diag_publish<0>(0, a, b, g, m, v);
+    __syncthreads();
 
     int failed_at = -1;
     for (int c0 = 0; c0 < NB; c0 += 4) {
-        if (!diag_pivot<0>(c0 + 0, a, b, g, m, vL, vM, &s_piv)) { failed_at = c0 + 0; break; }
-        if (!diag_pivot<1>(c0 + 1, a, b, g, m, vL, vM, &s_piv)) { failed_at = c0 + 1; break; }
-        if (!diag_pivot<2>(c0 + 2, a, b, g, m, vL, vM, &s_piv)) { failed_at = c0 + 2; break; }
-        if (!diag_pivot<3>(c0 + 3, a, b, g, m, vL, vM, &s_piv)) { failed_at = c0 + 3; break; }
+        if (!diag_pivot<0>(c0 + 0, a, b, g, m, v)) { failed_at = c0 + 0; break; }
+        if (!diag_pivot<1>(c0 + 1, a, b, g, m, v)) { failed_at = c0 + 1; break; }
+        if (!diag_pivot<2>(c0 + 2, a, b, g, m, v)) { failed_at = c0 + 2; break; }
+        if (!diag_pivot<3>(c0 + 3, a, b, g, m, v)) { failed_at = c0 + 3; break; }
     }
     if (failed_at >= 0) {
         if (tid == 0) {

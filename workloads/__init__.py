@@ -252,14 +252,28 @@ def x_chunks(wl: Workload, key: str = "x") -> Iterator[np.ndarray]:
         yield x_chunk(wl, key, c, st)
 
 
-def x_full(wl: Workload, key: str = "x", out: Optional[np.ndarray] = None) -> np.ndarray:
-    """Whole input ``[d_in, n_tokens]`` assembled from its chunks."""
+def x_full(wl: Workload, key: str = "x", out: Optional[np.ndarray] = None, workers: int = 0) -> np.ndarray:
+    """Whole input ``[d_in, n_tokens]`` assembled from its chunks (drawn in a
+    thread pool: each chunk has its own seed, so the result does not depend
+    on the number of workers)."""
+    import concurrent.futures
+    import os
     s = wl.x(key)
     if out is None:
         out = np.empty((s.d_in, s.n_tokens), dtype=s.dtype)
     st = _x_state(wl, key)
-    for c in range(n_chunks(wl, key)):
+
+    def fill(c):
         t0 = c * s.chunk
         ch = x_chunk(wl, key, c, st)
         out[:, t0:t0 + ch.shape[1]] = ch
+
+    nc = n_chunks(wl, key)
+    workers = workers or min(16, len(os.sched_getaffinity(0)), nc)
+    if workers <= 1:
+        for c in range(nc):
+            fill(c)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(fill, range(nc)))
     return out
