@@ -53,6 +53,25 @@ TimedLaunch::~TimedLaunch() {
     if (slot >= 0) (void)hipEventRecord(g_pending[slot].b, stream);
 }
 
+namespace {
+SideStream g_side[64];
+}
+
+hipError_t side_stream(SideStream*& out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    SideStream& ss = g_side[dev];
+    if (!ss.side) {
+        if ((e = hipStreamCreateWithFlags(&ss.side, hipStreamNonBlocking)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
+    }
+    out = &ss;
+    return hipSuccess;
+}
+
 }  // namespace gptq
 
 using namespace gptq;

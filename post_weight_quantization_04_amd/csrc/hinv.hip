@@ -32,7 +32,7 @@ constexpr int kLdsLd = NB + 8;   // padded LDS row (doubles)
 
 struct HinvWs {
     double* G;      // [n_pad, n_pad]
-    double* P;      // [n_pad / NB][NB][NB]
+    double* P;      // 2 x [n_pad / NB][NB][NB] (alternating steps)
     double* scal;   // [0] = lambda
     int* fail;      // device flag: set once a pivot fails
 };
@@ -45,8 +45,8 @@ HinvWs carve(void* ws, int64_t n) {
     HinvWs w;
     w.G = reinterpret_cast<double*>(p);
     p += round_up(np * np * 8, 256);
-    w.P = reinterpret_cast<double*>(p);
-    p += round_up(np * NB * 8, 256);
+    w.P = reinterpret_cast<double*>(p);  // two panel buffers
+    p += 2 * round_up(np * NB * 8, 256);
     w.scal = reinterpret_cast<double*>(p);
     p += 256;
     w.fail = reinterpret_cast<int*>(p);
@@ -130,20 +130,17 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(const float* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Diagonal block k: Cholesky factor L_kk and its inverse M = L_kk^-1 in one
-// workgroup, as Gauss-Jordan elimination of [A | I] with symmetric pivots.
-// Pivot c with p = A_cc uses the raw vectors
-//     a_i = A_ic for i > c, 0 otherwise          (column c of A)
-//     b_j = B_cj for j <= c, 0 otherwise         (row c of B)
-// and every thread updates its own entries with no case split:
-//     A_ij -= (a_i / p) a_j        B_ij -= (a_i / p) b_j
-// (the zeros leave finished rows and unreached columns untouched); then the
-// owners of column c store L_ic = a_i / sqrt(p), L_cc = sqrt(p), and the
-// owners of row c store M_cj = b_j / sqrt(p).  The owners of column c+1 and
-// row c+1 publish the next raw vectors and pivot into the other LDS buffer
-// right after their update, so one barrier per pivot suffices.
-// 512 threads; thread t owns rows 2(t/16)..+1, columns 4(t%16)..+3 of both
-// A and B in registers.
+// Diagonal block k: M = L_kk^-1 where A = L_kk L_kk^T is the 64x64 block,
+// by the same blocked route one level down, on 16x16 sub-blocks in LDS.
+// Sub-step s (columns 16s .. 16s+15):
+//   1. one wave inverts the Cholesky factor of the sub-block A_ss by
+//      Gauss-Jordan elimination in registers (gj16 below): Ls = L_ss^-1;
+//   2. P_i = A_is Ls^T for sub-blocks i > s, and M_sj = Ls A_sj in place for
+//      j < s (one 16x16x16 MFMA product per wave);
+//   3. A_ij -= P_i P_j^T (s < j <= i), A_is = -P_i Ls, A_ij -= P_i M_sj
+//      (j < s), for every i > s.
+// Only lower-triangle entries are read; the block returned holds exact
+// zeros above the diagonal.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ double rsqrt_f64(double x) {
     double y = __builtin_amdgcn_rsq(x);
@@ -152,111 +149,208 @@ __device__ __forceinline__ double rsqrt_f64(double x) {
     return y;
 }
 
-struct DiagVec {
-    double a[2][NB];
-    double b[2][NB];
-    double piv[2];
+constexpr int kSb = 16;           // sub-block width
+constexpr int kDLd = NB + 1;      // padded LDS row (doubles)
+
+struct DiagLds {
+    double g[NB][kDLd];           // the block: Schur complement, then the inverse
+    double p[3][kSb][kSb + 1];    // P_i of the current sub-step
+    int status;
 };
 
-// publish the raw vectors of pivot c (into buffer c & 1) from registers
-template <int CC>
-__device__ __forceinline__ void diag_publish(int c, int a, int b, const double (&g)[2][4], const double (&m)[2][4],
-                                             DiagVec& v) {
-    constexpr int CR = CC & 1;
-    const int buf = c & 1;
-    if (b == (c >> 2)) {
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int i = 2 * a + r;
-            v.a[buf][i] = (i > c) ? g[r][CC] : 0.0;
-            if (i == c) v.piv[buf] = g[r][CC];
-        }
-    }
-    if (a == (c >> 1)) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int j = 4 * b + q;
-            v.b[buf][j] = (j <= c) ? m[CR][q] : 0.0;
-        }
-    }
+// Lane-crossing moves of a double within one wave (no LDS):
+//   bcast_in_row<N>: lane N of each 16-lane row, to the whole row (DPP
+//     row_newbcast);
+//   bcast_row<R>: row R (lanes 16R .. 16R+15), to all four rows, lane
+//     position kept (permlane16 then permlane32 swap);
+//   read_lane: one lane's value, uniform.
+__device__ __forceinline__ uint32_t lo32(double x) { return (uint32_t)__builtin_bit_cast(uint64_t, x); }
+__device__ __forceinline__ uint32_t hi32(double x) { return (uint32_t)(__builtin_bit_cast(uint64_t, x) >> 32); }
+__device__ __forceinline__ double join64(uint32_t lo, uint32_t hi) {
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+template <int N>
+__device__ __forceinline__ double bcast_in_row(double x) {
+    const uint32_t lo = __builtin_amdgcn_mov_dpp((int)lo32(x), 0x150 + N, 0xF, 0xF, false);
+    const uint32_t hi = __builtin_amdgcn_mov_dpp((int)hi32(x), 0x150 + N, 0xF, 0xF, false);
+    return join64(lo, hi);
+}
+template <int R>
+__device__ __forceinline__ uint32_t bcast_row32(uint32_t v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);  // {rows 0,0,2,2}, {rows 1,1,3,3}
+    const uint32_t y = (R & 1) ? a[1] : a[0];
+    const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);  // {low half twice}, {high half twice}
+    return (R & 2) ? b[1] : b[0];
+}
+template <int R>
+__device__ __forceinline__ double bcast_row(double x) {
+    return join64(bcast_row32<R>(lo32(x)), bcast_row32<R>(hi32(x)));
+}
+__device__ __forceinline__ double read_lane(double x, int l) {
+    return join64((uint32_t)__builtin_amdgcn_readlane((int)lo32(x), l), (uint32_t)__builtin_amdgcn_readlane((int)hi32(x), l));
 }
 
-template <int CC>
-__device__ __forceinline__ bool diag_pivot(int c, int a, int b, double (&g)[2][4], double (&m)[2][4], DiagVec& v) {
-    constexpr int CR = CC & 1;
-    const int buf = c & 1;
-    const double pv = v.piv[buf];
-    if (!(pv > 0.0)) return false;  // uniform: every thread reads the same value
-    const double rs = rsqrt_f64(pv);
+// Pivot C of the 16x16 elimination [A | I] -> [* | Ls] in one wave, raw
+// symmetric form: t_r = A_rC / p for r > C (0 otherwise); A_rj -= t_r A_Cj
+// for j > C; B_rj -= t_r B_Cj for j <= C; then row C of B is scaled by
+// 1/sqrt(p).  Lane (g = lane/16, j = lane%16) holds A[4g+e][j] and
+// B[4g+e][j], e = 0..3.  `first` records 1 + the first pivot that is not
+// positive (the elimination then runs on without effect on the result).
+template <int C>
+__device__ __forceinline__ void gj_step(int g, int j, double (&a)[4], double (&b)[4], int& first) {
+    constexpr int R = C >> 2, S = C & 3;
+    const double p = read_lane(a[S], kSb * R + C);
+    if (!(p > 0.0) && first == 0) first = C + 1;
+    const double rs = rsqrt_f64(p);
     const double inv = rs * rs;
-    double ti[2], aj[4], bj[4];
+    const double ar = bcast_row<R>(a[S]);  // A[C][j]
+    const double br = bcast_row<R>(b[S]);  // B[C][j]
+    const double aj = (j > C) ? ar : 0.0;
+    const double bj = (j <= C) ? br : 0.0;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) ti[r] = v.a[buf][2 * a + r] * inv;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        aj[q] = v.a[buf][4 * b + q];
-        bj[q] = v.b[buf][4 * b + q];
+    for (int e = 0; e < 4; ++e) {
+        const double v = bcast_in_row<C>(a[e]);  // A[4g+e][C]
+        const double t = (4 * g + e > C) ? v * inv : 0.0;
+        a[e] = fma(-t, aj, a[e]);
+        b[e] = fma(-t, bj, b[e]);
     }
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            g[r][q] = fma(-ti[r], aj[q], g[r][q]);
-            m[r][q] = fma(-ti[r], bj[q], m[r][q]);
-        }
-    if (b == (c >> 2)) {  // column c of L
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int i = 2 * a + r;
-            g[r][CC] = (i > c) ? g[r][CC] * rs : ((i == c) ? pv * rs : g[r][CC]);
-        }
-    }
-    if (a == (c >> 1)) {  // row c of M
-#pragma unroll
-        for (int q = 0; q < 4; ++q) m[CR][q] *= rs;
-    }
-    if (c + 1 < NB) diag_publish<(CC + 1) & 3>(c + 1, a, b, g, m, v);
-    __syncthreads();
-    return true;
+    if (g == R) b[S] *= rs;
 }
 
-__global__ __launch_bounds__(512) void chol_diag_kernel(double* __restrict__ G, int64_t np, int k,
+// Sub-block s of L.g (one wave): Ls = inverse of its Cholesky factor,
+// written in place.  Returns 0, or 1 + the local column of the first pivot
+// that is not positive (wave-uniform).
+__device__ __forceinline__ int gj16(DiagLds& L, int s, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    const int o = kSb * s;
+    double a[4], b[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        a[e] = (r >= j) ? L.g[o + r][o + j] : L.g[o + j][o + r];  // symmetric from the lower triangle
+        b[e] = (r == j) ? 1.0 : 0.0;
+    }
+    int first = 0;
+    gj_step<0>(g, j, a, b, first);
+    gj_step<1>(g, j, a, b, first);
+    gj_step<2>(g, j, a, b, first);
+    gj_step<3>(g, j, a, b, first);
+    gj_step<4>(g, j, a, b, first);
+    gj_step<5>(g, j, a, b, first);
+    gj_step<6>(g, j, a, b, first);
+    gj_step<7>(g, j, a, b, first);
+    gj_step<8>(g, j, a, b, first);
+    gj_step<9>(g, j, a, b, first);
+    gj_step<10>(g, j, a, b, first);
+    gj_step<11>(g, j, a, b, first);
+    gj_step<12>(g, j, a, b, first);
+    gj_step<13>(g, j, a, b, first);
+    gj_step<14>(g, j, a, b, first);
+    gj_step<15>(g, j, a, b, first);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) L.g[o + 4 * g + e][o + j] = b[e];
+    return first;
+}
+
+// 16x16x16 product on MFMA 16x16x4 f64: acc = X Y with X[i][k] = fx(i, k),
+// Y[k][j] = fy(k, j); lane l gets C[4v + l/16][l%16] in acc[v].
+template <typename FX, typename FY>
+__device__ __forceinline__ double4v mm16(FX fx, FY fy, int lane) {
+    double4v acc = {};
+#pragma unroll
+    for (int kk = 0; kk < kSb; kk += 4) {
+        const int k = kk + (lane >> 4);
+        acc = mfma16x16x4_f64(fx(lane & 15, k), fy(k, lane & 15), acc);
+    }
+    return acc;
+}
+
+// Factor and invert the block held in L.g (256 threads).  Returns 0 or
+// 1 + the local column of the first pivot that is not positive
+// (block-uniform).
+__device__ int diag64(DiagLds& L) {
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    for (int s = 0; s < NB / kSb; ++s) {
+        const int o = kSb * s;
+        if (w == 0) {
+            const int st = gj16(L, s, lane);
+            if (lane == 0) L.status = st;
+        }
+        __syncthreads();
+        const int st = L.status;
+        if (st) return o + st;
+        // 2. panel: waves 0..2 take one tile each
+        if (w < 3) {
+            const int np_ = NB / kSb - 1 - s;  // number of P tiles
+            if (w < np_) {
+                const int i = s + 1 + w;
+                const double4v acc = mm16([&](int a, int k) { return L.g[kSb * i + a][o + k]; },
+                                          [&](int k, int b) { return L.g[o + b][o + k]; }, lane);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) L.p[w][4 * v + (lane >> 4)][lane & 15] = acc[v];
+            } else {
+                const int j = w - np_;
+                const double4v acc = mm16([&](int a, int k) { return L.g[o + a][o + k]; },
+                                          [&](int k, int b) { return L.g[o + k][kSb * j + b]; }, lane);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) L.g[o + 4 * v + (lane >> 4)][kSb * j + (lane & 15)] = acc[v];
+            }
+        }
+        __syncthreads();
+        // 3. update of every tile (i, j), i > s, j <= i
+        int t = 0;
+        for (int i = s + 1; i < NB / kSb; ++i) {
+            for (int j = 0; j <= i; ++j, ++t) {
+                if ((t & 3) != w) continue;
+                const int pi = i - s - 1;
+                double4v acc;
+                if (j > s) {
+                    const int pj = j - s - 1;
+                    acc = mm16([&](int a, int k) { return L.p[pi][a][k]; },
+                               [&](int k, int b) { return L.p[pj][b][k]; }, lane);
+                } else {
+                    acc = mm16([&](int a, int k) { return L.p[pi][a][k]; },
+                               [&](int k, int b) { return L.g[o + k][kSb * j + b]; }, lane);
+                }
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    double& d = L.g[kSb * i + 4 * v + (lane >> 4)][kSb * j + (lane & 15)];
+                    d = (j == s) ? -acc[v] : d - acc[v];
+                }
+            }
+        }
+        __syncthreads();
+    }
+    return 0;
+}
+
+__global__ __launch_bounds__(256) void chol_diag_kernel(double* __restrict__ G, int64_t np, int k,
                                                         int32_t* __restrict__ info, int* __restrict__ fail) {
-    __shared__ __align__(16) DiagVec v;
+    __shared__ __align__(16) DiagLds L;
     if (*fail) return;
     const int tid = threadIdx.x;
-    const int a = tid >> 4, b = tid & 15;  // rows 2a, 2a+1; columns 4b .. 4b+3
     double* blk = G + (int64_t)k * NB * np + (int64_t)k * NB;
-    double g[2][4], m[2][4];
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            g[r][c] = blk[(int64_t)(2 * a + r) * np + 4 * b + c];
-            m[r][c] = (2 * a + r == 4 * b + c) ? 1.0 : 0.0;
-        }
-    diag_publish<0>(0, a, b, g, m, v);
-    __syncthreads();
-
-    int failed_at = -1;
-    for (int c0 = 0; c0 < NB; c0 += 4) {
-        if (!diag_pivot<0>(c0 + 0, a, b, g, m, v)) { failed_at = c0 + 0; break; }
-        if (!diag_pivot<1>(c0 + 1, a, b, g, m, v)) { failed_at = c0 + 1; break; }
-        if (!diag_pivot<2>(c0 + 2, a, b, g, m, v)) { failed_at = c0 + 2; break; }
-        if (!diag_pivot<3>(c0 + 3, a, b, g, m, v)) { failed_at = c0 + 3; break; }
+    for (int m = 0; m < NB * NB / 256; ++m) {
+        const int idx = tid + 256 * m;
+        L.g[idx >> 6][idx & 63] = blk[(int64_t)(idx >> 6) * np + (idx & 63)];
     }
-    if (failed_at >= 0) {
+    __syncthreads();
+    const int st = diag64(L);
+    if (st) {
         if (tid == 0) {
-            *info = k * NB + failed_at + 1;
+            *info = k * NB + st;
             *fail = 1;
         }
         return;
     }
-    // write back M = L^-1 (exactly zero above the diagonal)
+    // write back M = L^-1 with exact zeros above the diagonal
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) blk[(int64_t)(2 * a + r) * np + 4 * b + q] = m[r][q];
+    for (int m = 0; m < NB * NB / 256; ++m) {
+        const int idx = tid + 256 * m;
+        const int r = idx >> 6, c = idx & 63;
+        blk[(int64_t)r * np + c] = (c <= r) ? L.g[r][c] : 0.0;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -390,15 +484,53 @@ __global__ __launch_bounds__(kGemmThreads) void chol_panel_kernel(double* __rest
     }
 }
 
-// Update of step k over blocks (i, j), k < i, j <= i.
+// Tile sets of the update of step k (blocks (i, j) with k < i, j <= i):
+//   kSetAll   every block;
+//   kSetNext  the blocks step k+1 reads first: column block k+1 (i >= k+1)
+//             and row block k+1 (j <= k), T blocks in all;
+//   kSetRest  the others: i > k+1, j <= i, j != k+1.
+enum { kSetAll = 0, kSetNext = 1, kSetRest = 2 };
+
+__host__ __device__ inline int64_t tiles_in_set(int set, int k, int T) {
+    const int64_t all = (int64_t)T * (T + 1) / 2 - (int64_t)(k + 1) * (k + 2) / 2;
+    if (set == kSetAll) return all;
+    const int64_t next = (k + 1 < T) ? T : 0;
+    return set == kSetNext ? next : all - next;
+}
+
+__device__ __forceinline__ void set_tile(int set, int k, int T, int64_t b, int64_t& i, int64_t& j) {
+    if (set == kSetAll) {
+        tri_index((int64_t)(k + 1) * (k + 2) / 2 + b, i, j);
+    } else if (set == kSetNext) {
+        const int64_t ncol = T - (k + 1);  // column block k+1, rows k+1 .. T-1
+        if (b < ncol) {
+            i = k + 1 + b;
+            j = k + 1;
+        } else {
+            i = k + 1;
+            j = b - ncol;
+        }
+    } else {
+        // rows i >= k+2 hold i blocks each (j in 0..i without k+1); rows
+        // before i contribute i(i-1)/2 - (k+1)(k+2)/2 blocks
+        const int64_t c0 = (int64_t)(k + 1) * (k + 2) / 2;
+        int64_t r = (int64_t)((1.0 + sqrt(1.0 + 8.0 * (double)(b + c0))) * 0.5);
+        while (r * (r - 1) / 2 - c0 > b) --r;
+        while ((r + 1) * r / 2 - c0 <= b) ++r;
+        i = r;
+        const int64_t jj = b - (r * (r - 1) / 2 - c0);
+        j = (jj < k + 1) ? jj : jj + 1;
+    }
+}
+
+// Update of step k over the blocks of one tile set.
 __global__ __launch_bounds__(kGemmThreads) void chol_trail_kernel(double* __restrict__ G, int64_t np,
-                                                                  const double* __restrict__ P, int k,
-                                                                  const int* __restrict__ fail) {
+                                                                  const double* __restrict__ P, int k, int T,
+                                                                  int set, const int* __restrict__ fail) {
     __shared__ GemmLds s;
     if (*fail) return;
-    const int64_t base = (int64_t)(k + 1) * (k + 2) / 2;
     int64_t i, j;
-    tri_index(base + blockIdx.x, i, j);
+    set_tile(set, k, T, blockIdx.x, i, j);
     const double* Pi = P + i * NB * NB;
     double* Gij = G + i * NB * np + j * NB;
     double4v acc[2][2];
@@ -429,15 +561,28 @@ __global__ __launch_bounds__(256) void store_u_kernel(const double* __restrict__
 
 size_t hinv_workspace_bytes(int64_t n) {
     const int64_t np = round_up(n, NB);
-    return (size_t)(round_up(np * np * 8, 256) + round_up(np * NB * 8, 256) + 256 + 256);
+    return (size_t)(round_up(np * np * 8, 256) + 2 * round_up(np * NB * 8, 256) + 256 + 256);
 }
 
+
+// Schedule with one step of lookahead.  After the panel of step k, the
+// update of step k is split: the blocks step k+1 needs first (column and row
+// block k+1) run on the caller's stream and are followed at once by the
+// diagonal block and panel of step k+1, while the remaining blocks of step k
+// run concurrently on a side stream.  The next early update waits for them
+// (it touches blocks they update).  The panel buffer alternates between
+// steps because the side stream still reads panel k while panel k+1 is
+// formed.  Everything is joined back into the caller's stream.
 hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, float* U, uint8_t* dead,
                                int32_t* info, double* lambda_out, void* ws, hipStream_t s) {
     if (n == 0) return hipSuccess;
     HinvWs w = carve(ws, n);
     const int64_t np = round_up(n, NB);
     const int T = (int)(np / NB);
+    double* Pbuf[2] = {w.P, w.P + round_up(np * NB * 8, 256) / 8};
+    SideStream* ss = nullptr;
+    hipError_t e = side_stream(ss);
+    if (e != hipSuccess) return e;
     {
         TimedLaunch t(K_HINV_DIAGSUM, s);
         hipLaunchKernelGGL(diag_stats_kernel, dim3(1), dim3(1024), 0, s, H, n, damp_frac, dead, w.scal, lambda_out,
@@ -448,22 +593,39 @@ hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, floa
         hipLaunchKernelGGL(load_reversed_kernel, dim3((unsigned)((int64_t)T * (T + 1) / 2)), dim3(256), 0, s, H, n,
                            np, (const double*)w.scal, w.G);
     }
-    for (int k = 0; k < T; ++k) {
+    auto diag_and_panel = [&](int k) {
         {
             TimedLaunch t(K_CHOL_DIAG, s);
-            hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(512), 0, s, w.G, np, k, info, w.fail);
+            hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, s, w.G, np, k, info, w.fail);
         }
         if (T > 1) {
             TimedLaunch t(K_CHOL_PANEL, s);
-            hipLaunchKernelGGL(chol_panel_kernel, dim3(T - 1), dim3(kGemmThreads), 0, s, w.G, np, w.P, k,
+            hipLaunchKernelGGL(chol_panel_kernel, dim3(T - 1), dim3(kGemmThreads), 0, s, w.G, np, Pbuf[k & 1], k,
                                (const int*)w.fail);
         }
-        const int64_t tiles = (int64_t)T * (T + 1) / 2 - (int64_t)(k + 1) * (k + 2) / 2;
-        if (tiles > 0) {
-            TimedLaunch t(K_CHOL_TRAIL, s);
-            hipLaunchKernelGGL(chol_trail_kernel, dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, w.G, np,
-                               (const double*)w.P, k, (const int*)w.fail);
+    };
+    diag_and_panel(0);
+    for (int k = 0; k < T; ++k) {
+        const double* Pk = Pbuf[k & 1];
+        const int64_t n_rest = tiles_in_set(kSetRest, k, T);
+        const int64_t n_next = tiles_in_set(kSetNext, k, T);
+        if (n_rest > 0) {
+            if ((e = hipEventRecord(ss->fork, s)) != hipSuccess) return e;
+            if ((e = hipStreamWaitEvent(ss->side, ss->fork, 0)) != hipSuccess) return e;
+            {
+                TimedLaunch t(K_CHOL_TRAIL, ss->side);
+                hipLaunchKernelGGL(chol_trail_kernel, dim3((unsigned)n_rest), dim3(kGemmThreads), 0, ss->side, w.G,
+                                   np, Pk, k, T, (int)kSetRest, (const int*)w.fail);
+            }
+            if ((e = hipEventRecord(ss->join, ss->side)) != hipSuccess) return e;
         }
+        if (n_next > 0) {
+            TimedLaunch t(K_CHOL_TRAIL, s);
+            hipLaunchKernelGGL(chol_trail_kernel, dim3((unsigned)n_next), dim3(kGemmThreads), 0, s, w.G, np, Pk, k,
+                               T, (int)kSetNext, (const int*)w.fail);
+        }
+        if (k + 1 < T) diag_and_panel(k + 1);
+        if (n_rest > 0 && (e = hipStreamWaitEvent(s, ss->join, 0)) != hipSuccess) return e;
     }
     {
         TimedLaunch t(K_HINV_STORE, s);

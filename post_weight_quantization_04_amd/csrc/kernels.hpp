@@ -35,6 +35,16 @@ struct TimedLaunch {
     hipStream_t stream;
 };
 
+// Per-device side stream with fork/join events, used by the lookahead
+// schedules (created once at default priority; host-side state, not
+// thread-safe).
+struct SideStream {
+    hipStream_t side = nullptr;
+    hipEvent_t fork = nullptr;  // recorded on the caller's stream, waited on by the side stream
+    hipEvent_t join = nullptr;  // recorded on the side stream, waited on by the caller's stream
+};
+hipError_t side_stream(SideStream*& out);
+
 // ---- stage 1 ---------------------------------------------------------------
 hipError_t launch_hessian(float* H, int64_t n, const void* X, int x_is_f16, int64_t ntok,
                           int64_t ldx, hipStream_t s);

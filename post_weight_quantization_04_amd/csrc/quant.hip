@@ -34,7 +34,7 @@ __host__ __device__ inline int64_t rup(int64_t a, int64_t b) { return (a + b - 1
 
 struct QuantWs {
     float* Wk;     // [d_out, d_in] working weights
-    float* E;      // [d_out, block] scaled errors of the current block
+    float* E[2];   // [d_out, block] scaled errors, alternating between blocks
     float* rdiag;  // [d_in] 1 / U_jj
 };
 
@@ -43,8 +43,10 @@ QuantWs carve(void* ws, int64_t d_out, int64_t d_in, int64_t block) {
     QuantWs w;
     w.Wk = reinterpret_cast<float*>(p);
     p += rup(d_out * d_in * 4, 256);
-    w.E = reinterpret_cast<float*>(p);
-    p += rup(d_out * block * 4, 256);
+    for (int i = 0; i < 2; ++i) {
+        w.E[i] = reinterpret_cast<float*>(p);
+        p += rup(d_out * block * 4, 256);
+    }
     w.rdiag = reinterpret_cast<float*>(p);
     return w;
 }
@@ -376,7 +378,7 @@ struct TrailRegs {
 template <bool kVec>
 __device__ __forceinline__ void trail_fetch(TrailRegs<kVec>& r, const float* __restrict__ E, int64_t ldE,
                                             const float* __restrict__ U, int64_t d_out, int64_t d_in, int64_t r0,
-                                            int64_t c0, int64_t b0, int K, int kc, int tid) {
+                                            int64_t c0, int64_t b0, int K, int kc, int tid, int64_t c_end) {
     {
         const int64_t R = r0 + (tid >> 1);
         const int k = kc + (tid & 1) * 16;
@@ -393,12 +395,12 @@ __device__ __forceinline__ void trail_fetch(TrailRegs<kVec>& r, const float* __r
         const int k = kc + (tid >> 3);
         const int64_t col = c0 + (tid & 7) * 16;
         const float* src = U + (b0 + k) * d_in + col;
-        if (kVec && k < K && col + 16 <= d_in) {
+        if (kVec && k < K && col + 16 <= c_end) {
 #pragma unroll
             for (int e = 0; e < 16; e += 4) *reinterpret_cast<float4v*>(&r.u[e]) = *reinterpret_cast<const float4v*>(src + e);
         } else {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) r.u[e] = (k < K && col + e < d_in) ? src[e] : 0.0f;
+            for (int e = 0; e < 16; ++e) r.u[e] = (k < K && col + e < c_end) ? src[e] : 0.0f;
         }
     }
 }
@@ -416,12 +418,13 @@ __device__ __forceinline__ void trail_stash(const TrailRegs<kVec>& r, TrailLds& 
 template <bool kVec>
 __global__ __launch_bounds__(256) void trail_kernel(float* __restrict__ Wk, int64_t d_out, int64_t d_in,
                                                     const float* __restrict__ E, int64_t ldE,
-                                                    const float* __restrict__ U, int64_t b0, int64_t b1) {
+                                                    const float* __restrict__ U, int64_t b0, int64_t b1,
+                                                    int64_t c_begin, int64_t c_end) {
     __shared__ TrailLds s;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wi = w >> 1, wj = w & 1;
     const int64_t r0 = (int64_t)blockIdx.y * kTT;
-    const int64_t c0 = b1 + (int64_t)blockIdx.x * kTT;
+    const int64_t c0 = c_begin + (int64_t)blockIdx.x * kTT;
     const int K = (int)(b1 - b0);
     const int nchunks = (K + kTK - 1) / kTK;
 
@@ -432,12 +435,12 @@ __global__ __launch_bounds__(256) void trail_kernel(float* __restrict__ Wk, int6
         for (int q = 0; q < 2; ++q) acc[m][q] = (float16v){};
 
     TrailRegs<kVec> regs;
-    trail_fetch<kVec>(regs, E, ldE, U, d_out, d_in, r0, c0, b0, K, 0, tid);
+    trail_fetch<kVec>(regs, E, ldE, U, d_out, d_in, r0, c0, b0, K, 0, tid, c_end);
     for (int c = 0; c < nchunks; ++c) {
         const int buf = c & 1;
         trail_stash<kVec>(regs, s, buf, tid);
         __syncthreads();
-        if (c + 1 < nchunks) trail_fetch<kVec>(regs, E, ldE, U, d_out, d_in, r0, c0, b0, K, (c + 1) * kTK, tid);
+        if (c + 1 < nchunks) trail_fetch<kVec>(regs, E, ldE, U, d_out, d_in, r0, c0, b0, K, (c + 1) * kTK, tid, c_end);
         const float* Es = s.E[buf];
         const float* Us = s.U[buf];
 #pragma unroll
@@ -461,7 +464,7 @@ __global__ __launch_bounds__(256) void trail_kernel(float* __restrict__ Wk, int6
             for (int v = 0; v < 16; ++v) {
                 const int64_t row = r0 + wi * 64 + 32 * m + acc32_row(v, lane);
                 const int64_t col = c0 + wj * 64 + 32 * q + (lane & 31);
-                if (row < d_out && col < d_in) {
+                if (row < d_out && col < c_end) {
                     float* p = Wk + row * d_in + col;
                     *p = *p - acc[m][q][v];
                 }
@@ -471,7 +474,7 @@ __global__ __launch_bounds__(256) void trail_kernel(float* __restrict__ Wk, int6
 }  // namespace
 
 size_t quant_workspace_bytes(int64_t d_out, int64_t d_in, int64_t block) {
-    return (size_t)(rup(d_out * d_in * 4, 256) + rup(d_out * block * 4, 256) + rup(d_in * 4, 256));
+    return (size_t)(rup(d_out * d_in * 4, 256) + 2 * rup(d_out * block * 4, 256) + rup(d_in * 4, 256));
 }
 
 hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d_in, const float* U,
@@ -518,11 +521,42 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
         }
     }
     const unsigned row_tiles = (unsigned)((d_out + kRowsPerWg - 1) / kRowsPerWg);
-    for (int64_t b0 = 0; b0 < d_in; b0 += block) {
+    SideStream* ss = nullptr;
+    hipError_t err = side_stream(ss);
+    if (err != hipSuccess) return err;
+    auto trail = [&](hipStream_t st, int64_t b0, int64_t b1, const float* Eb, int64_t cb, int64_t ce) {
+        if (ce <= cb) return;
+        TimedLaunch t(K_Q_TRAIL, st);
+        dim3 grid((unsigned)((ce - cb + kTT - 1) / kTT), (unsigned)((d_out + kTT - 1) / kTT));
+        if (vec)
+            hipLaunchKernelGGL(trail_kernel<true>, grid, dim3(256), 0, st, w.Wk, d_out, d_in, Eb, block, U, b0, b1, cb,
+                               ce);
+        else
+            hipLaunchKernelGGL(trail_kernel<false>, grid, dim3(256), 0, st, w.Wk, d_out, d_in, Eb, block, U, b0, b1,
+                               cb, ce);
+    };
+    // Lookahead: after the sweep of block b, the columns of block b+1 receive
+    // its update on the caller's stream and the next sweep starts at once,
+    // while the columns after block b+1 are updated on the side stream.  The
+    // caller's stream waits for that side update before it forks the next
+    // one (the next early update touches those columns), and the
+    // scaled-error buffer alternates so that sweep b+1 can write its errors
+    // while the side update of block b still reads them.
+    bool rest_pending = false;
+    auto join_rest = [&]() -> hipError_t {
+        if (!rest_pending) return hipSuccess;
+        rest_pending = false;
+        return hipStreamWaitEvent(s, ss->join, 0);
+    };
+    int bi = 0;
+    for (int64_t b0 = 0; b0 < d_in; b0 += block, ++bi) {
         const int64_t b1 = std::min(b0 + block, d_in);
         const int bw = (int)(b1 - b0);
         const int nw = (bw + kSub - 1) / kSub;
+        float* Eb = w.E[bi & 1];
         if (group > block && b0 % group == 0) {
+            // the grid spans later blocks: it needs every earlier update
+            if ((err = join_rest()) != hipSuccess) return err;
             TimedLaunch t(K_Q_GROUPGRID, s);
             hipLaunchKernelGGL(group_grid_kernel, dim3(rows4), dim3(256), 0, s, (const float*)w.Wk, d_out, d_in, b0,
                                group, b0 / group, ng, maxq, scales, zeros, minmax);
@@ -531,20 +565,22 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
             TimedLaunch t(K_Q_SWEEP, s);
             const size_t lds = sweep_lds_bytes(bw);
             hipLaunchKernelGGL(sweep_kernel, dim3(row_tiles), dim3(64 * nw), lds, s, (const float*)w.Wk, d_out, d_in, U,
-                               (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes, w.E,
+                               (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes, Eb,
                                block, err_row);
         }
-        if (b1 < d_in) {
-            TimedLaunch t(K_Q_TRAIL, s);
-            dim3 grid((unsigned)((d_in - b1 + kTT - 1) / kTT), (unsigned)((d_out + kTT - 1) / kTT));
-            if (vec)
-                hipLaunchKernelGGL(trail_kernel<true>, grid, dim3(256), 0, s, w.Wk, d_out, d_in, (const float*)w.E,
-                                   block, U, b0, b1);
-            else
-                hipLaunchKernelGGL(trail_kernel<false>, grid, dim3(256), 0, s, w.Wk, d_out, d_in, (const float*)w.E,
-                                   block, U, b0, b1);
+        if (b1 >= d_in) break;
+        if ((err = join_rest()) != hipSuccess) return err;
+        const int64_t next_end = std::min(b1 + block, d_in);
+        if (next_end < d_in) {
+            if ((err = hipEventRecord(ss->fork, s)) != hipSuccess) return err;
+            if ((err = hipStreamWaitEvent(ss->side, ss->fork, 0)) != hipSuccess) return err;
+            trail(ss->side, b0, b1, Eb, next_end, d_in);
+            if ((err = hipEventRecord(ss->join, ss->side)) != hipSuccess) return err;
+            rest_pending = true;
         }
+        trail(s, b0, b1, Eb, b1, next_end);
     }
+    if ((err = join_rest()) != hipSuccess) return err;
     return hipGetLastError();
 }
 
