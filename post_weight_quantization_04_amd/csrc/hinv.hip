@@ -27,7 +27,6 @@ namespace {
 
 constexpr int NB = kCholNB;  // 64
 constexpr int kGemmThreads = 256;
-constexpr int kKc = 32;        // k per LDS stage of the tile GEMM
 constexpr int kLdsLd = NB + 8;   // padded LDS row (doubles)
 
 struct HinvWs {
@@ -357,50 +356,71 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(double* __restrict__ G, 
 // 64x64x64 float64 tile product on MFMA 16x16x4 f64:  acc += A B.
 // A is given row-major [64 rows][64 k] (lda); B is row-major [64 k][64 cols]
 // (ldb) or, with kBT, its transpose given row-major [64 cols][64 k].
-// Four waves in a 2x2 grid, each 32x32 as 2x2 MFMA tiles.  K runs in two
-// chunks of 32: chunk 1 is fetched into registers while the MFMAs consume
-// chunk 0 (two LDS buffers, one barrier per chunk).
+// All of K is fetched into registers at once (16 doubles of A and of B per
+// thread, every load in flight together), staged in LDS k-major, and the
+// four waves (2x2 grid, 32x32 each as 2x2 MFMA tiles) run 16 k-steps after
+// one barrier.  A direct B is staged with its columns XOR-swizzled by the k
+// row (low four bits) so that the staging writes spread over the banks;
+// the reads undo the swizzle.
 // ---------------------------------------------------------------------------
 struct GemmLds {
-    double A[2][kKc][kLdsLd];
-    double B[2][kKc][kLdsLd];
+    double A[NB][kLdsLd];  // [k][row]
+    double B[NB][kLdsLd];  // [k][col] (swizzled when B is given direct)
 };
 
-template <bool kBT>
 struct GemmRegs {
-    double a[8];
-    double b[8];
+    double a[16];
+    double b[16];
 };
 
-// thread -> A^T: row tid&63, k run (tid>>6)*8 ; B direct: k row tid>>3, cols (tid&7)*8 ;
-// B^T: col tid&63, k run (tid>>6)*8
+__device__ __forceinline__ int swz(int k, int col) { return col ^ (k & 15); }
+
+// A^T: row tid&63, k run (tid>>6)*16 ; B direct: k row tid>>2, cols (tid&3)*16 ;
+// B^T: col tid&63, k run (tid>>6)*16
 template <bool kBT>
-__device__ __forceinline__ void gemm_fetch(GemmRegs<kBT>& r, const double* __restrict__ A, int64_t lda,
-                                           const double* __restrict__ B, int64_t ldb, int k0, int tid) {
-    const double* sa = A + (int64_t)(tid & 63) * lda + k0 + (tid >> 6) * 8;
+__device__ __forceinline__ void gemm_fetch(GemmRegs& r, const double* __restrict__ A, int64_t lda,
+                                           const double* __restrict__ B, int64_t ldb, int tid) {
+    const double* sa = A + (int64_t)(tid & 63) * lda + (tid >> 6) * 16;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r.a[e] = sa[e];
+    for (int e = 0; e < 16; ++e) r.a[e] = sa[e];
+    const double* sb = kBT ? B + (int64_t)(tid & 63) * ldb + (tid >> 6) * 16 : B + (int64_t)(tid >> 2) * ldb + (tid & 3) * 16;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) r.b[e] = sb[e];
+}
+
+template <bool kBT>
+__device__ __forceinline__ void gemm_stash(const GemmRegs& r, GemmLds& s, int tid) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s.A[(tid >> 6) * 16 + e][tid & 63] = r.a[e];
     if (kBT) {
-        const double* sb = B + (int64_t)(tid & 63) * ldb + k0 + (tid >> 6) * 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) r.b[e] = sb[e];
+        for (int e = 0; e < 16; ++e) s.B[(tid >> 6) * 16 + e][tid & 63] = r.b[e];
     } else {
-        const double* sb = B + (int64_t)(k0 + (tid >> 3)) * ldb + (tid & 7) * 8;
+        const int k = tid >> 2;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) r.b[e] = sb[e];
+        for (int e = 0; e < 16; ++e) s.B[k][swz(k, (tid & 3) * 16 + e)] = r.b[e];
     }
 }
 
 template <bool kBT>
-__device__ __forceinline__ void gemm_stash(const GemmRegs<kBT>& r, GemmLds& s, int buf, int tid) {
+__device__ __forceinline__ void gemm_compute(const GemmLds& s, double4v (&acc)[2][2]) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wi = w >> 1, wj = w & 1;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s.A[buf][(tid >> 6) * 8 + e][tid & 63] = r.a[e];
-    if (kBT) {
+    for (int ks = 0; ks < NB; ks += 4) {
+        const int k = ks + (lane >> 4);
+        double av[2], bv[2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s.B[buf][(tid >> 6) * 8 + e][tid & 63] = r.b[e];
-    } else {
+        for (int m = 0; m < 2; ++m) av[m] = s.A[k][wi * 32 + 16 * m + (lane & 15)];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s.B[buf][tid >> 3][(tid & 7) * 8 + e] = r.b[e];
+        for (int q = 0; q < 2; ++q) {
+            const int col = wj * 32 + 16 * q + (lane & 15);
+            bv[q] = s.B[k][kBT ? col : swz(k, col)];
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) acc[m][q] = mfma16x16x4_f64(av[m], bv[q], acc[m][q]);
     }
 }
 
@@ -408,49 +428,65 @@ template <bool kBT>
 __device__ __forceinline__ void tile_gemm_f64(const double* __restrict__ A, int64_t lda,
                                               const double* __restrict__ B, int64_t ldb, GemmLds& s,
                                               double4v (&acc)[2][2]) {
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wi = w >> 1, wj = w & 1;
-    GemmRegs<kBT> regs;
-    gemm_fetch<kBT>(regs, A, lda, B, ldb, 0, tid);
-    constexpr int nch = NB / kKc;
-#pragma unroll
-    for (int c = 0; c < nch; ++c) {
-        const int buf = c & 1;
-        gemm_stash<kBT>(regs, s, buf, tid);
-        __syncthreads();
-        if (c + 1 < nch) gemm_fetch<kBT>(regs, A, lda, B, ldb, (c + 1) * kKc, tid);
-#pragma unroll
-        for (int ks = 0; ks < kKc; ks += 4) {
-            double av[2], bv[2];
-#pragma unroll
-            for (int m = 0; m < 2; ++m) av[m] = s.A[buf][ks + (lane >> 4)][wi * 32 + 16 * m + (lane & 15)];
-#pragma unroll
-            for (int q = 0; q < 2; ++q) bv[q] = s.B[buf][ks + (lane >> 4)][wj * 32 + 16 * q + (lane & 15)];
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int q = 0; q < 2; ++q) acc[m][q] = mfma16x16x4_f64(av[m], bv[q], acc[m][q]);
-        }
-    }
+    GemmRegs regs;
+    gemm_fetch<kBT>(regs, A, lda, B, ldb, threadIdx.x);
+    gemm_stash<kBT>(regs, s, threadIdx.x);
+    __syncthreads();
+    gemm_compute<kBT>(s, acc);
 }
 
-// mode 0: C = acc ; mode 1: C -= acc ; mode 2: C = -acc
+// C[row][col] of the accumulator element (m, q, v) of this thread
+__device__ __forceinline__ int acc_row(int m, int v) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    return (w >> 1) * 32 + 16 * m + 4 * v + (lane >> 4);
+}
+__device__ __forceinline__ int acc_col(int q) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    return (w & 1) * 32 + 16 * q + (lane & 15);
+}
+
+// C -= A B with C's old values loaded behind the operand loads, so that
+// their latency overlaps the staging and the products
+template <bool kBT>
+__device__ __forceinline__ void tile_gemm_sub_f64(const double* __restrict__ A, int64_t lda,
+                                                  const double* __restrict__ B, int64_t ldb, double* __restrict__ C,
+                                                  int64_t ldc, GemmLds& s) {
+    GemmRegs regs;
+    gemm_fetch<kBT>(regs, A, lda, B, ldb, threadIdx.x);
+    double c[2][2][4];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) c[m][q][v] = C[(int64_t)acc_row(m, v) * ldc + acc_col(q)];
+    gemm_stash<kBT>(regs, s, threadIdx.x);
+    __syncthreads();
+    double4v acc[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) acc[m][q] = (double4v){};
+    gemm_compute<kBT>(s, acc);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) C[(int64_t)acc_row(m, v) * ldc + acc_col(q)] = c[m][q][v] - acc[m][q][v];
+}
+
+// mode 0: C = acc ; mode 2: C = -acc
 template <int kMode>
 __device__ __forceinline__ void tile_store_f64(double* __restrict__ C, int64_t ldc, const double4v (&acc)[2][2]) {
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wi = w >> 1, wj = w & 1;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int row = wi * 32 + 16 * m + 4 * v + (lane >> 4);
-                const int col = wj * 32 + 16 * q + (lane & 15);
-                double* p = C + (int64_t)row * ldc + col;
-                if (kMode == 0) *p = acc[m][q][v];
-                else if (kMode == 1) *p = *p - acc[m][q][v];
-                else *p = -acc[m][q][v];
+                double* p = C + (int64_t)acc_row(m, v) * ldc + acc_col(q);
+                *p = (kMode == 0) ? acc[m][q][v] : -acc[m][q][v];
             }
 }
 
@@ -523,7 +559,7 @@ __device__ __forceinline__ void set_tile(int set, int k, int T, int64_t b, int64
     }
 }
 
-// Update of step k over the blocks of one tile set.
+// Update of step k over the blocks of one tile set, one block per workgroup.
 __global__ __launch_bounds__(kGemmThreads) void chol_trail_kernel(double* __restrict__ G, int64_t np,
                                                                   const double* __restrict__ P, int k, int T,
                                                                   int set, const int* __restrict__ fail) {
@@ -533,17 +569,15 @@ __global__ __launch_bounds__(kGemmThreads) void chol_trail_kernel(double* __rest
     set_tile(set, k, T, blockIdx.x, i, j);
     const double* Pi = P + i * NB * NB;
     double* Gij = G + i * NB * np + j * NB;
-    double4v acc[2][2];
-    zero_acc(acc);
     if (j < k) {
-        tile_gemm_f64<false>(Pi, NB, G + (int64_t)k * NB * np + j * NB, np, s, acc);
-        tile_store_f64<1>(Gij, np, acc);
+        tile_gemm_sub_f64<false>(Pi, NB, G + (int64_t)k * NB * np + j * NB, np, Gij, np, s);
     } else if (j == k) {
+        double4v acc[2][2];
+        zero_acc(acc);
         tile_gemm_f64<false>(Pi, NB, G + (int64_t)k * NB * np + (int64_t)k * NB, np, s, acc);
         tile_store_f64<2>(Gij, np, acc);
     } else {
-        tile_gemm_f64<true>(Pi, NB, P + j * NB * NB, NB, s, acc);
-        tile_store_f64<1>(Gij, np, acc);
+        tile_gemm_sub_f64<true>(Pi, NB, P + j * NB * NB, NB, Gij, np, s);
     }
 }
 
