@@ -144,13 +144,13 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, i
 // ---------------------------------------------------------------------------
 // In-block sweep.  Dynamic LDS: Us [bw][bw+4] f32 (the U block, staged once),
 // rdg [bw] f32 (1 / U_jj), Ebuf [nw][16][kEld] f32, red [nw][64][2] f32,
-// errs [nw][64] f32, codes [64][nw*16] u8.  U entries are read with
-// wave-uniform addresses (LDS broadcast).
+// errs [nw][64] f32.  U entries are read with wave-uniform addresses (LDS
+// broadcast).  Codes and scaled errors go from registers to global memory.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline size_t sweep_lds_bytes(int bw) {
     const int nw = (bw + kSub - 1) / kSub;
     return (size_t)bw * (bw + 4) * 4 + (size_t)bw * 4 + (size_t)nw * kSub * kEld * 4 + (size_t)nw * 64 * 2 * 4 +
-           (size_t)nw * 64 * 4 + (size_t)64 * nw * kSub;
+           (size_t)nw * 64 * 4;
 }
 
 // Folds the 16 scaled errors of an earlier sub-block into this wave's
@@ -176,11 +176,24 @@ __device__ __forceinline__ void fold_in(float (&wv)[kSub], const float* __restri
 // Rounds this wave's columns in order, compensating the later columns of
 // the sub-block at once.  U rows of the sub-block and 1/U_jj are read into
 // registers before the dependent chain starts.
+// The rounding decision needs x = fl32(w / s) exactly.  With y = fl32(1/s)
+// computed once per grid, q0 = fl32(w y), r = fma(-q0, s, w) (exact) and
+// fl32(q0 + r y) is the correctly rounded quotient (Markstein's theorem for
+// round-to-nearest; no overflow or underflow at these magnitudes), which
+// replaces the full IEEE division sequence in the dependent chain.
+__device__ __forceinline__ float div_rn(float w, float s, float y) {
+    const float q0 = w * y;
+    const float r = __builtin_fmaf(-q0, s, w);
+    return __builtin_fmaf(r, y, q0);
+}
+
 template <bool kFull>
-__device__ __forceinline__ void sweep_sub(float (&wv)[kSub], float s, float zf, float maxq,
+__device__ __forceinline__ void sweep_sub(float (&wv)[kSub], float s, float sinv, float zf, float maxq,
                                           const float* __restrict__ ublk, int uld, const float* __restrict__ rd,
-                                          float* __restrict__ ebq, uint8_t* __restrict__ crow, int lane, int cq,
-                                          float& errsq) {
+                                          float* __restrict__ ebq, uint32_t (&cw)[kSub / 4], float (&ev)[kSub],
+                                          int lane, int cq, float& errsq) {
+#pragma unroll
+    for (int i = 0; i < kSub / 4; ++i) cw[i] = 0;
     float r[kSub];
 #pragma unroll
     for (int t = 0; t < kSub; ++t) r[t] = rd[t];
@@ -191,13 +204,14 @@ __device__ __forceinline__ void sweep_sub(float (&wv)[kSub], float s, float zf, 
 #pragma unroll
             for (int t2 = t + 1; t2 < kSub; ++t2) u[t2] = ublk[t * uld + t2];
             const float w = wv[t];
-            const float x = w / s;
+            const float x = div_rn(w, s, sinv);
             const float v = x + zf;
             float qf = __builtin_rintf(v);
             qf = fminf(fmaxf(qf, 0.0f), maxq);
             const float what = (qf - zf) * s;
             const float e = (w - what) * r[t];
-            crow[t] = (uint8_t)qf;
+            cw[t >> 2] |= (uint32_t)qf << (8 * (t & 3));
+            ev[t] = e;
             ebq[t * kEld + lane] = e;
             errsq += e * e;
 #pragma unroll
@@ -222,7 +236,6 @@ __global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk
     float* Ebuf = rdg + bw;                                               // nw*16*kEld
     float* red = Ebuf + nw * kSub * kEld;                                 // nw*64*2
     float* errs = red + nw * 64 * 2;                                      // nw*64
-    uint8_t* cbuf = reinterpret_cast<uint8_t*>(errs + nw * 64);           // 64 * nw*16
 
     const int lane = threadIdx.x & 63;
     const int q = wave_id();
@@ -232,29 +245,17 @@ __global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk
     const int64_t c0q = b0 + kSub * q;
     const float maxq = (float)((1 << bits) - 1);
 
-    // stage the U block (upper part; the rest is never read) and 1/U_jj,
-    // with every thread's loads in flight before its LDS stores
-    {
-        constexpr int kPer = (kMaxBlock * kMaxBlock + 511) / 512;  // elements per thread at 512 threads
-        float t[kPer];
-        const int nth = blockDim.x;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int e = threadIdx.x + i * nth;
-            const int r = e / bw, c = e % bw;
-            t[i] = (e < bw * bw && c >= r) ? U[(b0 + r) * d_in + b0 + c] : 0.0f;
-        }
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int e = threadIdx.x + i * nth;
-            if (e < bw * bw) Us[(e / bw) * uld + e % bw] = t[i];
-        }
-        for (int e = threadIdx.x; e < bw; e += nth) rdg[e] = rdiag[b0 + e];
-    }
-
+    // this wave's columns of the working weights and the row grid: loads
+    // issued first so that their latency overlaps the staging below
     float wv[kSub];
+    const bool vec_row = rowok && cq == kSub && ((d_in | c0q) & 3) == 0;  // 16-byte aligned full row slice
+    if (vec_row) {
 #pragma unroll
-    for (int t = 0; t < kSub; ++t) wv[t] = (rowok && t < cq) ? Wk[R * d_in + c0q + t] : 0.0f;
+        for (int t = 0; t < kSub; t += 4) *reinterpret_cast<float4v*>(&wv[t]) = *reinterpret_cast<const float4v*>(Wk + R * d_in + c0q + t);
+    } else {
+#pragma unroll
+        for (int t = 0; t < kSub; ++t) wv[t] = (rowok && t < cq) ? Wk[R * d_in + c0q + t] : 0.0f;
+    }
 
     float s = 1.0f, zf = 0.0f;
     if (group == 0) {
@@ -271,6 +272,44 @@ __global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk
             zf = (float)zeros[R * ng + gi];
         }
     }
+
+    // stage the U block (upper part; the rest is never read) and 1/U_jj,
+    // with every thread's loads in flight before its LDS stores
+    const int nth = blockDim.x;
+    if (bw == kMaxBlock && nth == 512 && ((b0 | d_in) & 3) == 0 &&
+        (reinterpret_cast<uintptr_t>(U) & 15) == 0) {
+        // full block: 16-byte loads, 8 per thread
+        float4v t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = threadIdx.x + i * 512;
+            const int r = e >> 5, c = (e & 31) * 4;
+            t[i] = (c + 3 >= r) ? *reinterpret_cast<const float4v*>(U + (b0 + r) * d_in + b0 + c) : (float4v){};
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = threadIdx.x + i * 512;
+            const int r = e >> 5, c = (e & 31) * 4;
+            *reinterpret_cast<float4v*>(Us + r * uld + c) = t[i];
+        }
+    } else {
+        constexpr int kPer = (kMaxBlock * kMaxBlock + 511) / 512;  // elements per thread at 512 threads
+        float t[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = threadIdx.x + i * nth;
+            const int r = e / bw, c = e % bw;
+            t[i] = (e < bw * bw && c >= r) ? U[(b0 + r) * d_in + b0 + c] : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = threadIdx.x + i * nth;
+            if (e < bw * bw) Us[(e / bw) * uld + e % bw] = t[i];
+        }
+    }
+    for (int e = threadIdx.x; e < bw; e += nth) rdg[e] = rdiag[b0 + e];
+
+    float sinv = 1.0f / s;
     float errsq = 0.0f;
     __syncthreads();
 
@@ -308,6 +347,7 @@ __global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk
             hi = fmaxf(hi, 0.0f);
             Grid g = make_grid(lo, hi, maxq);
             s = g.s;
+            sinv = 1.0f / s;
             zf = g.z;
             if (q == p && rowok) {
                 const int64_t gi = (b0 + kSub * p) / group;
@@ -321,28 +361,37 @@ __global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk
         }
         if (q == p) {
             float* ebq = Ebuf + p * kSub * kEld;
-            uint8_t* crow = cbuf + lane * (nw * kSub) + kSub * p;
             const float* ublk = Us + (kSub * p) * uld + kSub * p;
             const float* rd = rdg + kSub * p;
+            uint32_t cw[kSub / 4];
+            float ev[kSub];
             if (cq == kSub)
-                sweep_sub<true>(wv, s, zf, maxq, ublk, uld, rd, ebq, crow, lane, cq, errsq);
+                sweep_sub<true>(wv, s, sinv, zf, maxq, ublk, uld, rd, ebq, cw, ev, lane, cq, errsq);
             else
-                sweep_sub<false>(wv, s, zf, maxq, ublk, uld, rd, ebq, crow, lane, cq, errsq);
+                sweep_sub<false>(wv, s, sinv, zf, maxq, ublk, uld, rd, ebq, cw, ev, lane, cq, errsq);
+            // this sub-block's codes and scaled errors are final: store them
+            // now so that the stores drain while the later sub-blocks run
+            const int64_t ce = kSub * (int64_t)p;  // column of the block
+            const bool vec_out = vec_row && (ldE & 3) == 0 && (d_in & 15) == 0 && ((b0 + ce) & 15) == 0 &&
+                                 ((reinterpret_cast<uintptr_t>(codes) | reinterpret_cast<uintptr_t>(E)) & 15) == 0;
+            if (vec_out) {
+                *reinterpret_cast<uint4*>(codes + R * d_in + b0 + ce) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+#pragma unroll
+                for (int t = 0; t < kSub; t += 4) *reinterpret_cast<float4v*>(E + R * ldE + ce + t) = *reinterpret_cast<const float4v*>(&ev[t]);
+            } else if (rowok) {
+#pragma unroll
+                for (int t = 0; t < kSub; ++t)
+                    if (t < cq) {
+                        codes[R * d_in + b0 + ce + t] = (uint8_t)(cw[t >> 2] >> (8 * (t & 3)));
+                        E[R * ldE + ce + t] = ev[t];
+                    }
+            }
         }
         __syncthreads();
     }
     errs[q * 64 + lane] = errsq;
     __syncthreads();
 
-    // write codes and scaled errors of the block, row-contiguous
-    const int nthreads = blockDim.x;
-    const int64_t rows_here = min((int64_t)kRowsPerWg, d_out - (int64_t)blockIdx.x * kRowsPerWg);
-    for (int e = threadIdx.x; e < rows_here * bw; e += nthreads) {
-        const int r = e / bw, c = e % bw;
-        const int64_t RR = (int64_t)blockIdx.x * kRowsPerWg + r;
-        codes[RR * d_in + b0 + c] = cbuf[r * (nw * kSub) + c];
-        E[RR * ldE + c] = Ebuf[(c / kSub) * kSub * kEld + (c % kSub) * kEld + r];
-    }
     if (err_row && q == 0 && rowok) {
         float acc = err_row[R];
         for (int qq = 0; qq < nw; ++qq) acc += errs[qq * 64 + lane];
@@ -368,27 +417,31 @@ struct TrailLds {
     float U[2][kTK * kUs];
 };
 
-template <bool kVec>
+// Per-thread staging registers for a tile of kRT rows: E holds kRT/8 floats
+// (row tid / (256/kRT), k run of kRT/8), U 16 floats (k row tid/8, 16 columns).
+template <int kRT>
 struct TrailRegs {
-    float e[16];
+    static constexpr int kE = kRT / 8;
+    float e[kE];
     float u[16];
 };
 
-// thread -> E: row tid/2, k run (tid&1)*16 .. +16 ; U: k row tid/8, cols (tid&7)*16 .. +16
-template <bool kVec>
-__device__ __forceinline__ void trail_fetch(TrailRegs<kVec>& r, const float* __restrict__ E, int64_t ldE,
+template <bool kVec, int kRT>
+__device__ __forceinline__ void trail_fetch(TrailRegs<kRT>& r, const float* __restrict__ E, int64_t ldE,
                                             const float* __restrict__ U, int64_t d_out, int64_t d_in, int64_t r0,
                                             int64_t c0, int64_t b0, int K, int kc, int tid, int64_t c_end) {
+    constexpr int kE = TrailRegs<kRT>::kE;
+    constexpr int kPerRow = kTK / kE;  // threads per E row
     {
-        const int64_t R = r0 + (tid >> 1);
-        const int k = kc + (tid & 1) * 16;
+        const int64_t R = r0 + tid / kPerRow;
+        const int k = kc + (tid % kPerRow) * kE;
         const float* src = E + R * ldE + k;
-        if (kVec && R < d_out && k + 16 <= K) {
+        if (kVec && R < d_out && k + kE <= K) {
 #pragma unroll
-            for (int e = 0; e < 16; e += 4) *reinterpret_cast<float4v*>(&r.e[e]) = *reinterpret_cast<const float4v*>(src + e);
+            for (int e = 0; e < kE; e += 4) *reinterpret_cast<float4v*>(&r.e[e]) = *reinterpret_cast<const float4v*>(src + e);
         } else {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) r.e[e] = (R < d_out && k + e < K) ? src[e] : 0.0f;
+            for (int e = 0; e < kE; ++e) r.e[e] = (R < d_out && k + e < K) ? src[e] : 0.0f;
         }
     }
     {
@@ -405,68 +458,91 @@ __device__ __forceinline__ void trail_fetch(TrailRegs<kVec>& r, const float* __r
     }
 }
 
-template <bool kVec>
-__device__ __forceinline__ void trail_stash(const TrailRegs<kVec>& r, TrailLds& s, int buf, int tid) {
-    float* Es = s.E[buf] + (tid >> 1) * kEs + (tid & 1) * 16;
+template <int kRT>
+__device__ __forceinline__ void trail_stash(const TrailRegs<kRT>& r, TrailLds& s, int buf, int tid) {
+    constexpr int kE = TrailRegs<kRT>::kE;
+    constexpr int kPerRow = kTK / kE;
+    float* Es = s.E[buf] + (tid / kPerRow) * kEs + (tid % kPerRow) * kE;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) Es[e] = r.e[e];
+    for (int e = 0; e < kE; ++e) Es[e] = r.e[e];
     float* Us = s.U[buf] + (tid >> 3) * kUs + (tid & 7) * 16;
 #pragma unroll
     for (int e = 0; e < 16; e += 4) *reinterpret_cast<float4v*>(&Us[e]) = *reinterpret_cast<const float4v*>(&r.u[e]);
 }
 
-template <bool kVec>
+// W[r0 .. r0+kRT, c0 .. c0+128] -= E[rows, 0..K) U[b0 .. b1, cols] for the
+// tile (blockIdx.y, blockIdx.x) of columns [c_begin, c_end).  Four waves in
+// a 2x2 grid, each kRT/2 x 64 as (kRT/64) x 2 MFMA 32x32x2 f32 tiles; K in
+// chunks of 32 through two LDS buffers with a register prefetch.
+template <bool kVec, int kRT>
 __global__ __launch_bounds__(256) void trail_kernel(float* __restrict__ Wk, int64_t d_out, int64_t d_in,
                                                     const float* __restrict__ E, int64_t ldE,
                                                     const float* __restrict__ U, int64_t b0, int64_t b1,
                                                     int64_t c_begin, int64_t c_end) {
+    constexpr int kM = kRT / 64;  // MFMA row tiles per wave
     __shared__ TrailLds s;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wi = w >> 1, wj = w & 1;
-    const int64_t r0 = (int64_t)blockIdx.y * kTT;
+    const int64_t r0 = (int64_t)blockIdx.y * kRT;
     const int64_t c0 = c_begin + (int64_t)blockIdx.x * kTT;
     const int K = (int)(b1 - b0);
     const int nchunks = (K + kTK - 1) / kTK;
 
-    float16v acc[2][2];
+    float16v acc[kM][2];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < kM; ++m)
 #pragma unroll
         for (int q = 0; q < 2; ++q) acc[m][q] = (float16v){};
 
-    TrailRegs<kVec> regs;
-    trail_fetch<kVec>(regs, E, ldE, U, d_out, d_in, r0, c0, b0, K, 0, tid, c_end);
+    TrailRegs<kRT> regs;
+    trail_fetch<kVec, kRT>(regs, E, ldE, U, d_out, d_in, r0, c0, b0, K, 0, tid, c_end);
+    // the 64-row tile (latency-bound) reads its W tile early; the 128-row
+    // tile would need 64 more registers for it and lose occupancy
+    constexpr bool kPre = kRT == 64;
+    float wold[kM][2][16];
+    if (kPre) {
+#pragma unroll
+        for (int m = 0; m < kM; ++m)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int64_t row = r0 + wi * (kRT / 2) + 32 * m + acc32_row(v, lane);
+                    const int64_t col = c0 + wj * 64 + 32 * q + (lane & 31);
+                    wold[m][q][v] = (row < d_out && col < c_end) ? Wk[row * d_in + col] : 0.0f;
+                }
+    }
     for (int c = 0; c < nchunks; ++c) {
         const int buf = c & 1;
-        trail_stash<kVec>(regs, s, buf, tid);
+        trail_stash<kRT>(regs, s, buf, tid);
         __syncthreads();
-        if (c + 1 < nchunks) trail_fetch<kVec>(regs, E, ldE, U, d_out, d_in, r0, c0, b0, K, (c + 1) * kTK, tid, c_end);
+        if (c + 1 < nchunks) trail_fetch<kVec, kRT>(regs, E, ldE, U, d_out, d_in, r0, c0, b0, K, (c + 1) * kTK, tid, c_end);
         const float* Es = s.E[buf];
         const float* Us = s.U[buf];
 #pragma unroll
         for (int ks = 0; ks < kTK; ks += 2) {
-            float a[2], b[2];
+            float a[kM], b[2];
 #pragma unroll
-            for (int m = 0; m < 2; ++m) a[m] = Es[(wi * 64 + 32 * m + (lane & 31)) * kEs + ks + (lane >> 5)];
+            for (int m = 0; m < kM; ++m) a[m] = Es[(wi * (kRT / 2) + 32 * m + (lane & 31)) * kEs + ks + (lane >> 5)];
 #pragma unroll
             for (int q = 0; q < 2; ++q) b[q] = Us[(ks + (lane >> 5)) * kUs + wj * 64 + 32 * q + (lane & 31)];
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
+            for (int m = 0; m < kM; ++m)
 #pragma unroll
                 for (int q = 0; q < 2; ++q) acc[m][q] = mfma32x32x2_f32(a[m], b[q], acc[m][q]);
         }
     }
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < kM; ++m)
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int64_t row = r0 + wi * 64 + 32 * m + acc32_row(v, lane);
+                const int64_t row = r0 + wi * (kRT / 2) + 32 * m + acc32_row(v, lane);
                 const int64_t col = c0 + wj * 64 + 32 * q + (lane & 31);
                 if (row < d_out && col < c_end) {
                     float* p = Wk + row * d_in + col;
-                    *p = *p - acc[m][q][v];
+                    *p = (kPre ? wold[m][q][v] : *p) - acc[m][q][v];
                 }
             }
 }
@@ -524,16 +600,25 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
     SideStream* ss = nullptr;
     hipError_t err = side_stream(ss);
     if (err != hipSuccess) return err;
-    auto trail = [&](hipStream_t st, int64_t b0, int64_t b1, const float* Eb, int64_t cb, int64_t ce) {
+    // kRT = 128-row tiles for the bulk update; the early update of the next
+    // block (a single column tile) uses 64-row tiles for twice the workgroups
+    auto trail = [&](hipStream_t st, int64_t b0, int64_t b1, const float* Eb, int64_t cb, int64_t ce, bool narrow) {
         if (ce <= cb) return;
         TimedLaunch t(K_Q_TRAIL, st);
-        dim3 grid((unsigned)((ce - cb + kTT - 1) / kTT), (unsigned)((d_out + kTT - 1) / kTT));
-        if (vec)
-            hipLaunchKernelGGL(trail_kernel<true>, grid, dim3(256), 0, st, w.Wk, d_out, d_in, Eb, block, U, b0, b1, cb,
-                               ce);
-        else
-            hipLaunchKernelGGL(trail_kernel<false>, grid, dim3(256), 0, st, w.Wk, d_out, d_in, Eb, block, U, b0, b1,
+        const int rt = narrow ? 64 : 128;
+        dim3 grid((unsigned)((ce - cb + kTT - 1) / kTT), (unsigned)((d_out + rt - 1) / rt));
+        if (vec && narrow)
+            hipLaunchKernelGGL((trail_kernel<true, 64>), grid, dim3(256), 0, st, w.Wk, d_out, d_in, Eb, block, U, b0, b1,
                                cb, ce);
+        else if (vec)
+            hipLaunchKernelGGL((trail_kernel<true, 128>), grid, dim3(256), 0, st, w.Wk, d_out, d_in, Eb, block, U, b0,
+                               b1, cb, ce);
+        else if (narrow)
+            hipLaunchKernelGGL((trail_kernel<false, 64>), grid, dim3(256), 0, st, w.Wk, d_out, d_in, Eb, block, U, b0,
+                               b1, cb, ce);
+        else
+            hipLaunchKernelGGL((trail_kernel<false, 128>), grid, dim3(256), 0, st, w.Wk, d_out, d_in, Eb, block, U, b0,
+                               b1, cb, ce);
     };
     // Lookahead: after the sweep of block b, the columns of block b+1 receive
     // its update on the caller's stream and the next sweep starts at once,
@@ -574,11 +659,11 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
         if (next_end < d_in) {
             if ((err = hipEventRecord(ss->fork, s)) != hipSuccess) return err;
             if ((err = hipStreamWaitEvent(ss->side, ss->fork, 0)) != hipSuccess) return err;
-            trail(ss->side, b0, b1, Eb, next_end, d_in);
+            trail(ss->side, b0, b1, Eb, next_end, d_in, false);
             if ((err = hipEventRecord(ss->join, ss->side)) != hipSuccess) return err;
             rest_pending = true;
         }
-        trail(s, b0, b1, Eb, b1, next_end);
+        trail(s, b0, b1, Eb, b1, next_end, true);
     }
     if ((err = join_rest()) != hipSuccess) return err;
     return hipGetLastError();
