@@ -23,6 +23,8 @@ constexpr int kWave = 64;
 //   16x16x4 f64: A[i][k] from lane i + 16*k, B[k][j] from lane j + 16*k;
 //     result lane l holds C[4*v + l/16][l % 16] for v = 0..3 (measured on
 //     gfx950; rows interleave across the four lane groups).
+//   16x16x4 f32: same operand map; result lane l holds C[4*(l/16) + v][l % 16]
+//     (measured on gfx950: the f32 and f64 variants differ).
 // The k order inside a group is the hardware's; a product A B^T of two
 // operands loaded with the same lane->k map is independent of it.
 // ---------------------------------------------------------------------------
@@ -31,6 +33,9 @@ __device__ __forceinline__ float16v mfma32x32x16_f16(half8 a, half8 b, float16v 
 }
 __device__ __forceinline__ float16v mfma32x32x2_f32(float a, float b, float16v c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float4v mfma16x16x4_f32(float a, float b, float4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ double4v mfma16x16x4_f64(double a, double b, double4v c) {
     return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);

@@ -156,7 +156,7 @@ __host__ __device__ inline size_t sweep_lds_bytes(int bw) {
 // Folds the 16 scaled errors of an earlier sub-block into this wave's
 // columns: w_c -= sum_t e_t U[t][c].  kFull: all 16 columns present (no
 // guards, so every LDS read can be issued ahead of the FMAs).
-template <bool kFull>
+template <bool kFull, bool kVecU>
 __device__ __forceinline__ void fold_in(float (&wv)[kSub], const float* __restrict__ ebp,
                                         const float* __restrict__ ublk, int uld, int lane, int cq) {
     float e[kSub];
@@ -165,11 +165,66 @@ __device__ __forceinline__ void fold_in(float (&wv)[kSub], const float* __restri
 #pragma unroll
     for (int t = 0; t < kSub; ++t) {
         float u[kSub];
+        if (kVecU) {  // rows 16-byte aligned: uld and the column offset are multiples of 4
 #pragma unroll
-        for (int c = 0; c < kSub; ++c) u[c] = ublk[t * uld + c];
+            for (int c = 0; c < kSub; c += 4) *reinterpret_cast<float4v*>(&u[c]) = *reinterpret_cast<const float4v*>(ublk + t * uld + c);
+        } else {
+#pragma unroll
+            for (int c = 0; c < kSub; ++c) u[c] = ublk[t * uld + c];
+        }
 #pragma unroll
         for (int c = 0; c < kSub; ++c)
             if (kFull || c < cq) wv[c] -= e[t] * u[c];
+    }
+}
+
+// 4x4 transpose across the four 16-lane rows of a wave: on entry register m
+// of lane row g holds X[g][m]; on exit register j of lane row m holds X[j][m]
+// (permlane32 swaps exchange row pairs {0,1} <-> {2,3}, permlane16 swaps odd
+// and even rows).  The swaps are written as inline asm with both registers
+// read-write: the compiler's two-result builtins lost the second result in
+// this pattern.  Each swap is preceded by the two wait states a permlane
+// read needs after a VALU write of its operands.
+__device__ __forceinline__ void swap32(float& x, float& y) {
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void swap16(float& x, float& y) {
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void xpose_rows4(float& r0, float& r1, float& r2, float& r3) {
+    swap32(r0, r2);  // r0 = rows {X[0][0], X[1][0], X[0][2], X[1][2]}, r2 = {X[2][0], X[3][0], X[2][2], X[3][2]}
+    swap32(r1, r3);
+    swap16(r0, r1);  // r0 = {X[0][0..3]} by row, r1 = {X[1][0..3]}
+    swap16(r2, r3);
+}
+
+// The same fold-in on MFMA, for a wave whose 16 columns are all present:
+// D^T = U_blk^T E^T (16 columns x 64 rows, four 16x16 tiles, K = 16), so that
+// every lane reads its own operand words instead of a broadcast U row.
+// Tile m leaves D[16m + l%16][4(l/16) + v] in lane l, register v; the row
+// transpose then gives lane r the 16 deltas of its own row.
+__device__ __forceinline__ void fold_in_mfma(float (&wv)[kSub], const float* __restrict__ ebp,
+                                             const float* __restrict__ ublk, int uld, int lane) {
+    const int i = lane & 15, g = lane >> 4;
+    float4v acc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = (float4v){};
+#pragma unroll
+    for (int kk = 0; kk < kSub; kk += 4) {
+        const float a = ublk[(kk + g) * uld + i];  // U_blk^T[i][kk+g]
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[m] = mfma16x16x4_f32(a, ebp[(kk + g) * kEld + 16 * m + i], acc[m]);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        // plain VALU copies: the asm reads registers the MFMA hazard rules
+        // no longer apply to
+        float r0 = acc[0][v] + 0.0f, r1 = acc[1][v] + 0.0f, r2 = acc[2][v] + 0.0f, r3 = acc[3][v] + 0.0f;
+        xpose_rows4(r0, r1, r2, r3);
+        wv[v] -= r0;
+        wv[4 + v] -= r1;
+        wv[8 + v] -= r2;
+        wv[12 + v] -= r3;
     }
 }
 
@@ -187,7 +242,7 @@ __device__ __forceinline__ float div_rn(float w, float s, float y) {
     return __builtin_fmaf(r, y, q0);
 }
 
-template <bool kFull>
+template <bool kFull, bool kVecU>
 __device__ __forceinline__ void sweep_sub(float (&wv)[kSub], float s, float sinv, float zf, float maxq,
                                           const float* __restrict__ ublk, int uld, const float* __restrict__ rd,
                                           float* __restrict__ ebq, uint32_t (&cw)[kSub / 4], float (&ev)[kSub],
@@ -201,8 +256,13 @@ __device__ __forceinline__ void sweep_sub(float (&wv)[kSub], float s, float sinv
     for (int t = 0; t < kSub; ++t) {
         if (kFull || t < cq) {
             float u[kSub];
+            if (kVecU) {
 #pragma unroll
-            for (int t2 = t + 1; t2 < kSub; ++t2) u[t2] = ublk[t * uld + t2];
+                for (int c = 4 * ((t + 1) / 4); c < kSub; c += 4) *reinterpret_cast<float4v*>(&u[c]) = *reinterpret_cast<const float4v*>(ublk + t * uld + c);
+            } else {
+#pragma unroll
+                for (int t2 = t + 1; t2 < kSub; ++t2) u[t2] = ublk[t * uld + t2];
+            }
             const float w = wv[t];
             const float x = div_rn(w, s, sinv);
             const float v = x + zf;
@@ -221,6 +281,9 @@ __device__ __forceinline__ void sweep_sub(float (&wv)[kSub], float s, float sinv
     }
 }
 
+// kAllFull: the block width is a multiple of 16, so every wave owns 16
+// columns and the unguarded code paths are the only ones compiled.
+template <bool kAllFull>
 __global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk, int64_t d_out, int64_t d_in,
                                                     const float* __restrict__ U, const float* __restrict__ rdiag,
                                                     int64_t b0, int64_t b1, int bits, int64_t group, int64_t ng,
@@ -241,7 +304,7 @@ __global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk
     const int q = wave_id();
     const int64_t R = (int64_t)blockIdx.x * kRowsPerWg + lane;
     const bool rowok = R < d_out;
-    const int cq = min(kSub, bw - kSub * q);  // >= 1
+    const int cq = kAllFull ? kSub : min(kSub, bw - kSub * q);  // >= 1
     const int64_t c0q = b0 + kSub * q;
     const float maxq = (float)((1 << bits) - 1);
 
@@ -314,14 +377,19 @@ __global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk
     __syncthreads();
 
     for (int p = 0; p < nw; ++p) {
+        // wave p carries the dependent chain of this phase: it gets issue
+        // priority over the waves that only fold errors in for later phases
+        if (q == p) __builtin_amdgcn_s_setprio(2);
         if (p > 0 && q >= p) {
             // fold in the scaled errors of sub-block p-1 (16 full columns)
             const float* ebp = Ebuf + (p - 1) * kSub * kEld;
             const float* ublk = Us + (kSub * (p - 1)) * uld + kSub * q;
-            if (cq == kSub)
-                fold_in<true>(wv, ebp, ublk, uld, lane, cq);
+            if (kAllFull)
+                fold_in_mfma(wv, ebp, ublk, uld, lane);
+            else if (cq == kSub)
+                fold_in<true, false>(wv, ebp, ublk, uld, lane, cq);
             else
-                fold_in<false>(wv, ebp, ublk, uld, lane, cq);
+                fold_in<false, false>(wv, ebp, ublk, uld, lane, cq);
         }
         if (group > 0 && group <= bw && ((int64_t)kSub * p) % group == 0) {
             // group start at column b0 + 16p: grid from the current weights
@@ -365,10 +433,11 @@ __global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk
             const float* rd = rdg + kSub * p;
             uint32_t cw[kSub / 4];
             float ev[kSub];
-            if (cq == kSub)
-                sweep_sub<true>(wv, s, sinv, zf, maxq, ublk, uld, rd, ebq, cw, ev, lane, cq, errsq);
+            if (kAllFull || cq == kSub)
+                sweep_sub<true, kAllFull>(wv, s, sinv, zf, maxq, ublk, uld, rd, ebq, cw, ev, lane, cq, errsq);
             else
-                sweep_sub<false>(wv, s, sinv, zf, maxq, ublk, uld, rd, ebq, cw, ev, lane, cq, errsq);
+                sweep_sub<false, false>(wv, s, sinv, zf, maxq, ublk, uld, rd, ebq, cw, ev, lane, cq, errsq);
+            __builtin_amdgcn_s_setprio(0);
             // this sub-block's codes and scaled errors are final: store them
             // now so that the stores drain while the later sub-blocks run
             const int64_t ce = kSub * (int64_t)p;  // column of the block
@@ -591,8 +660,11 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
     {
         const size_t ldsmax = sweep_lds_bytes((int)std::min(block, d_in));
         if (ldsmax > 64 * 1024) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_kernel),
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_kernel<true>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsmax);
+            if (e == hipSuccess)
+                e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_kernel<false>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsmax);
             if (e != hipSuccess) return e;
         }
     }
@@ -649,9 +721,14 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
         {
             TimedLaunch t(K_Q_SWEEP, s);
             const size_t lds = sweep_lds_bytes(bw);
-            hipLaunchKernelGGL(sweep_kernel, dim3(row_tiles), dim3(64 * nw), lds, s, (const float*)w.Wk, d_out, d_in, U,
-                               (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes, Eb,
-                               block, err_row);
+            if (bw % kSub == 0)
+                hipLaunchKernelGGL(sweep_kernel<true>, dim3(row_tiles), dim3(64 * nw), lds, s, (const float*)w.Wk, d_out,
+                                   d_in, U, (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes,
+                                   Eb, block, err_row);
+            else
+                hipLaunchKernelGGL(sweep_kernel<false>, dim3(row_tiles), dim3(64 * nw), lds, s, (const float*)w.Wk, d_out,
+                                   d_in, U, (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes,
+                                   Eb, block, err_row);
         }
         if (b1 >= d_in) break;
         if ((err = join_rest()) != hipSuccess) return err;
