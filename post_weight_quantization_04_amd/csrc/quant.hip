@@ -142,15 +142,23 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, i
 }
 
 // ---------------------------------------------------------------------------
-// In-block sweep.  Dynamic LDS: Us [bw][bw+4] f32 (the U block, staged once),
-// rdg [bw] f32 (1 / U_jj), Ebuf [nw][16][kEld] f32, red [nw][64][2] f32,
-// errs [nw][64] f32.  U entries are read with wave-uniform addresses (LDS
-// broadcast).  Codes and scaled errors go from registers to global memory.
+// In-block sweep.  Dynamic LDS: Up, the upper block triangle of the U block
+// as nw(nw+1)/2 packed 16x16 sub-blocks (a, b), a <= b, row stride 16 (the
+// strictly lower sub-blocks are never read); rdg [bw] f32 (1 / U_jj);
+// Ebuf [2][16][kEld] f32 (scaled errors of the current and previous
+// sub-block; only the previous one is folded in); red [nw][64][2] f32;
+// errs [nw][64] f32.  Codes and scaled errors go from registers to global
+// memory.  About 51 KB at bw = 128, so a sweep workgroup fits on a CU next
+// to a trailing-update workgroup.
 // ---------------------------------------------------------------------------
+constexpr int kUld = kSub;  // row stride inside a packed U sub-block
+
+__host__ __device__ inline int ublk_index(int a, int b, int nw) { return a * nw - a * (a - 1) / 2 + (b - a); }
+
 __host__ __device__ inline size_t sweep_lds_bytes(int bw) {
     const int nw = (bw + kSub - 1) / kSub;
-    return (size_t)bw * (bw + 4) * 4 + (size_t)bw * 4 + (size_t)nw * kSub * kEld * 4 + (size_t)nw * 64 * 2 * 4 +
-           (size_t)nw * 64 * 4;
+    return (size_t)nw * (nw + 1) / 2 * kSub * kSub * 4 + (size_t)bw * 4 + (size_t)2 * kSub * kEld * 4 +
+           (size_t)nw * 64 * 2 * 4 + (size_t)nw * 64 * 4;
 }
 
 // Folds the 16 scaled errors of an earlier sub-block into this wave's
@@ -165,7 +173,7 @@ __device__ __forceinline__ void fold_in(float (&wv)[kSub], const float* __restri
 #pragma unroll
     for (int t = 0; t < kSub; ++t) {
         float u[kSub];
-        if (kVecU) {  // rows 16-byte aligned: uld and the column offset are multiples of 4
+        if (kVecU) {  // packed sub-block rows are 64 bytes apart
 #pragma unroll
             for (int c = 0; c < kSub; c += 4) *reinterpret_cast<float4v*>(&u[c]) = *reinterpret_cast<const float4v*>(ublk + t * uld + c);
         } else {
@@ -293,11 +301,11 @@ __global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk
     extern __shared__ __align__(16) unsigned char smem[];
     const int bw = (int)(b1 - b0);
     const int nw = (bw + kSub - 1) / kSub;
-    const int uld = bw + 4;
-    float* Us = reinterpret_cast<float*>(smem);                         // bw*uld
-    float* rdg = Us + bw * uld;                                           // bw
-    float* Ebuf = rdg + bw;                                               // nw*16*kEld
-    float* red = Ebuf + nw * kSub * kEld;                                 // nw*64*2
+    const int uld = kUld;
+    float* Up = reinterpret_cast<float*>(smem);                         // nw(nw+1)/2 * 256
+    float* rdg = Up + nw * (nw + 1) / 2 * kSub * kSub;                    // bw
+    float* Ebuf = rdg + bw;                                               // 2*16*kEld
+    float* red = Ebuf + 2 * kSub * kEld;                                  // nw*64*2
     float* errs = red + nw * 64 * 2;                                      // nw*64
 
     const int lane = threadIdx.x & 63;
@@ -347,13 +355,14 @@ __global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk
         for (int i = 0; i < 8; ++i) {
             const int e = threadIdx.x + i * 512;
             const int r = e >> 5, c = (e & 31) * 4;
-            t[i] = (c + 3 >= r) ? *reinterpret_cast<const float4v*>(U + (b0 + r) * d_in + b0 + c) : (float4v){};
+            t[i] = ((r >> 4) <= (c >> 4)) ? *reinterpret_cast<const float4v*>(U + (b0 + r) * d_in + b0 + c) : (float4v){};
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int e = threadIdx.x + i * 512;
             const int r = e >> 5, c = (e & 31) * 4;
-            *reinterpret_cast<float4v*>(Us + r * uld + c) = t[i];
+            if ((r >> 4) <= (c >> 4))
+                *reinterpret_cast<float4v*>(Up + ublk_index(r >> 4, c >> 4, nw) * (kSub * kSub) + (r & 15) * kUld + (c & 15)) = t[i];
         }
     } else {
         constexpr int kPer = (kMaxBlock * kMaxBlock + 511) / 512;  // elements per thread at 512 threads
@@ -367,7 +376,9 @@ __global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int e = threadIdx.x + i * nth;
-            if (e < bw * bw) Us[(e / bw) * uld + e % bw] = t[i];
+            const int r = e / bw, c = e % bw;
+            if (e < bw * bw && (r >> 4) <= (c >> 4))
+                Up[ublk_index(r >> 4, c >> 4, nw) * (kSub * kSub) + (r & 15) * kUld + (c & 15)] = t[i];
         }
     }
     for (int e = threadIdx.x; e < bw; e += nth) rdg[e] = rdiag[b0 + e];
@@ -382,8 +393,8 @@ __global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk
         if (q == p) __builtin_amdgcn_s_setprio(2);
         if (p > 0 && q >= p) {
             // fold in the scaled errors of sub-block p-1 (16 full columns)
-            const float* ebp = Ebuf + (p - 1) * kSub * kEld;
-            const float* ublk = Us + (kSub * (p - 1)) * uld + kSub * q;
+            const float* ebp = Ebuf + ((p - 1) & 1) * kSub * kEld;
+            const float* ublk = Up + ublk_index(p - 1, q, nw) * (kSub * kSub);
             if (kAllFull)
                 fold_in_mfma(wv, ebp, ublk, uld, lane);
             else if (cq == kSub)
@@ -428,8 +439,8 @@ __global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk
             }
         }
         if (q == p) {
-            float* ebq = Ebuf + p * kSub * kEld;
-            const float* ublk = Us + (kSub * p) * uld + kSub * p;
+            float* ebq = Ebuf + (p & 1) * kSub * kEld;
+            const float* ublk = Up + ublk_index(p, p, nw) * (kSub * kSub);
             const float* rd = rdg + kSub * p;
             uint32_t cw[kSub / 4];
             float ev[kSub];
@@ -470,13 +481,15 @@ __global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk
 
 // ---------------------------------------------------------------------------
 // Lazy trailing update W[:, b1:] -= E[:, :K] U[b0:b1, b1:], K = b1 - b0.
-// 128x128 tile per workgroup; 4 waves in 2x2, each 64x64 = 2x2 MFMA 32x32.
-// K runs in chunks of 32: chunk c+1 is fetched into registers while the
-// MFMAs consume chunk c from one of two LDS buffers (one barrier per chunk).
+// kRT x 128 tile per workgroup (kRT = 64 in use); 4 waves in 2x2, each
+// kRT/2 x 64 as (kRT/64) x 2 MFMA 32x32x2 f32 tiles.  K runs in chunks of
+// 32: chunk c+1 is fetched into registers while the MFMAs consume chunk c
+// from one of two LDS buffers (one barrier per chunk).
 // E is staged row-major with an odd row stride, so the A-operand reads
 // (32 rows, one k) hit distinct banks.
 // ---------------------------------------------------------------------------
-constexpr int kTT = 128;
+constexpr int kTT = 128;         // columns per trailing-update tile
+constexpr int kTrailRows = 64;   // rows per trailing-update tile
 constexpr int kTK = 32;
 constexpr int kEs = kTK + 1;   // E stage row stride (odd)
 constexpr int kUs = kTT + 4;   // U stage row stride
@@ -565,8 +578,8 @@ __global__ __launch_bounds__(256) void trail_kernel(float* __restrict__ Wk, int6
 
     TrailRegs<kRT> regs;
     trail_fetch<kVec, kRT>(regs, E, ldE, U, d_out, d_in, r0, c0, b0, K, 0, tid, c_end);
-    // the 64-row tile (latency-bound) reads its W tile early; the 128-row
-    // tile would need 64 more registers for it and lose occupancy
+    // the 64-row tile reads its W tile early (a 128-row tile would need 64
+    // more registers for it and lose occupancy)
     constexpr bool kPre = kRT == 64;
     float wold[kM][2][16];
     if (kPre) {
@@ -672,25 +685,19 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
     SideStream* ss = nullptr;
     hipError_t err = side_stream(ss);
     if (err != hipSuccess) return err;
-    // kRT = 128-row tiles for the bulk update; the early update of the next
-    // block (a single column tile) uses 64-row tiles for twice the workgroups
-    auto trail = [&](hipStream_t st, int64_t b0, int64_t b1, const float* Eb, int64_t cb, int64_t ce, bool narrow) {
+    // 64-row tiles: twice the workgroups of a square tile and room for the W
+    // tile to be read ahead of the products (measured faster than 128-row
+    // tiles for both the early and the bulk update)
+    auto trail = [&](hipStream_t st, int64_t b0, int64_t b1, const float* Eb, int64_t cb, int64_t ce) {
         if (ce <= cb) return;
         TimedLaunch t(K_Q_TRAIL, st);
-        const int rt = narrow ? 64 : 128;
-        dim3 grid((unsigned)((ce - cb + kTT - 1) / kTT), (unsigned)((d_out + rt - 1) / rt));
-        if (vec && narrow)
-            hipLaunchKernelGGL((trail_kernel<true, 64>), grid, dim3(256), 0, st, w.Wk, d_out, d_in, Eb, block, U, b0, b1,
-                               cb, ce);
-        else if (vec)
-            hipLaunchKernelGGL((trail_kernel<true, 128>), grid, dim3(256), 0, st, w.Wk, d_out, d_in, Eb, block, U, b0,
-                               b1, cb, ce);
-        else if (narrow)
-            hipLaunchKernelGGL((trail_kernel<false, 64>), grid, dim3(256), 0, st, w.Wk, d_out, d_in, Eb, block, U, b0,
-                               b1, cb, ce);
+        dim3 grid((unsigned)((ce - cb + kTT - 1) / kTT), (unsigned)((d_out + kTrailRows - 1) / kTrailRows));
+        if (vec)
+            hipLaunchKernelGGL((trail_kernel<true, kTrailRows>), grid, dim3(256), 0, st, w.Wk, d_out, d_in, Eb, block, U,
+                               b0, b1, cb, ce);
         else
-            hipLaunchKernelGGL((trail_kernel<false, 128>), grid, dim3(256), 0, st, w.Wk, d_out, d_in, Eb, block, U, b0,
-                               b1, cb, ce);
+            hipLaunchKernelGGL((trail_kernel<false, kTrailRows>), grid, dim3(256), 0, st, w.Wk, d_out, d_in, Eb, block, U,
+                               b0, b1, cb, ce);
     };
     // Lookahead: after the sweep of block b, the columns of block b+1 receive
     // its update on the caller's stream and the next sweep starts at once,
@@ -736,11 +743,11 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
         if (next_end < d_in) {
             if ((err = hipEventRecord(ss->fork, s)) != hipSuccess) return err;
             if ((err = hipStreamWaitEvent(ss->side, ss->fork, 0)) != hipSuccess) return err;
-            trail(ss->side, b0, b1, Eb, next_end, d_in, false);
+            trail(ss->side, b0, b1, Eb, next_end, d_in);
             if ((err = hipEventRecord(ss->join, ss->side)) != hipSuccess) return err;
             rest_pending = true;
         }
-        trail(s, b0, b1, Eb, b1, next_end, true);
+        trail(s, b0, b1, Eb, b1, next_end);
     }
     if ((err = join_rest()) != hipSuccess) return err;
     return hipGetLastError();
