@@ -31,8 +31,8 @@ NB = 64  # panel width of the blocked factorization (kCholNB in the library)
 KERNEL_CLASS = {
     "hessian_f16": ("f16", "mfma"),
     "hessian_f32": ("f32", "mfma"),
-    "chol_panel": ("f64", "mfma"),
-    "chol_trail": ("f64", "mfma"),
+    "chol_step": ("f64", "mfma"),
+    "chol_next": ("f64", "mfma"),
     "q_trail": ("f32", "mfma"),
 }
 
@@ -42,20 +42,27 @@ def algorithmic_flops(name: str, d_out: int, d_in: int, n_tok: int, block: int) 
     n = d_in
     if name.startswith("hessian"):
         return float(n) * (n + 1) * n_tok
-    if name == "chol_trail":
-        tot = 0.0
+    if name in ("chol_step", "chol_next"):
+        # blocked Cholesky of the reversed H with the inverse factor built
+        # alongside; per step k, with m = n - 64(k+1) trailing rows and
+        # c = 64(k+1) inverse columns, the update costs m(m+1)·64 (lower
+        # trailing part) + 2·m·c·64 (inverse part).  chol_next does the part
+        # of column and row block k+1; chol_step the rest of the update plus
+        # the 64x64 diagonal block (2/3·64³) and the panel (2·m·64² + 2·64²·64k).
+        nxt = step = 0.0
         T = (n + NB - 1) // NB
         for k in range(T):
             m = max(0, n - (k + 1) * NB)
-            tot += m * (m + 1) * NB + 2.0 * m * min(n, (k + 1) * NB) * NB
-        return tot
-    if name == "chol_panel":
-        tot = 0.0
-        T = (n + NB - 1) // NB
-        for k in range(T):
-            m = max(0, n - (k + 1) * NB)
-            tot += 2.0 * m * NB * NB + 2.0 * NB * NB * min(n, k * NB)
-        return tot
+            c = min(n, (k + 1) * NB)
+            total = m * (m + 1) * NB + 2.0 * m * c * NB
+            part = 0.0
+            if m > 0:
+                w = min(NB, m)
+                part = 2.0 * NB * ((m - w) * w + w * (w + 1) / 2) + 2.0 * w * c * NB
+            nxt += part
+            step += total - part
+            step += 2.0 / 3.0 * NB ** 3 + 2.0 * m * NB * NB + 2.0 * NB * NB * min(n, k * NB)
+        return nxt if name == "chol_next" else step
     if name == "q_trail":
         tot = 0.0
         for b0 in range(0, n, block):
@@ -202,7 +209,7 @@ def main(argv=None) -> int:
             if cnt:
                 kernel_ms[name] = ms
                 kernel_launches[name] = cnt
-    dominant = max((k for k in kernel_ms if k in KERNEL_CLASS), key=lambda k: kernel_ms[k], default="chol_trail")
+    dominant = max((k for k in kernel_ms if k in KERNEL_CLASS), key=lambda k: kernel_ms[k], default="chol_step")
 
     # timed region: K steps, with the dominant kernel's launches bracketed by events
     _lib.timing_enable(dominant)

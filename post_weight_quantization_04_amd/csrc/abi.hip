@@ -16,8 +16,8 @@ namespace gptq {
 // ---------------------------------------------------------------------------
 namespace {
 const char* const kNames[K_COUNT] = {
-    "hessian_f16", "hessian_f32", "hinv_diag_stats", "hinv_load_reversed", "chol_diag", "chol_panel",
-    "chol_trail",  "hinv_store_u", "q_row_grid",     "q_convert",          "q_rdiag",   "q_group_grid",
+    "hessian_f16", "hessian_f32", "hinv_diag_stats", "hinv_load_reversed", "chol_step",
+    "chol_next",  "hinv_store_u", "q_row_grid",     "q_convert",          "q_rdiag",   "q_group_grid",
     "q_sweep",     "q_trail",
 };
 int g_timed = -1;

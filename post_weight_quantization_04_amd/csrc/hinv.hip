@@ -264,92 +264,102 @@ __device__ __forceinline__ double4v mm16(FX fx, FY fy, int lane) {
     return acc;
 }
 
-// Factor and invert the block held in L.g (256 threads).  Returns 0 or
-// 1 + the local column of the first pivot that is not positive
-// (block-uniform).
-__device__ int diag64(DiagLds& L) {
-    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
-    for (int s = 0; s < NB / kSb; ++s) {
-        const int o = kSb * s;
-        if (w == 0) {
-            const int st = gj16(L, s, lane);
-            if (lane == 0) L.status = st;
-        }
-        __syncthreads();
-        const int st = L.status;
-        if (st) return o + st;
-        // 2. panel: waves 0..2 take one tile each
-        if (w < 3) {
-            const int np_ = NB / kSb - 1 - s;  // number of P tiles
-            if (w < np_) {
-                const int i = s + 1 + w;
-                const double4v acc = mm16([&](int a, int k) { return L.g[kSb * i + a][o + k]; },
-                                          [&](int k, int b) { return L.g[o + b][o + k]; }, lane);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) L.p[w][4 * v + (lane >> 4)][lane & 15] = acc[v];
-            } else {
-                const int j = w - np_;
-                const double4v acc = mm16([&](int a, int k) { return L.g[o + a][o + k]; },
-                                          [&](int k, int b) { return L.g[o + k][kSb * j + b]; }, lane);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) L.g[o + 4 * v + (lane >> 4)][kSb * j + (lane & 15)] = acc[v];
-            }
-        }
-        __syncthreads();
-        // 3. update of every tile (i, j), i > s, j <= i
-        int t = 0;
-        for (int i = s + 1; i < NB / kSb; ++i) {
-            for (int j = 0; j <= i; ++j, ++t) {
-                if ((t & 3) != w) continue;
-                const int pi = i - s - 1;
-                double4v acc;
-                if (j > s) {
-                    const int pj = j - s - 1;
-                    acc = mm16([&](int a, int k) { return L.p[pi][a][k]; },
-                               [&](int k, int b) { return L.p[pj][b][k]; }, lane);
-                } else {
-                    acc = mm16([&](int a, int k) { return L.p[pi][a][k]; },
-                               [&](int k, int b) { return L.g[o + k][kSb * j + b]; }, lane);
-                }
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    double& d = L.g[kSb * i + 4 * v + (lane >> 4)][kSb * j + (lane & 15)];
-                    d = (j == s) ? -acc[v] : d - acc[v];
-                }
-            }
-        }
-        __syncthreads();
-    }
-    return 0;
+// The lanes of one wave exchange data through LDS: the wave's LDS
+// operations execute in order, so ordering the compiler is enough.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__global__ __launch_bounds__(256) void chol_diag_kernel(double* __restrict__ G, int64_t np, int k,
-                                                        int32_t* __restrict__ info, int* __restrict__ fail) {
-    __shared__ __align__(16) DiagLds L;
-    if (*fail) return;
-    const int tid = threadIdx.x;
-    double* blk = G + (int64_t)k * NB * np + (int64_t)k * NB;
-#pragma unroll
-    for (int m = 0; m < NB * NB / 256; ++m) {
-        const int idx = tid + 256 * m;
-        L.g[idx >> 6][idx & 63] = blk[(int64_t)(idx >> 6) * np + (idx & 63)];
+// Factor and invert the block held in L.g (256 threads).  Returns 0 or
+// 1 + the local column of the first pivot that is not positive
+// (block-uniform).  One sub-step of lookahead: while wave 0 forms P_{s+1},
+// updates the diagonal sub-block s+1 with it and runs that sub-block's
+// pivots, waves 1..3 do every other panel and update tile of sub-step s.
+// Two barriers per sub-step order the roles:
+//   phase 1  wave 0: P_{s+1} = A_{s+1,s} Ls^T;  waves 1..3: P_i (i > s+1)
+//            and M_sj = Ls A_sj (j < s), in place;
+//   phase 2  wave 0: A_{s+1,s+1} -= P_{s+1} P_{s+1}^T, pivots of s+1;
+//            waves 1..3: the other tiles (i, j), i > s, j <= i.
+__device__ int diag64(DiagLds& L) {
+    const int lane = threadIdx.x & 63, w = wave_id();
+    constexpr int S = NB / kSb;
+    if (w == 0) {
+        const int st = gj16(L, 0, lane);
+        if (lane == 0) L.status = st;
     }
     __syncthreads();
-    const int st = diag64(L);
-    if (st) {
-        if (tid == 0) {
-            *info = k * NB + st;
-            *fail = 1;
-        }
-        return;
-    }
-    // write back M = L^-1 with exact zeros above the diagonal
+    if (L.status) return L.status;
+    for (int s = 0; s < S; ++s) {
+        const int o = kSb * s;
+        auto panel_p = [&](int i, int slot) {  // P_i = A_is Ls^T
+            const double4v acc = mm16([&](int a, int k) { return L.g[kSb * i + a][o + k]; },
+                                      [&](int k, int b) { return L.g[o + b][o + k]; }, lane);
 #pragma unroll
-    for (int m = 0; m < NB * NB / 256; ++m) {
-        const int idx = tid + 256 * m;
-        const int r = idx >> 6, c = idx & 63;
-        blk[(int64_t)r * np + c] = (c <= r) ? L.g[r][c] : 0.0;
+            for (int v = 0; v < 4; ++v) L.p[slot][4 * v + (lane >> 4)][lane & 15] = acc[v];
+        };
+        // phase 1
+        if (w == 0) {
+            if (s + 1 < S) panel_p(s + 1, 0);
+        } else {
+            const int nP = S - 2 - s > 0 ? S - 2 - s : 0;  // P_i, i = s+2 .. S-1
+            for (int q = w - 1; q < nP + s; q += 3) {
+                if (q < nP) {
+                    panel_p(s + 2 + q, q + 1);
+                } else {
+                    const int j = q - nP;
+                    const double4v acc = mm16([&](int a, int k) { return L.g[o + a][o + k]; },
+                                              [&](int k, int b) { return L.g[o + k][kSb * j + b]; }, lane);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) L.g[o + 4 * v + (lane >> 4)][kSb * j + (lane & 15)] = acc[v];
+                }
+            }
+        }
+        __syncthreads();
+        // phase 2
+        if (w == 0) {
+            if (s + 1 < S) {
+                const int o1 = o + kSb;
+                const double4v acc = mm16([&](int a, int k) { return L.p[0][a][k]; },
+                                          [&](int k, int b) { return L.p[0][b][k]; }, lane);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    double& d = L.g[o1 + 4 * v + (lane >> 4)][o1 + (lane & 15)];
+                    d = d - acc[v];
+                }
+                wave_lds_sync();
+                const int st = gj16(L, s + 1, lane);
+                if (lane == 0) L.status = st;
+            }
+        } else {
+            int t = 0;
+            for (int i = s + 1; i < S; ++i) {
+                for (int j = 0; j <= i; ++j) {
+                    if (i == s + 1 && j == s + 1) continue;  // wave 0's
+                    if (t++ % 3 != w - 1) continue;
+                    const int pi = i - s - 1;
+                    double4v acc;
+                    if (j > s) {
+                        const int pj = j - s - 1;
+                        acc = mm16([&](int a, int k) { return L.p[pi][a][k]; },
+                                   [&](int k, int b) { return L.p[pj][b][k]; }, lane);
+                    } else {
+                        acc = mm16([&](int a, int k) { return L.p[pi][a][k]; },
+                                   [&](int k, int b) { return L.g[o + k][kSb * j + b]; }, lane);
+                    }
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        double& d = L.g[kSb * i + 4 * v + (lane >> 4)][kSb * j + (lane & 15)];
+                        d = (j == s) ? -acc[v] : d - acc[v];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (s + 1 < S && L.status) return kSb * (s + 1) + L.status;
     }
+    return 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -377,29 +387,43 @@ __device__ __forceinline__ int swz(int k, int col) { return col ^ (k & 15); }
 
 // A^T: row tid&63, k run (tid>>6)*16 ; B direct: k row tid>>2, cols (tid&3)*16 ;
 // B^T: col tid&63, k run (tid>>6)*16
+__device__ __forceinline__ void gemm_fetch_a(double (&a)[16], const double* __restrict__ A, int64_t lda, int tid) {
+    const double* sa = A + (int64_t)(tid & 63) * lda + (tid >> 6) * 16;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) a[e] = sa[e];
+}
+template <bool kBT>
+__device__ __forceinline__ void gemm_fetch_b(double (&b)[16], const double* __restrict__ B, int64_t ldb, int tid) {
+    const double* sb = kBT ? B + (int64_t)(tid & 63) * ldb + (tid >> 6) * 16 : B + (int64_t)(tid >> 2) * ldb + (tid & 3) * 16;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) b[e] = sb[e];
+}
 template <bool kBT>
 __device__ __forceinline__ void gemm_fetch(GemmRegs& r, const double* __restrict__ A, int64_t lda,
                                            const double* __restrict__ B, int64_t ldb, int tid) {
-    const double* sa = A + (int64_t)(tid & 63) * lda + (tid >> 6) * 16;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) r.a[e] = sa[e];
-    const double* sb = kBT ? B + (int64_t)(tid & 63) * ldb + (tid >> 6) * 16 : B + (int64_t)(tid >> 2) * ldb + (tid & 3) * 16;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) r.b[e] = sb[e];
+    gemm_fetch_a(r.a, A, lda, tid);
+    gemm_fetch_b<kBT>(r.b, B, ldb, tid);
 }
 
-template <bool kBT>
-__device__ __forceinline__ void gemm_stash(const GemmRegs& r, GemmLds& s, int tid) {
+__device__ __forceinline__ void gemm_stash_a(const double (&a)[16], GemmLds& s, int tid) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s.A[(tid >> 6) * 16 + e][tid & 63] = r.a[e];
+    for (int e = 0; e < 16; ++e) s.A[(tid >> 6) * 16 + e][tid & 63] = a[e];
+}
+template <bool kBT>
+__device__ __forceinline__ void gemm_stash_b(const double (&b)[16], GemmLds& s, int tid) {
     if (kBT) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s.B[(tid >> 6) * 16 + e][tid & 63] = r.b[e];
+        for (int e = 0; e < 16; ++e) s.B[(tid >> 6) * 16 + e][tid & 63] = b[e];
     } else {
         const int k = tid >> 2;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s.B[k][swz(k, (tid & 3) * 16 + e)] = r.b[e];
+        for (int e = 0; e < 16; ++e) s.B[k][swz(k, (tid & 3) * 16 + e)] = b[e];
     }
+}
+template <bool kBT>
+__device__ __forceinline__ void gemm_stash(const GemmRegs& r, GemmLds& s, int tid) {
+    gemm_stash_a(r.a, s, tid);
+    gemm_stash_b<kBT>(r.b, s, tid);
 }
 
 template <bool kBT>
@@ -497,26 +521,87 @@ __device__ __forceinline__ void zero_acc(double4v (&acc)[2][2]) {
         for (int q = 0; q < 2; ++q) acc[m][q] = (double4v){};
 }
 
-// Panel of step k: blocks t < k form M_kt = Linv_kk G_kt (in place); blocks
-// t >= k form P_i = G_ik Linv_kk^T with i = t + 1.
-__global__ __launch_bounds__(kGemmThreads) void chol_panel_kernel(double* __restrict__ G, int64_t np,
-                                                                  double* __restrict__ P, int k,
-                                                                  const int* __restrict__ fail) {
-    __shared__ GemmLds s;
-    if (*fail) return;
-    const int t = blockIdx.x;
-    const double* Lkk = G + (int64_t)k * NB * np + (int64_t)k * NB;
+// Diagonal block and panel of step k in one launch.  Every workgroup factors
+// and inverts the diagonal block itself (the work is latency-bound, so the
+// copies cost no time) with its own panel operand already in flight, then
+// forms its panel tile: t < k: M_kt = M_kk G_kt (in place); t >= k:
+// P_i = G_ik M_kk^T with i = t + 1, into the panel buffer.  Workgroup 0 also
+// writes M_kk (exact zeros above the diagonal) to tile 0 of the panel buffer,
+// which the update of step k reads; G_kk itself is rewritten only later (by
+// the early update), because other workgroups may still be reading it.
+union DiagPanelLds {
+    DiagLds diag;  // the factorization, then
+    GemmLds gemm;  // the panel product (M_kk passes through registers)
+};
+
+__device__ void diag_panel_body(DiagPanelLds& u, double* __restrict__ G, int64_t np, double* __restrict__ P, int k,
+                                int T, int t, int32_t* __restrict__ info, int* __restrict__ fail) {
+    const int tid = threadIdx.x;
+    const bool has_tile = t < T - 1;
+    const bool inv_row = t < k;  // M_kt rather than P_{t+1}
+    double opnd[16];
+    if (has_tile) {
+        if (inv_row) gemm_fetch_b<false>(opnd, G + (int64_t)k * NB * np + (int64_t)t * NB, np, tid);
+        else gemm_fetch_a(opnd, G + (int64_t)(t + 1) * NB * np + (int64_t)k * NB, np, tid);
+    }
+    DiagLds& L = u.diag;
+    const double* blk = G + (int64_t)k * NB * np + (int64_t)k * NB;
+#pragma unroll
+    for (int m = 0; m < NB * NB / kGemmThreads; ++m) {
+        const int idx = tid + kGemmThreads * m;
+        L.g[idx >> 6][idx & 63] = blk[(int64_t)(idx >> 6) * np + (idx & 63)];
+    }
+    __syncthreads();
+    const int st = diag64(L);
+    if (st) {
+        if (t == 0 && tid == 0) {
+            *info = k * NB + st;
+            *fail = 1;
+        }
+        return;
+    }
+    if (t == 0) {
+#pragma unroll
+        for (int m = 0; m < NB * NB / kGemmThreads; ++m) {
+            const int idx = tid + kGemmThreads * m;
+            const int r = idx >> 6, c = idx & 63;
+            P[idx] = (c <= r) ? L.g[r][c] : 0.0;
+        }
+    }
+    if (!has_tile) return;
+    // element e = (kk, x) of the stage: M[x][kk] goes to A^T[kk][x] (M_kk as
+    // A) or to B[kk][x] (M_kk^T as B); read out before the LDS is restaged
+    double mv[NB * NB / kGemmThreads];
+#pragma unroll
+    for (int m = 0; m < NB * NB / kGemmThreads; ++m) {
+        const int e = tid + kGemmThreads * m;
+        const int kk = e >> 6, x = e & 63;
+        mv[m] = (kk <= x) ? L.g[x][kk] : 0.0;
+    }
+    __syncthreads();
+    GemmLds& s = u.gemm;
     double4v acc[2][2];
     zero_acc(acc);
-    if (t < k) {
-        double* Gkt = G + (int64_t)k * NB * np + (int64_t)t * NB;
-        tile_gemm_f64<false>(Lkk, np, Gkt, np, s, acc);
-        tile_store_f64<0>(Gkt, np, acc);
+    if (inv_row) {
+#pragma unroll
+        for (int m = 0; m < NB * NB / kGemmThreads; ++m) {
+            const int e = tid + kGemmThreads * m;
+            s.A[e >> 6][e & 63] = mv[m];
+        }
+        gemm_stash_b<false>(opnd, s, tid);
+        __syncthreads();
+        gemm_compute<false>(s, acc);
+        tile_store_f64<0>(G + (int64_t)k * NB * np + (int64_t)t * NB, np, acc);
     } else {
-        const int i = t + 1;
-        const double* Gik = G + (int64_t)i * NB * np + (int64_t)k * NB;
-        tile_gemm_f64<true>(Gik, np, Lkk, np, s, acc);
-        tile_store_f64<0>(P + (int64_t)i * NB * NB, NB, acc);
+        gemm_stash_a(opnd, s, tid);
+#pragma unroll
+        for (int m = 0; m < NB * NB / kGemmThreads; ++m) {
+            const int e = tid + kGemmThreads * m;
+            s.B[e >> 6][e & 63] = mv[m];
+        }
+        __syncthreads();
+        gemm_compute<true>(s, acc);
+        tile_store_f64<0>(P + (int64_t)(t + 1) * NB * NB, NB, acc);
     }
 }
 
@@ -559,14 +644,20 @@ __device__ __forceinline__ void set_tile(int set, int k, int T, int64_t b, int64
     }
 }
 
-// Update of step k over the blocks of one tile set, one block per workgroup.
-__global__ __launch_bounds__(kGemmThreads) void chol_trail_kernel(double* __restrict__ G, int64_t np,
-                                                                  const double* __restrict__ P, int k, int T,
-                                                                  int set, const int* __restrict__ fail) {
-    __shared__ GemmLds s;
+// Diagonal block and panel of step 0 (later steps run inside chol_step_kernel).
+__global__ __launch_bounds__(kGemmThreads) void chol_diag_panel_kernel(double* __restrict__ G, int64_t np,
+                                                                       double* __restrict__ P, int T,
+                                                                       int32_t* __restrict__ info,
+                                                                       int* __restrict__ fail) {
+    __shared__ __align__(16) DiagPanelLds u;
     if (*fail) return;
-    int64_t i, j;
-    set_tile(set, k, T, blockIdx.x, i, j);
+    diag_panel_body(u, G, np, P, 0, T, blockIdx.x, info, fail);
+}
+
+// Update of block (i, j) by step k.  M_kk is read from tile 0 of the panel
+// buffer P.
+__device__ void trail_body(GemmLds& s, double* __restrict__ G, int64_t np, const double* __restrict__ P, int k,
+                           int64_t i, int64_t j) {
     const double* Pi = P + i * NB * NB;
     double* Gij = G + i * NB * np + j * NB;
     if (j < k) {
@@ -574,10 +665,53 @@ __global__ __launch_bounds__(kGemmThreads) void chol_trail_kernel(double* __rest
     } else if (j == k) {
         double4v acc[2][2];
         zero_acc(acc);
-        tile_gemm_f64<false>(Pi, NB, G + (int64_t)k * NB * np + (int64_t)k * NB, np, s, acc);
+        tile_gemm_f64<false>(Pi, NB, P, NB, s, acc);
         tile_store_f64<2>(Gij, np, acc);
     } else {
         tile_gemm_sub_f64<true>(Pi, NB, P + j * NB * NB, NB, Gij, np, s);
+    }
+}
+
+// The early update of step k: the blocks step k+1 reads first (column and
+// row block k+1), one per workgroup, plus one workgroup that copies M_kk
+// into G_kk (nothing reads G_kk after the diagonal-block launch of step k).
+__global__ __launch_bounds__(kGemmThreads) void chol_next_kernel(double* __restrict__ G, int64_t np,
+                                                                 const double* __restrict__ P, int k, int T,
+                                                                 const int* __restrict__ fail) {
+    __shared__ GemmLds s;
+    if (*fail) return;
+    if (blockIdx.x == tiles_in_set(kSetNext, k, T)) {
+        double* Gkk = G + (int64_t)k * NB * np + (int64_t)k * NB;
+#pragma unroll
+        for (int m = 0; m < NB * NB / kGemmThreads; ++m) {
+            const int idx = threadIdx.x + kGemmThreads * m;
+            Gkk[(int64_t)(idx >> 6) * np + (idx & 63)] = P[idx];
+        }
+        return;
+    }
+    int64_t i, j;
+    set_tile(kSetNext, k, T, blockIdx.x, i, j);
+    trail_body(s, G, np, P, k, i, j);
+}
+
+// One launch for the diagonal block and panel of step k1 = k+1 (workgroups
+// 0 .. npan-1, dispatched first) and the rest of the update of step k (the
+// others).  Both need only the early update of step k; they touch disjoint
+// blocks (the rest excludes column and row block k+1) and different panel
+// buffers, so no stream or event separates them.
+__global__ __launch_bounds__(kGemmThreads) void chol_step_kernel(double* __restrict__ G, int64_t np,
+                                                                 double* __restrict__ Pk1,
+                                                                 const double* __restrict__ Pk, int k, int T,
+                                                                 int npan, int32_t* __restrict__ info,
+                                                                 int* __restrict__ fail) {
+    __shared__ __align__(16) DiagPanelLds u;
+    if (*fail) return;
+    if ((int)blockIdx.x < npan) {
+        diag_panel_body(u, G, np, Pk1, k + 1, T, blockIdx.x, info, fail);
+    } else {
+        int64_t i, j;
+        set_tile(kSetRest, k, T, (int64_t)blockIdx.x - npan, i, j);
+        trail_body(u.gemm, G, np, Pk, k, i, j);
     }
 }
 
@@ -599,14 +733,11 @@ size_t hinv_workspace_bytes(int64_t n) {
 }
 
 
-// Schedule with one step of lookahead.  After the panel of step k, the
-// update of step k is split: the blocks step k+1 needs first (column and row
-// block k+1) run on the caller's stream and are followed at once by the
-// diagonal block and panel of step k+1, while the remaining blocks of step k
-// run concurrently on a side stream.  The next early update waits for them
-// (it touches blocks they update).  The panel buffer alternates between
-// steps because the side stream still reads panel k while panel k+1 is
-// formed.  Everything is joined back into the caller's stream.
+// Schedule with one step of lookahead, on the caller's stream only: per step
+// k, the early update (the blocks step k+1 reads first), then one launch that
+// holds both the diagonal block and panel of step k+1 and the rest of the
+// update of step k.  The panel buffer alternates between steps; its tile 0
+// holds M_kk.
 hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, float* U, uint8_t* dead,
                                int32_t* info, double* lambda_out, void* ws, hipStream_t s) {
     if (n == 0) return hipSuccess;
@@ -614,9 +745,7 @@ hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, floa
     const int64_t np = round_up(n, NB);
     const int T = (int)(np / NB);
     double* Pbuf[2] = {w.P, w.P + round_up(np * NB * 8, 256) / 8};
-    SideStream* ss = nullptr;
-    hipError_t e = side_stream(ss);
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
     {
         TimedLaunch t(K_HINV_DIAGSUM, s);
         hipLaunchKernelGGL(diag_stats_kernel, dim3(1), dim3(1024), 0, s, H, n, damp_frac, dead, w.scal, lambda_out,
@@ -627,39 +756,26 @@ hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, floa
         hipLaunchKernelGGL(load_reversed_kernel, dim3((unsigned)((int64_t)T * (T + 1) / 2)), dim3(256), 0, s, H, n,
                            np, (const double*)w.scal, w.G);
     }
-    auto diag_and_panel = [&](int k) {
-        {
-            TimedLaunch t(K_CHOL_DIAG, s);
-            hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(256), 0, s, w.G, np, k, info, w.fail);
-        }
-        if (T > 1) {
-            TimedLaunch t(K_CHOL_PANEL, s);
-            hipLaunchKernelGGL(chol_panel_kernel, dim3(T - 1), dim3(kGemmThreads), 0, s, w.G, np, Pbuf[k & 1], k,
-                               (const int*)w.fail);
-        }
-    };
-    diag_and_panel(0);
+    const int npan = std::max(T - 1, 1);  // workgroups of a diagonal-block + panel launch
+    {
+        TimedLaunch t(K_CHOL_STEP, s);
+        hipLaunchKernelGGL(chol_diag_panel_kernel, dim3((unsigned)npan), dim3(kGemmThreads), 0, s, w.G, np, Pbuf[0], T,
+                           info, w.fail);
+    }
     for (int k = 0; k < T; ++k) {
-        const double* Pk = Pbuf[k & 1];
+        {
+            TimedLaunch t(K_CHOL_NEXT, s);
+            const int64_t n_next = tiles_in_set(kSetNext, k, T);
+            hipLaunchKernelGGL(chol_next_kernel, dim3((unsigned)(n_next + 1)), dim3(kGemmThreads), 0, s, w.G, np,
+                               (const double*)Pbuf[k & 1], k, T, (const int*)w.fail);
+        }
+        const int np1 = (k + 1 < T) ? npan : 0;
         const int64_t n_rest = tiles_in_set(kSetRest, k, T);
-        const int64_t n_next = tiles_in_set(kSetNext, k, T);
-        if (n_rest > 0) {
-            if ((e = hipEventRecord(ss->fork, s)) != hipSuccess) return e;
-            if ((e = hipStreamWaitEvent(ss->side, ss->fork, 0)) != hipSuccess) return e;
-            {
-                TimedLaunch t(K_CHOL_TRAIL, ss->side);
-                hipLaunchKernelGGL(chol_trail_kernel, dim3((unsigned)n_rest), dim3(kGemmThreads), 0, ss->side, w.G,
-                                   np, Pk, k, T, (int)kSetRest, (const int*)w.fail);
-            }
-            if ((e = hipEventRecord(ss->join, ss->side)) != hipSuccess) return e;
+        if (np1 + n_rest > 0) {
+            TimedLaunch t(K_CHOL_STEP, s);
+            hipLaunchKernelGGL(chol_step_kernel, dim3((unsigned)(np1 + n_rest)), dim3(kGemmThreads), 0, s, w.G, np,
+                               Pbuf[(k + 1) & 1], (const double*)Pbuf[k & 1], k, T, np1, info, w.fail);
         }
-        if (n_next > 0) {
-            TimedLaunch t(K_CHOL_TRAIL, s);
-            hipLaunchKernelGGL(chol_trail_kernel, dim3((unsigned)n_next), dim3(kGemmThreads), 0, s, w.G, np, Pk, k,
-                               T, (int)kSetNext, (const int*)w.fail);
-        }
-        if (k + 1 < T) diag_and_panel(k + 1);
-        if (n_rest > 0 && (e = hipStreamWaitEvent(s, ss->join, 0)) != hipSuccess) return e;
     }
     {
         TimedLaunch t(K_HINV_STORE, s);

@@ -13,9 +13,8 @@ enum KernelId {
     K_HESS_F32,
     K_HINV_DIAGSUM,
     K_HINV_LOAD,
-    K_CHOL_DIAG,
-    K_CHOL_PANEL,
-    K_CHOL_TRAIL,
+    K_CHOL_STEP,
+    K_CHOL_NEXT,
     K_HINV_STORE,
     K_Q_ROWGRID,
     K_Q_CONVERT,

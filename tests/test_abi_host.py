@@ -52,7 +52,7 @@ def test_status_strings(clib):
 def test_kernel_names(clib):
     from post_weight_quantization_04_amd import _lib
     names = _lib.kernel_names()
-    assert len(names) == clib.gptq_kernel_count() and "q_trail" in names and "chol_trail" in names
+    assert len(names) == clib.gptq_kernel_count() and "q_trail" in names and "chol_step" in names
     assert clib.gptq_kernel_name(-1) is None
     assert clib.gptq_timing_enable(1000) == 1
     assert clib.gptq_timing_enable(-1) == 0
