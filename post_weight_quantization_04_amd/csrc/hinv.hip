@@ -282,7 +282,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 //            and M_sj = Ls A_sj (j < s), in place;
 //   phase 2  wave 0: A_{s+1,s+1} -= P_{s+1} P_{s+1}^T, pivots of s+1;
 //            waves 1..3: the other tiles (i, j), i > s, j <= i.
-__device__ int diag64(DiagLds& L) {
+__device__ __forceinline__ int diag64(DiagLds& L) {
     const int lane = threadIdx.x & 63, w = wave_id();
     constexpr int S = NB / kSb;
     if (w == 0) {
@@ -534,7 +534,7 @@ union DiagPanelLds {
     GemmLds gemm;  // the panel product (M_kk passes through registers)
 };
 
-__device__ void diag_panel_body(DiagPanelLds& u, double* __restrict__ G, int64_t np, double* __restrict__ P, int k,
+__device__ __forceinline__ void diag_panel_body(DiagPanelLds& u, double* __restrict__ G, int64_t np, double* __restrict__ P, int k,
                                 int T, int t, int32_t* __restrict__ info, int* __restrict__ fail) {
     const int tid = threadIdx.x;
     const bool has_tile = t < T - 1;
@@ -645,7 +645,7 @@ __device__ __forceinline__ void set_tile(int set, int k, int T, int64_t b, int64
 }
 
 // Diagonal block and panel of step 0 (later steps run inside chol_step_kernel).
-__global__ __launch_bounds__(kGemmThreads) void chol_diag_panel_kernel(double* __restrict__ G, int64_t np,
+__global__ __launch_bounds__(kGemmThreads, 2) void chol_diag_panel_kernel(double* __restrict__ G, int64_t np,
                                                                        double* __restrict__ P, int T,
                                                                        int32_t* __restrict__ info,
                                                                        int* __restrict__ fail) {
@@ -656,7 +656,7 @@ __global__ __launch_bounds__(kGemmThreads) void chol_diag_panel_kernel(double* _
 
 // Update of block (i, j) by step k.  M_kk is read from tile 0 of the panel
 // buffer P.
-__device__ void trail_body(GemmLds& s, double* __restrict__ G, int64_t np, const double* __restrict__ P, int k,
+__device__ __forceinline__ void trail_body(GemmLds& s, double* __restrict__ G, int64_t np, const double* __restrict__ P, int k,
                            int64_t i, int64_t j) {
     const double* Pi = P + i * NB * NB;
     double* Gij = G + i * NB * np + j * NB;
@@ -675,7 +675,7 @@ __device__ void trail_body(GemmLds& s, double* __restrict__ G, int64_t np, const
 // The early update of step k: the blocks step k+1 reads first (column and
 // row block k+1), one per workgroup, plus one workgroup that copies M_kk
 // into G_kk (nothing reads G_kk after the diagonal-block launch of step k).
-__global__ __launch_bounds__(kGemmThreads) void chol_next_kernel(double* __restrict__ G, int64_t np,
+__global__ __launch_bounds__(kGemmThreads, 2) void chol_next_kernel(double* __restrict__ G, int64_t np,
                                                                  const double* __restrict__ P, int k, int T,
                                                                  const int* __restrict__ fail) {
     __shared__ GemmLds s;
@@ -699,7 +699,7 @@ __global__ __launch_bounds__(kGemmThreads) void chol_next_kernel(double* __restr
 // others).  Both need only the early update of step k; they touch disjoint
 // blocks (the rest excludes column and row block k+1) and different panel
 // buffers, so no stream or event separates them.
-__global__ __launch_bounds__(kGemmThreads) void chol_step_kernel(double* __restrict__ G, int64_t np,
+__global__ __launch_bounds__(kGemmThreads, 2) void chol_step_kernel(double* __restrict__ G, int64_t np,
                                                                  double* __restrict__ Pk1,
                                                                  const double* __restrict__ Pk, int k, int T,
                                                                  int npan, int32_t* __restrict__ info,
