@@ -367,15 +367,19 @@ __device__ __forceinline__ int diag64(DiagLds& L) {
 // A is given row-major [64 rows][64 k] (lda); B is row-major [64 k][64 cols]
 // (ldb) or, with kBT, its transpose given row-major [64 cols][64 k].
 // All of K is fetched into registers at once (16 doubles of A and of B per
-// thread, every load in flight together), staged in LDS k-major, and the
-// four waves (2x2 grid, 32x32 each as 2x2 MFMA tiles) run 16 k-steps after
-// one barrier.  A direct B is staged with its columns XOR-swizzled by the k
-// row (low four bits) so that the staging writes spread over the banks;
-// the reads undo the swizzle.
+// thread, every load in flight together).  K is staged in LDS in two halves
+// of 32 through one buffer (36.9 KB, so more workgroups fit on a CU); in
+// every fetch map the threads 0..127 hold k < 32 and 128..255 the rest, so
+// each half is written by two whole waves.  The four waves (2x2 grid, 32x32
+// each as 2x2 MFMA tiles) run 8 k-steps per half.  A direct B is staged with
+// its columns XOR-swizzled by the k row (low four bits) so that the staging
+// writes spread over the banks; the reads undo the swizzle.
 // ---------------------------------------------------------------------------
+constexpr int kHalf = NB / 2;
+
 struct GemmLds {
-    double A[NB][kLdsLd];  // [k][row]
-    double B[NB][kLdsLd];  // [k][col] (swizzled when B is given direct)
+    double A[kHalf][kLdsLd];  // [k - 32h][row]
+    double B[kHalf][kLdsLd];  // [k - 32h][col] (swizzled when B is given direct)
 };
 
 struct GemmRegs {
@@ -405,33 +409,31 @@ __device__ __forceinline__ void gemm_fetch(GemmRegs& r, const double* __restrict
     gemm_fetch_b<kBT>(r.b, B, ldb, tid);
 }
 
-__device__ __forceinline__ void gemm_stash_a(const double (&a)[16], GemmLds& s, int tid) {
+// stage this thread's part of half h (threads 128h .. 128h+127 hold it)
+__device__ __forceinline__ void gemm_stash_a(const double (&a)[16], GemmLds& s, int tid, int h) {
+    if ((tid >> 7) != h) return;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s.A[(tid >> 6) * 16 + e][tid & 63] = a[e];
+    for (int e = 0; e < 16; ++e) s.A[((tid >> 6) & 1) * 16 + e][tid & 63] = a[e];
 }
 template <bool kBT>
-__device__ __forceinline__ void gemm_stash_b(const double (&b)[16], GemmLds& s, int tid) {
+__device__ __forceinline__ void gemm_stash_b(const double (&b)[16], GemmLds& s, int tid, int h) {
+    if ((tid >> 7) != h) return;
     if (kBT) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s.B[(tid >> 6) * 16 + e][tid & 63] = b[e];
+        for (int e = 0; e < 16; ++e) s.B[((tid >> 6) & 1) * 16 + e][tid & 63] = b[e];
     } else {
-        const int k = tid >> 2;
+        const int k = (tid >> 2) & (kHalf - 1);
 #pragma unroll
         for (int e = 0; e < 16; ++e) s.B[k][swz(k, (tid & 3) * 16 + e)] = b[e];
     }
 }
-template <bool kBT>
-__device__ __forceinline__ void gemm_stash(const GemmRegs& r, GemmLds& s, int tid) {
-    gemm_stash_a(r.a, s, tid);
-    gemm_stash_b<kBT>(r.b, s, tid);
-}
 
 template <bool kBT>
-__device__ __forceinline__ void gemm_compute(const GemmLds& s, double4v (&acc)[2][2]) {
+__device__ __forceinline__ void gemm_compute_half(const GemmLds& s, double4v (&acc)[2][2]) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wi = w >> 1, wj = w & 1;
 #pragma unroll
-    for (int ks = 0; ks < NB; ks += 4) {
+    for (int ks = 0; ks < kHalf; ks += 4) {
         const int k = ks + (lane >> 4);
         double av[2], bv[2];
 #pragma unroll
@@ -448,15 +450,27 @@ __device__ __forceinline__ void gemm_compute(const GemmLds& s, double4v (&acc)[2
     }
 }
 
+// both halves from fetched registers
+template <bool kBT>
+__device__ __forceinline__ void gemm_stage_compute(const GemmRegs& r, GemmLds& s, double4v (&acc)[2][2]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (h) __syncthreads();  // every wave is done with half 0
+        gemm_stash_a(r.a, s, tid, h);
+        gemm_stash_b<kBT>(r.b, s, tid, h);
+        __syncthreads();
+        gemm_compute_half<kBT>(s, acc);
+    }
+}
+
 template <bool kBT>
 __device__ __forceinline__ void tile_gemm_f64(const double* __restrict__ A, int64_t lda,
                                               const double* __restrict__ B, int64_t ldb, GemmLds& s,
                                               double4v (&acc)[2][2]) {
     GemmRegs regs;
     gemm_fetch<kBT>(regs, A, lda, B, ldb, threadIdx.x);
-    gemm_stash<kBT>(regs, s, threadIdx.x);
-    __syncthreads();
-    gemm_compute<kBT>(s, acc);
+    gemm_stage_compute<kBT>(regs, s, acc);
 }
 
 // C[row][col] of the accumulator element (m, q, v) of this thread
@@ -484,14 +498,12 @@ __device__ __forceinline__ void tile_gemm_sub_f64(const double* __restrict__ A, 
         for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int v = 0; v < 4; ++v) c[m][q][v] = C[(int64_t)acc_row(m, v) * ldc + acc_col(q)];
-    gemm_stash<kBT>(regs, s, threadIdx.x);
-    __syncthreads();
     double4v acc[2][2];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int q = 0; q < 2; ++q) acc[m][q] = (double4v){};
-    gemm_compute<kBT>(s, acc);
+    gemm_stage_compute<kBT>(regs, s, acc);
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -582,27 +594,31 @@ __device__ __forceinline__ void diag_panel_body(DiagPanelLds& u, double* __restr
     GemmLds& s = u.gemm;
     double4v acc[2][2];
     zero_acc(acc);
-    if (inv_row) {
+    // m = 0..7 fall in k-half 0 (kk = 4m + tid/64 < 32), m = 8..15 in half 1
 #pragma unroll
-        for (int m = 0; m < NB * NB / kGemmThreads; ++m) {
-            const int e = tid + kGemmThreads * m;
-            s.A[e >> 6][e & 63] = mv[m];
-        }
-        gemm_stash_b<false>(opnd, s, tid);
-        __syncthreads();
-        gemm_compute<false>(s, acc);
-        tile_store_f64<0>(G + (int64_t)k * NB * np + (int64_t)t * NB, np, acc);
-    } else {
-        gemm_stash_a(opnd, s, tid);
+    for (int h = 0; h < 2; ++h) {
+        if (h) __syncthreads();
+        if (inv_row) {
 #pragma unroll
-        for (int m = 0; m < NB * NB / kGemmThreads; ++m) {
-            const int e = tid + kGemmThreads * m;
-            s.B[e >> 6][e & 63] = mv[m];
+            for (int m = 8 * h; m < 8 * h + 8; ++m) {
+                const int e = tid + kGemmThreads * m;
+                s.A[(e >> 6) - kHalf * h][e & 63] = mv[m];
+            }
+            gemm_stash_b<false>(opnd, s, tid, h);
+        } else {
+            gemm_stash_a(opnd, s, tid, h);
+#pragma unroll
+            for (int m = 8 * h; m < 8 * h + 8; ++m) {
+                const int e = tid + kGemmThreads * m;
+                s.B[(e >> 6) - kHalf * h][e & 63] = mv[m];
+            }
         }
         __syncthreads();
-        gemm_compute<true>(s, acc);
-        tile_store_f64<0>(P + (int64_t)(t + 1) * NB * NB, NB, acc);
+        if (inv_row) gemm_compute_half<false>(s, acc);
+        else gemm_compute_half<true>(s, acc);
     }
+    if (inv_row) tile_store_f64<0>(G + (int64_t)k * NB * np + (int64_t)t * NB, np, acc);
+    else tile_store_f64<0>(P + (int64_t)(t + 1) * NB * NB, NB, acc);
 }
 
 // Tile sets of the update of step k (blocks (i, j) with k < i, j <= i):
