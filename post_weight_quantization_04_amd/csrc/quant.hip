@@ -495,7 +495,7 @@ constexpr int kEs = kTK + 1;   // E stage row stride (odd)
 constexpr int kUs = kTT + 4;   // U stage row stride
 
 struct TrailLds {
-    float E[2][kTT * kEs];
+    float E[2][kTrailRows * kEs];  // sized for the 64-row tiles in use (50.7 KB in all: three workgroups per CU)
     float U[2][kTK * kUs];
 };
 
@@ -561,6 +561,7 @@ __global__ __launch_bounds__(256) void trail_kernel(float* __restrict__ Wk, int6
                                                     const float* __restrict__ E, int64_t ldE,
                                                     const float* __restrict__ U, int64_t b0, int64_t b1,
                                                     int64_t c_begin, int64_t c_end) {
+    static_assert(kRT <= kTrailRows, "the E stage is sized for kTrailRows rows");
     constexpr int kM = kRT / 64;  // MFMA row tiles per wave
     __shared__ TrailLds s;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
