@@ -141,11 +141,12 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(const float* __restr
 // Only lower-triangle entries are read; the block returned holds exact
 // zeros above the diagonal.
 // ---------------------------------------------------------------------------
+// 1/sqrt(x) to float64 accuracy: v_rsq_f64 refined by the second-order
+// step y0 (1 + e/2 + 3e^2/8), e = 1 - x y0^2.
 __device__ __forceinline__ double rsqrt_f64(double x) {
-    double y = __builtin_amdgcn_rsq(x);
-    const double h = 0.5 * x * y;
-    y = fma(y, fma(-h, y, 0.5), y);
-    return y;
+    const double y = __builtin_amdgcn_rsq(x);
+    const double e = fma(-(x * y), y, 1.0);
+    return fma(fma(0.375, e, 0.5) * e, y, y);
 }
 
 constexpr int kSb = 16;           // sub-block width
@@ -189,65 +190,84 @@ __device__ __forceinline__ double read_lane(double x, int l) {
     return join64((uint32_t)__builtin_amdgcn_readlane((int)lo32(x), l), (uint32_t)__builtin_amdgcn_readlane((int)hi32(x), l));
 }
 
-// Pivot C of the 16x16 elimination [A | I] -> [* | Ls] in one wave, raw
-// symmetric form: t_r = A_rC / p for r > C (0 otherwise); A_rj -= t_r A_Cj
-// for j > C; B_rj -= t_r B_Cj for j <= C; then row C of B is scaled by
-// 1/sqrt(p).  Lane (g = lane/16, j = lane%16) holds A[4g+e][j] and
-// B[4g+e][j], e = 0..3.  `first` records 1 + the first pivot that is not
-// positive (the elimination then runs on without effect on the result).
+// 1/x to float64 accuracy: v_rcp_f64 refined by the cubic step
+// y0 (1 + e + e^2), e = 1 - x y0 (three dependent FMAs).
+__device__ __forceinline__ double rcp_f64(double x) {
+    const double y = __builtin_amdgcn_rcp(x);
+    const double e = fma(-x, y, 1.0);
+    return fma(fma(e, e, e), y, y);
+}
+
+// Pivot C of the symmetric elimination of a 16x16 block A = L D L^T, kept
+// in one array per lane.  With u_r = A_rC / p (p the pivot), every row r
+// below C takes A_rj -= u_r A_Cj; column C of row r then keeps A_rC, which
+// is -p times the entry (r, C) of L_unit^-1 (row operations applied to the
+// identity).  That scaling is the same in every row, so the later pivots
+// update those entries in place like the rest.  The pivot row is cleared
+// from column C on after it has been broadcast (the broadcast copy carries
+// a zero at C, which leaves column C as it is), so that no later pivot
+// touches a row above it.  Lane (g = lane/16, j = lane%16) holds rows
+// 4g .. 4g+3 of column j; pj collects the pivot of column j.  `first`
+// records 1 + the first pivot that is not positive.
 template <int C>
-__device__ __forceinline__ void gj_step(int g, int j, double (&a)[4], double (&b)[4], int& first) {
+__device__ __forceinline__ void gj_step(int g, int j, double (&x)[4], double& pj, int& first) {
     constexpr int R = C >> 2, S = C & 3;
-    const double p = read_lane(a[S], kSb * R + C);
+    const double p = read_lane(x[S], kSb * R + C);
     if (!(p > 0.0) && first == 0) first = C + 1;
-    const double rs = rsqrt_f64(p);
-    const double inv = rs * rs;
-    const double ar = bcast_row<R>(a[S]);  // A[C][j]
-    const double br = bcast_row<R>(b[S]);  // B[C][j]
-    const double aj = (j > C) ? ar : 0.0;
-    const double bj = (j <= C) ? br : 0.0;
+    const double inv = rcp_f64(p);
+    const double yrow = bcast_row<R>((j == C) ? 0.0 : x[S]);  // A[C][j], zero at j = C
+    if (g == R && j >= C) x[S] = 0.0;
+    if (j == C) pj = p;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const double v = bcast_in_row<C>(a[e]);  // A[4g+e][C]
-        const double t = (4 * g + e > C) ? v * inv : 0.0;
-        a[e] = fma(-t, aj, a[e]);
-        b[e] = fma(-t, bj, b[e]);
+        const double u = bcast_in_row<C>(x[e]) * inv;  // A[4g+e][C] / p, zero for rows <= C
+        x[e] = fma(-u, yrow, x[e]);
     }
-    if (g == R) b[S] *= rs;
 }
 
 // Sub-block s of L.g (one wave): Ls = inverse of its Cholesky factor,
-// written in place.  Returns 0, or 1 + the local column of the first pivot
-// that is not positive (wave-uniform).
+// written in place (exact zeros above the diagonal).  After the pivots,
+// entry (r, j < r) is -p_j (L_unit^-1)_rj and Ls = D^-1/2 L_unit^-1.
+// Returns 0, or 1 + the local column of the first pivot that is not
+// positive (wave-uniform).
 __device__ __forceinline__ int gj16(DiagLds& L, int s, int lane) {
     const int g = lane >> 4, j = lane & 15;
     const int o = kSb * s;
-    double a[4], b[4];
+    double x[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int r = 4 * g + e;
-        a[e] = (r >= j) ? L.g[o + r][o + j] : L.g[o + j][o + r];  // symmetric from the lower triangle
-        b[e] = (r == j) ? 1.0 : 0.0;
+        x[e] = (r >= j) ? L.g[o + r][o + j] : L.g[o + j][o + r];  // symmetric from the lower triangle
     }
+    double pj = 1.0;
     int first = 0;
-    gj_step<0>(g, j, a, b, first);
-    gj_step<1>(g, j, a, b, first);
-    gj_step<2>(g, j, a, b, first);
-    gj_step<3>(g, j, a, b, first);
-    gj_step<4>(g, j, a, b, first);
-    gj_step<5>(g, j, a, b, first);
-    gj_step<6>(g, j, a, b, first);
-    gj_step<7>(g, j, a, b, first);
-    gj_step<8>(g, j, a, b, first);
-    gj_step<9>(g, j, a, b, first);
-    gj_step<10>(g, j, a, b, first);
-    gj_step<11>(g, j, a, b, first);
-    gj_step<12>(g, j, a, b, first);
-    gj_step<13>(g, j, a, b, first);
-    gj_step<14>(g, j, a, b, first);
-    gj_step<15>(g, j, a, b, first);
+    gj_step<0>(g, j, x, pj, first);
+    gj_step<1>(g, j, x, pj, first);
+    gj_step<2>(g, j, x, pj, first);
+    gj_step<3>(g, j, x, pj, first);
+    gj_step<4>(g, j, x, pj, first);
+    gj_step<5>(g, j, x, pj, first);
+    gj_step<6>(g, j, x, pj, first);
+    gj_step<7>(g, j, x, pj, first);
+    gj_step<8>(g, j, x, pj, first);
+    gj_step<9>(g, j, x, pj, first);
+    gj_step<10>(g, j, x, pj, first);
+    gj_step<11>(g, j, x, pj, first);
+    gj_step<12>(g, j, x, pj, first);
+    gj_step<13>(g, j, x, pj, first);
+    gj_step<14>(g, j, x, pj, first);
+    gj_step<15>(g, j, x, pj, first);
+    const double nrj = -rcp_f64(pj);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) L.g[o + 4 * g + e][o + j] = b[e];
+    for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        // the pivot of row r sits in lane 16 g + r (column r of the same row group)
+        const int src = 4 * (kSb * g + r);
+        const double pr = join64((uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)lo32(pj)),
+                                 (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)hi32(pj)));
+        const double rs = rsqrt_f64(pr);
+        L.g[o + r][o + j] = (r < j) ? 0.0 : (r == j) ? rs : rs * (x[e] * nrj);
+    }
     return first;
 }
 
