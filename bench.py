@@ -32,7 +32,7 @@ KERNEL_CLASS = {
     "hessian_f16": ("f16", "mfma"),
     "hessian_f32": ("f32", "mfma"),
     "chol_step": ("f64", "mfma"),
-    "chol_next": ("f64", "mfma"),
+    "q_step": ("f32", "mfma"),
     "q_trail": ("f32", "mfma"),
 }
 
@@ -40,9 +40,8 @@ KERNEL_CLASS = {
 # kernel class -> (source file, kernel symbol) for the HBM traffic record
 KERNEL_SOURCE = {
     "chol_step": ("hinv.hip", "chol_step_kernel"),
-    "chol_next": ("hinv.hip", "chol_next_kernel"),
     "q_trail": ("quant.hip", "trail_kernel"),
-    "q_sweep": ("quant.hip", "sweep_kernel"),
+    "q_step": ("quant.hip", "step_kernel"),
     "hessian_f16": ("hessian.hip", "hessian_f16_kernel"),
 }
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "attn_proj_4096x4096_traffic.json")
@@ -73,38 +72,38 @@ def recorded_traffic(name: str):
     return rec["bytes_per_launch"]
 
 
-def algorithmic_flops(name: str, d_out: int, d_in: int, n_tok: int, block: int) -> float:
+def algorithmic_flops(name: str, d_out: int, d_in: int, n_tok: int, block: int, group: int = 0) -> float:
     """Flops the method needs in the work a kernel class does in one layer."""
     n = d_in
     if name.startswith("hessian"):
         return float(n) * (n + 1) * n_tok
-    if name in ("chol_step", "chol_next"):
+    if name == "chol_step":
         # blocked Cholesky of the reversed H with the inverse factor built
         # alongside; per step k, with m = n - 64(k+1) trailing rows and
         # c = 64(k+1) inverse columns, the update costs m(m+1)·64 (lower
-        # trailing part) + 2·m·c·64 (inverse part).  chol_next does the part
-        # of column and row block k+1; chol_step the rest of the update plus
-        # the 64x64 diagonal block (2/3·64³) and the panel (2·m·64² + 2·64²·64k).
-        nxt = step = 0.0
+        # trailing part) + 2·m·c·64 (inverse part), the 64x64 diagonal block
+        # 2/3·64³ and the panel 2·m·64² + 2·64²·64k.
+        tot = 0.0
         T = (n + NB - 1) // NB
         for k in range(T):
             m = max(0, n - (k + 1) * NB)
             c = min(n, (k + 1) * NB)
-            total = m * (m + 1) * NB + 2.0 * m * c * NB
-            part = 0.0
-            if m > 0:
-                w = min(NB, m)
-                part = 2.0 * NB * ((m - w) * w + w * (w + 1) / 2) + 2.0 * w * c * NB
-            nxt += part
-            step += total - part
-            step += 2.0 / 3.0 * NB ** 3 + 2.0 * m * NB * NB + 2.0 * NB * NB * min(n, k * NB)
-        return nxt if name == "chol_next" else step
-    if name == "q_trail":
-        tot = 0.0
+            tot += m * (m + 1) * NB + 2.0 * m * c * NB
+            tot += 2.0 / 3.0 * NB ** 3 + 2.0 * m * NB * NB + 2.0 * NB * NB * min(n, k * NB)
+        return tot
+    if name in ("q_step", "q_trail"):
+        # the lazy trailing update W[:, b1:] -= E U[b0:b1, b1:] of every block;
+        # q_step carries all of it except, for groups wider than the block,
+        # the part a group start takes up front (q_trail)
+        step = trail = 0.0
         for b0 in range(0, n, block):
             b1 = min(b0 + block, n)
-            tot += 2.0 * d_out * (b1 - b0) * (n - b1)
-        return tot
+            f = 2.0 * d_out * (b1 - b0) * (n - b1)
+            if group > block and b1 % group == 0 and b1 < n:
+                trail += 2.0 * d_out * (b1 - b0) * (n - b1)
+            else:
+                step += f
+        return step if name == "q_step" else trail
     return 0.0
 
 
@@ -281,7 +280,7 @@ def main(argv=None) -> int:
         return 1
 
     dclass, bound = KERNEL_CLASS.get(dominant, ("f32", "alu"))
-    flops_step = algorithmic_flops(dominant, d_out, d_in, n_tok, wl.block_size)
+    flops_step = algorithmic_flops(dominant, d_out, d_in, n_tok, wl.block_size, wl.group_size)
     dom_ms_step = dom_ms / max(args.steps, 1)
     achieved = flops_step / (dom_ms_step * 1e-3) / 1e12 if dom_ms_step > 0 else 0.0
     peak = PEAK_TFLOPS[dclass]

@@ -16,9 +16,8 @@ namespace gptq {
 // ---------------------------------------------------------------------------
 namespace {
 const char* const kNames[K_COUNT] = {
-    "hessian_f16", "hessian_f32", "hinv_diag_stats", "hinv_load_reversed", "chol_step",
-    "chol_next",  "hinv_store_u", "q_row_grid",     "q_convert",          "q_rdiag",   "q_group_grid",
-    "q_sweep",     "q_trail",
+    "hessian_f16", "hessian_f32", "hinv_diag_stats", "hinv_load_reversed", "chol_step", "hinv_store_u",
+    "q_row_grid",  "q_convert",   "q_rdiag",         "q_group_grid",       "q_step",    "q_trail",
 };
 int g_timed = -1;
 struct EventPair {
@@ -51,25 +50,6 @@ TimedLaunch::TimedLaunch(int id, hipStream_t s) : slot(-1), stream(s) {
 
 TimedLaunch::~TimedLaunch() {
     if (slot >= 0) (void)hipEventRecord(g_pending[slot].b, stream);
-}
-
-namespace {
-SideStream g_side[64];
-}
-
-hipError_t side_stream(SideStream*& out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    SideStream& ss = g_side[dev];
-    if (!ss.side) {
-        if ((e = hipStreamCreateWithFlags(&ss.side, hipStreamNonBlocking)) != hipSuccess) return e;
-        if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
-        if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
-    }
-    out = &ss;
-    return hipSuccess;
 }
 
 }  // namespace gptq

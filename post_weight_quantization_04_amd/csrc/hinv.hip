@@ -641,43 +641,216 @@ __device__ __forceinline__ void diag_panel_body(DiagPanelLds& u, double* __restr
     else tile_store_f64<0>(P + (int64_t)(t + 1) * NB * NB, NB, acc);
 }
 
-// Tile sets of the update of step k (blocks (i, j) with k < i, j <= i):
-//   kSetAll   every block;
-//   kSetNext  the blocks step k+1 reads first: column block k+1 (i >= k+1)
-//             and row block k+1 (j <= k), T blocks in all;
-//   kSetRest  the others: i > k+1, j <= i, j != k+1.
-enum { kSetAll = 0, kSetNext = 1, kSetRest = 2 };
-
-__host__ __device__ inline int64_t tiles_in_set(int set, int k, int T) {
-    const int64_t all = (int64_t)T * (T + 1) / 2 - (int64_t)(k + 1) * (k + 2) / 2;
-    if (set == kSetAll) return all;
-    const int64_t next = (k + 1 < T) ? T : 0;
-    return set == kSetNext ? next : all - next;
+// A 64x64 tile held in accumulator layout (element (m, q, v) of each
+// thread at acc_row(m, v), acc_col(q)).
+__device__ __forceinline__ void tile_load_acc(double (&c)[2][2][4], const double* __restrict__ C, int64_t ldc) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) c[m][q][v] = C[(int64_t)acc_row(m, v) * ldc + acc_col(q)];
 }
 
-__device__ __forceinline__ void set_tile(int set, int k, int T, int64_t b, int64_t& i, int64_t& j) {
-    if (set == kSetAll) {
-        tri_index((int64_t)(k + 1) * (k + 2) / 2 + b, i, j);
-    } else if (set == kSetNext) {
-        const int64_t ncol = T - (k + 1);  // column block k+1, rows k+1 .. T-1
-        if (b < ncol) {
-            i = k + 1 + b;
-            j = k + 1;
+// Stage half h (k = 32h .. 32h+31) of an accumulator-layout tile X as the
+// operand A = X (s.A[k][row]); the columns of half h sit in waves w & 1 == h.
+__device__ __forceinline__ void stash_acc_as_a(const double (&x)[2][2][4], GemmLds& s, int h) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if ((w & 1) != h) return;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) s.A[16 * q + (lane & 15)][acc_row(m, v)] = x[m][q][v];
+}
+
+// ... as the direct operand B = X (s.B[k][swz(k, col)]); the rows of half h
+// sit in waves w >> 1 == h.
+__device__ __forceinline__ void stash_acc_as_b(const double (&x)[2][2][4], GemmLds& s, int h) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if ((w >> 1) != h) return;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int kl = 16 * m + 4 * v + (lane >> 4);
+                s.B[kl][swz(kl, acc_col(q))] = x[m][q][v];
+            }
+}
+
+// Diagonal block and panel of step k1 = k+1, with the update of step k of
+// the blocks they read applied in the same workgroup (in registers, none of
+// it written back): every workgroup forms D = G_k1k1 - P_k1 P_k1^T (the
+// diagonal block after step k) and its own operand after step k,
+//   t >= k1:  G_{t+1,k1} - P_{t+1} P_k1^T   (column block k1),
+//   t == k:   -P_k1 M_kk                    (row block k1, G_{k1,k} = -P_k1 M_kk),
+//   t <  k:   G_{k1,t} - P_k1 M_kt          (row block k1, M_kt in place in G_kt),
+// with P_i and M_kk from the panel buffer of step k (Pk).  D is factored and
+// inverted as in diag_panel_body and the panel tile formed from the
+// updated operand: t < k1: M_k1t = M_k1k1 G_k1t (in place); t >= k1:
+// P_{t+1} = G_{t+1,k1} M_k1k1^T into the panel buffer of step k1 (Pk1).
+// The column-block blocks G_{t+1,k1} keep their old values: step k1
+// overwrites them from P_{t+1} alone.
+// The diagonal block and the product staging in separate storage (71 KB),
+// so that D goes to LDS as soon as it is formed.
+struct DiagPanelNextLds {
+    DiagLds diag;
+    GemmLds gemm;
+};
+
+__device__ __forceinline__ void diag_panel_next_body(DiagPanelNextLds& u, double* __restrict__ G, int64_t np,
+                                                     double* __restrict__ Pk1, const double* __restrict__ Pk, int k,
+                                                     int T, int t, int32_t* __restrict__ info,
+                                                     int* __restrict__ fail) {
+    const int tid = threadIdx.x;
+    const int k1 = k + 1;
+    const bool has_tile = t < T - 1;
+    const bool inv_row = t < k1;
+    GemmLds& s = u.gemm;
+    DiagLds& L = u.diag;
+    const double* Pd = Pk + (int64_t)k1 * NB * NB;  // P_k1 of step k
+    // operands of both products in flight at once: P_k1 serves as A and as
+    // B^T of the first product and as one operand of the second
+    double pd[16];
+    gemm_fetch_a(pd, Pd, NB, tid);
+    double xo[16];
+    double c2[2][2][4];
+    if (has_tile) {
+        if (!inv_row) {
+            gemm_fetch_a(xo, Pk + (int64_t)(t + 1) * NB * NB, NB, tid);
+            tile_load_acc(c2, G + (int64_t)(t + 1) * NB * np + (int64_t)k1 * NB, np);
+        } else if (t == k) {
+            gemm_fetch_b<false>(xo, Pk, NB, tid);  // M_kk (zeros above the diagonal)
         } else {
-            i = k + 1;
-            j = b - ncol;
+            gemm_fetch_b<false>(xo, G + (int64_t)k * NB * np + (int64_t)t * NB, np, tid);
+            tile_load_acc(c2, G + (int64_t)k1 * NB * np + (int64_t)t * NB, np);
         }
-    } else {
-        // rows i >= k+2 hold i blocks each (j in 0..i without k+1); rows
-        // before i contribute i(i-1)/2 - (k+1)(k+2)/2 blocks
-        const int64_t c0 = (int64_t)(k + 1) * (k + 2) / 2;
-        int64_t r = (int64_t)((1.0 + sqrt(1.0 + 8.0 * (double)(b + c0))) * 0.5);
-        while (r * (r - 1) / 2 - c0 > b) --r;
-        while ((r + 1) * r / 2 - c0 <= b) ++r;
-        i = r;
-        const int64_t jj = b - (r * (r - 1) / 2 - c0);
-        j = (jj < k + 1) ? jj : jj + 1;
     }
+    {
+        const double* blk = G + (int64_t)k1 * NB * np + (int64_t)k1 * NB;
+#pragma unroll
+        for (int m = 0; m < NB * NB / kGemmThreads; ++m) {
+            const int idx = tid + kGemmThreads * m;
+            L.g[idx >> 6][idx & 63] = blk[(int64_t)(idx >> 6) * np + (idx & 63)];
+        }
+    }
+    double4v acc[2][2];
+    zero_acc(acc);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (h) __syncthreads();
+        gemm_stash_a(pd, s, tid, h);
+        gemm_stash_b<true>(pd, s, tid, h);
+        __syncthreads();
+        gemm_compute_half<true>(s, acc);
+    }
+    // D = G_k1k1 - P_k1 P_k1^T in place (every element is this thread's own)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) L.g[acc_row(m, v)][acc_col(q)] -= acc[m][q][v];
+    if (has_tile) {
+        zero_acc(acc);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            __syncthreads();
+            if (!inv_row) {
+                gemm_stash_a(xo, s, tid, h);
+                gemm_stash_b<true>(pd, s, tid, h);
+            } else {
+                gemm_stash_a(pd, s, tid, h);
+                gemm_stash_b<false>(xo, s, tid, h);
+            }
+            __syncthreads();
+            if (!inv_row) gemm_compute_half<true>(s, acc);
+            else gemm_compute_half<false>(s, acc);
+        }
+        const bool neg = inv_row && t == k;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) c2[m][q][v] = neg ? -acc[m][q][v] : c2[m][q][v] - acc[m][q][v];
+    }
+    __syncthreads();
+    const int st = diag64(L);
+    if (st) {
+        if (t == 0 && tid == 0) {
+            *info = k1 * NB + st;
+            *fail = 1;
+        }
+        return;
+    }
+    if (t == 0) {
+#pragma unroll
+        for (int m = 0; m < NB * NB / kGemmThreads; ++m) {
+            const int idx = tid + kGemmThreads * m;
+            const int r = idx >> 6, c = idx & 63;
+            Pk1[idx] = (c <= r) ? L.g[r][c] : 0.0;
+        }
+    }
+    if (!has_tile) return;
+    double mv[NB * NB / kGemmThreads];
+#pragma unroll
+    for (int m = 0; m < NB * NB / kGemmThreads; ++m) {
+        const int e = tid + kGemmThreads * m;
+        const int kk = e >> 6, x = e & 63;
+        mv[m] = (kk <= x) ? L.g[x][kk] : 0.0;
+    }
+    __syncthreads();
+    zero_acc(acc);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (h) __syncthreads();
+        if (inv_row) {
+#pragma unroll
+            for (int m = 8 * h; m < 8 * h + 8; ++m) {
+                const int e = tid + kGemmThreads * m;
+                s.A[(e >> 6) - kHalf * h][e & 63] = mv[m];
+            }
+            stash_acc_as_b(c2, s, h);
+        } else {
+            stash_acc_as_a(c2, s, h);
+#pragma unroll
+            for (int m = 8 * h; m < 8 * h + 8; ++m) {
+                const int e = tid + kGemmThreads * m;
+                s.B[(e >> 6) - kHalf * h][e & 63] = mv[m];
+            }
+        }
+        __syncthreads();
+        if (inv_row) gemm_compute_half<false>(s, acc);
+        else gemm_compute_half<true>(s, acc);
+    }
+    if (inv_row) tile_store_f64<0>(G + (int64_t)k1 * NB * np + (int64_t)t * NB, np, acc);
+    else tile_store_f64<0>(Pk1 + (int64_t)(t + 1) * NB * NB, NB, acc);
+}
+
+// The rest of the update of step k: the blocks (i, j), j <= i, with
+// i > k+1 and j != k+1 (column and row block k+1 are updated inside the
+// diagonal-block workgroups of step k+1).  Of the T(T+1)/2 - (k+1)(k+2)/2
+// blocks below row k, T - k - 1 lie in column block k+1 and k + 1 in row
+// block k+1.
+__host__ __device__ inline int64_t rest_tiles(int k, int T) {
+    const int64_t all = (int64_t)T * (T + 1) / 2 - (int64_t)(k + 1) * (k + 2) / 2;
+    return (k + 1 < T) ? all - T : all;
+}
+
+__device__ __forceinline__ void rest_tile(int k, int64_t b, int64_t& i, int64_t& j) {
+    // rows i >= k+2 hold i blocks each (j in 0..i without k+1); rows before
+    // i contribute i(i-1)/2 - (k+1)(k+2)/2 blocks
+    const int64_t c0 = (int64_t)(k + 1) * (k + 2) / 2;
+    int64_t r = (int64_t)((1.0 + sqrt(1.0 + 8.0 * (double)(b + c0))) * 0.5);
+    while (r * (r - 1) / 2 - c0 > b) --r;
+    while ((r + 1) * r / 2 - c0 <= b) ++r;
+    i = r;
+    const int64_t jj = b - (r * (r - 1) / 2 - c0);
+    j = (jj < k + 1) ? jj : jj + 1;
 }
 
 // Diagonal block and panel of step 0 (later steps run inside chol_step_kernel).
@@ -708,45 +881,33 @@ __device__ __forceinline__ void trail_body(GemmLds& s, double* __restrict__ G, i
     }
 }
 
-// The early update of step k: the blocks step k+1 reads first (column and
-// row block k+1), one per workgroup, plus one workgroup that copies M_kk
-// into G_kk (nothing reads G_kk after the diagonal-block launch of step k).
-__global__ __launch_bounds__(kGemmThreads, 2) void chol_next_kernel(double* __restrict__ G, int64_t np,
-                                                                 const double* __restrict__ P, int k, int T,
-                                                                 const int* __restrict__ fail) {
-    __shared__ GemmLds s;
-    if (*fail) return;
-    if (blockIdx.x == tiles_in_set(kSetNext, k, T)) {
-        double* Gkk = G + (int64_t)k * NB * np + (int64_t)k * NB;
-#pragma unroll
-        for (int m = 0; m < NB * NB / kGemmThreads; ++m) {
-            const int idx = threadIdx.x + kGemmThreads * m;
-            Gkk[(int64_t)(idx >> 6) * np + (idx & 63)] = P[idx];
-        }
-        return;
-    }
-    int64_t i, j;
-    set_tile(kSetNext, k, T, blockIdx.x, i, j);
-    trail_body(s, G, np, P, k, i, j);
-}
-
-// One launch for the diagonal block and panel of step k1 = k+1 (workgroups
-// 0 .. npan-1, dispatched first) and the rest of the update of step k (the
-// others).  Both need only the early update of step k; they touch disjoint
-// blocks (the rest excludes column and row block k+1) and different panel
-// buffers, so no stream or event separates them.
+// One launch per step k: the diagonal block and panel of step k1 = k+1
+// together with the update of step k of the blocks they read (workgroups
+// 0 .. npan-1, dispatched first), one workgroup that copies M_kk into G_kk
+// (nothing reads G_kk after the launch that factored it), and the rest of
+// the update of step k (the others).  The parts touch disjoint blocks (the
+// rest excludes column and row block k1) and different panel buffers, so
+// nothing but the launch order separates the steps.
 __global__ __launch_bounds__(kGemmThreads, 2) void chol_step_kernel(double* __restrict__ G, int64_t np,
                                                                  double* __restrict__ Pk1,
                                                                  const double* __restrict__ Pk, int k, int T,
                                                                  int npan, int32_t* __restrict__ info,
                                                                  int* __restrict__ fail) {
-    __shared__ __align__(16) DiagPanelLds u;
+    __shared__ __align__(16) DiagPanelNextLds u;
     if (*fail) return;
-    if ((int)blockIdx.x < npan) {
-        diag_panel_body(u, G, np, Pk1, k + 1, T, blockIdx.x, info, fail);
+    const int b = (int)blockIdx.x;
+    if (b < npan) {
+        diag_panel_next_body(u, G, np, Pk1, Pk, k, T, b, info, fail);
+    } else if (b == npan) {
+        double* Gkk = G + (int64_t)k * NB * np + (int64_t)k * NB;
+#pragma unroll
+        for (int m = 0; m < NB * NB / kGemmThreads; ++m) {
+            const int idx = threadIdx.x + kGemmThreads * m;
+            Gkk[(int64_t)(idx >> 6) * np + (idx & 63)] = Pk[idx];
+        }
     } else {
         int64_t i, j;
-        set_tile(kSetRest, k, T, (int64_t)blockIdx.x - npan, i, j);
+        rest_tile(k, (int64_t)(b - npan - 1), i, j);
         trail_body(u.gemm, G, np, Pk, k, i, j);
     }
 }
@@ -769,11 +930,11 @@ size_t hinv_workspace_bytes(int64_t n) {
 }
 
 
-// Schedule with one step of lookahead, on the caller's stream only: per step
-// k, the early update (the blocks step k+1 reads first), then one launch that
-// holds both the diagonal block and panel of step k+1 and the rest of the
-// update of step k.  The panel buffer alternates between steps; its tile 0
-// holds M_kk.
+// Schedule with one step of lookahead, on the caller's stream only: the
+// diagonal block and panel of step 0, then per step k one launch that holds
+// the diagonal block and panel of step k+1 (with the part of step k's update
+// they read) and the rest of step k's update.  The panel buffer alternates
+// between steps; its tile 0 holds M_kk.
 hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, float* U, uint8_t* dead,
                                int32_t* info, double* lambda_out, void* ws, hipStream_t s) {
     if (n == 0) return hipSuccess;
@@ -799,19 +960,11 @@ hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, floa
                            info, w.fail);
     }
     for (int k = 0; k < T; ++k) {
-        {
-            TimedLaunch t(K_CHOL_NEXT, s);
-            const int64_t n_next = tiles_in_set(kSetNext, k, T);
-            hipLaunchKernelGGL(chol_next_kernel, dim3((unsigned)(n_next + 1)), dim3(kGemmThreads), 0, s, w.G, np,
-                               (const double*)Pbuf[k & 1], k, T, (const int*)w.fail);
-        }
         const int np1 = (k + 1 < T) ? npan : 0;
-        const int64_t n_rest = tiles_in_set(kSetRest, k, T);
-        if (np1 + n_rest > 0) {
-            TimedLaunch t(K_CHOL_STEP, s);
-            hipLaunchKernelGGL(chol_step_kernel, dim3((unsigned)(np1 + n_rest)), dim3(kGemmThreads), 0, s, w.G, np,
-                               Pbuf[(k + 1) & 1], (const double*)Pbuf[k & 1], k, T, np1, info, w.fail);
-        }
+        const int64_t n_rest = rest_tiles(k, T);
+        TimedLaunch t(K_CHOL_STEP, s);
+        hipLaunchKernelGGL(chol_step_kernel, dim3((unsigned)(np1 + 1 + n_rest)), dim3(kGemmThreads), 0, s, w.G, np,
+                           Pbuf[(k + 1) & 1], (const double*)Pbuf[k & 1], k, T, np1, info, w.fail);
     }
     {
         TimedLaunch t(K_HINV_STORE, s);

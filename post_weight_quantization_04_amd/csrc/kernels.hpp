@@ -14,13 +14,12 @@ enum KernelId {
     K_HINV_DIAGSUM,
     K_HINV_LOAD,
     K_CHOL_STEP,
-    K_CHOL_NEXT,
     K_HINV_STORE,
     K_Q_ROWGRID,
     K_Q_CONVERT,
     K_Q_RDIAG,
     K_Q_GROUPGRID,
-    K_Q_SWEEP,
+    K_Q_STEP,
     K_Q_TRAIL,
     K_COUNT
 };
@@ -33,16 +32,6 @@ struct TimedLaunch {
     int slot;
     hipStream_t stream;
 };
-
-// Per-device side stream with fork/join events, used by the lookahead
-// schedules (created once at default priority; host-side state, not
-// thread-safe).
-struct SideStream {
-    hipStream_t side = nullptr;
-    hipEvent_t fork = nullptr;  // recorded on the caller's stream, waited on by the side stream
-    hipEvent_t join = nullptr;  // recorded on the side stream, waited on by the caller's stream
-};
-hipError_t side_stream(SideStream*& out);
 
 // ---- stage 1 ---------------------------------------------------------------
 hipError_t launch_hessian(float* H, int64_t n, const void* X, int x_is_f16, int64_t ntok,

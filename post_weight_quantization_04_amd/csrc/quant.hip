@@ -206,6 +206,23 @@ __device__ __forceinline__ void xpose_rows4(float& r0, float& r1, float& r2, flo
     swap16(r2, r3);
 }
 
+// Tile m of acc holds D[16m + l%16][4(l/16) + v] in lane l, register v
+// (D[row][c], 64 rows x 16 columns); the row transpose gives lane r the 16
+// entries of its own row, which are subtracted from wv.
+__device__ __forceinline__ void sub_row_deltas(float (&wv)[kSub], const float4v (&acc)[4]) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        // plain VALU copies: the asm reads registers the MFMA hazard rules
+        // no longer apply to
+        float r0 = acc[0][v] + 0.0f, r1 = acc[1][v] + 0.0f, r2 = acc[2][v] + 0.0f, r3 = acc[3][v] + 0.0f;
+        xpose_rows4(r0, r1, r2, r3);
+        wv[v] -= r0;
+        wv[4 + v] -= r1;
+        wv[8 + v] -= r2;
+        wv[12 + v] -= r3;
+    }
+}
+
 // The same fold-in on MFMA, for a wave whose 16 columns are all present:
 // D^T = U_blk^T E^T (16 columns x 64 rows, four 16x16 tiles, K = 16), so that
 // every lane reads its own operand words instead of a broadcast U row.
@@ -223,17 +240,32 @@ __device__ __forceinline__ void fold_in_mfma(float (&wv)[kSub], const float* __r
 #pragma unroll
         for (int m = 0; m < 4; ++m) acc[m] = mfma16x16x4_f32(a, ebp[(kk + g) * kEld + 16 * m + i], acc[m]);
     }
+    sub_row_deltas(wv, acc);
+}
+
+// Near update of this wave's columns by the scaled errors of the previous
+// block, before the sweep: wv[c] -= sum_k E_prev[row][k] U[bp0 + k][c0q + c]
+// over the kp columns of that block (the part of the lazy trailing update
+// that lands on this block), on MFMA 16x16x4 f32 as in fold_in_mfma.
+// E_prev^T is staged in LDS (et[k][row], zero rows up to a multiple of 4)
+// and the U operand comes prefetched in registers, ua[j] =
+// U[bp0 + 4j + l/16][c0q + l%16].
+constexpr int kEtl = kRowsPerWg + 1;  // padded LDS row of the staged E_prev^T
+
+__device__ __forceinline__ void near_update(float (&wv)[kSub], const float (&ua)[kMaxBlock / 4],
+                                            const float* __restrict__ et, int kp, int lane) {
+    const int i = lane & 15, g = lane >> 4;
+    float4v acc[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        // plain VALU copies: the asm reads registers the MFMA hazard rules
-        // no longer apply to
-        float r0 = acc[0][v] + 0.0f, r1 = acc[1][v] + 0.0f, r2 = acc[2][v] + 0.0f, r3 = acc[3][v] + 0.0f;
-        xpose_rows4(r0, r1, r2, r3);
-        wv[v] -= r0;
-        wv[4 + v] -= r1;
-        wv[8 + v] -= r2;
-        wv[12 + v] -= r3;
+    for (int m = 0; m < 4; ++m) acc[m] = (float4v){};
+#pragma unroll
+    for (int j = 0; j < kMaxBlock / 4; ++j) {
+        if (4 * j < kp) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) acc[m] = mfma16x16x4_f32(ua[j], et[(4 * j + g) * kEtl + 16 * m + i], acc[m]);
+        }
     }
+    sub_row_deltas(wv, acc);
 }
 
 // Rounds this wave's columns in order, compensating the later columns of
@@ -289,16 +321,21 @@ __device__ __forceinline__ void sweep_sub(float (&wv)[kSub], float s, float sinv
     }
 }
 
-// kAllFull: the block width is a multiple of 16, so every wave owns 16
-// columns and the unguarded code paths are the only ones compiled.
+// Sweep of rows 64 rt .. 64 rt + 63 (512 threads).  kAllFull: the block
+// width is a multiple of 16, so every wave owns 16 columns and the unguarded
+// code paths are the only ones compiled.  With kp > 0 the scaled errors Ep
+// of the previous block [bp0, bp0 + kp) are applied to this block's columns
+// first (near_update); the LDS then holds E_prev^T after the sweep's own
+// regions.
 template <bool kAllFull>
-__global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk, int64_t d_out, int64_t d_in,
-                                                    const float* __restrict__ U, const float* __restrict__ rdiag,
-                                                    int64_t b0, int64_t b1, int bits, int64_t group, int64_t ng,
-                                                    float* __restrict__ scales, int32_t* __restrict__ zeros,
-                                                    float* __restrict__ minmax, uint8_t* __restrict__ codes,
-                                                    float* __restrict__ E, int64_t ldE, float* __restrict__ err_row) {
-    extern __shared__ __align__(16) unsigned char smem[];
+__device__ __forceinline__ void sweep_body(unsigned char* smem, int rt, const float* __restrict__ Wk, int64_t d_out,
+                                           int64_t d_in, const float* __restrict__ U,
+                                           const float* __restrict__ rdiag, int64_t b0, int64_t b1, int bits,
+                                           int64_t group, int64_t ng, float* __restrict__ scales,
+                                           int32_t* __restrict__ zeros, float* __restrict__ minmax,
+                                           uint8_t* __restrict__ codes, float* __restrict__ E, int64_t ldE,
+                                           float* __restrict__ err_row, const float* __restrict__ Ep, int64_t bp0,
+                                           int kp) {
     const int bw = (int)(b1 - b0);
     const int nw = (bw + kSub - 1) / kSub;
     const int uld = kUld;
@@ -307,12 +344,15 @@ __global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk
     float* Ebuf = rdg + bw;                                               // 2*16*kEld
     float* red = Ebuf + 2 * kSub * kEld;                                  // nw*64*2
     float* errs = red + nw * 64 * 2;                                      // nw*64
+    float* et = errs + nw * 64;                                           // [kp rounded up to 4][kEtl]
 
     const int lane = threadIdx.x & 63;
     const int q = wave_id();
-    const int64_t R = (int64_t)blockIdx.x * kRowsPerWg + lane;
+    const int64_t R = (int64_t)rt * kRowsPerWg + lane;
     const bool rowok = R < d_out;
-    const int cq = kAllFull ? kSub : min(kSub, bw - kSub * q);  // >= 1
+    // waves past the block (q >= nw: a narrow block in a 512-thread launch)
+    // hold no columns and only take part in the barriers
+    const int cq = (q >= nw) ? 0 : kAllFull ? kSub : min(kSub, bw - kSub * q);
     const int64_t c0q = b0 + kSub * q;
     const float maxq = (float)((1 << bits) - 1);
 
@@ -341,6 +381,29 @@ __global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk
         if (rowok) {
             s = scales[R * ng + gi];
             zf = (float)zeros[R * ng + gi];
+        }
+    }
+
+    // near update operands: U rows of the previous block for this wave's
+    // columns, and 16 entries of E_prev per thread (row tid/8, k run 16 (tid%8))
+    float ua[kMaxBlock / 4];
+    float ep[16];
+    const int er = threadIdx.x >> 3, ek = (threadIdx.x & 7) * 16;
+    if (kp > 0) {
+        const int i = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int j = 0; j < kMaxBlock / 4; ++j) {
+            const int k = 4 * j + g;
+            ua[j] = (k < kp && i < cq) ? U[(bp0 + k) * d_in + c0q + i] : 0.0f;
+        }
+        const int64_t Re = (int64_t)rt * kRowsPerWg + er;
+        const float* src = Ep + Re * ldE + ek;
+        if (Re < d_out && ek + 16 <= kp && (ldE & 3) == 0 && (reinterpret_cast<uintptr_t>(Ep) & 15) == 0) {
+#pragma unroll
+            for (int e = 0; e < 16; e += 4) *reinterpret_cast<float4v*>(&ep[e]) = *reinterpret_cast<const float4v*>(src + e);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) ep[e] = (Re < d_out && ek + e < kp) ? src[e] : 0.0f;
         }
     }
 
@@ -382,16 +445,23 @@ __global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk
         }
     }
     for (int e = threadIdx.x; e < bw; e += nth) rdg[e] = rdiag[b0 + e];
+    if (kp > 0) {
+        const int kp4 = (kp + 3) & ~3;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            if (ek + e < kp4) et[(ek + e) * kEtl + er] = ep[e];
+    }
 
     float sinv = 1.0f / s;
     float errsq = 0.0f;
     __syncthreads();
+    if (kp > 0) near_update(wv, ua, et, kp, lane);
 
     for (int p = 0; p < nw; ++p) {
         // wave p carries the dependent chain of this phase: it gets issue
         // priority over the waves that only fold errors in for later phases
         if (q == p) __builtin_amdgcn_s_setprio(2);
-        if (p > 0 && q >= p) {
+        if (p > 0 && q >= p && q < nw) {
             // fold in the scaled errors of sub-block p-1 (16 full columns)
             const float* ebp = Ebuf + ((p - 1) & 1) * kSub * kEld;
             const float* ublk = Up + ublk_index(p - 1, q, nw) * (kSub * kSub);
@@ -469,7 +539,7 @@ __global__ __launch_bounds__(512) void sweep_kernel(const float* __restrict__ Wk
         }
         __syncthreads();
     }
-    errs[q * 64 + lane] = errsq;
+    if (q < nw) errs[q * 64 + lane] = errsq;
     __syncthreads();
 
     if (err_row && q == 0 && rowok) {
@@ -630,6 +700,137 @@ __global__ __launch_bounds__(256) void trail_kernel(float* __restrict__ Wk, int6
             }
 }
 
+// ---------------------------------------------------------------------------
+// The far part of the lazy trailing update inside the per-block launch:
+// W[r0 .. r0+128, c0 .. c0+256] -= E_prev[rows, :kp] U[bp0 .. bp0+kp, cols]
+// for the tile tb (row tile tb % rest_rows, column tile tb / rest_rows) of
+// the columns [c_begin, d_in).  512 threads: eight waves in a 4x2 grid, each
+// 32 rows x 128 columns as four MFMA 32x32x2 f32 tiles; K in chunks of 32
+// through two LDS buffers with a register prefetch, and the W tile read
+// ahead of the products.  The launch is one workgroup per CU (its LDS), so
+// the per-wave work is large and the registers plentiful.
+// ---------------------------------------------------------------------------
+constexpr int kRestRows = 128;
+constexpr int kRestCols = 256;
+constexpr int kRUs = kRestCols + 4;  // U stage row stride
+
+__host__ __device__ inline size_t rest_lds_bytes() {
+    return (size_t)(2 * kRestRows * kEs + 2 * kTK * kRUs) * 4;
+}
+
+__device__ __forceinline__ void rest_fetch(float (&e)[8], float (&u)[16], const float* __restrict__ E, int64_t ldE,
+                                           const float* __restrict__ U, int64_t d_out, int64_t d_in, int64_t r0,
+                                           int64_t c0, int64_t bp0, int kp, int kc, int tid, bool vec) {
+    {
+        const int64_t R = r0 + (tid >> 2);
+        const int k = kc + (tid & 3) * 8;
+        const float* src = E + R * ldE + k;
+        if (vec && R < d_out && k + 8 <= kp) {
+#pragma unroll
+            for (int x = 0; x < 8; x += 4) *reinterpret_cast<float4v*>(&e[x]) = *reinterpret_cast<const float4v*>(src + x);
+        } else {
+#pragma unroll
+            for (int x = 0; x < 8; ++x) e[x] = (R < d_out && k + x < kp) ? src[x] : 0.0f;
+        }
+    }
+    {
+        const int k = kc + (tid >> 4);
+        const int64_t col = c0 + (tid & 15) * 16;
+        const float* src = U + (bp0 + k) * d_in + col;
+        if (vec && k < kp && col + 16 <= d_in) {
+#pragma unroll
+            for (int x = 0; x < 16; x += 4) *reinterpret_cast<float4v*>(&u[x]) = *reinterpret_cast<const float4v*>(src + x);
+        } else {
+#pragma unroll
+            for (int x = 0; x < 16; ++x) u[x] = (k < kp && col + x < d_in) ? src[x] : 0.0f;
+        }
+    }
+}
+
+__device__ __forceinline__ void rest_body(unsigned char* smem, int64_t tb, int rest_rows, float* __restrict__ Wk,
+                                          int64_t d_out, int64_t d_in, const float* __restrict__ E, int64_t ldE,
+                                          const float* __restrict__ U, int64_t bp0, int kp, int64_t c_begin,
+                                          bool vec) {
+    float* Es = reinterpret_cast<float*>(smem);  // [2][kRestRows * kEs]
+    float* Us = Es + 2 * kRestRows * kEs;        // [2][kTK * kRUs]
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wi = w >> 1, wj = w & 1;
+    const int64_t r0 = (tb % rest_rows) * kRestRows;
+    const int64_t c0 = c_begin + (tb / rest_rows) * kRestCols;
+    const int nchunks = (kp + kTK - 1) / kTK;
+
+    float16v acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = (float16v){};
+    float e[8], u[16];
+    rest_fetch(e, u, E, ldE, U, d_out, d_in, r0, c0, bp0, kp, 0, tid, vec);
+    float wold[4][16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t row = r0 + wi * 32 + acc32_row(v, lane);
+            const int64_t col = c0 + wj * 128 + 32 * q + (lane & 31);
+            wold[q][v] = (row < d_out && col < d_in) ? Wk[row * d_in + col] : 0.0f;
+        }
+    for (int c = 0; c < nchunks; ++c) {
+        const int buf = c & 1;
+        {
+            float* ed = Es + buf * kRestRows * kEs + (tid >> 2) * kEs + (tid & 3) * 8;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) ed[x] = e[x];
+            float* ud = Us + buf * kTK * kRUs + (tid >> 4) * kRUs + (tid & 15) * 16;
+#pragma unroll
+            for (int x = 0; x < 16; x += 4) *reinterpret_cast<float4v*>(&ud[x]) = *reinterpret_cast<const float4v*>(&u[x]);
+        }
+        __syncthreads();
+        if (c + 1 < nchunks) rest_fetch(e, u, E, ldE, U, d_out, d_in, r0, c0, bp0, kp, (c + 1) * kTK, tid, vec);
+        const float* Eb = Es + buf * kRestRows * kEs;
+        const float* Ub = Us + buf * kTK * kRUs;
+#pragma unroll
+        for (int ks = 0; ks < kTK; ks += 2) {
+            const float a = Eb[(wi * 32 + (lane & 31)) * kEs + ks + (lane >> 5)];
+            float b[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) b[q] = Ub[(ks + (lane >> 5)) * kRUs + wj * 128 + 32 * q + (lane & 31)];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[q] = mfma32x32x2_f32(a, b[q], acc[q]);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t row = r0 + wi * 32 + acc32_row(v, lane);
+            const int64_t col = c0 + wj * 128 + 32 * q + (lane & 31);
+            if (row < d_out && col < d_in) Wk[row * d_in + col] = wold[q][v] - acc[q][v];
+        }
+}
+
+// One launch per lazy block [b0, b1): workgroups 0 .. row_tiles-1 sweep the
+// block (after the near update by the previous block's errors when kp > 0);
+// the others apply the previous block's errors to the columns from b1 on
+// (n_rest tiles).  The two parts touch disjoint columns of W and different
+// error buffers, so nothing but the launch order separates the blocks.
+template <bool kAllFull>
+__global__ __launch_bounds__(512) void step_kernel(float* __restrict__ Wk, int64_t d_out, int64_t d_in,
+                                                   const float* __restrict__ U, const float* __restrict__ rdiag,
+                                                   int64_t b0, int64_t b1, int bits, int64_t group, int64_t ng,
+                                                   float* __restrict__ scales, int32_t* __restrict__ zeros,
+                                                   float* __restrict__ minmax, uint8_t* __restrict__ codes,
+                                                   float* __restrict__ E, int64_t ldE, float* __restrict__ err_row,
+                                                   const float* __restrict__ Ep, int64_t bp0, int kp, int row_tiles,
+                                                   int rest_rows, int vec_rest) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int b = (int)blockIdx.x;
+    if (b < row_tiles)
+        sweep_body<kAllFull>(smem, b, Wk, d_out, d_in, U, rdiag, b0, b1, bits, group, ng, scales, zeros, minmax,
+                             codes, E, ldE, err_row, Ep, bp0, kp);
+    else
+        rest_body(smem, (int64_t)(b - row_tiles), rest_rows, Wk, d_out, d_in, Ep, ldE, U, bp0, kp, b1,
+                  vec_rest != 0);
+}
+
 }  // namespace
 
 size_t quant_workspace_bytes(int64_t d_out, int64_t d_in, int64_t block) {
@@ -671,86 +872,67 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
     if (err_row)
         hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((d_out + 255) / 256)), dim3(256), 0, s, err_row, d_out);
     const bool vec = (reinterpret_cast<uintptr_t>(U) % 16 == 0) && (d_in % 4 == 0) && (block % 4 == 0);  // E rows are 16-byte aligned when block % 4 == 0
-    {
-        const size_t ldsmax = sweep_lds_bytes((int)std::min(block, d_in));
-        if (ldsmax > 64 * 1024) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_kernel<true>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsmax);
-            if (e == hipSuccess)
-                e = hipFuncSetAttribute(reinterpret_cast<const void*>(&sweep_kernel<false>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsmax);
-            if (e != hipSuccess) return e;
-        }
+    const int bmax = (int)std::min(block, d_in);
+    const size_t near_bytes = (size_t)((bmax + 3) & ~3) * kEtl * 4;
+    const size_t ldsmax = std::max(sweep_lds_bytes(bmax) + near_bytes, rest_lds_bytes());
+    if (ldsmax > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel<true>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsmax);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel<false>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsmax);
+        if (e != hipSuccess) return e;
     }
-    const unsigned row_tiles = (unsigned)((d_out + kRowsPerWg - 1) / kRowsPerWg);
-    SideStream* ss = nullptr;
-    hipError_t err = side_stream(ss);
-    if (err != hipSuccess) return err;
-    // 64-row tiles: twice the workgroups of a square tile and room for the W
-    // tile to be read ahead of the products (measured faster than 128-row
-    // tiles for both the early and the bulk update)
-    auto trail = [&](hipStream_t st, int64_t b0, int64_t b1, const float* Eb, int64_t cb, int64_t ce) {
-        if (ce <= cb) return;
-        TimedLaunch t(K_Q_TRAIL, st);
-        dim3 grid((unsigned)((ce - cb + kTT - 1) / kTT), (unsigned)((d_out + kTrailRows - 1) / kTrailRows));
-        if (vec)
-            hipLaunchKernelGGL((trail_kernel<true, kTrailRows>), grid, dim3(256), 0, st, w.Wk, d_out, d_in, Eb, block, U,
-                               b0, b1, cb, ce);
-        else
-            hipLaunchKernelGGL((trail_kernel<false, kTrailRows>), grid, dim3(256), 0, st, w.Wk, d_out, d_in, Eb, block, U,
-                               b0, b1, cb, ce);
-    };
-    // Lookahead: after the sweep of block b, the columns of block b+1 receive
-    // its update on the caller's stream and the next sweep starts at once,
-    // while the columns after block b+1 are updated on the side stream.  The
-    // caller's stream waits for that side update before it forks the next
-    // one (the next early update touches those columns), and the
-    // scaled-error buffer alternates so that sweep b+1 can write its errors
-    // while the side update of block b still reads them.
-    bool rest_pending = false;
-    auto join_rest = [&]() -> hipError_t {
-        if (!rest_pending) return hipSuccess;
-        rest_pending = false;
-        return hipStreamWaitEvent(s, ss->join, 0);
-    };
+    const int row_tiles = (int)((d_out + kRowsPerWg - 1) / kRowsPerWg);
+    const int rest_rows = (int)((d_out + kRestRows - 1) / kRestRows);
+    hipError_t err = hipSuccess;
+    // One launch per lazy block on the caller's stream: the sweep of block b
+    // (its columns first receive block b-1's update, in registers) and, in
+    // the same launch, block b-1's update of every column from b1 on.  A
+    // group wider than the block needs its columns fully updated before its
+    // grid is formed: at such a group start the previous block's update of
+    // the columns from b0 on runs as its own launch first.
     int bi = 0;
     for (int64_t b0 = 0; b0 < d_in; b0 += block, ++bi) {
         const int64_t b1 = std::min(b0 + block, d_in);
         const int bw = (int)(b1 - b0);
         const int nw = (bw + kSub - 1) / kSub;
         float* Eb = w.E[bi & 1];
+        const float* Ep = bi > 0 ? w.E[(bi - 1) & 1] : nullptr;
+        const int64_t bp0 = b0 - block;
+        int kp = bi > 0 ? (int)block : 0;
         if (group > block && b0 % group == 0) {
-            // the grid spans later blocks: it needs every earlier update
-            if ((err = join_rest()) != hipSuccess) return err;
+            if (kp > 0) {
+                TimedLaunch t(K_Q_TRAIL, s);
+                dim3 grid((unsigned)((d_in - b0 + kTT - 1) / kTT), (unsigned)((d_out + kTrailRows - 1) / kTrailRows));
+                if (vec)
+                    hipLaunchKernelGGL((trail_kernel<true, kTrailRows>), grid, dim3(256), 0, s, w.Wk, d_out, d_in, Ep,
+                                       block, U, bp0, b0, b0, d_in);
+                else
+                    hipLaunchKernelGGL((trail_kernel<false, kTrailRows>), grid, dim3(256), 0, s, w.Wk, d_out, d_in, Ep,
+                                       block, U, bp0, b0, b0, d_in);
+                kp = 0;
+            }
             TimedLaunch t(K_Q_GROUPGRID, s);
             hipLaunchKernelGGL(group_grid_kernel, dim3(rows4), dim3(256), 0, s, (const float*)w.Wk, d_out, d_in, b0,
                                group, b0 / group, ng, maxq, scales, zeros, minmax);
         }
-        {
-            TimedLaunch t(K_Q_SWEEP, s);
-            const size_t lds = sweep_lds_bytes(bw);
-            if (bw % kSub == 0)
-                hipLaunchKernelGGL(sweep_kernel<true>, dim3(row_tiles), dim3(64 * nw), lds, s, (const float*)w.Wk, d_out,
-                                   d_in, U, (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes,
-                                   Eb, block, err_row);
-            else
-                hipLaunchKernelGGL(sweep_kernel<false>, dim3(row_tiles), dim3(64 * nw), lds, s, (const float*)w.Wk, d_out,
-                                   d_in, U, (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes,
-                                   Eb, block, err_row);
-        }
-        if (b1 >= d_in) break;
-        if ((err = join_rest()) != hipSuccess) return err;
-        const int64_t next_end = std::min(b1 + block, d_in);
-        if (next_end < d_in) {
-            if ((err = hipEventRecord(ss->fork, s)) != hipSuccess) return err;
-            if ((err = hipStreamWaitEvent(ss->side, ss->fork, 0)) != hipSuccess) return err;
-            trail(ss->side, b0, b1, Eb, next_end, d_in);
-            if ((err = hipEventRecord(ss->join, ss->side)) != hipSuccess) return err;
-            rest_pending = true;
-        }
-        trail(s, b0, b1, Eb, b1, next_end);
+        const int64_t rest_cols = (kp > 0 && b1 < d_in) ? (d_in - b1 + kRestCols - 1) / kRestCols : 0;
+        const int64_t n_rest = rest_cols * rest_rows;
+        size_t lds = sweep_lds_bytes(bw) + (kp > 0 ? (size_t)((kp + 3) & ~3) * kEtl * 4 : 0);
+        if (n_rest > 0) lds = std::max(lds, rest_lds_bytes());
+        TimedLaunch t(K_Q_STEP, s);
+        const dim3 grid((unsigned)(row_tiles + n_rest));
+        if (bw % kSub == 0)
+            hipLaunchKernelGGL(step_kernel<true>, grid, dim3(512), lds, s, w.Wk, d_out, d_in, U,
+                               (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes, Eb, block,
+                               err_row, Ep, bp0, kp, row_tiles, rest_rows, (int)vec);
+        else
+            hipLaunchKernelGGL(step_kernel<false>, grid, dim3(512), lds, s, w.Wk, d_out, d_in, U,
+                               (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes, Eb, block,
+                               err_row, Ep, bp0, kp, row_tiles, rest_rows, (int)vec);
     }
-    if ((err = join_rest()) != hipSuccess) return err;
+    (void)err;
     return hipGetLastError();
 }
 
