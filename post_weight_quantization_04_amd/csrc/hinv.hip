@@ -30,13 +30,18 @@ constexpr int kGemmThreads = 256;
 constexpr int kLdsLd = NB + 8;   // padded LDS row (doubles)
 
 struct HinvWs {
-    double* G;      // [n_pad, n_pad]
+    double* G;      // n_pad x n_pad by 64x64 tiles (see gt)
     double* P;      // 2 x [n_pad / NB][NB][NB] (alternating steps)
     double* scal;   // [0] = lambda
     int* fail;      // device flag: set once a pivot fails
 };
 
 __host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// G is stored by 64x64 tiles: tile (I, J) of the n_pad x n_pad matrix is
+// NB*NB contiguous doubles, row-major inside (row stride NB), so that every
+// tile the factorization reads or writes is one contiguous 32 KB block.
+__host__ __device__ inline int64_t gt(int64_t np, int64_t I, int64_t J) { return (I * (np / NB) + J) * NB * NB; }
 
 HinvWs carve(void* ws, int64_t n) {
     const int64_t np = round_up(n, NB);
@@ -124,7 +129,7 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(const float* __restr
         } else {
             g = 0.0;
         }
-        G[i * np + j] = g;
+        G[gt(np, TI, TJ) + e] = g;
     }
 }
 
@@ -386,20 +391,22 @@ __device__ __forceinline__ int diag64(DiagLds& L) {
 // 64x64x64 float64 tile product on MFMA 16x16x4 f64:  acc += A B.
 // A is given row-major [64 rows][64 k] (lda); B is row-major [64 k][64 cols]
 // (ldb) or, with kBT, its transpose given row-major [64 cols][64 k].
-// All of K is fetched into registers at once (16 doubles of A and of B per
-// thread, every load in flight together).  K is staged in LDS in two halves
-// of 32 through one buffer (36.9 KB, so more workgroups fit on a CU); in
-// every fetch map the threads 0..127 hold k < 32 and 128..255 the rest, so
-// each half is written by two whole waves.  The four waves (2x2 grid, 32x32
-// each as 2x2 MFMA tiles) run 8 k-steps per half.  A direct B is staged with
-// its columns XOR-swizzled by the k row (low four bits) so that the staging
-// writes spread over the banks; the reads undo the swizzle.
+// Every operand tile is fetched in 16-byte pieces that run along its rows
+// (thread t holds row 8e + t/32, columns 2(t%32) and 2(t%32)+1, in
+// registers 2e and 2e+1, e = 0..7), so each wave's load covers two whole
+// 512-byte rows; all of K is in registers at once (16 doubles of A and of B
+// per thread, every load in flight together).  K is staged in LDS in two
+// halves of 32 through one buffer (33.8 KB): A and a transposed B row-major
+// with an odd row stride (33 doubles), so that the MFMA reads of 16 rows at
+// one k fall on distinct banks; a direct B as [k][col] rows.  The four waves
+// (2x2 grid, 32x32 each as 2x2 MFMA tiles) run 8 k-steps per half.
 // ---------------------------------------------------------------------------
 constexpr int kHalf = NB / 2;
+constexpr int kRs = kHalf + 1;  // row stride of a row-major half stage (doubles)
 
 struct GemmLds {
-    double A[kHalf][kLdsLd];  // [k - 32h][row]
-    double B[kHalf][kLdsLd];  // [k - 32h][col] (swizzled when B is given direct)
+    double A[NB * kRs];  // A[row][k - 32h] at row * kRs
+    double B[NB * kRs];  // B^T[col][k - 32h] at col * kRs, or B[k - 32h][col] at (k - 32h) * NB
 };
 
 struct GemmRegs {
@@ -407,45 +414,60 @@ struct GemmRegs {
     double b[16];
 };
 
-__device__ __forceinline__ int swz(int k, int col) { return col ^ (k & 15); }
+typedef double double2v __attribute__((ext_vector_type(2)));
 
-// A^T: row tid&63, k run (tid>>6)*16 ; B direct: k row tid>>2, cols (tid&3)*16 ;
-// B^T: col tid&63, k run (tid>>6)*16
-__device__ __forceinline__ void gemm_fetch_a(double (&a)[16], const double* __restrict__ A, int64_t lda, int tid) {
-    const double* sa = A + (int64_t)(tid & 63) * lda + (tid >> 6) * 16;
+__device__ __forceinline__ void tile_fetch(double (&r)[16], const double* __restrict__ src, int64_t ld, int tid) {
+    const double* p = src + (int64_t)(tid >> 5) * ld + 2 * (tid & 31);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) a[e] = sa[e];
+    for (int e = 0; e < 8; ++e) {
+        const double2v v = *reinterpret_cast<const double2v*>(p + (int64_t)(8 * e) * ld);
+        r[2 * e] = v[0];
+        r[2 * e + 1] = v[1];
+    }
+}
+__device__ __forceinline__ void gemm_fetch_a(double (&a)[16], const double* __restrict__ A, int64_t lda, int tid) {
+    tile_fetch(a, A, lda, tid);
 }
 template <bool kBT>
 __device__ __forceinline__ void gemm_fetch_b(double (&b)[16], const double* __restrict__ B, int64_t ldb, int tid) {
-    const double* sb = kBT ? B + (int64_t)(tid & 63) * ldb + (tid >> 6) * 16 : B + (int64_t)(tid >> 2) * ldb + (tid & 3) * 16;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) b[e] = sb[e];
+    tile_fetch(b, B, ldb, tid);
 }
 template <bool kBT>
 __device__ __forceinline__ void gemm_fetch(GemmRegs& r, const double* __restrict__ A, int64_t lda,
                                            const double* __restrict__ B, int64_t ldb, int tid) {
-    gemm_fetch_a(r.a, A, lda, tid);
-    gemm_fetch_b<kBT>(r.b, B, ldb, tid);
+    tile_fetch(r.a, A, lda, tid);
+    tile_fetch(r.b, B, ldb, tid);
 }
 
-// stage this thread's part of half h (threads 128h .. 128h+127 hold it)
-__device__ __forceinline__ void gemm_stash_a(const double (&a)[16], GemmLds& s, int tid, int h) {
-    if ((tid >> 7) != h) return;
+// stage half h of a fetched tile kept row-major by k (A, or B given
+// transposed): the threads whose two columns lie in that half write them
+__device__ __forceinline__ void stash_rows(const double (&r)[16], double* __restrict__ S, int tid, int h) {
+    const int col = 2 * (tid & 31);
+    if ((col >> 5) != h) return;
+    const int c = col - kHalf * h;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s.A[((tid >> 6) & 1) * 16 + e][tid & 63] = a[e];
+    for (int e = 0; e < 8; ++e) {
+        const int row = 8 * e + (tid >> 5);
+        S[row * kRs + c] = r[2 * e];
+        S[row * kRs + c + 1] = r[2 * e + 1];
+    }
+}
+// stage half h of a direct B (rows are k): registers 2e, e in 4h .. 4h+3
+__device__ __forceinline__ void stash_direct(const double (&r)[16], double* __restrict__ S, int tid, int h) {
+    const int col = 2 * (tid & 31);
+#pragma unroll
+    for (int e = 4 * h; e < 4 * h + 4; ++e) {
+        const int k = 8 * e + (tid >> 5) - kHalf * h;
+        *reinterpret_cast<double2v*>(&S[k * NB + col]) = (double2v){r[2 * e], r[2 * e + 1]};
+    }
+}
+__device__ __forceinline__ void gemm_stash_a(const double (&a)[16], GemmLds& s, int tid, int h) {
+    stash_rows(a, s.A, tid, h);
 }
 template <bool kBT>
 __device__ __forceinline__ void gemm_stash_b(const double (&b)[16], GemmLds& s, int tid, int h) {
-    if ((tid >> 7) != h) return;
-    if (kBT) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s.B[((tid >> 6) & 1) * 16 + e][tid & 63] = b[e];
-    } else {
-        const int k = (tid >> 2) & (kHalf - 1);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s.B[k][swz(k, (tid & 3) * 16 + e)] = b[e];
-    }
+    if (kBT) stash_rows(b, s.B, tid, h);
+    else stash_direct(b, s.B, tid, h);
 }
 
 template <bool kBT>
@@ -457,11 +479,11 @@ __device__ __forceinline__ void gemm_compute_half(const GemmLds& s, double4v (&a
         const int k = ks + (lane >> 4);
         double av[2], bv[2];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) av[m] = s.A[k][wi * 32 + 16 * m + (lane & 15)];
+        for (int m = 0; m < 2; ++m) av[m] = s.A[(wi * 32 + 16 * m + (lane & 15)) * kRs + k];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int col = wj * 32 + 16 * q + (lane & 15);
-            bv[q] = s.B[k][kBT ? col : swz(k, col)];
+            bv[q] = kBT ? s.B[col * kRs + k] : s.B[k * NB + col];
         }
 #pragma unroll
         for (int m = 0; m < 2; ++m)
@@ -573,15 +595,15 @@ __device__ __forceinline__ void diag_panel_body(DiagPanelLds& u, double* __restr
     const bool inv_row = t < k;  // M_kt rather than P_{t+1}
     double opnd[16];
     if (has_tile) {
-        if (inv_row) gemm_fetch_b<false>(opnd, G + (int64_t)k * NB * np + (int64_t)t * NB, np, tid);
-        else gemm_fetch_a(opnd, G + (int64_t)(t + 1) * NB * np + (int64_t)k * NB, np, tid);
+        if (inv_row) gemm_fetch_b<false>(opnd, G + gt(np, k, t), NB, tid);
+        else gemm_fetch_a(opnd, G + gt(np, t + 1, k), NB, tid);
     }
     DiagLds& L = u.diag;
-    const double* blk = G + (int64_t)k * NB * np + (int64_t)k * NB;
+    const double* blk = G + gt(np, k, k);
 #pragma unroll
     for (int m = 0; m < NB * NB / kGemmThreads; ++m) {
         const int idx = tid + kGemmThreads * m;
-        L.g[idx >> 6][idx & 63] = blk[(int64_t)(idx >> 6) * np + (idx & 63)];
+        L.g[idx >> 6][idx & 63] = blk[idx];
     }
     __syncthreads();
     const int st = diag64(L);
@@ -601,8 +623,9 @@ __device__ __forceinline__ void diag_panel_body(DiagPanelLds& u, double* __restr
         }
     }
     if (!has_tile) return;
-    // element e = (kk, x) of the stage: M[x][kk] goes to A^T[kk][x] (M_kk as
-    // A) or to B[kk][x] (M_kk^T as B); read out before the LDS is restaged
+    // element e = (kk, x): M[x][kk] is A[x][kk] (M_kk as A) or B^T[x][kk]
+    // (M_kk^T as B), both staged row-major by k; read out before the LDS is
+    // restaged
     double mv[NB * NB / kGemmThreads];
 #pragma unroll
     for (int m = 0; m < NB * NB / kGemmThreads; ++m) {
@@ -622,7 +645,7 @@ __device__ __forceinline__ void diag_panel_body(DiagPanelLds& u, double* __restr
 #pragma unroll
             for (int m = 8 * h; m < 8 * h + 8; ++m) {
                 const int e = tid + kGemmThreads * m;
-                s.A[(e >> 6) - kHalf * h][e & 63] = mv[m];
+                s.A[(e & 63) * kRs + (e >> 6) - kHalf * h] = mv[m];
             }
             gemm_stash_b<false>(opnd, s, tid, h);
         } else {
@@ -630,14 +653,14 @@ __device__ __forceinline__ void diag_panel_body(DiagPanelLds& u, double* __restr
 #pragma unroll
             for (int m = 8 * h; m < 8 * h + 8; ++m) {
                 const int e = tid + kGemmThreads * m;
-                s.B[(e >> 6) - kHalf * h][e & 63] = mv[m];
+                s.B[(e & 63) * kRs + (e >> 6) - kHalf * h] = mv[m];
             }
         }
         __syncthreads();
         if (inv_row) gemm_compute_half<false>(s, acc);
         else gemm_compute_half<true>(s, acc);
     }
-    if (inv_row) tile_store_f64<0>(G + (int64_t)k * NB * np + (int64_t)t * NB, np, acc);
+    if (inv_row) tile_store_f64<0>(G + gt(np, k, t), NB, acc);
     else tile_store_f64<0>(P + (int64_t)(t + 1) * NB * NB, NB, acc);
 }
 
@@ -653,7 +676,8 @@ __device__ __forceinline__ void tile_load_acc(double (&c)[2][2][4], const double
 }
 
 // Stage half h (k = 32h .. 32h+31) of an accumulator-layout tile X as the
-// operand A = X (s.A[k][row]); the columns of half h sit in waves w & 1 == h.
+// operand A = X (row-major by k); the columns of half h sit in waves
+// w & 1 == h.
 __device__ __forceinline__ void stash_acc_as_a(const double (&x)[2][2][4], GemmLds& s, int h) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     if ((w & 1) != h) return;
@@ -662,11 +686,11 @@ __device__ __forceinline__ void stash_acc_as_a(const double (&x)[2][2][4], GemmL
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) s.A[16 * q + (lane & 15)][acc_row(m, v)] = x[m][q][v];
+            for (int v = 0; v < 4; ++v) s.A[acc_row(m, v) * kRs + 16 * q + (lane & 15)] = x[m][q][v];
 }
 
-// ... as the direct operand B = X (s.B[k][swz(k, col)]); the rows of half h
-// sit in waves w >> 1 == h.
+// ... as the direct operand B = X ([k][col] rows); the rows of half h sit
+// in waves w >> 1 == h.
 __device__ __forceinline__ void stash_acc_as_b(const double (&x)[2][2][4], GemmLds& s, int h) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     if ((w >> 1) != h) return;
@@ -677,7 +701,7 @@ __device__ __forceinline__ void stash_acc_as_b(const double (&x)[2][2][4], GemmL
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int kl = 16 * m + 4 * v + (lane >> 4);
-                s.B[kl][swz(kl, acc_col(q))] = x[m][q][v];
+                s.B[kl * NB + acc_col(q)] = x[m][q][v];
             }
 }
 
@@ -721,20 +745,20 @@ __device__ __forceinline__ void diag_panel_next_body(DiagPanelNextLds& u, double
     if (has_tile) {
         if (!inv_row) {
             gemm_fetch_a(xo, Pk + (int64_t)(t + 1) * NB * NB, NB, tid);
-            tile_load_acc(c2, G + (int64_t)(t + 1) * NB * np + (int64_t)k1 * NB, np);
+            tile_load_acc(c2, G + gt(np, t + 1, k1), NB);
         } else if (t == k) {
             gemm_fetch_b<false>(xo, Pk, NB, tid);  // M_kk (zeros above the diagonal)
         } else {
-            gemm_fetch_b<false>(xo, G + (int64_t)k * NB * np + (int64_t)t * NB, np, tid);
-            tile_load_acc(c2, G + (int64_t)k1 * NB * np + (int64_t)t * NB, np);
+            gemm_fetch_b<false>(xo, G + gt(np, k, t), NB, tid);
+            tile_load_acc(c2, G + gt(np, k1, t), NB);
         }
     }
     {
-        const double* blk = G + (int64_t)k1 * NB * np + (int64_t)k1 * NB;
+        const double* blk = G + gt(np, k1, k1);
 #pragma unroll
         for (int m = 0; m < NB * NB / kGemmThreads; ++m) {
             const int idx = tid + kGemmThreads * m;
-            L.g[idx >> 6][idx & 63] = blk[(int64_t)(idx >> 6) * np + (idx & 63)];
+            L.g[idx >> 6][idx & 63] = blk[idx];
         }
     }
     double4v acc[2][2];
@@ -812,7 +836,7 @@ __device__ __forceinline__ void diag_panel_next_body(DiagPanelNextLds& u, double
 #pragma unroll
             for (int m = 8 * h; m < 8 * h + 8; ++m) {
                 const int e = tid + kGemmThreads * m;
-                s.A[(e >> 6) - kHalf * h][e & 63] = mv[m];
+                s.A[(e & 63) * kRs + (e >> 6) - kHalf * h] = mv[m];
             }
             stash_acc_as_b(c2, s, h);
         } else {
@@ -820,14 +844,14 @@ __device__ __forceinline__ void diag_panel_next_body(DiagPanelNextLds& u, double
 #pragma unroll
             for (int m = 8 * h; m < 8 * h + 8; ++m) {
                 const int e = tid + kGemmThreads * m;
-                s.B[(e >> 6) - kHalf * h][e & 63] = mv[m];
+                s.B[(e & 63) * kRs + (e >> 6) - kHalf * h] = mv[m];
             }
         }
         __syncthreads();
         if (inv_row) gemm_compute_half<false>(s, acc);
         else gemm_compute_half<true>(s, acc);
     }
-    if (inv_row) tile_store_f64<0>(G + (int64_t)k1 * NB * np + (int64_t)t * NB, np, acc);
+    if (inv_row) tile_store_f64<0>(G + gt(np, k1, t), NB, acc);
     else tile_store_f64<0>(Pk1 + (int64_t)(t + 1) * NB * NB, NB, acc);
 }
 
@@ -868,16 +892,16 @@ __global__ __launch_bounds__(kGemmThreads, 2) void chol_diag_panel_kernel(double
 __device__ __forceinline__ void trail_body(GemmLds& s, double* __restrict__ G, int64_t np, const double* __restrict__ P, int k,
                            int64_t i, int64_t j) {
     const double* Pi = P + i * NB * NB;
-    double* Gij = G + i * NB * np + j * NB;
+    double* Gij = G + gt(np, i, j);
     if (j < k) {
-        tile_gemm_sub_f64<false>(Pi, NB, G + (int64_t)k * NB * np + j * NB, np, Gij, np, s);
+        tile_gemm_sub_f64<false>(Pi, NB, G + gt(np, k, j), NB, Gij, NB, s);
     } else if (j == k) {
         double4v acc[2][2];
         zero_acc(acc);
         tile_gemm_f64<false>(Pi, NB, P, NB, s, acc);
-        tile_store_f64<2>(Gij, np, acc);
+        tile_store_f64<2>(Gij, NB, acc);
     } else {
-        tile_gemm_sub_f64<true>(Pi, NB, P + j * NB * NB, NB, Gij, np, s);
+        tile_gemm_sub_f64<true>(Pi, NB, P + j * NB * NB, NB, Gij, NB, s);
     }
 }
 
@@ -899,11 +923,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void chol_step_kernel(double* __re
     if (b < npan) {
         diag_panel_next_body(u, G, np, Pk1, Pk, k, T, b, info, fail);
     } else if (b == npan) {
-        double* Gkk = G + (int64_t)k * NB * np + (int64_t)k * NB;
+        double* Gkk = G + gt(np, k, k);
 #pragma unroll
         for (int m = 0; m < NB * NB / kGemmThreads; ++m) {
             const int idx = threadIdx.x + kGemmThreads * m;
-            Gkk[(int64_t)(idx >> 6) * np + (idx & 63)] = Pk[idx];
+            Gkk[idx] = Pk[idx];
         }
     } else {
         int64_t i, j;
@@ -917,9 +941,13 @@ __global__ __launch_bounds__(256) void store_u_kernel(const double* __restrict__
                                                       float* __restrict__ U, const int* __restrict__ fail) {
     if (*fail) return;
     const int64_t i = blockIdx.x;
-    const double* grow = G + (n - 1 - i) * np;
+    const int64_t r = n - 1 - i;
+    const double* grow = G + gt(np, r / NB, 0) + (r % NB) * NB;  // row r of tile column 0
     float* urow = U + i * n;
-    for (int64_t j = threadIdx.x; j < n; j += blockDim.x) urow[j] = (j >= i) ? (float)grow[n - 1 - j] : 0.0f;
+    for (int64_t j = threadIdx.x; j < n; j += blockDim.x) {
+        const int64_t c = n - 1 - j;
+        urow[j] = (j >= i) ? (float)grow[(c / NB) * NB * NB + (c % NB)] : 0.0f;
+    }
 }
 
 }  // namespace
