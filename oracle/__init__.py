@@ -6,7 +6,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 
 Pinned functions (see ``tests/test_oracle_pins.py``): ``hessian``, ``damp``,
 ``hinv_cholesky_upper``, ``grid``, ``quantize_values``, ``quantize``,
-``dequantize``, ``output_error``.  No function here is "parity unpinned".
+``dequantize``, ``output_error``, ``pack_codes``, ``unpack_codes``,
+``output_error_from_errors``.  No function here is "parity unpinned".
 """
 from .gptq import (  # noqa: F401
     NotPositiveDefinite,
@@ -18,7 +19,10 @@ from .gptq import (  # noqa: F401
     hinv_cholesky_upper,
     layer,
     output_error,
+    output_error_from_errors,
+    pack_codes,
     prepare,
     quantize,
     quantize_values,
+    unpack_codes,
 )

@@ -338,6 +338,51 @@ def output_error(W: np.ndarray, W_hat: np.ndarray, x_chunks: Iterable[np.ndarray
     return tot
 
 
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Few-bit storage of the codes: ``[d_out, ceil(d_in bits / 32)]`` uint32.
+
+    The pages keep the quantized weights as few-bit integers (aicassindra
+    "Post-training quantization in one paragraph": weights stored as 3- or
+    4-bit integers) and fix no bit layout.  Reading used here: each row's
+    codes form one little-endian bit stream, code j in bits
+    ``[j bits, (j+1) bits)``, least significant bit first, cut into 32-bit
+    words; the last word of a row is zero-padded.  Written bit by bit.
+    """
+    codes = np.asarray(codes)
+    d_out, d_in = codes.shape
+    nw = (d_in * bits + 31) // 32
+    out = np.zeros((d_out, nw), dtype=np.uint64)
+    for j in range(d_in):
+        c = codes[:, j].astype(np.uint64)
+        for b in range(bits):
+            t = j * bits + b
+            out[:, t // 32] |= ((c >> np.uint64(b)) & np.uint64(1)) << np.uint64(t % 32)
+    return out.astype(np.uint32)
+
+
+def unpack_codes(packed: np.ndarray, bits: int, d_in: int) -> np.ndarray:
+    """Inverse of ``pack_codes``: ``[d_out, d_in]`` uint8, bit by bit."""
+    packed = np.asarray(packed).astype(np.uint64)
+    d_out = packed.shape[0]
+    codes = np.zeros((d_out, d_in), dtype=np.uint64)
+    for j in range(d_in):
+        for b in range(bits):
+            t = j * bits + b
+            codes[:, j] |= ((packed[:, t // 32] >> np.uint64(t % 32)) & np.uint64(1)) << np.uint64(b)
+    return codes.astype(np.uint8)
+
+
+def output_error_from_errors(err_sq: np.ndarray, W0: np.ndarray, W_hat: np.ndarray, lam: float) -> np.ndarray:
+    """Per-row ``||dw X||^2`` without X, from the loss identity: the sum of
+    squared scaled errors of a row is ``dw H_damped dw^T = 2 ||dw X||^2 +
+    lambda ||dw||^2`` (aicassindra "The reconstruction objective, written
+    out" with the damped Hessian of "The Cholesky trick"; pinned as P8), so
+    ``||dw X||^2 = (sum e^2 - lambda ||dw||^2) / 2`` with ``dw = W0 - What``
+    and W0 the weights with dead columns zeroed."""
+    D = np.asarray(W0, np.float64) - np.asarray(W_hat, np.float64)
+    return (np.asarray(err_sq, np.float64) - float(lam) * np.sum(D * D, axis=1)) / 2.0
+
+
 def layer(W: np.ndarray, x_chunks: Iterable[np.ndarray], bits: int, group_size: int, block_size: int,
           damp_frac: float = 0.01):
     """The whole path on one layer: returns ``(H, U, dead, lam, QuantResult)``."""

@@ -391,3 +391,58 @@ def test_tie_aware_replay():
     hint2[i2, j2] = (int(hint2[i2, j2]) + 1) % 16
     h = oracle.quantize(W, U, 4, 0, 16, hint=hint2)
     assert h.hard >= 1
+
+
+# ---------------------------------------------------------------------------
+# P9: few-bit storage.  The row's stream is the integer sum_j c_j 2^(bits j);
+# its 32-bit limbs, least significant first, are the words (an independent
+# definition through Python integers), and special widths reduce to byte and
+# nibble layouts
+# ---------------------------------------------------------------------------
+def _limbs(row, bits, nw):
+    v = 0
+    for j, c in enumerate(row):
+        v += int(c) << (bits * j)
+    return [(v >> (32 * w)) & 0xFFFFFFFF for w in range(nw)]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("d_in", [1, 7, 31, 32, 33, 100, 129])
+def test_pack_codes_is_the_bit_stream(bits, d_in):
+    rng = np.random.default_rng(bits * 1000 + d_in)
+    codes = rng.integers(0, 1 << bits, (5, d_in)).astype(np.uint8)
+    P = oracle.pack_codes(codes, bits)
+    nw = (d_in * bits + 31) // 32
+    assert P.shape == (5, nw) and P.dtype == np.uint32
+    for r in range(5):
+        assert [int(x) for x in P[r]] == _limbs(codes[r], bits, nw)
+    np.testing.assert_array_equal(oracle.unpack_codes(P, bits, d_in), codes)
+
+
+def test_pack_codes_worked_3bit():
+    # 11 codes of 3 bits: 33 bits, two words; code 10 (= 0b011) puts its two
+    # low bits in bits 30-31 of word 0 and a zero in bit 0 of word 1
+    codes = np.array([[1, 2, 3, 4, 5, 6, 7, 0, 1, 2, 3]], dtype=np.uint8)
+    np.testing.assert_array_equal(oracle.pack_codes(codes, 3), np.array([[0xD11F58D1, 0]], dtype=np.uint32))
+
+
+def test_pack_codes_byte_and_nibble_layouts():
+    rng = np.random.default_rng(5)
+    c8 = rng.integers(0, 256, (3, 12)).astype(np.uint8)
+    np.testing.assert_array_equal(oracle.pack_codes(c8, 8), c8.view("<u4"))
+    c4 = rng.integers(0, 16, (3, 16)).astype(np.uint8)
+    nib = (c4[:, 0::2] | (c4[:, 1::2] << 4)).astype(np.uint8)
+    np.testing.assert_array_equal(oracle.pack_codes(c4, 4), nib.view("<u4"))
+
+
+@pytest.mark.parametrize("g,dead", [(0, ()), (16, (3, 17))])
+def test_output_error_from_errors(g, dead):
+    W, X = _spd_problem(12, 48, 150, 43, dead=dead)
+    H = oracle.hessian([X])
+    Hd, dmask, lam = oracle.damp(H)
+    U = oracle.hinv_cholesky_upper(Hd)
+    r = oracle.quantize(W, U, 4, g, 16, dead=dmask)
+    W0 = W.copy(); W0[:, dmask] = 0.0
+    per_row = oracle.output_error_from_errors(r.err_sq, W0, r.w_hat, lam)
+    direct = np.array([oracle.output_error(W0[i:i + 1], r.w_hat[i:i + 1], [X]) for i in range(W.shape[0])])
+    np.testing.assert_allclose(per_row, direct, rtol=1e-9)
