@@ -9,6 +9,9 @@
  *   3. U upper with H^-1 = U^T U                  (gptq_prepare_hinv)
  *   4. fixed-order, block-lazy quantize-and-compensate sweep
  *                                                 (gptq_quantize_layer)
+ * and, after the path, few-bit storage of the codes, dequantization and the
+ * per-row output error (gptq_pack_codes, gptq_dequantize,
+ * gptq_output_error).
  *
  * Conventions shared by every entry point
  *   - Tensor arguments are DEVICE pointers allocated and owned by the caller;
@@ -160,6 +163,68 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in,
                         const uint8_t* dead, int bits, int64_t group_size, int64_t block_size,
                         uint8_t* codes, float* scales, int32_t* zeros, float* err_row,
                         float* minmax, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Few-bit storage of the codes (aicassindra.com "tm_gptq_math",
+ * "Post-training quantization in one paragraph": the quantized weights are
+ * kept as few-bit integers; the pages fix no bit layout).  Layout: each
+ * row's codes form one little-endian bit stream, code j in bits
+ * [j bits, (j+1) bits), least significant bit first, cut into 32-bit words;
+ * a row holds gptq_packed_words(d_in, bits) = ceil(d_in bits / 32) words,
+ * the last one zero-padded.  Codes may straddle two words.
+ *
+ * gptq_packed_words: words per row, or -1 for d_in < 0 or bits outside
+ *   [2, 8].
+ * gptq_pack_codes:
+ *   codes   [d_out, d_in] uint8 input (bits above the low `bits` ignored).
+ *   packed  [d_out, gptq_packed_words(d_in, bits)] uint32 output.
+ * Errors: GPTQ_EINVAL (negative sizes, bits outside [2, 8], null pointer),
+ * GPTQ_EUNSUPPORTED (d_out or d_in above 2^24).
+ */
+int64_t gptq_packed_words(int64_t d_in, int bits);
+int gptq_pack_codes(const uint8_t* codes, int64_t d_out, int64_t d_in, int bits, uint32_t* packed,
+                    void* stream);
+
+/*
+ * Dequantization What = s (q - z) from packed codes (aicassindra
+ * "Post-training quantization in one paragraph", the grid of "A worked
+ * two-weight example").  The exact product of the scale and the integer
+ * q - z is rounded once to the output type, to nearest even (one fp32
+ * multiply, or one mixed-precision multiply with an fp16 result).
+ *   packed      [d_out, gptq_packed_words(d_in, bits)] uint32 (as above).
+ *   scales      [d_out, n_groups] float32, zeros [d_out, n_groups] int32,
+ *               n_groups = 1 if group_size == 0 else d_in / group_size
+ *               (the outputs of gptq_quantize_layer).
+ *   out         [d_out, d_in] of out_dtype (GPTQ_F16 or GPTQ_F32).
+ * Errors: GPTQ_EINVAL (negative sizes, bits outside [2, 8], negative
+ * group_size or one not dividing d_in, unknown out_dtype, null pointer),
+ * GPTQ_EUNSUPPORTED (d_out or d_in above 2^24).
+ */
+int gptq_dequantize(const uint32_t* packed, int bits, int64_t d_out, int64_t d_in, const float* scales,
+                    const int32_t* zeros, int64_t group_size, void* out, int out_dtype, void* stream);
+
+/*
+ * Per-row layer output error ||dw X||^2 without X, from the loss identity
+ * (aicassindra "The reconstruction objective, written out" with the damped
+ * Hessian of "The Cholesky trick for the inverse Hessian"): a row's sum of
+ * squared scaled errors is dw H_damped dw^T = 2 ||dw X||^2 + lambda ||dw||^2,
+ * so out_row[r] = (err_row[r] - lambda ||dw_r||^2) / 2 with dw = W0 - What,
+ * W0 the weights with the dead columns zeroed and What dequantized from the
+ * packed codes.  ||dw||^2 is summed in float64.
+ *   W        [d_out, d_in] of w_dtype: the weights given to
+ *            gptq_quantize_layer.
+ *   dead     [d_in] uint8 or NULL (no dead columns).
+ *   packed, scales, zeros, group_size: as for gptq_dequantize.
+ *   err_row  [d_out] float32: the err_row output of gptq_quantize_layer.
+ *   lambda   device float64 scalar: the damping of gptq_prepare_hinv
+ *            (its lambda_out).
+ *   out_row  [d_out] float32 output.
+ * Errors: as gptq_dequantize (w_dtype in place of out_dtype), plus
+ * GPTQ_EINVAL for a null err_row, lambda or out_row.
+ */
+int gptq_output_error(const void* W, int w_dtype, const uint8_t* dead, const uint32_t* packed, int bits,
+                      const float* scales, const int32_t* zeros, int64_t group_size, int64_t d_out, int64_t d_in,
+                      const float* err_row, const double* lambda, float* out_row, void* stream);
 
 /* Human-readable name of a gptq_status value (static string). */
 const char* gptq_status_string(int status);

@@ -24,6 +24,10 @@ EXPORTS = (
     "gptq_quantize_layer_workspace",
     "gptq_quantize_layer",
     "gptq_status_string",
+    "gptq_packed_words",
+    "gptq_pack_codes",
+    "gptq_dequantize",
+    "gptq_output_error",
     "gptq_kernel_count",
     "gptq_kernel_name",
     "gptq_timing_enable",
@@ -59,6 +63,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "gptq_quantize_layer": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _sz, _vp]),
         "gptq_status_string": (ctypes.c_char_p, [_i32]),
+        "gptq_packed_words": (_i64, [_i64, _i32]),
+        "gptq_pack_codes": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp]),
+        "gptq_dequantize": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i64, _vp, _i32, _vp]),
+        "gptq_output_error": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
         "gptq_kernel_count": (_i32, []),
         "gptq_kernel_name": (ctypes.c_char_p, [_i32]),
         "gptq_timing_enable": (_i32, [_i32]),
@@ -151,6 +159,35 @@ def quantize_layer(W, U, dead, bits: int, group_size: int, block_size: int, code
                                     workspace.numel() * workspace.element_size() if workspace is not None else 0,
                                     _stream(stream))
     _check("gptq_quantize_layer", rc)
+
+
+# ---------------------------------------------------------------------------
+# few-bit storage, dequantization, output error
+# ---------------------------------------------------------------------------
+def packed_words(d_in: int, bits: int) -> int:
+    return int(load().gptq_packed_words(d_in, int(bits)))
+
+
+def pack_codes(codes, bits: int, packed, stream=None) -> None:
+    d_out, d_in = codes.shape
+    rc = load().gptq_pack_codes(_ptr(codes), d_out, d_in, int(bits), _ptr(packed), _stream(stream))
+    _check("gptq_pack_codes", rc)
+
+
+def dequantize(packed, bits: int, d_in: int, scales, zeros, group_size: int, out, stream=None) -> None:
+    d_out = packed.shape[0]
+    rc = load().gptq_dequantize(_ptr(packed), int(bits), d_out, d_in, _ptr(scales), _ptr(zeros), int(group_size),
+                                _ptr(out), _dtype_code(out), _stream(stream))
+    _check("gptq_dequantize", rc)
+
+
+def output_error(W, dead, packed, bits: int, scales, zeros, group_size: int, err_row, lam, out_row,
+                 stream=None) -> None:
+    d_out, d_in = W.shape
+    rc = load().gptq_output_error(_ptr(W), _dtype_code(W), _ptr(dead), _ptr(packed), int(bits), _ptr(scales),
+                                  _ptr(zeros), int(group_size), d_out, d_in, _ptr(err_row), _ptr(lam),
+                                  _ptr(out_row), _stream(stream))
+    _check("gptq_output_error", rc)
 
 
 # ---------------------------------------------------------------------------

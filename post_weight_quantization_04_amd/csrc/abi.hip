@@ -18,6 +18,7 @@ namespace {
 const char* const kNames[K_COUNT] = {
     "hessian_f16", "hessian_f32", "hinv_diag_stats", "hinv_load_reversed", "chol_step", "hinv_store_u",
     "q_row_grid",  "q_convert",   "q_rdiag",         "q_group_grid",       "q_step",    "q_trail",
+    "pack_codes",  "dequantize",  "output_error",
 };
 int g_timed = -1;
 struct EventPair {
@@ -161,6 +162,44 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in,
         return GPTQ_EWORKSPACE;
     return hip_status(launch_quantize(W, w_dtype == GPTQ_F16, d_out, d_in, U, dead, bits, group_size, block_size,
                                       codes, scales, zeros, err_row, minmax, workspace, as_stream(stream)));
+}
+
+int64_t gptq_packed_words(int64_t d_in, int bits) {
+    if (d_in < 0 || bits < 2 || bits > 8) return -1;
+    return packed_words(d_in, bits);
+}
+
+int gptq_pack_codes(const uint8_t* codes, int64_t d_out, int64_t d_in, int bits, uint32_t* packed, void* stream) {
+    if (d_out < 0 || d_in < 0 || bits < 2 || bits > 8) return GPTQ_EINVAL;
+    if (d_out == 0 || d_in == 0) return GPTQ_OK;
+    if (!codes || !packed) return GPTQ_EINVAL;
+    if (d_in > ((int64_t)1 << 24) || d_out > ((int64_t)1 << 24)) return GPTQ_EUNSUPPORTED;
+    return hip_status(launch_pack(codes, d_out, d_in, bits, packed, as_stream(stream)));
+}
+
+int gptq_dequantize(const uint32_t* packed, int bits, int64_t d_out, int64_t d_in, const float* scales,
+                    const int32_t* zeros, int64_t group_size, void* out, int out_dtype, void* stream) {
+    if (d_out < 0 || d_in < 0 || bits < 2 || bits > 8 || group_size < 0) return GPTQ_EINVAL;
+    if (out_dtype != GPTQ_F16 && out_dtype != GPTQ_F32) return GPTQ_EINVAL;
+    if (group_size > 0 && d_in > 0 && d_in % group_size != 0) return GPTQ_EINVAL;
+    if (d_out == 0 || d_in == 0) return GPTQ_OK;
+    if (!packed || !scales || !zeros || !out) return GPTQ_EINVAL;
+    if (d_in > ((int64_t)1 << 24) || d_out > ((int64_t)1 << 24)) return GPTQ_EUNSUPPORTED;
+    return hip_status(
+        launch_dequant(packed, bits, d_out, d_in, scales, zeros, group_size, out, out_dtype == GPTQ_F16, as_stream(stream)));
+}
+
+int gptq_output_error(const void* W, int w_dtype, const uint8_t* dead, const uint32_t* packed, int bits,
+                      const float* scales, const int32_t* zeros, int64_t group_size, int64_t d_out, int64_t d_in,
+                      const float* err_row, const double* lambda, float* out_row, void* stream) {
+    if (d_out < 0 || d_in < 0 || bits < 2 || bits > 8 || group_size < 0) return GPTQ_EINVAL;
+    if (w_dtype != GPTQ_F16 && w_dtype != GPTQ_F32) return GPTQ_EINVAL;
+    if (group_size > 0 && d_in > 0 && d_in % group_size != 0) return GPTQ_EINVAL;
+    if (d_out == 0 || d_in == 0) return GPTQ_OK;
+    if (!W || !packed || !scales || !zeros || !err_row || !lambda || !out_row) return GPTQ_EINVAL;
+    if (d_in > ((int64_t)1 << 24) || d_out > ((int64_t)1 << 24)) return GPTQ_EUNSUPPORTED;
+    return hip_status(launch_output_error(W, w_dtype == GPTQ_F16, dead, packed, bits, scales, zeros, group_size,
+                                          d_out, d_in, err_row, lambda, out_row, as_stream(stream)));
 }
 
 }  // extern "C"

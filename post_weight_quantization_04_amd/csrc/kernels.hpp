@@ -21,6 +21,9 @@ enum KernelId {
     K_Q_GROUPGRID,
     K_Q_STEP,
     K_Q_TRAIL,
+    K_PACK,
+    K_DEQUANT,
+    K_OUTERR,
     K_COUNT
 };
 
@@ -49,5 +52,16 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
                            const uint8_t* dead, int bits, int64_t group, int64_t block,
                            uint8_t* codes, float* scales, int32_t* zeros, float* err_row,
                            float* minmax, void* ws, hipStream_t s);
+
+// ---- few-bit storage, dequantization, output error ---------------------------
+int64_t packed_words(int64_t d_in, int bits);
+hipError_t launch_pack(const uint8_t* codes, int64_t d_out, int64_t d_in, int bits, uint32_t* packed,
+                       hipStream_t s);
+hipError_t launch_dequant(const uint32_t* packed, int bits, int64_t d_out, int64_t d_in, const float* scales,
+                          const int32_t* zeros, int64_t group, void* out, int out_is_f16, hipStream_t s);
+hipError_t launch_output_error(const void* W, int w_is_f16, const uint8_t* dead, const uint32_t* packed, int bits,
+                               const float* scales, const int32_t* zeros, int64_t group, int64_t d_out,
+                               int64_t d_in, const float* err_row, const double* lambda, float* out,
+                               hipStream_t s);
 
 }  // namespace gptq

@@ -99,3 +99,30 @@ def quantize(W, factor: Factor, bits: int, group_size: int, block_size: int, ws:
     _lib.quantize_layer(W, factor.U, factor.dead if use_dead else None, bits, group_size, block_size, out.codes,
                         out.scales, out.zeros, out.err_row, out.minmax, buf, stream=stream)
     return out
+
+
+def pack(codes, bits: int, stream=None):
+    """Few-bit storage of ``codes [d_out, d_in]`` (uint32 words, see
+    ``gptq_pack_codes``)."""
+    import torch
+    d_out, d_in = codes.shape
+    packed = torch.empty((d_out, max(_lib.packed_words(d_in, bits), 1)), dtype=torch.int32, device=codes.device)
+    _lib.pack_codes(codes, bits, packed, stream=stream)
+    return packed
+
+
+def dequantize(packed, bits: int, d_in: int, scales, zeros, group_size: int, dtype=None, stream=None):
+    """``What = s (q - z)`` from packed codes, as ``dtype`` (float16 or float32)."""
+    import torch
+    out = torch.empty((packed.shape[0], d_in), dtype=dtype or torch.float32, device=packed.device)
+    _lib.dequantize(packed, bits, d_in, scales, zeros, group_size, out, stream=stream)
+    return out
+
+
+def output_error(W, factor: Factor, q: Quantized, packed, bits: int, group_size: int, stream=None):
+    """Per-row ``||dw X||^2`` from the loss identity (``gptq_output_error``)."""
+    import torch
+    out = torch.empty((W.shape[0],), dtype=torch.float32, device=W.device)
+    _lib.output_error(W, factor.dead, packed, bits, q.scales, q.zeros, group_size, q.err_row, factor.lam, out,
+                      stream=stream)
+    return out

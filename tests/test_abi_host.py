@@ -114,3 +114,28 @@ def test_workspace_sizes_monotone(clib):
     q1 = clib.gptq_quantize_layer_workspace(64, 128, 32)
     q2 = clib.gptq_quantize_layer_workspace(64, 128, 128)
     assert 0 < q1 < q2 and q1 >= 64 * 128 * 4
+
+
+def test_pack_dequant_argument_errors(clib):
+    p = ctypes.c_void_p(256)
+    assert clib.gptq_packed_words(100, 3) == 10 and clib.gptq_packed_words(32, 4) == 4
+    assert clib.gptq_packed_words(33, 4) == 5 and clib.gptq_packed_words(0, 8) == 0
+    assert clib.gptq_packed_words(10, 1) == -1 and clib.gptq_packed_words(-1, 4) == -1
+    pack = clib.gptq_pack_codes
+    assert pack(p, 8, 64, 1, p, None) == 1 and pack(p, 8, 64, 9, p, None) == 1
+    assert pack(None, 8, 64, 4, p, None) == 1 and pack(p, 8, 64, 4, None, None) == 1
+    assert pack(p, -1, 64, 4, p, None) == 1 and pack(p, 0, 64, 4, p, None) == 0
+
+    def deq(d_out=8, d_in=64, bits=4, group=0, dtype=1, P=p, S=p, Z=p, O=p):
+        return clib.gptq_dequantize(P, bits, d_out, d_in, S, Z, group, O, dtype, None)
+
+    assert deq(bits=9) == 1 and deq(group=-1) == 1 and deq(group=48) == 1 and deq(dtype=3) == 1
+    assert deq(P=None) == 1 and deq(S=None) == 1 and deq(Z=None) == 1 and deq(O=None) == 1
+    assert deq(d_in=0) == 0 and deq(d_out=0) == 0
+
+    def oerr(d_out=8, d_in=64, bits=4, group=0, dtype=1, W=p, E=p, L=p, O=p):
+        return clib.gptq_output_error(W, dtype, None, p, bits, p, p, group, d_out, d_in, E, L, O, None)
+
+    assert oerr(bits=1) == 1 and oerr(group=48) == 1 and oerr(dtype=7) == 1
+    assert oerr(W=None) == 1 and oerr(E=None) == 1 and oerr(L=None) == 1 and oerr(O=None) == 1
+    assert oerr(d_out=0) == 0
