@@ -146,6 +146,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-breakdown", action="store_true")
+    ap.add_argument("--no-after-path", action="store_true",
+                    help="skip timing few-bit storage, dequantization and the output error after the path")
     ap.add_argument("--counter-pass", action="store_true",
                     help="for hardware-counter runs: two untimed layer passes, then three copies of a 256 MiB "
                          "buffer whose counter readings calibrate FETCH_SIZE / WRITE_SIZE; no timing, no JSON")
@@ -296,6 +298,43 @@ def main(argv=None) -> int:
         "launches_per_step": dom_launches // max(args.steps, 1),
     }
 
+    # after the path (not part of a step): few-bit storage, dequantization to
+    # fp16 and the identity-based output error of the layer just quantized;
+    # each is one streaming kernel, reported against the HBM peak with its
+    # algorithmic bytes
+    after = {}
+    if not args.no_after_path:
+        bits, g = wl.bits, wl.group_size
+        ng = d_in // g if g else 1
+        nw = _lib.packed_words(d_in, bits)
+        packed = layer.pack(qout.codes, bits)
+        wh = torch.empty((d_out, d_in), dtype=torch.float16, device=dev)
+        oe = torch.empty((d_out,), dtype=torch.float32, device=dev)
+        sz = d_out * ng * 8
+        jobs = {
+            "pack_codes": (lambda: _lib.pack_codes(qout.codes, bits, packed), d_out * d_in + d_out * nw * 4),
+            "dequantize_f16": (lambda: _lib.dequantize(packed, bits, d_in, qout.scales, qout.zeros, g, wh),
+                               d_out * nw * 4 + sz + d_out * d_in * 2),
+            "output_error": (lambda: _lib.output_error(Wd, fac.dead, packed, bits, qout.scales, qout.zeros, g,
+                                                       qout.err_row, fac.lam, oe),
+                             d_out * d_in * Wd.element_size() + d_out * nw * 4 + sz + d_out * 8 + d_in),
+        }
+        for name, (fn, nbytes) in jobs.items():
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 20
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / reps
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            after[name] = {"ms": round(ms, 4), "bytes": int(nbytes), "GB/s": round(gbs, 1),
+                           "frac_hbm": round(gbs / PEAK_HBM_GBS, 3)}
+        after["output_error_sum"] = float(oe.sum().item())
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host ...", file=sys.stderr, flush=True)
@@ -324,6 +363,7 @@ def main(argv=None) -> int:
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "after_path": after or None,
     }
     print(json.dumps(out), flush=True)
     return 0
