@@ -394,7 +394,7 @@ def test_tie_aware_replay():
 
 
 # ---------------------------------------------------------------------------
-# P9: few-bit storage.  The row's stream is the integer sum_j c_j 2^(bits j);
+# S1: few-bit storage.  The row's stream is the integer sum_j c_j 2^(bits j);
 # its 32-bit limbs, least significant first, are the words (an independent
 # definition through Python integers), and special widths reduce to byte and
 # nibble layouts
