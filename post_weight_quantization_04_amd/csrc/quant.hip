@@ -702,16 +702,17 @@ __global__ __launch_bounds__(256) void trail_kernel(float* __restrict__ Wk, int6
 
 // ---------------------------------------------------------------------------
 // The far part of the lazy trailing update inside the per-block launch:
-// W[r0 .. r0+128, c0 .. c0+256] -= E_prev[rows, :kp] U[bp0 .. bp0+kp, cols]
-// for the tile tb (row tile tb % rest_rows, column tile tb / rest_rows) of
-// the columns [c_begin, d_in).  512 threads: eight waves in a 4x2 grid, each
-// 32 rows x 128 columns as four MFMA 32x32x2 f32 tiles; K in chunks of 32
+// W[r0 .. r0+128, c0 .. c_end) -= E_prev[rows, :kp] U[bp0 .. bp0+kp, cols]
+// for one sub-tile of at most 256 columns.  512 threads: eight waves in a
+// 4x2 grid, each 32 rows x 128 columns as four MFMA 32x32x2 f32 tiles (the
+// products of 32-column pieces past c_end are skipped); K in chunks of 32
 // through two LDS buffers with a register prefetch, and the W tile read
 // ahead of the products.  The launch is one workgroup per CU (its LDS), so
 // the per-wave work is large and the registers plentiful.
 // ---------------------------------------------------------------------------
 constexpr int kRestRows = 128;
 constexpr int kRestCols = 256;
+constexpr int kStrip = 64;           // unit of the far-update partition: 128 rows x 64 columns
 constexpr int kRUs = kRestCols + 4;  // U stage row stride
 
 __host__ __device__ inline size_t rest_lds_bytes() {
@@ -720,7 +721,7 @@ __host__ __device__ inline size_t rest_lds_bytes() {
 
 __device__ __forceinline__ void rest_fetch(float (&e)[8], float (&u)[16], const float* __restrict__ E, int64_t ldE,
                                            const float* __restrict__ U, int64_t d_out, int64_t d_in, int64_t r0,
-                                           int64_t c0, int64_t bp0, int kp, int kc, int tid, bool vec) {
+                                           int64_t c0, int64_t c_end, int64_t bp0, int kp, int kc, int tid, bool vec) {
     {
         const int64_t R = r0 + (tid >> 2);
         const int k = kc + (tid & 3) * 8;
@@ -737,42 +738,54 @@ __device__ __forceinline__ void rest_fetch(float (&e)[8], float (&u)[16], const 
         const int k = kc + (tid >> 4);
         const int64_t col = c0 + (tid & 15) * 16;
         const float* src = U + (bp0 + k) * d_in + col;
-        if (vec && k < kp && col + 16 <= d_in) {
+        if (vec && k < kp && col + 16 <= c_end) {
 #pragma unroll
             for (int x = 0; x < 16; x += 4) *reinterpret_cast<float4v*>(&u[x]) = *reinterpret_cast<const float4v*>(src + x);
         } else {
 #pragma unroll
-            for (int x = 0; x < 16; ++x) u[x] = (k < kp && col + x < d_in) ? src[x] : 0.0f;
+            for (int x = 0; x < 16; ++x) u[x] = (k < kp && col + x < c_end) ? src[x] : 0.0f;
         }
     }
 }
 
-__device__ __forceinline__ void rest_body(unsigned char* smem, int64_t tb, int rest_rows, float* __restrict__ Wk,
-                                          int64_t d_out, int64_t d_in, const float* __restrict__ E, int64_t ldE,
-                                          const float* __restrict__ U, int64_t bp0, int kp, int64_t c_begin,
-                                          bool vec) {
+// products of one K chunk for a wave's NQ 32-column pieces
+template <int NQ>
+__device__ __forceinline__ void rest_chunk(const float* Eb, const float* Ub, int wi, int colw, int lane,
+                                           float16v (&acc)[4]) {
+#pragma unroll
+    for (int ks = 0; ks < kTK; ks += 2) {
+        const float a = Eb[(wi * 32 + (lane & 31)) * kEs + ks + (lane >> 5)];
+        float b[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) b[q] = Ub[(ks + (lane >> 5)) * kRUs + colw + 32 * q + (lane & 31)];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) acc[q] = mfma32x32x2_f32(a, b[q], acc[q]);
+    }
+}
+
+__device__ __forceinline__ void rest_body(unsigned char* smem, int64_t r0, int64_t c0, int64_t c_end,
+                                          float* __restrict__ Wk, int64_t d_out, int64_t d_in,
+                                          const float* __restrict__ E, int64_t ldE, const float* __restrict__ U,
+                                          int64_t bp0, int kp, bool vec) {
     float* Es = reinterpret_cast<float*>(smem);  // [2][kRestRows * kEs]
     float* Us = Es + 2 * kRestRows * kEs;        // [2][kTK * kRUs]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wi = w >> 1, wj = w & 1;
-    const int64_t r0 = (tb % rest_rows) * kRestRows;
-    const int64_t c0 = c_begin + (tb / rest_rows) * kRestCols;
     const int nchunks = (kp + kTK - 1) / kTK;
+    // the sub-tile's 64-column strips split between the two column halves of
+    // the wave grid: each wave takes ns 32-column pieces (fewer at c_end)
+    const int ns = (int)((c_end - c0 + kStrip - 1) / kStrip);
+    const int colw = wj * ns * 32;
+    const int64_t cw = c0 + colw;
+    const int nq = (int)std::min<int64_t>(ns, std::max<int64_t>(0, (c_end - cw + 31) / 32));
+    const bool inner = (r0 + kRestRows <= d_out) && (cw + 32 * nq <= c_end);
 
     float16v acc[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = (float16v){};
     float e[8], u[16];
-    rest_fetch(e, u, E, ldE, U, d_out, d_in, r0, c0, bp0, kp, 0, tid, vec);
+    rest_fetch(e, u, E, ldE, U, d_out, d_in, r0, c0, c_end, bp0, kp, 0, tid, vec);
     float wold[4][16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t row = r0 + wi * 32 + acc32_row(v, lane);
-            const int64_t col = c0 + wj * 128 + 32 * q + (lane & 31);
-            wold[q][v] = (row < d_out && col < d_in) ? Wk[row * d_in + col] : 0.0f;
-        }
     for (int c = 0; c < nchunks; ++c) {
         const int buf = c & 1;
         {
@@ -784,34 +797,84 @@ __device__ __forceinline__ void rest_body(unsigned char* smem, int64_t tb, int r
             for (int x = 0; x < 16; x += 4) *reinterpret_cast<float4v*>(&ud[x]) = *reinterpret_cast<const float4v*>(&u[x]);
         }
         __syncthreads();
-        if (c + 1 < nchunks) rest_fetch(e, u, E, ldE, U, d_out, d_in, r0, c0, bp0, kp, (c + 1) * kTK, tid, vec);
+        if (c + 1 < nchunks)
+            rest_fetch(e, u, E, ldE, U, d_out, d_in, r0, c0, c_end, bp0, kp, (c + 1) * kTK, tid, vec);
+        if (c == 0) {
+            // the old W tile, behind the next chunk's operands (so that their
+            // wait does not include it); addresses outside the sub-tile are
+            // clamped to its first element, so that every load is issued
+            // without a branch (those values are never stored)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (q < nq) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int64_t row = r0 + wi * 32 + acc32_row(v, lane);
+                        const int64_t col = cw + 32 * q + (lane & 31);
+                        const bool ok = row < d_out && col < c_end;
+                        wold[q][v] = Wk[ok ? row * d_in + col : r0 * d_in + c0];
+                    }
+                }
+        }
         const float* Eb = Es + buf * kRestRows * kEs;
         const float* Ub = Us + buf * kTK * kRUs;
-#pragma unroll
-        for (int ks = 0; ks < kTK; ks += 2) {
-            const float a = Eb[(wi * 32 + (lane & 31)) * kEs + ks + (lane >> 5)];
-            float b[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) b[q] = Ub[(ks + (lane >> 5)) * kRUs + wj * 128 + 32 * q + (lane & 31)];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[q] = mfma32x32x2_f32(a, b[q], acc[q]);
+        switch (nq) {
+            case 4: rest_chunk<4>(Eb, Ub, wi, colw, lane, acc); break;
+            case 3: rest_chunk<3>(Eb, Ub, wi, colw, lane, acc); break;
+            case 2: rest_chunk<2>(Eb, Ub, wi, colw, lane, acc); break;
+            case 1: rest_chunk<1>(Eb, Ub, wi, colw, lane, acc); break;
+            default: break;
         }
     }
+    if (nchunks == 0) return;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
+        if (q < nq) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t row = r0 + wi * 32 + acc32_row(v, lane);
-            const int64_t col = c0 + wj * 128 + 32 * q + (lane & 31);
-            if (row < d_out && col < d_in) Wk[row * d_in + col] = wold[q][v] - acc[q][v];
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = r0 + wi * 32 + acc32_row(v, lane);
+                const int64_t col = cw + 32 * q + (lane & 31);
+                if (inner || (row < d_out && col < c_end)) Wk[row * d_in + col] = wold[q][v] - acc[q][v];
+            }
         }
 }
 
+// The far update of one launch is split into units of 128 rows x 64
+// columns (unit u: row tile u / nstrip, strip u % nstrip of the columns
+// [c_begin, d_in)), dealt out as contiguous ranges: the sweeping workgroups
+// take `per_sweep` units each after their sweep, the far-only workgroups
+// share the rest evenly.  With one workgroup per CU every range starts at
+// once, so the launch ends when the longest range does.
+struct FarSplit {
+    int64_t c_begin;
+    int64_t n_units;
+    int nstrip;      // strips per row tile
+    int per_sweep;   // units of each sweeping workgroup
+    int q, r;        // far-only workgroups: q units each, the first r one more
+};
+
+__device__ __forceinline__ void far_range(unsigned char* smem, int64_t u0, int64_t u1, int64_t c_begin, int nstrip,
+                                          float* __restrict__ Wk, int64_t d_out, int64_t d_in,
+                                          const float* __restrict__ E, int64_t ldE, const float* __restrict__ U,
+                                          int64_t bp0, int kp, bool vec) {
+    for (int64_t u = u0; u < u1;) {
+        const int64_t rt = u / nstrip;
+        const int st = (int)(u - rt * nstrip);
+        const int ns = (int)std::min<int64_t>(std::min(kRestCols / kStrip, nstrip - st), u1 - u);
+        const int64_t c0 = c_begin + (int64_t)st * kStrip;
+        const int64_t c_end = std::min<int64_t>(d_in, c0 + (int64_t)ns * kStrip);
+        __syncthreads();  // the LDS stages of the previous sub-tile (or the sweep) are free again
+        rest_body(smem, rt * kRestRows, c0, c_end, Wk, d_out, d_in, E, ldE, U, bp0, kp, vec);
+        u += ns;
+    }
+}
+
 // One launch per lazy block [b0, b1): workgroups 0 .. row_tiles-1 sweep the
-// block (after the near update by the previous block's errors when kp > 0);
-// the others apply the previous block's errors to the columns from b1 on
-// (n_rest tiles).  The two parts touch disjoint columns of W and different
-// error buffers, so nothing but the launch order separates the blocks.
+// block (after the near update by the previous block's errors when kp > 0),
+// then take their share of the previous block's update of the columns from
+// b1 on; the other workgroups do only that update.  The two parts touch
+// disjoint columns of W and different error buffers, so nothing but the
+// launch order separates the blocks.
 template <bool kAllFull>
 __global__ __launch_bounds__(512) void step_kernel(float* __restrict__ Wk, int64_t d_out, int64_t d_in,
                                                    const float* __restrict__ U, const float* __restrict__ rdiag,
@@ -820,15 +883,46 @@ __global__ __launch_bounds__(512) void step_kernel(float* __restrict__ Wk, int64
                                                    float* __restrict__ minmax, uint8_t* __restrict__ codes,
                                                    float* __restrict__ E, int64_t ldE, float* __restrict__ err_row,
                                                    const float* __restrict__ Ep, int64_t bp0, int kp, int row_tiles,
-                                                   int rest_rows, int vec_rest) {
+                                                   FarSplit fs, int vec_rest) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int b = (int)blockIdx.x;
-    if (b < row_tiles)
+    int64_t u0, u1;
+    if (b < row_tiles) {
         sweep_body<kAllFull>(smem, b, Wk, d_out, d_in, U, rdiag, b0, b1, bits, group, ng, scales, zeros, minmax,
                              codes, E, ldE, err_row, Ep, bp0, kp);
-    else
-        rest_body(smem, (int64_t)(b - row_tiles), rest_rows, Wk, d_out, d_in, Ep, ldE, U, bp0, kp, b1,
-                  vec_rest != 0);
+        u0 = std::min<int64_t>((int64_t)b * fs.per_sweep, fs.n_units);
+        u1 = std::min<int64_t>(u0 + fs.per_sweep, fs.n_units);
+    } else {
+        const int f = b - row_tiles;
+        u0 = (int64_t)row_tiles * fs.per_sweep + (int64_t)f * fs.q + std::min(f, fs.r);
+        u1 = u0 + fs.q + (f < fs.r ? 1 : 0);
+    }
+    if (u1 > u0) far_range(smem, u0, u1, fs.c_begin, fs.nstrip, Wk, d_out, d_in, Ep, ldE, U, bp0, kp, vec_rest != 0);
+}
+
+// Deal the far update's units (n_units in all) to the launch: every CU
+// holds one workgroup; the sweeping workgroups (n_sweep of them) are busy
+// for about kSweepUnits units' time first, so they take that much less.
+constexpr double kSweepUnits = 3.0;
+
+int far_split(int64_t n_units, int n_sweep, int n_cu, FarSplit& fs) {
+    fs.per_sweep = 0;
+    fs.q = fs.r = 0;
+    if (n_units <= 0) return 0;
+    const int n_far = std::max(0, n_cu - n_sweep);
+    if (n_far == 0) {  // more sweeping workgroups than CUs: they do it all
+        fs.per_sweep = (int)((n_units + n_sweep - 1) / n_sweep);
+        return 0;
+    }
+    const double t = ((double)n_units + n_sweep * kSweepUnits) / (double)(n_sweep + n_far);
+    fs.per_sweep = (int)std::max(0.0, std::floor(t - kSweepUnits));
+    const int64_t rest = n_units - (int64_t)n_sweep * fs.per_sweep;
+    const int nf = (int)std::min<int64_t>(n_far, rest);
+    if (nf > 0) {
+        fs.q = (int)(rest / nf);
+        fs.r = (int)(rest % nf);
+    }
+    return nf;
 }
 
 }  // namespace
@@ -885,6 +979,14 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
     }
     const int row_tiles = (int)((d_out + kRowsPerWg - 1) / kRowsPerWg);
     const int rest_rows = (int)((d_out + kRestRows - 1) / kRestRows);
+    int n_cu = 0;
+    {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        n_cu = std::max(n_cu, 1);
+    }
     hipError_t err = hipSuccess;
     // One launch per lazy block on the caller's stream: the sweep of block b
     // (its columns first receive block b-1's update, in registers) and, in
@@ -917,20 +1019,24 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
             hipLaunchKernelGGL(group_grid_kernel, dim3(rows4), dim3(256), 0, s, (const float*)w.Wk, d_out, d_in, b0,
                                group, b0 / group, ng, maxq, scales, zeros, minmax);
         }
-        const int64_t rest_cols = (kp > 0 && b1 < d_in) ? (d_in - b1 + kRestCols - 1) / kRestCols : 0;
-        const int64_t n_rest = rest_cols * rest_rows;
+        FarSplit fs;
+        fs.c_begin = b1;
+        fs.nstrip = (int)((d_in - b1 + kStrip - 1) / kStrip);
+        const int64_t n_units = (kp > 0 && b1 < d_in) ? (int64_t)rest_rows * fs.nstrip : 0;
+        fs.n_units = n_units;
+        const int n_far = far_split(n_units, row_tiles, n_cu, fs);
         size_t lds = sweep_lds_bytes(bw) + (kp > 0 ? (size_t)((kp + 3) & ~3) * kEtl * 4 : 0);
-        if (n_rest > 0) lds = std::max(lds, rest_lds_bytes());
+        if (n_units > 0) lds = std::max(lds, rest_lds_bytes());
         TimedLaunch t(K_Q_STEP, s);
-        const dim3 grid((unsigned)(row_tiles + n_rest));
+        const dim3 grid((unsigned)(row_tiles + n_far));
         if (bw % kSub == 0)
             hipLaunchKernelGGL(step_kernel<true>, grid, dim3(512), lds, s, w.Wk, d_out, d_in, U,
                                (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes, Eb, block,
-                               err_row, Ep, bp0, kp, row_tiles, rest_rows, (int)vec);
+                               err_row, Ep, bp0, kp, row_tiles, fs, (int)vec);
         else
             hipLaunchKernelGGL(step_kernel<false>, grid, dim3(512), lds, s, w.Wk, d_out, d_in, U,
                                (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes, Eb, block,
-                               err_row, Ep, bp0, kp, row_tiles, rest_rows, (int)vec);
+                               err_row, Ep, bp0, kp, row_tiles, fs, (int)vec);
     }
     (void)err;
     return hipGetLastError();
