@@ -7,10 +7,12 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 Pinned functions (see ``tests/test_oracle_pins.py``): ``hessian``, ``damp``,
 ``hinv_cholesky_upper``, ``grid``, ``quantize_values``, ``quantize``,
 ``dequantize``, ``output_error``, ``pack_codes``, ``unpack_codes``,
-``output_error_from_errors``.  No function here is "parity unpinned".
+``output_error_from_errors``, ``obq_quantize``.  No function here is
+"parity unpinned".
 """
 from .gptq import (  # noqa: F401
     NotPositiveDefinite,
+    ObqResult,
     QuantResult,
     damp,
     dequantize,
@@ -18,6 +20,7 @@ from .gptq import (  # noqa: F401
     hessian,
     hinv_cholesky_upper,
     layer,
+    obq_quantize,
     output_error,
     output_error_from_errors,
     pack_codes,

@@ -28,10 +28,19 @@ Readings of passages the pages leave open (the grid form, rounding, clamping,
 the precision of the rounding decision, dead-channel handling) are stated on
 the function that applies them.
 
+The greedy-order variant the fixed order replaces (``obq_quantize``: per
+row, quantize next the weight with the smallest ``e_q^2 / [H^-1]_qq``,
+compensate, and downdate the inverse by the Schur complement; aicassindra
+"Greedy quantization with error compensation", mbrenndoerfer "Mathematical
+Details of the Update") is here too, as the check of the device's variant.
+
 Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
 (worked example, Schur re-inversion, lazy-batch invariance, row decoupling,
 Kronecker brute force, diagonal-H reduction to round-to-nearest, the
-loss identity, per-step optimality, dead-channel removal, non-PD detection).
+loss identity, per-step optimality, dead-channel removal, non-PD detection;
+for the greedy variant: the worked example's first pick and score, fixed
+order equal to the sweep, brute-force re-optimization scores, the loss
+identity).
 """
 from __future__ import annotations
 
@@ -381,6 +390,127 @@ def output_error_from_errors(err_sq: np.ndarray, W0: np.ndarray, W_hat: np.ndarr
     and W0 the weights with dead columns zeroed."""
     D = np.asarray(W0, np.float64) - np.asarray(W_hat, np.float64)
     return (np.asarray(err_sq, np.float64) - float(lam) * np.sum(D * D, axis=1)) / 2.0
+
+
+# ----------------------------------------------------------------------------
+# The greedy-order variant (OBQ) that the fixed order replaces
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass
+class ObqResult:
+    codes: np.ndarray       # [d_out, d_in] uint8
+    scales: np.ndarray      # [d_out] float32
+    zeros: np.ndarray       # [d_out] int32
+    order: np.ndarray       # [d_out, d_in] int32: the column quantized at each step
+    w_hat: np.ndarray       # [d_out, d_in] fp64 s (q - z)
+    loss: np.ndarray        # [d_out] fp64 sum over the steps of e_q^2 / [Hf^-1]_qq
+    ties: int = 0           # replay: picks or codes adopted from the hint at a near-tie
+    hard: int = 0           # replay: adopted where the hint was not near a tie
+
+
+def obq_quantize(W: np.ndarray, Hinv: np.ndarray, bits: int, dead: Optional[np.ndarray] = None,
+                 fixed_order: bool = False, order_hint: Optional[np.ndarray] = None,
+                 code_hint: Optional[np.ndarray] = None, pick_tol: float = 1e-9,
+                 tie_tol: float = 1e-4, fixed_grid: Optional[Tuple[np.ndarray, np.ndarray]] = None,
+                 trace: Optional[list] = None) -> ObqResult:
+    """Greedy-order quantization of each row with error compensation (OBQ).
+
+    Per row, with ``Hf^-1`` the inverse Hessian restricted to the free
+    (not yet quantized) weights, starting from ``Hinv`` = the inverse of the
+    damped Hessian (aicassindra "Greedy quantization with error
+    compensation"; mbrenndoerfer "Mathematical Details of the Update"):
+
+    repeat until no weight is free:
+      round every free weight to the grid, ``e_q = w_q - quant(w_q)``;
+      pick the free q with the smallest ``e_q^2 / [Hf^-1]_qq`` (the lowest
+      index among equal scores; with ``fixed_order`` simply the next column);
+      move the free weights by ``delta = -(e_q / [Hf^-1]_qq) Hf^-1[:, q]``,
+      which leaves ``w_q`` at its grid value;
+      remove q: ``[Hf^-1]_ij -= [Hf^-1]_iq [Hf^-1]_qj / [Hf^-1]_qq``
+      (the Schur complement; row and column q become zero).
+
+    Grid, rounding and dead channels as in ``quantize`` with
+    ``group_size == 0``: one grid per row from the input W, the rounding
+    decision in fp32, dead columns zeroed after the grid.  ``loss`` sums the
+    pick scores; it equals ``dw H_damped dw^T`` with ``dw = W0 - What``
+    (every step's compensation is the constrained optimum).
+
+    Replay (parity with a device run): with ``order_hint``, where the
+    hinted pick differs from the own pick it is adopted and counted as a tie
+    when its score is within ``pick_tol`` (relative) of the smallest,
+    else as a hard mismatch; with ``code_hint`` the picked weight's code is
+    compared as in ``quantize`` (tie within ``tie_tol`` grid units of the
+    midpoint).  Adopting keeps the replay on the device's path.
+
+    ``fixed_grid`` = (scales, zeros) per row overrides the grid (the worked
+    example's grid of step 0.5); ``trace``, if a list, receives
+    ``(row, q, score_q, w)`` after every step, ``w`` the row's weights then.
+    """
+    W = np.array(W, dtype=np.float64, copy=True)
+    Hinv = np.asarray(Hinv, dtype=np.float64)
+    d_out, d_in = W.shape
+    if Hinv.shape != (d_in, d_in):
+        raise ValueError("Hinv shape")
+    if not (1 <= bits <= 16):
+        raise ValueError("bits")
+    maxq = 2 ** bits - 1
+    if fixed_grid is not None:
+        s = np.asarray(fixed_grid[0], F32).reshape(d_out)
+        z = np.asarray(fixed_grid[1], F32).reshape(d_out)
+    else:
+        mn = W.astype(F32).min(axis=1) if d_in else np.zeros(d_out, F32)
+        mx = W.astype(F32).max(axis=1) if d_in else np.zeros(d_out, F32)
+        s, z = grid(mn, mx, bits)
+    if dead is not None and np.any(dead):
+        W[:, np.asarray(dead, bool)] = 0.0
+    codes = np.zeros((d_out, d_in), np.uint8)
+    order = np.zeros((d_out, d_in), np.int32)
+    w_hat = np.zeros((d_out, d_in))
+    loss = np.zeros(d_out)
+    ties = hard = 0
+    for r in range(d_out):
+        w = W[r].copy()
+        Hf = Hinv.copy()
+        free = np.ones(d_in, bool)
+        sr = np.full(d_in, s[r], F32)
+        zr = np.full(d_in, z[r], F32)
+        for t in range(d_in):
+            q_all, v_all = quantize_values(w, sr, zr, bits)
+            wq_all = float(s[r]) * (q_all.astype(np.float64) - float(z[r]))
+            e_all = w - wq_all
+            score = np.full(d_in, np.inf)
+            diag = np.diag(Hf)
+            score[free] = e_all[free] ** 2 / diag[free]
+            q = t if fixed_order else int(np.argmin(score))
+            if order_hint is not None and int(order_hint[r, t]) != q:
+                h = int(order_hint[r, t])
+                if free[h] and score[h] <= score[q] * (1.0 + pick_tol):
+                    ties += 1
+                else:
+                    hard += 1
+                q = h
+            code = q_all[q]
+            if code_hint is not None and int(code_hint[r, q]) != int(code):
+                hc = float(code_hint[r, q])
+                if abs(hc - code) == 1.0 and abs(float(v_all[q]) - (hc + code) / 2.0) <= tie_tol:
+                    ties += 1
+                else:
+                    hard += 1
+                code = np.float32(min(max(hc, 0.0), maxq))
+            wq = float(s[r]) * (float(code) - float(z[r]))
+            e = w[q] - wq
+            d = Hf[q, q]
+            loss[r] += e * e / d
+            col = Hf[:, q].copy()
+            w[free] -= (e / d) * col[free]
+            w[q] = wq
+            Hf -= np.outer(col, Hf[q, :]) / d
+            free[q] = False
+            codes[r, q] = np.uint8(code)
+            order[r, t] = q
+            w_hat[r, q] = wq
+            if trace is not None:
+                trace.append((r, q, e * e / d, w.copy()))
+    return ObqResult(codes, s.astype(F32), z.astype(np.int32), order, w_hat, loss, ties, hard)
 
 
 def layer(W: np.ndarray, x_chunks: Iterable[np.ndarray], bits: int, group_size: int, block_size: int,

@@ -446,3 +446,132 @@ def test_output_error_from_errors(g, dead):
     per_row = oracle.output_error_from_errors(r.err_sq, W0, r.w_hat, lam)
     direct = np.array([oracle.output_error(W0[i:i + 1], r.w_hat[i:i + 1], [X]) for i in range(W.shape[0])])
     np.testing.assert_allclose(per_row, direct, rtol=1e-9)
+
+
+# ---------------------------------------------------------------------------
+# G: the greedy-order variant (aicassindra "Greedy quantization with error
+# compensation"; mbrenndoerfer "Mathematical Details of the Update")
+# ---------------------------------------------------------------------------
+def test_obq_worked_example_first_pick():
+    # the page's example quantizes w_1 first; the greedy rule agrees (its
+    # score e^2 / [H^-1]_11 is the page's compensated error 0.0384, against
+    # 0.08 for w_2), and the compensation moves w_2 to the page's 0.38
+    g = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    H = np.array(g["H"])
+    w = np.array([g["w"]])
+    tr = []
+    r = oracle.obq_quantize(w, np.linalg.inv(H), 4, fixed_grid=(np.array([g["grid_step"]]), np.array([0])),
+                            trace=tr)
+    _, q0, score0, w_after = tr[0]
+    assert q0 == 0
+    assert score0 == pytest.approx(g["error_with_compensation"], abs=1e-12)
+    assert w_after[0] == pytest.approx(g["q1"], abs=1e-12)
+    assert w_after[1] == pytest.approx(g["w2_after"], abs=1e-12)
+    assert list(r.order[0]) == [0, 1]
+    # both weights land on 0.5; the loss is dw H dw^T of the final error
+    dw = w[0] - r.w_hat[0]
+    assert r.loss[0] == pytest.approx(dw @ H @ dw, rel=1e-12)
+
+
+def _greedy_by_direct_solves(w0, H, s, z, bits):
+    """Greedy order by explicit re-optimization on H (no inverse, no Schur
+    downdate): at each step every free weight is tried, the others free
+    weights re-optimized by solving H_FF d_F = -H_Fq d_q, and the one with
+    the smallest increase of d^T H d (from the current point) is fixed."""
+    d_in = w0.size
+    w = w0.astype(np.float64).copy()
+    free = np.ones(d_in, bool)
+    order, codes = [], np.zeros(d_in, np.int64)
+    maxq = 2 ** bits - 1
+    for _ in range(d_in):
+        best = None
+        for q in np.nonzero(free)[0]:
+            v = np.float32(np.float32(np.float32(w[q]) / s) + z)
+            c = float(np.clip(np.rint(v), 0, maxq))
+            dq = s * (c - z) - w[q]                      # the move of w_q onto the grid
+            F = free.copy()
+            F[q] = False
+            d = np.zeros(d_in)
+            d[q] = dq
+            if F.any():
+                d[F] = np.linalg.solve(H[np.ix_(F, F)], -H[F, q] * dq)
+            inc = d @ H @ d
+            if best is None or inc < best[0] - 1e-15 * abs(best[0]):
+                best = (inc, q, c, d)
+        _, q, c, d = best
+        w = w + d
+        w[q] = s * (c - z)
+        free[q] = False
+        order.append(q)
+        codes[q] = int(c)
+    return np.array(order), codes
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_obq_matches_greedy_by_direct_solves(seed):
+    rng = np.random.default_rng(100 + seed)
+    d_in = 5
+    A = rng.standard_normal((d_in, 3 * d_in))
+    H = A @ A.T + 0.1 * np.eye(d_in)
+    w = rng.standard_normal((1, d_in)) * 0.3
+    s, z = og.grid(w.astype(F32).min(axis=1), w.astype(F32).max(axis=1), 3)
+    r = oracle.obq_quantize(w, np.linalg.inv(H), 3)
+    order, codes = _greedy_by_direct_solves(w[0], H, float(s[0]), float(z[0]), 3)
+    assert list(r.order[0]) == list(order)
+    assert list(r.codes[0]) == list(codes)
+
+
+@pytest.mark.parametrize("dead", [(), (2, 9)])
+def test_obq_fixed_order_is_the_sweep(dead):
+    # the fixed left-to-right order with the Schur downdate equals the
+    # Cholesky-row sweep, and the pick scores sum to its sum of squared
+    # scaled errors
+    W, X = _spd_problem(6, 24, 200, 7, dead)
+    H = oracle.hessian([X])
+    U, dm, lam = oracle.prepare(H)
+    Hd, dm2, _ = oracle.damp(H)
+    r = oracle.obq_quantize(W, np.linalg.inv(Hd), 4, dead=dm, fixed_order=True)
+    g = oracle.quantize(W, U, 4, 0, 8, dead=dm)
+    assert np.array_equal(r.codes, g.codes)
+    np.testing.assert_allclose(r.w_hat, g.w_hat, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(r.loss, g.err_sq, rtol=1e-9)
+
+
+@pytest.mark.parametrize("dead", [(), (1, 5)])
+def test_obq_loss_identity(dead):
+    W, X = _spd_problem(5, 16, 120, 11, dead)
+    H = oracle.hessian([X])
+    Hd, dm, lam = oracle.damp(H)
+    r = oracle.obq_quantize(W, np.linalg.inv(Hd), 3, dead=dm)
+    W0 = W.copy()
+    W0[:, dm] = 0.0
+    D = W0 - r.w_hat
+    np.testing.assert_allclose(r.loss, np.einsum("ri,ij,rj->r", D, Hd, D), rtol=1e-9)
+    # every row's order is a permutation, and each code is the rounding of
+    # the weight as it stood when it was picked (checked by the grid values)
+    for row in r.order:
+        assert sorted(row) == list(range(16))
+    assert np.all(r.codes <= 7)
+
+
+def test_obq_diagonal_h_is_round_to_nearest():
+    rng = np.random.default_rng(5)
+    W = rng.standard_normal((4, 12)) * 0.05
+    Hinv = np.diag(1.0 / rng.uniform(0.5, 2.0, 12))
+    r = oracle.obq_quantize(W, Hinv, 4)
+    s, z = og.grid(W.astype(F32).min(axis=1), W.astype(F32).max(axis=1), 4)
+    q, _ = og.quantize_values(W, s[:, None], z[:, None], 4)
+    assert np.array_equal(r.codes, q.astype(np.uint8))
+
+
+def test_obq_replay_counts():
+    W, X = _spd_problem(3, 10, 80, 13)
+    Hd, dm, lam = oracle.damp(oracle.hessian([X]))
+    Hinv = np.linalg.inv(Hd)
+    r = oracle.obq_quantize(W, Hinv, 4)
+    same = oracle.obq_quantize(W, Hinv, 4, order_hint=r.order, code_hint=r.codes)
+    assert same.ties == 0 and same.hard == 0 and np.array_equal(same.codes, r.codes)
+    bad = r.order.copy()
+    bad[0, [0, -1]] = bad[0, [-1, 0]]  # the last pick first: not a near-tie
+    rep = oracle.obq_quantize(W, Hinv, 4, order_hint=bad)
+    assert rep.hard >= 1 and list(rep.order[0]) == list(bad[0][:1]) + list(rep.order[0][1:])
