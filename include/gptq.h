@@ -226,6 +226,39 @@ int gptq_output_error(const void* W, int w_dtype, const uint8_t* dead, const uin
                       const float* scales, const int32_t* zeros, int64_t group_size, int64_t d_out, int64_t d_in,
                       const float* err_row, const double* lambda, float* out_row, void* stream);
 
+/*
+ * Greedy-order quantization of small layers (OBQ), the variant the fixed
+ * column order replaces (aicassindra "Greedy quantization with error
+ * compensation" and "GPTQ's speedups: fixed order and lazy batches";
+ * mbrenndoerfer "Mathematical Details of the Update" for the Schur
+ * downdate).  Per row, with Hf^-1 the inverse Hessian restricted to the
+ * free weights (initially H_damped^-1 = U^T U): round every free weight to
+ * the row's grid, quantize next the one with the smallest
+ * e_q^2 / [Hf^-1]_qq (lowest index among equal scores), move the free
+ * weights by -(e_q / [Hf^-1]_qq) Hf^-1[:, q], then
+ * Hf^-1 -= Hf^-1[:, q] Hf^-1[q, :] / [Hf^-1]_qq.  The grid, the fp32 rounding
+ * decision and the dead columns are those of gptq_quantize_layer with
+ * group_size 0; the inverse and the weights are kept in float64.
+ *   W          [d_out, d_in] of w_dtype, d_in <= 128.
+ *   U          [d_in, d_in] float32 from gptq_prepare_hinv.
+ *   dead       [d_in] uint8 or NULL.
+ *   codes      [d_out, d_in] uint8 output; scales [d_out] float32 and
+ *              zeros [d_out] int32 outputs (the per-row grid).
+ *   order      [d_out, d_in] int32 output or NULL: the column quantized at
+ *              each step.
+ *   loss       [d_out] float64 output or NULL: the sum of the pick scores,
+ *              equal to dw H_damped dw^T with dw = W0 - What.
+ *   workspace  at least gptq_obq_workspace(d_in) bytes of device memory,
+ *              256-byte aligned (H^-1 in float64).
+ * Errors: GPTQ_EINVAL (negative sizes, bits outside [2, 8], unknown
+ * w_dtype, null required pointer), GPTQ_EUNSUPPORTED (d_in above 128 or
+ * d_out above 2^24), GPTQ_EWORKSPACE.  Empty inputs return GPTQ_OK.
+ */
+size_t gptq_obq_workspace(int64_t d_in);
+int gptq_obq_quantize(const void* W, int w_dtype, int64_t d_out, int64_t d_in, const float* U, const uint8_t* dead,
+                      int bits, uint8_t* codes, float* scales, int32_t* zeros, int32_t* order, double* loss,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a gptq_status value (static string). */
 const char* gptq_status_string(int status);
 

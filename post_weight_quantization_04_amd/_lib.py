@@ -28,6 +28,8 @@ EXPORTS = (
     "gptq_pack_codes",
     "gptq_dequantize",
     "gptq_output_error",
+    "gptq_obq_workspace",
+    "gptq_obq_quantize",
     "gptq_kernel_count",
     "gptq_kernel_name",
     "gptq_timing_enable",
@@ -67,6 +69,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "gptq_pack_codes": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp]),
         "gptq_dequantize": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i64, _vp, _i32, _vp]),
         "gptq_output_error": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
+        "gptq_obq_workspace": (_sz, [_i64]),
+        "gptq_obq_quantize": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _sz, _vp]),
         "gptq_kernel_count": (_i32, []),
         "gptq_kernel_name": (ctypes.c_char_p, [_i32]),
         "gptq_timing_enable": (_i32, [_i32]),
@@ -188,6 +193,21 @@ def output_error(W, dead, packed, bits: int, scales, zeros, group_size: int, err
                                   _ptr(zeros), int(group_size), d_out, d_in, _ptr(err_row), _ptr(lam),
                                   _ptr(out_row), _stream(stream))
     _check("gptq_output_error", rc)
+
+
+def obq_workspace(d_in: int) -> int:
+    return int(load().gptq_obq_workspace(int(d_in)))
+
+
+def obq_quantize(W, U, dead, bits: int, codes, scales, zeros, order=None, loss=None, workspace=None,
+                 stream=None) -> None:
+    d_out, d_in = W.shape
+    rc = load().gptq_obq_quantize(_ptr(W), _dtype_code(W), d_out, d_in, _ptr(U), _ptr(dead), int(bits),
+                                  _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(order), _ptr(loss),
+                                  _ptr(workspace),
+                                  workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                  _stream(stream))
+    _check("gptq_obq_quantize", rc)
 
 
 # ---------------------------------------------------------------------------

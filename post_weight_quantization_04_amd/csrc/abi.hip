@@ -18,7 +18,7 @@ namespace {
 const char* const kNames[K_COUNT] = {
     "hessian_f16", "hessian_f32", "hinv_diag_stats", "hinv_load_reversed", "chol_step", "hinv_store_u",
     "q_row_grid",  "q_convert",   "q_rdiag",         "q_group_grid",       "q_step",    "q_trail",
-    "pack_codes",  "dequantize",  "output_error",
+    "pack_codes",  "dequantize",  "output_error", "obq_hinv", "obq_rows",
 };
 int g_timed = -1;
 struct EventPair {
@@ -162,6 +162,26 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in,
         return GPTQ_EWORKSPACE;
     return hip_status(launch_quantize(W, w_dtype == GPTQ_F16, d_out, d_in, U, dead, bits, group_size, block_size,
                                       codes, scales, zeros, err_row, minmax, workspace, as_stream(stream)));
+}
+
+size_t gptq_obq_workspace(int64_t d_in) {
+    if (d_in <= 0 || d_in > 128) return 0;
+    return obq_workspace_bytes(d_in);
+}
+
+int gptq_obq_quantize(const void* W, int w_dtype, int64_t d_out, int64_t d_in, const float* U, const uint8_t* dead,
+                      int bits, uint8_t* codes, float* scales, int32_t* zeros, int32_t* order, double* loss,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (d_out < 0 || d_in < 0) return GPTQ_EINVAL;
+    if (w_dtype != GPTQ_F16 && w_dtype != GPTQ_F32) return GPTQ_EINVAL;
+    if (bits < 2 || bits > 8) return GPTQ_EINVAL;
+    if (d_out == 0 || d_in == 0) return GPTQ_OK;
+    if (!W || !U || !codes || !scales || !zeros) return GPTQ_EINVAL;
+    if (d_in > 128 || d_out > ((int64_t)1 << 24)) return GPTQ_EUNSUPPORTED;
+    if (!workspace || workspace_bytes < obq_workspace_bytes(d_in) || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return GPTQ_EWORKSPACE;
+    return hip_status(launch_obq(W, w_dtype == GPTQ_F16, d_out, d_in, U, dead, bits, codes, scales, zeros, order, loss,
+                                 workspace, as_stream(stream)));
 }
 
 int64_t gptq_packed_words(int64_t d_in, int bits) {

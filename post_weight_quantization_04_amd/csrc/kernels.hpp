@@ -24,6 +24,8 @@ enum KernelId {
     K_PACK,
     K_DEQUANT,
     K_OUTERR,
+    K_OBQ_HINV,
+    K_OBQ_ROWS,
     K_COUNT
 };
 
@@ -63,5 +65,11 @@ hipError_t launch_output_error(const void* W, int w_is_f16, const uint8_t* dead,
                                const float* scales, const int32_t* zeros, int64_t group, int64_t d_out,
                                int64_t d_in, const float* err_row, const double* lambda, float* out,
                                hipStream_t s);
+
+// ---- greedy-order variant (small layers) -------------------------------------
+size_t obq_workspace_bytes(int64_t d_in);
+hipError_t launch_obq(const void* W, int w_is_f16, int64_t d_out, int64_t d_in, const float* U, const uint8_t* dead,
+                      int bits, uint8_t* codes, float* scales, int32_t* zeros, int32_t* order, double* loss,
+                      void* ws, hipStream_t s);
 
 }  // namespace gptq

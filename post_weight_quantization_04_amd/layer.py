@@ -126,3 +126,31 @@ def output_error(W, factor: Factor, q: Quantized, packed, bits: int, group_size:
     _lib.output_error(W, factor.dead, packed, bits, q.scales, q.zeros, group_size, q.err_row, factor.lam, out,
                       stream=stream)
     return out
+
+
+@dataclasses.dataclass
+class GreedyQuantized:
+    codes: "torch.Tensor"    # [d_out, d_in] uint8
+    scales: "torch.Tensor"   # [d_out] float32
+    zeros: "torch.Tensor"    # [d_out] int32
+    order: "torch.Tensor"    # [d_out, d_in] int32: the column quantized at each step
+    loss: "torch.Tensor"     # [d_out] float64: dw H_damped dw^T
+
+
+def quantize_greedy(W, factor: Factor, bits: int, ws: Optional[Workspace] = None, use_dead: bool = True,
+                    stream=None) -> GreedyQuantized:
+    """Greedy-order (OBQ) quantization of a small layer (``d_in <= 128``,
+    ``gptq_obq_quantize``)."""
+    import torch
+    d_out, d_in = W.shape
+    dev = W.device
+    out = GreedyQuantized(torch.empty((d_out, d_in), dtype=torch.uint8, device=dev),
+                          torch.empty((d_out,), dtype=torch.float32, device=dev),
+                          torch.empty((d_out,), dtype=torch.int32, device=dev),
+                          torch.empty((d_out, d_in), dtype=torch.int32, device=dev),
+                          torch.empty((d_out,), dtype=torch.float64, device=dev))
+    ws = ws or Workspace(dev)
+    buf = ws.get(_lib.obq_workspace(d_in))
+    _lib.obq_quantize(W, factor.U, factor.dead if use_dead else None, bits, out.codes, out.scales, out.zeros,
+                      out.order, out.loss, buf, stream=stream)
+    return out

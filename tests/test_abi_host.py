@@ -139,3 +139,19 @@ def test_pack_dequant_argument_errors(clib):
     assert oerr(bits=1) == 1 and oerr(group=48) == 1 and oerr(dtype=7) == 1
     assert oerr(W=None) == 1 and oerr(E=None) == 1 and oerr(L=None) == 1 and oerr(O=None) == 1
     assert oerr(d_out=0) == 0
+
+
+def test_greedy_variant_argument_errors(clib):
+    p = ctypes.c_void_p(256)
+    assert clib.gptq_obq_workspace(128) == 128 * 128 * 8 and clib.gptq_obq_workspace(129) == 0
+    assert clib.gptq_obq_workspace(0) == 0
+
+    def obq(d_out=8, d_in=64, bits=4, dtype=1, W=p, U=p, C=p, S=p, Z=p, ws=p, wsb=1 << 20):
+        return clib.gptq_obq_quantize(W, dtype, d_out, d_in, U, None, bits, C, S, Z, None, None, ws, wsb, None)
+
+    assert obq(bits=1) == 1 and obq(bits=9) == 1 and obq(dtype=2) == 1 and obq(d_out=-1) == 1
+    assert obq(W=None) == 1 and obq(U=None) == 1 and obq(C=None) == 1 and obq(S=None) == 1 and obq(Z=None) == 1
+    assert obq(d_in=129) == 2                       # GPTQ_EUNSUPPORTED: the inverse lives in registers
+    assert obq(ws=None) == 4 and obq(wsb=64 * 64 * 8 - 1) == 4
+    assert obq(ws=ctypes.c_void_p(256 + 8)) == 4    # not 256-byte aligned
+    assert obq(d_out=0) == 0 and obq(d_in=0) == 0

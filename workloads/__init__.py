@@ -151,6 +151,9 @@ WORKLOADS: Dict[str, Workload] = {
                          (XSpec("x", 11008, 16384, "float16", "relu", dead_frac=0.01),),
                          bits=3, group_size=0, block_size=128),
     "decoder_block": _decoder_block(),
+    "small_proj": _lowrank_1("small_proj", 4096, 128, 2048, "float16", "float16", 16, 4, 0, 128, 0.02, seed=7,
+                             description="W 4096x128 fp16, X 128x2048 fp16 (rank-16 factor), 4-bit per-row: a layer "
+                                         "small enough for the greedy (per-row order) variant"),
 }
 
 # ``attn_proj_g128`` uses the very same weight matrix as ``attn_proj``: both
