@@ -25,6 +25,7 @@ if ROOT not in sys.path:
 METRIC = "ms per 4096×4096 4-bit GPTQ layer (XXᵀ+Cholesky+sweep); % MFMA/HBM peak"
 PEAK_TFLOPS = {"f16": 2500.0, "f32": 157.3, "f64": 78.6}
 PEAK_HBM_GBS = 8000.0
+PEAK_FP64_VALU = 78.6  # TFLOP/s, MI355X fp64 vector (256 CUs at 2.4 GHz)
 NB = 64  # panel width of the blocked factorization (kCholNB in the library)
 
 # kernel -> (dtype class of its arithmetic, bound)
@@ -46,6 +47,7 @@ KERNEL_SOURCE = {
     "pack_codes": ("pack.hip", "pack_codes_kernel"),
     "dequantize": ("pack.hip", "dequant_kernel"),
     "output_error": ("pack.hip", "output_error_kernel"),
+    "obq_rows": ("obq.hip", "obq_row_kernel"),
 }
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "attn_proj_4096x4096_traffic.json")
 
@@ -140,6 +142,69 @@ def cpu_baseline(W, X_chunks, bits, group, block, damp, rows: int):
     }
 
 
+def greedy_variant(torch, wlm, _lib, layer, reps: int = 10) -> dict:
+    """The greedy-order (OBQ) variant against the fixed order on the small
+    layer (4096x128, where a per-row order is affordable): time per layer of
+    each, the rows kernel against the fp64 vector peak, and the two output
+    errors ||dW X||^2 (the pages expect the fixed order to lose almost
+    nothing)."""
+    w = wlm.get("small_proj")
+    spec = w.layers[0]
+    d_out, d_in = spec.d_out, spec.d_in
+    dev = torch.device("cuda:0")
+    W = torch.from_numpy(wlm.make_weight(w)).to(dev)
+    X = torch.from_numpy(wlm.x_full(w)).to(dev)
+    H = layer.hessian(X)
+    f = layer.prepare(H, w.damp)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    ws = layer.Workspace(dev)
+    res = {}
+    obq_ms = timed(lambda: res.__setitem__("g", layer.quantize_greedy(W, f, w.bits, ws=ws)))
+    q_ms = timed(lambda: res.__setitem__("q", layer.quantize(W, f, w.bits, 0, w.block_size, ws=ws)))
+    _lib.timing_enable("obq_rows")
+    for _ in range(reps):
+        layer.quantize_greedy(W, f, w.bits, ws=ws)
+    torch.cuda.synchronize()
+    rows_ms, rows_n = _lib.timing_read()
+    _lib.timing_enable(None)
+    rows_ms /= max(rows_n, 1)
+    # the rows kernel's fp64 multiply-adds: the Schur downdate touches the
+    # whole d_in x d_in inverse at each of the d_in steps of every row
+    flops = 2.0 * d_out * d_in ** 3
+    achieved = flops / (rows_ms * 1e-3) / 1e12
+    g, q = res["g"], res["q"]
+    dead = f.dead.bool()
+    W0 = W.double().clone()
+    W0[:, dead] = 0.0
+    lam = float(f.lam.double().item())
+    What = g.scales.double()[:, None] * (g.codes.double() - g.zeros.double()[:, None])
+    D = W0 - What
+    obq_err = float(((g.loss - lam * (D * D).sum(1)) / 2.0).sum().item())
+    packed = layer.pack(q.codes, w.bits)
+    gptq_err = float(layer.output_error(W, f, q, packed, w.bits, 0).double().sum().item())
+    return {
+        "workload": "small_proj: W 4096x128 fp16, X 128x2048 fp16 (rank-16), 4-bit per row",
+        "obq_ms_per_layer": round(obq_ms, 4),
+        "fixed_order_ms_per_layer": round(q_ms, 4),
+        "obq_rows_kernel": {"bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_FP64_VALU,
+                            "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP64_VALU, 4),
+                            "avg_launch_ms": round(rows_ms, 4), "flops": flops},
+        "output_error": {"obq": obq_err, "fixed_order": gptq_err, "ratio_obq_to_fixed": round(obq_err / gptq_err, 4)},
+    }
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +216,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-kernel-breakdown", action="store_true")
     ap.add_argument("--no-after-path", action="store_true",
                     help="skip timing few-bit storage, dequantization and the output error after the path")
+    ap.add_argument("--no-greedy", action="store_true",
+                    help="skip the greedy-order (OBQ) variant on the 4096x128 small layer")
     ap.add_argument("--counter-pass", action="store_true",
                     help="for hardware-counter runs: two untimed layer passes, then three copies of a 256 MiB "
                          "buffer whose counter readings calibrate FETCH_SIZE / WRITE_SIZE; no timing, no JSON")
@@ -237,6 +304,8 @@ def main(argv=None) -> int:
         jobs, _ = storage_jobs()
         for fn, _ in jobs.values():
             fn()
+        torch.cuda.synchronize()
+        greedy_variant(torch, wlm, _lib, layer, reps=1)
         torch.cuda.synchronize()
         a = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
@@ -348,6 +417,10 @@ def main(argv=None) -> int:
                            "frac_hbm": round(gbs / PEAK_HBM_GBS, 3), "traffic": recorded_traffic(cls)}
         after["output_error_sum"] = float(oe.sum().item())
 
+    greedy = None
+    if not args.no_greedy:
+        greedy = greedy_variant(torch, wlm, _lib, layer)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host ...", file=sys.stderr, flush=True)
@@ -377,6 +450,7 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "after_path": after or None,
+        "greedy_variant": greedy,
     }
     print(json.dumps(out), flush=True)
     return 0
