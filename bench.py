@@ -393,6 +393,21 @@ def main(argv=None) -> int:
         "launches_per_step": dom_launches // max(args.steps, 1),
     }
 
+    # every MFMA kernel class of the step against the peak of its own MFMA
+    # class (times from the per-kernel pass above): the contractions the
+    # method names are H = 2XX^T (hessian_*) and the lazy trailing update,
+    # carried by q_step together with the in-block sweep it overlaps
+    mfma_kernels = {}
+    for name, ms in kernel_ms.items():
+        if name not in KERNEL_CLASS or ms <= 0:
+            continue
+        cls_, bnd = KERNEL_CLASS[name]
+        fl = algorithmic_flops(name, d_out, d_in, n_tok, wl.block_size, wl.group_size)
+        ach = fl / (ms * 1e-3) / 1e12
+        mfma_kernels[name] = {"ms_per_step": round(ms, 4), "flops": fl, "achieved": round(ach, 2),
+                              "peak": PEAK_TFLOPS[cls_], "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS[cls_], 4),
+                              "traffic": recorded_traffic(name)}
+
     # after the path (not part of a step): few-bit storage, dequantization to
     # fp16 and the identity-based output error of the layer just quantized;
     # each is one streaming kernel, reported against the HBM peak with its
@@ -448,6 +463,7 @@ def main(argv=None) -> int:
         "kernel_launches_per_step": kernel_launches,
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,
+        "mfma_kernels": mfma_kernels or None,
         "cpu_baseline": cpu,
         "after_path": after or None,
         "greedy_variant": greedy,

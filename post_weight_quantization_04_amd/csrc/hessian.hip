@@ -6,6 +6,8 @@
 // of X rows I and J are staged through LDS; products run on MFMA with fp32
 // accumulation (f16 inputs: 32x32x16 f16, exact products; f32 inputs:
 // 32x32x2 f32).  Each call adds its token range into H once at the end.
+// The MFMA instruction sequence over the tokens is the same for every slab
+// size, so the sums are the same bits whatever the slab and prefetch depth.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -44,49 +46,129 @@ __device__ __forceinline__ void store_quarter(float* __restrict__ H, int64_t n, 
 
 // ---------------------------------------------------------------------------
 // float16 inputs
+//
+// The products of one 128x128 tile over a 2048-token chunk take ~14 us of
+// MFMA time per CU pair, while a load from the memory-side cache takes a
+// large fraction of a microsecond under this load; with only the next slab in
+// flight the loop waits on every slab.  Here each thread keeps kDepth slabs
+// of kK tokens in flight in registers (static register sets, the slab loop
+// unrolled by kDepth), while the MFMAs consume the current slab from one of
+// two LDS buffers.  Tiles are dealt out so that each XCD (workgroups are
+// dispatched round-robin over the 8 XCDs) takes a contiguous run of a
+// super-tile order of the lower triangle, keeping the X panels it reads
+// few and resident in its own L2.
 // ---------------------------------------------------------------------------
-constexpr int kK16 = 64;       // tokens per LDS stage
-constexpr int kLd16 = kK16 + 8;  // padded LDS row (halves)
+constexpr int kXcds = 8;
+constexpr int kSuper = 4;  // super-tile edge, in 128-row tiles
 
-// Each thread moves 4 rows x 8 halves of a 128 x 64 slab: row (tid>>3) + 32 i,
-// halves (tid&7)*8 .. +8.
-template <bool kVec>
-__device__ __forceinline__ void fetch_slab_f16(half8 (&v)[4], const half_t* __restrict__ X, int64_t n, int64_t ldx,
-                                               int64_t ntok, int r0, int64_t k0, int tid) {
-    const int kk = (tid & 7) * 8;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t row = r0 + (tid >> 3) + 32 * i;
-        const int64_t k = k0 + kk;
-        if (kVec && row < n && k + 8 <= ntok) {
-            v[i] = *reinterpret_cast<const half8*>(X + row * ldx + k);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[i][e] = (row < n && k + e < ntok) ? X[row * ldx + k + e] : (half_t)0;
+// Tile t of the super-tile order: super-rows P (kSuper tile rows each), in
+// each super-row the super-tiles Q <= P left to right, in each super-tile the
+// tiles row by row (only J <= I on the diagonal super-tile).
+__host__ __device__ inline void tile_of_super(int t, int T, int& I, int& J) {
+    const int SP = (T + kSuper - 1) / kSuper;
+    for (int P = 0; P < SP; ++P) {
+        const int r0 = P * kSuper, r1 = min(T, r0 + kSuper);
+        for (int Q = 0; Q <= P; ++Q) {
+            const int c0 = Q * kSuper, c1 = min(T, c0 + kSuper);
+            int cnt = 0;
+            if (Q < P) {
+                cnt = (r1 - r0) * (c1 - c0);
+                if (t < cnt) {
+                    I = r0 + t / (c1 - c0);
+                    J = c0 + t % (c1 - c0);
+                    return;
+                }
+            } else {
+                const int m = r1 - r0;
+                cnt = m * (m + 1) / 2;
+                if (t < cnt) {
+                    int i = 0;
+                    while ((i + 1) * (i + 2) / 2 <= t) ++i;
+                    I = r0 + i;
+                    J = c0 + (t - i * (i + 1) / 2);
+                    return;
+                }
+            }
+            t -= cnt;
         }
+    }
+    I = J = 0;  // not reached for t < T(T+1)/2
+}
+
+// Thread tid moves kK/16 half8 pieces of each 128 x kK slab: piece i is row
+// tid / (kK/8) + i * (256 / (kK/8)), halves (tid % (kK/8)) * 8 .. +8.
+template <int kK>
+struct Slab {
+    static constexpr int kChunks = kK / 8;              // half8 pieces per row
+    static constexpr int kRowsPerPass = kThreads / kChunks;
+    static constexpr int kPieces = kTile / kRowsPerPass;  // per thread
+    static constexpr int kLd = kK + 8;                  // padded LDS row (halves)
+};
+
+// A slab whose tokens all lie below ntok, with 16-byte aligned rows: one
+// unconditional 16-byte load per piece.  Rows past n are clamped to row n-1:
+// they only feed accumulator entries that are never stored.
+template <int kK>
+__device__ __forceinline__ void fetch_full(half8 (&v)[Slab<kK>::kPieces], const half_t* __restrict__ X, int64_t n,
+                                           int64_t ldx, int r0, int64_t k0, int tid) {
+    using S = Slab<kK>;
+    const int64_t k = k0 + (tid % S::kChunks) * 8;
+#pragma unroll
+    for (int i = 0; i < S::kPieces; ++i) {
+        const int64_t row = min((int64_t)(r0 + tid / S::kChunks + S::kRowsPerPass * i), n - 1);
+        v[i] = *reinterpret_cast<const half8*>(X + row * ldx + k);
     }
 }
 
-__device__ __forceinline__ void stash_slab_f16(const half8 (&v)[4], half_t (*S)[kLd16], int tid) {
-    const int kk = (tid & 7) * 8;
+// The last, partial slab (or any slab of an unaligned X): element loads,
+// tokens past ntok read as zero.
+template <int kK>
+__device__ __forceinline__ void fetch_tail(half8 (&v)[Slab<kK>::kPieces], const half_t* __restrict__ X, int64_t n,
+                                           int64_t ldx, int64_t ntok, int r0, int64_t k0, int tid) {
+    using S = Slab<kK>;
+    const int64_t k = k0 + (tid % S::kChunks) * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<half8*>(&S[(tid >> 3) + 32 * i][kk]) = v[i];
+    for (int i = 0; i < S::kPieces; ++i) {
+        const int64_t row = min((int64_t)(r0 + tid / S::kChunks + S::kRowsPerPass * i), n - 1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[i][e] = (k + e < ntok) ? X[row * ldx + k + e] : (half_t)0;
+    }
 }
 
-// Token slab k+1 is fetched into registers while the MFMAs consume slab k
-// from one of two LDS buffers (one barrier per slab).
-template <bool kVec>
-__global__ __launch_bounds__(kThreads) void hessian_f16_kernel(float* __restrict__ H, int64_t n,
-                                                              const half_t* __restrict__ X, int64_t ldx,
-                                                              int64_t ntok) {
-    __shared__ half_t As[2][kTile][kLd16];
-    __shared__ half_t Bs[2][kTile][kLd16];
+template <int kK>
+__device__ __forceinline__ void stash_slab(const half8 (&v)[Slab<kK>::kPieces], half_t* S_, int tid) {
+    using S = Slab<kK>;
+    const int kk = (tid % S::kChunks) * 8;
+#pragma unroll
+    for (int i = 0; i < S::kPieces; ++i)
+        *reinterpret_cast<half8*>(&S_[(tid / S::kChunks + S::kRowsPerPass * i) * S::kLd + kk]) = v[i];
+}
+
+constexpr int kKf16 = 32;    // tokens per slab (41 KB of LDS: three workgroups fit a CU)
+constexpr int kDepthf16 = 2;  // slabs in flight per thread
+
+// Slabs below nfull take the unconditional path; the rest (at most the last
+// one, or all when X is unaligned) the element path.  Diagonal tiles load
+// their one panel twice so that every tile issues the same loads.  The slab
+// loop runs in two parts: a steady part in which every fetch is a full slab
+// (so the compiler can count the loads in flight and wait only for the
+// oldest set), and a generic part for the last slabs.
+template <int kK, int kDepth>
+__global__ __launch_bounds__(kThreads, 2) void hessian_f16_kernel(float* __restrict__ H, int64_t n,
+                                                                 const half_t* __restrict__ X, int64_t ldx,
+                                                                 int64_t ntok, int64_t nfull, int T,
+                                                                 int per_xcd) {
+    using S = Slab<kK>;
+    __shared__ half_t As[2][kTile * S::kLd];
+    __shared__ half_t Bs[2][kTile * S::kLd];
+    const int t = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+    if (t >= T * (T + 1) / 2) return;
     int I, J;
-    tile_of(blockIdx.x, I, J);
-    const bool diag = (I == J);
+    tile_of_super(t, T, I, J);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wi = w >> 1, wj = w & 1;
-    const bool active = !(diag && wi < wj);  // upper quarter of a diagonal tile
+    const bool active = !(I == J && wi < wj);  // upper quarter of a diagonal tile
+    const int rA = I * kTile, rB = J * kTile;
 
     float16v acc[2][2];
 #pragma unroll
@@ -94,39 +176,88 @@ __global__ __launch_bounds__(kThreads) void hessian_f16_kernel(float* __restrict
 #pragma unroll
         for (int q = 0; q < 2; ++q) acc[m][q] = (float16v){};
 
-    half8 ra[4], rb[4];
-    fetch_slab_f16<kVec>(ra, X, n, ldx, ntok, I * kTile, 0, tid);
-    if (!diag) fetch_slab_f16<kVec>(rb, X, n, ldx, ntok, J * kTile, 0, tid);
-    const int64_t nslab = (ntok + kK16 - 1) / kK16;
-    for (int64_t sl = 0; sl < nslab; ++sl) {
-        const int buf = (int)(sl & 1);
-        stash_slab_f16(ra, As[buf], tid);
-        if (!diag) stash_slab_f16(rb, Bs[buf], tid);
-        __syncthreads();
-        if (sl + 1 < nslab) {
-            fetch_slab_f16<kVec>(ra, X, n, ldx, ntok, I * kTile, (sl + 1) * kK16, tid);
-            if (!diag) fetch_slab_f16<kVec>(rb, X, n, ldx, ntok, J * kTile, (sl + 1) * kK16, tid);
+    const int64_t nslab = (ntok + kK - 1) / kK;
+    half8 ra[kDepth][S::kPieces], rb[kDepth][S::kPieces];
+
+    auto fetch = [&](half8(&va)[S::kPieces], half8(&vb)[S::kPieces], int64_t f) {
+        if (f < nfull) {
+            fetch_full<kK>(va, X, n, ldx, rA, f * kK, tid);
+            fetch_full<kK>(vb, X, n, ldx, rB, f * kK, tid);
+        } else if (f < nslab) {
+            fetch_tail<kK>(va, X, n, ldx, ntok, rA, f * kK, tid);
+            fetch_tail<kK>(vb, X, n, ldx, ntok, rB, f * kK, tid);
         }
-        half_t(*Ap)[kLd16] = As[buf];
-        half_t(*Bp)[kLd16] = diag ? As[buf] : Bs[buf];
-        if (active) {
+    };
+    // stash slab sl from its registers, then (after the barrier) the MFMAs;
+    // buffer sl&1 was last read by slab sl-2, which every wave finished
+    // before the previous barrier
+    auto stash = [&](const half8(&va)[S::kPieces], const half8(&vb)[S::kPieces], int64_t sl) {
+        stash_slab<kK>(va, As[sl & 1], tid);
+        stash_slab<kK>(vb, Bs[sl & 1], tid);
+        __syncthreads();
+    };
+    auto compute = [&](int64_t sl) {
+        if (!active) return;
+        const half_t* Ap = As[sl & 1];
+        const half_t* Bp = Bs[sl & 1];
+        half8 a[kK / 16][2], b[kK / 16][2];
 #pragma unroll
-            for (int ks = 0; ks < kK16; ks += 16) {
-                half8 a[2], b[2];
+        for (int ks = 0; ks < kK / 16; ++ks) {
 #pragma unroll
-                for (int m = 0; m < 2; ++m)
-                    a[m] = *reinterpret_cast<const half8*>(&Ap[wi * 64 + 32 * m + (lane & 31)][ks + 8 * (lane >> 5)]);
+            for (int m = 0; m < 2; ++m)
+                a[ks][m] = *reinterpret_cast<const half8*>(
+                    &Ap[(wi * 64 + 32 * m + (lane & 31)) * S::kLd + 16 * ks + 8 * (lane >> 5)]);
 #pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    b[q] = *reinterpret_cast<const half8*>(&Bp[wj * 64 + 32 * q + (lane & 31)][ks + 8 * (lane >> 5)]);
+            for (int q = 0; q < 2; ++q)
+                b[ks][q] = *reinterpret_cast<const half8*>(
+                    &Bp[(wj * 64 + 32 * q + (lane & 31)) * S::kLd + 16 * ks + 8 * (lane >> 5)]);
+        }
 #pragma unroll
-                for (int m = 0; m < 2; ++m)
+        for (int ks = 0; ks < kK / 16; ++ks)
 #pragma unroll
-                    for (int q = 0; q < 2; ++q) acc[m][q] = mfma32x32x16_f16(a[m], b[q], acc[m][q]);
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) acc[m][q] = mfma32x32x16_f16(a[ks][m], b[ks][q], acc[m][q]);
+    };
+
+    // steady part: slabs [0, nsteady), every fetch (slab sl + kDepth) full;
+    // its first fetches are unconditional too, so that on entry the compiler
+    // sees exactly kDepth full sets of loads in flight
+    const int64_t nsteady = nfull > kDepth ? ((nfull - kDepth) / kDepth) * kDepth : 0;
+    int64_t s0 = 0;
+    if (nsteady > 0) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            fetch_full<kK>(ra[d], X, n, ldx, rA, (int64_t)d * kK, tid);
+            fetch_full<kK>(rb[d], X, n, ldx, rB, (int64_t)d * kK, tid);
+            __builtin_amdgcn_sched_barrier(0);  // issue the sets in slab order
+        }
+        for (; s0 < nsteady; s0 += kDepth) {
+#pragma unroll
+            for (int d = 0; d < kDepth; ++d) {
+                const int64_t sl = s0 + d;
+                stash(ra[d], rb[d], sl);
+                fetch_full<kK>(ra[d], X, n, ldx, rA, (sl + kDepth) * kK, tid);
+                fetch_full<kK>(rb[d], X, n, ldx, rB, (sl + kDepth) * kK, tid);
+                compute(sl);
             }
         }
+    } else {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) fetch(ra[d], rb[d], d);
     }
-    if (active) store_quarter(H, n, I * kTile + wi * 64, J * kTile + wj * 64, acc, lane);
+    // generic part: the last slabs
+    for (; s0 < nslab; s0 += kDepth) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            const int64_t sl = s0 + d;
+            if (sl >= nslab) break;
+            stash(ra[d], rb[d], sl);
+            fetch(ra[d], rb[d], sl + kDepth);
+            compute(sl);
+        }
+    }
+    if (active) store_quarter(H, n, rA + wi * 64, rB + wj * 64, acc, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -208,13 +339,12 @@ hipError_t launch_hessian(float* H, int64_t n, const void* X, int x_is_f16, int6
     const uintptr_t addr = reinterpret_cast<uintptr_t>(X);
     if (x_is_f16) {
         TimedLaunch t(K_HESS_F16, s);
+        // full slabs take 16-byte loads when every row start is 16-byte aligned
         const bool vec = (addr % 16 == 0) && (ldx % 8 == 0);
-        if (vec)
-            hipLaunchKernelGGL(hessian_f16_kernel<true>, dim3((unsigned)tiles), dim3(kThreads), 0, s, H, n,
-                               static_cast<const half_t*>(X), ldx, ntok);
-        else
-            hipLaunchKernelGGL(hessian_f16_kernel<false>, dim3((unsigned)tiles), dim3(kThreads), 0, s, H, n,
-                               static_cast<const half_t*>(X), ldx, ntok);
+        const int64_t nfull = vec ? ntok / kKf16 : 0;
+        const int per_xcd = (int)((tiles + kXcds - 1) / kXcds);
+        hipLaunchKernelGGL((hessian_f16_kernel<kKf16, kDepthf16>), dim3((unsigned)(per_xcd * kXcds)), dim3(kThreads),
+                           0, s, H, n, static_cast<const half_t*>(X), ldx, ntok, nfull, (int)T, per_xcd);
     } else {
         TimedLaunch t(K_HESS_F32, s);
         const bool vec = (addr % 16 == 0) && (ldx % 4 == 0);
