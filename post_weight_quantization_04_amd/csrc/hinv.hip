@@ -27,11 +27,18 @@ namespace {
 
 constexpr int NB = kCholNB;  // 64
 constexpr int kGemmThreads = 256;
+// Steps are paired (every other update of the rest deferred, then applied
+// with the next step's as one 128-deep product) from this many 64-wide tiles
+// on.  Measured on MI355X: at d_in = 11008 (172 tiles) the factorization
+// takes 25.5 ms paired against 29.0 ms unpaired (its trailing-matrix traffic
+// dominates); at 4096 (64 tiles) 2.46 against 2.21 ms (the odd steps'
+// longer critical part dominates).
+constexpr int kPairMinTiles = 128;
 constexpr int kLdsLd = NB + 8;   // padded LDS row (doubles)
 
 struct HinvWs {
     double* G;      // n_pad x n_pad by 64x64 tiles (see gt)
-    double* P;      // 2 x [n_pad / NB][NB][NB] (alternating steps)
+    double* P;      // 3 x [n_pad / NB][NB][NB] (step s uses buffer s % 3)
     double* scal;   // [0] = lambda
     int* fail;      // device flag: set once a pivot fails
 };
@@ -49,8 +56,8 @@ HinvWs carve(void* ws, int64_t n) {
     HinvWs w;
     w.G = reinterpret_cast<double*>(p);
     p += round_up(np * np * 8, 256);
-    w.P = reinterpret_cast<double*>(p);  // two panel buffers
-    p += 2 * round_up(np * NB * 8, 256);
+    w.P = reinterpret_cast<double*>(p);  // three panel buffers
+    p += 3 * round_up(np * NB * 8, 256);
     w.scal = reinterpret_cast<double*>(p);
     p += 256;
     w.fail = reinterpret_cast<int*>(p);
@@ -506,6 +513,21 @@ __device__ __forceinline__ void gemm_stage_compute(const GemmRegs& r, GemmLds& s
     }
 }
 
+// both halves from fetched registers, when the LDS stage may still be read
+// by a previous product
+template <bool kBT>
+__device__ __forceinline__ void gemm_stage_compute_after(const GemmRegs& r, GemmLds& s, double4v (&acc)[2][2]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        __syncthreads();
+        gemm_stash_a(r.a, s, tid, h);
+        gemm_stash_b<kBT>(r.b, s, tid, h);
+        __syncthreads();
+        gemm_compute_half<kBT>(s, acc);
+    }
+}
+
 template <bool kBT>
 __device__ __forceinline__ void tile_gemm_f64(const double* __restrict__ A, int64_t lda,
                                               const double* __restrict__ B, int64_t ldb, GemmLds& s,
@@ -552,6 +574,52 @@ __device__ __forceinline__ void tile_gemm_sub_f64(const double* __restrict__ A, 
         for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int v = 0; v < 4; ++v) C[(int64_t)acc_row(m, v) * ldc + acc_col(q)] = c[m][q][v] - acc[m][q][v];
+}
+
+// C -= A1 B1 + A2 B2 (kSub) or C = -(A1 B1 + A2 B2): one 128-deep product
+// with one read and one write of C.  The second pair's operands are fetched
+// into the same registers once the first pair is staged, so their latency
+// overlaps the first pair's second half; C's old values are loaded behind
+// the first pair's operands.
+template <bool kBT, bool kSub>
+__device__ __forceinline__ void tile_gemm2_f64(const double* __restrict__ A1, const double* __restrict__ B1,
+                                               const double* __restrict__ A2, const double* __restrict__ B2,
+                                               double* __restrict__ C, GemmLds& s) {
+    const int tid = threadIdx.x;
+    GemmRegs r;
+    gemm_fetch<kBT>(r, A1, NB, B1, NB, tid);
+    double c[2][2][4];
+    if (kSub) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) c[m][q][v] = C[acc_row(m, v) * NB + acc_col(q)];
+    }
+    double4v acc[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) acc[m][q] = (double4v){};
+    gemm_stash_a(r.a, s, tid, 0);
+    gemm_stash_b<kBT>(r.b, s, tid, 0);
+    __syncthreads();
+    gemm_compute_half<kBT>(s, acc);
+    __syncthreads();
+    gemm_stash_a(r.a, s, tid, 1);
+    gemm_stash_b<kBT>(r.b, s, tid, 1);
+    __syncthreads();
+    gemm_fetch<kBT>(r, A2, NB, B2, NB, tid);
+    gemm_compute_half<kBT>(s, acc);
+    gemm_stage_compute_after<kBT>(r, s, acc);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                C[acc_row(m, v) * NB + acc_col(q)] = kSub ? c[m][q][v] - acc[m][q][v] : -acc[m][q][v];
 }
 
 // mode 0: C = acc ; mode 2: C = -acc
@@ -725,10 +793,11 @@ struct DiagPanelNextLds {
     GemmLds gemm;
 };
 
+template <bool kPair>
 __device__ __forceinline__ void diag_panel_next_body(DiagPanelNextLds& u, double* __restrict__ G, int64_t np,
-                                                     double* __restrict__ Pk1, const double* __restrict__ Pk, int k,
-                                                     int T, int t, int32_t* __restrict__ info,
-                                                     int* __restrict__ fail) {
+                                                     double* __restrict__ Pk1, const double* __restrict__ Pk,
+                                                     const double* __restrict__ Pkm, int k, int T, int t,
+                                                     int32_t* __restrict__ info, int* __restrict__ fail) {
     const int tid = threadIdx.x;
     const int k1 = k + 1;
     const bool has_tile = t < T - 1;
@@ -742,6 +811,9 @@ __device__ __forceinline__ void diag_panel_next_body(DiagPanelNextLds& u, double
     gemm_fetch_a(pd, Pd, NB, tid);
     double xo[16];
     double c2[2][2][4];
+    // with kPair, step k-1's update is still owed too, and G_{k1,k-1} holds
+    // nothing yet (its step k-1 value -P_k1 M_{k-1,k-1} was never stored)
+    const bool neg = inv_row && (t == k || (kPair && t == k - 1));
     if (has_tile) {
         if (!inv_row) {
             gemm_fetch_a(xo, Pk + (int64_t)(t + 1) * NB * NB, NB, tid);
@@ -750,7 +822,7 @@ __device__ __forceinline__ void diag_panel_next_body(DiagPanelNextLds& u, double
             gemm_fetch_b<false>(xo, Pk, NB, tid);  // M_kk (zeros above the diagonal)
         } else {
             gemm_fetch_b<false>(xo, G + gt(np, k, t), NB, tid);
-            tile_load_acc(c2, G + gt(np, k1, t), NB);
+            if (!neg) tile_load_acc(c2, G + gt(np, k1, t), NB);
         }
     }
     {
@@ -794,13 +866,65 @@ __device__ __forceinline__ void diag_panel_next_body(DiagPanelNextLds& u, double
             if (!inv_row) gemm_compute_half<true>(s, acc);
             else gemm_compute_half<false>(s, acc);
         }
-        const bool neg = inv_row && t == k;
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
             for (int q = 0; q < 2; ++q)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) c2[m][q][v] = neg ? -acc[m][q][v] : c2[m][q][v] - acc[m][q][v];
+    }
+    if (kPair) {
+        // step k-1's part: D -= P'_k1 P'_k1^T and the operand's own term,
+        //   t >= k1:    - P'_{t+1} P'_k1^T
+        //   t == k-1:   - P'_k1 M_{k-1,k-1}
+        //   t <  k-1:   - P'_k1 M_{k-1,t}
+        // with P' and M_{k-1,k-1} from the panel buffer of step k-1 (Pkm)
+        double pm[16], xm[16];
+        gemm_fetch_a(pm, Pkm + (int64_t)k1 * NB * NB, NB, tid);
+        const bool xterm = has_tile && t != k;
+        if (xterm) {
+            if (!inv_row) gemm_fetch_a(xm, Pkm + (int64_t)(t + 1) * NB * NB, NB, tid);
+            else if (t == k - 1) gemm_fetch_b<false>(xm, Pkm, NB, tid);
+            else gemm_fetch_b<false>(xm, G + gt(np, k - 1, t), NB, tid);
+        }
+        zero_acc(acc);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            __syncthreads();
+            gemm_stash_a(pm, s, tid, h);
+            gemm_stash_b<true>(pm, s, tid, h);
+            __syncthreads();
+            gemm_compute_half<true>(s, acc);
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) L.g[acc_row(m, v)][acc_col(q)] -= acc[m][q][v];
+        if (xterm) {
+            zero_acc(acc);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                __syncthreads();
+                if (!inv_row) {
+                    gemm_stash_a(xm, s, tid, h);
+                    gemm_stash_b<true>(pm, s, tid, h);
+                } else {
+                    gemm_stash_a(pm, s, tid, h);
+                    gemm_stash_b<false>(xm, s, tid, h);
+                }
+                __syncthreads();
+                if (!inv_row) gemm_compute_half<true>(s, acc);
+                else gemm_compute_half<false>(s, acc);
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) c2[m][q][v] -= acc[m][q][v];
+        }
     }
     __syncthreads();
     const int st = diag64(L);
@@ -905,6 +1029,31 @@ __device__ __forceinline__ void trail_body(GemmLds& s, double* __restrict__ G, i
     }
 }
 
+// Update of block (i, j) by steps k-1 and k together (the update of step
+// k-1 was deferred): one 128-deep product per block.  P' and M_{k-1,k-1}
+// come from the panel buffer of step k-1 (Pm), P and M_kk from that of
+// step k (P); rows k-1 and k of the inverse (M_{k-1,j}, M_kj) are in place
+// in G.
+__device__ __forceinline__ void trail_body2(GemmLds& s, double* __restrict__ G, int64_t np,
+                                            const double* __restrict__ P, const double* __restrict__ Pm, int k,
+                                            int64_t i, int64_t j) {
+    const double* Pi = P + i * NB * NB;
+    const double* Pmi = Pm + i * NB * NB;
+    double* Gij = G + gt(np, i, j);
+    if (j < k - 1) {
+        tile_gemm2_f64<false, true>(Pmi, G + gt(np, k - 1, j), Pi, G + gt(np, k, j), Gij, s);
+    } else if (j == k - 1) {
+        tile_gemm2_f64<false, false>(Pmi, Pm, Pi, G + gt(np, k, j), Gij, s);
+    } else if (j == k) {
+        double4v acc[2][2];
+        zero_acc(acc);
+        tile_gemm_f64<false>(Pi, NB, P, NB, s, acc);
+        tile_store_f64<2>(Gij, NB, acc);
+    } else {
+        tile_gemm2_f64<true, true>(Pmi, Pm + j * NB * NB, Pi, P + j * NB * NB, Gij, s);
+    }
+}
+
 // One launch per step k: the diagonal block and panel of step k1 = k+1
 // together with the update of step k of the blocks they read (workgroups
 // 0 .. npan-1, dispatched first), one workgroup that copies M_kk into G_kk
@@ -912,16 +1061,18 @@ __device__ __forceinline__ void trail_body(GemmLds& s, double* __restrict__ G, i
 // the update of step k (the others).  The parts touch disjoint blocks (the
 // rest excludes column and row block k1) and different panel buffers, so
 // nothing but the launch order separates the steps.
+template <bool kPair>
 __global__ __launch_bounds__(kGemmThreads, 2) void chol_step_kernel(double* __restrict__ G, int64_t np,
                                                                  double* __restrict__ Pk1,
-                                                                 const double* __restrict__ Pk, int k, int T,
+                                                                 const double* __restrict__ Pk,
+                                                                 const double* __restrict__ Pkm, int k, int T,
                                                                  int npan, int32_t* __restrict__ info,
                                                                  int* __restrict__ fail) {
     __shared__ __align__(16) DiagPanelNextLds u;
     if (*fail) return;
     const int b = (int)blockIdx.x;
     if (b < npan) {
-        diag_panel_next_body(u, G, np, Pk1, Pk, k, T, b, info, fail);
+        diag_panel_next_body<kPair>(u, G, np, Pk1, Pk, Pkm, k, T, b, info, fail);
     } else if (b == npan) {
         double* Gkk = G + gt(np, k, k);
 #pragma unroll
@@ -932,7 +1083,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void chol_step_kernel(double* __re
     } else {
         int64_t i, j;
         rest_tile(k, (int64_t)(b - npan - 1), i, j);
-        trail_body(u.gemm, G, np, Pk, k, i, j);
+        if (kPair) trail_body2(u.gemm, G, np, Pk, Pkm, k, i, j);
+        else trail_body(u.gemm, G, np, Pk, k, i, j);
     }
 }
 
@@ -954,7 +1106,7 @@ __global__ __launch_bounds__(256) void store_u_kernel(const double* __restrict__
 
 size_t hinv_workspace_bytes(int64_t n) {
     const int64_t np = round_up(n, NB);
-    return (size_t)(round_up(np * np * 8, 256) + 2 * round_up(np * NB * 8, 256) + 256 + 256);
+    return (size_t)(round_up(np * np * 8, 256) + 3 * round_up(np * NB * 8, 256) + 256 + 256);
 }
 
 
@@ -969,7 +1121,8 @@ hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, floa
     HinvWs w = carve(ws, n);
     const int64_t np = round_up(n, NB);
     const int T = (int)(np / NB);
-    double* Pbuf[2] = {w.P, w.P + round_up(np * NB * 8, 256) / 8};
+    const int64_t pstride = round_up(np * NB * 8, 256) / 8;
+    double* Pbuf[3] = {w.P, w.P + pstride, w.P + 2 * pstride};  // step s: buffer s % 3
     hipError_t e = hipSuccess;
     {
         TimedLaunch t(K_HINV_DIAGSUM, s);
@@ -987,12 +1140,24 @@ hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, floa
         hipLaunchKernelGGL(chol_diag_panel_kernel, dim3((unsigned)npan), dim3(kGemmThreads), 0, s, w.G, np, Pbuf[0], T,
                            info, w.fail);
     }
+    // wide layers pair the steps: an even step's update of the rest is
+    // deferred and applied with the next step's as one 128-deep product
+    const bool paired = T >= kPairMinTiles;
     for (int k = 0; k < T; ++k) {
         const int np1 = (k + 1 < T) ? npan : 0;
-        const int64_t n_rest = rest_tiles(k, T);
+        const bool odd = (k & 1) != 0;
+        const int64_t n_rest = (paired && !odd) ? 0 : rest_tiles(k, T);
+        const dim3 grid((unsigned)(np1 + 1 + n_rest));
+        double* pk1 = Pbuf[(k + 1) % 3];
+        const double* pk = Pbuf[k % 3];
+        const double* pkm = Pbuf[(k + 2) % 3];  // step k-1
         TimedLaunch t(K_CHOL_STEP, s);
-        hipLaunchKernelGGL(chol_step_kernel, dim3((unsigned)(np1 + 1 + n_rest)), dim3(kGemmThreads), 0, s, w.G, np,
-                           Pbuf[(k + 1) & 1], (const double*)Pbuf[k & 1], k, T, np1, info, w.fail);
+        if (paired && odd)
+            hipLaunchKernelGGL(chol_step_kernel<true>, grid, dim3(kGemmThreads), 0, s, w.G, np, pk1, pk, pkm, k, T,
+                               np1, info, w.fail);
+        else
+            hipLaunchKernelGGL(chol_step_kernel<false>, grid, dim3(kGemmThreads), 0, s, w.G, np, pk1, pk, pkm, k, T,
+                               np1, info, w.fail);
     }
     {
         TimedLaunch t(K_HINV_STORE, s);
