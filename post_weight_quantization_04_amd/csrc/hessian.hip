@@ -1,8 +1,9 @@
 // Stage 1: H += 2 X X^T on the lower triangle (aicassindra.com
 // "tm_gptq_math", "Why it is second-order: the Hessian").
 //
-// One workgroup per 128x128 lower-triangle tile (I >= J) of H; four waves,
-// each owning a 64x64 quarter as 2x2 MFMA 32x32 accumulators.  Token slabs
+// One workgroup per lower-triangle tile (I >= J) of H, 128x128 on four waves
+// or, for wide layers, 256x256 on sixteen; each wave owns a 64x64 quarter as
+// 2x2 MFMA 32x32 accumulators.  Token slabs
 // of X rows I and J are staged through LDS; products run on MFMA with fp32
 // accumulation (f16 inputs: 32x32x16 f16, exact products; f32 inputs:
 // 32x32x2 f32).  Each call adds its token range into H once at the end.
@@ -59,7 +60,7 @@ __device__ __forceinline__ void store_quarter(float* __restrict__ H, int64_t n, 
 // few and resident in its own L2.
 // ---------------------------------------------------------------------------
 constexpr int kXcds = 8;
-constexpr int kSuper = 4;  // super-tile edge, in 128-row tiles
+constexpr int kSuper = 4;  // super-tile edge, in tiles
 
 // Tile t of the super-tile order: super-rows P (kSuper tile rows each), in
 // each super-row the super-tiles Q <= P left to right, in each super-tile the
@@ -95,23 +96,25 @@ __host__ __device__ inline void tile_of_super(int t, int T, int& I, int& J) {
     I = J = 0;  // not reached for t < T(T+1)/2
 }
 
-// Thread tid moves kK/16 half8 pieces of each 128 x kK slab: piece i is row
-// tid / (kK/8) + i * (256 / (kK/8)), halves (tid % (kK/8)) * 8 .. +8.
-template <int kK>
+// Thread tid of kThr moves the half8 pieces of a kTl x kK slab: piece i is
+// row tid / (kK/8) + i * (kThr / (kK/8)), halves (tid % (kK/8)) * 8 .. +8.
+template <int kTl, int kThr, int kK>
 struct Slab {
     static constexpr int kChunks = kK / 8;              // half8 pieces per row
-    static constexpr int kRowsPerPass = kThreads / kChunks;
-    static constexpr int kPieces = kTile / kRowsPerPass;  // per thread
+    static constexpr int kRowsPerPass = kThr / kChunks;
+    static constexpr int kPieces = kTl / kRowsPerPass;  // per thread
     static constexpr int kLd = kK + 8;                  // padded LDS row (halves)
 };
+template <int kTl, int kThr, int kK>
+using SlabRegs = half8[Slab<kTl, kThr, kK>::kPieces];
 
 // A slab whose tokens all lie below ntok, with 16-byte aligned rows: one
 // unconditional 16-byte load per piece.  Rows past n are clamped to row n-1:
 // they only feed accumulator entries that are never stored.
-template <int kK>
-__device__ __forceinline__ void fetch_full(half8 (&v)[Slab<kK>::kPieces], const half_t* __restrict__ X, int64_t n,
+template <int kTl, int kThr, int kK>
+__device__ __forceinline__ void fetch_full(SlabRegs<kTl, kThr, kK>& v, const half_t* __restrict__ X, int64_t n,
                                            int64_t ldx, int r0, int64_t k0, int tid) {
-    using S = Slab<kK>;
+    using S = Slab<kTl, kThr, kK>;
     const int64_t k = k0 + (tid % S::kChunks) * 8;
 #pragma unroll
     for (int i = 0; i < S::kPieces; ++i) {
@@ -122,10 +125,10 @@ __device__ __forceinline__ void fetch_full(half8 (&v)[Slab<kK>::kPieces], const 
 
 // The last, partial slab (or any slab of an unaligned X): element loads,
 // tokens past ntok read as zero.
-template <int kK>
-__device__ __forceinline__ void fetch_tail(half8 (&v)[Slab<kK>::kPieces], const half_t* __restrict__ X, int64_t n,
+template <int kTl, int kThr, int kK>
+__device__ __forceinline__ void fetch_tail(SlabRegs<kTl, kThr, kK>& v, const half_t* __restrict__ X, int64_t n,
                                            int64_t ldx, int64_t ntok, int r0, int64_t k0, int tid) {
-    using S = Slab<kK>;
+    using S = Slab<kTl, kThr, kK>;
     const int64_t k = k0 + (tid % S::kChunks) * 8;
 #pragma unroll
     for (int i = 0; i < S::kPieces; ++i) {
@@ -135,17 +138,24 @@ __device__ __forceinline__ void fetch_tail(half8 (&v)[Slab<kK>::kPieces], const 
     }
 }
 
-template <int kK>
-__device__ __forceinline__ void stash_slab(const half8 (&v)[Slab<kK>::kPieces], half_t* S_, int tid) {
-    using S = Slab<kK>;
+template <int kTl, int kThr, int kK>
+__device__ __forceinline__ void stash_slab(const SlabRegs<kTl, kThr, kK>& v, half_t* S_, int tid) {
+    using S = Slab<kTl, kThr, kK>;
     const int kk = (tid % S::kChunks) * 8;
 #pragma unroll
     for (int i = 0; i < S::kPieces; ++i)
         *reinterpret_cast<half8*>(&S_[(tid / S::kChunks + S::kRowsPerPass * i) * S::kLd + kk]) = v[i];
 }
 
-constexpr int kKf16 = 32;    // tokens per slab (41 KB of LDS: three workgroups fit a CU)
+constexpr int kKf16 = 32;    // tokens per slab
 constexpr int kDepthf16 = 2;  // slabs in flight per thread
+// Wide layers take 256x256 tiles on 16 waves (each wave still a 64x64
+// quarter): half the X bytes per product of 128x128 tiles, four waves per
+// SIMD to hide their latency, 80 KB of LDS.  Measured per 2048-token chunk:
+// 471 against 571 us at d_in = 11008, 82 against 85 us at 4096; below 16
+// such tiles per side (d_in <= 3840) too few tiles remain to fill the chip,
+// and the 128x128 tiles of four waves (41 KB of LDS) are used.
+constexpr int kWideTile = 256, kWideThreads = 1024, kWideMinT = 16;
 
 // Slabs below nfull take the unconditional path; the rest (at most the last
 // one, or all when X is unaligned) the element path.  Diagonal tiles load
@@ -153,22 +163,23 @@ constexpr int kDepthf16 = 2;  // slabs in flight per thread
 // loop runs in two parts: a steady part in which every fetch is a full slab
 // (so the compiler can count the loads in flight and wait only for the
 // oldest set), and a generic part for the last slabs.
-template <int kK, int kDepth>
-__global__ __launch_bounds__(kThreads, 2) void hessian_f16_kernel(float* __restrict__ H, int64_t n,
+template <int kTl, int kThr, int kK, int kDepth>
+__global__ __launch_bounds__(kThr, kThr == kThreads ? 2 : 1) void hessian_f16_kernel(float* __restrict__ H, int64_t n,
                                                                  const half_t* __restrict__ X, int64_t ldx,
                                                                  int64_t ntok, int64_t nfull, int T,
                                                                  int per_xcd) {
-    using S = Slab<kK>;
-    __shared__ half_t As[2][kTile * S::kLd];
-    __shared__ half_t Bs[2][kTile * S::kLd];
+    using S = Slab<kTl, kThr, kK>;
+    constexpr int kWg = kTl / 64;  // waves per tile dimension
+    __shared__ half_t As[2][kTl * S::kLd];
+    __shared__ half_t Bs[2][kTl * S::kLd];
     const int t = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
     if (t >= T * (T + 1) / 2) return;
     int I, J;
     tile_of_super(t, T, I, J);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wi = w >> 1, wj = w & 1;
-    const bool active = !(I == J && wi < wj);  // upper quarter of a diagonal tile
-    const int rA = I * kTile, rB = J * kTile;
+    const int wi = w / kWg, wj = w % kWg;
+    const bool active = !(I == J && wi < wj);  // above the diagonal of a diagonal tile
+    const int rA = I * kTl, rB = J * kTl;
 
     float16v acc[2][2];
 #pragma unroll
@@ -177,23 +188,23 @@ __global__ __launch_bounds__(kThreads, 2) void hessian_f16_kernel(float* __restr
         for (int q = 0; q < 2; ++q) acc[m][q] = (float16v){};
 
     const int64_t nslab = (ntok + kK - 1) / kK;
-    half8 ra[kDepth][S::kPieces], rb[kDepth][S::kPieces];
+    SlabRegs<kTl, kThr, kK> ra[kDepth], rb[kDepth];
 
-    auto fetch = [&](half8(&va)[S::kPieces], half8(&vb)[S::kPieces], int64_t f) {
+    auto fetch = [&](SlabRegs<kTl, kThr, kK>& va, SlabRegs<kTl, kThr, kK>& vb, int64_t f) {
         if (f < nfull) {
-            fetch_full<kK>(va, X, n, ldx, rA, f * kK, tid);
-            fetch_full<kK>(vb, X, n, ldx, rB, f * kK, tid);
+            fetch_full<kTl, kThr, kK>(va, X, n, ldx, rA, f * kK, tid);
+            fetch_full<kTl, kThr, kK>(vb, X, n, ldx, rB, f * kK, tid);
         } else if (f < nslab) {
-            fetch_tail<kK>(va, X, n, ldx, ntok, rA, f * kK, tid);
-            fetch_tail<kK>(vb, X, n, ldx, ntok, rB, f * kK, tid);
+            fetch_tail<kTl, kThr, kK>(va, X, n, ldx, ntok, rA, f * kK, tid);
+            fetch_tail<kTl, kThr, kK>(vb, X, n, ldx, ntok, rB, f * kK, tid);
         }
     };
     // stash slab sl from its registers, then (after the barrier) the MFMAs;
     // buffer sl&1 was last read by slab sl-2, which every wave finished
     // before the previous barrier
-    auto stash = [&](const half8(&va)[S::kPieces], const half8(&vb)[S::kPieces], int64_t sl) {
-        stash_slab<kK>(va, As[sl & 1], tid);
-        stash_slab<kK>(vb, Bs[sl & 1], tid);
+    auto stash = [&](const SlabRegs<kTl, kThr, kK>& va, const SlabRegs<kTl, kThr, kK>& vb, int64_t sl) {
+        stash_slab<kTl, kThr, kK>(va, As[sl & 1], tid);
+        stash_slab<kTl, kThr, kK>(vb, Bs[sl & 1], tid);
         __syncthreads();
     };
     auto compute = [&](int64_t sl) {
@@ -228,8 +239,8 @@ __global__ __launch_bounds__(kThreads, 2) void hessian_f16_kernel(float* __restr
     if (nsteady > 0) {
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
-            fetch_full<kK>(ra[d], X, n, ldx, rA, (int64_t)d * kK, tid);
-            fetch_full<kK>(rb[d], X, n, ldx, rB, (int64_t)d * kK, tid);
+            fetch_full<kTl, kThr, kK>(ra[d], X, n, ldx, rA, (int64_t)d * kK, tid);
+            fetch_full<kTl, kThr, kK>(rb[d], X, n, ldx, rB, (int64_t)d * kK, tid);
             __builtin_amdgcn_sched_barrier(0);  // issue the sets in slab order
         }
         for (; s0 < nsteady; s0 += kDepth) {
@@ -237,8 +248,8 @@ __global__ __launch_bounds__(kThreads, 2) void hessian_f16_kernel(float* __restr
             for (int d = 0; d < kDepth; ++d) {
                 const int64_t sl = s0 + d;
                 stash(ra[d], rb[d], sl);
-                fetch_full<kK>(ra[d], X, n, ldx, rA, (sl + kDepth) * kK, tid);
-                fetch_full<kK>(rb[d], X, n, ldx, rB, (sl + kDepth) * kK, tid);
+                fetch_full<kTl, kThr, kK>(ra[d], X, n, ldx, rA, (sl + kDepth) * kK, tid);
+                fetch_full<kTl, kThr, kK>(rb[d], X, n, ldx, rB, (sl + kDepth) * kK, tid);
                 compute(sl);
             }
         }
@@ -342,9 +353,19 @@ hipError_t launch_hessian(float* H, int64_t n, const void* X, int x_is_f16, int6
         // full slabs take 16-byte loads when every row start is 16-byte aligned
         const bool vec = (addr % 16 == 0) && (ldx % 8 == 0);
         const int64_t nfull = vec ? ntok / kKf16 : 0;
-        const int per_xcd = (int)((tiles + kXcds - 1) / kXcds);
-        hipLaunchKernelGGL((hessian_f16_kernel<kKf16, kDepthf16>), dim3((unsigned)(per_xcd * kXcds)), dim3(kThreads),
-                           0, s, H, n, static_cast<const half_t*>(X), ldx, ntok, nfull, (int)T, per_xcd);
+        const int64_t Tw = (n + kWideTile - 1) / kWideTile;
+        if (Tw >= kWideMinT) {
+            const int64_t tw = Tw * (Tw + 1) / 2;
+            const int per_xcd = (int)((tw + kXcds - 1) / kXcds);
+            hipLaunchKernelGGL((hessian_f16_kernel<kWideTile, kWideThreads, kKf16, kDepthf16>),
+                               dim3((unsigned)(per_xcd * kXcds)), dim3(kWideThreads), 0, s, H, n,
+                               static_cast<const half_t*>(X), ldx, ntok, nfull, (int)Tw, per_xcd);
+        } else {
+            const int per_xcd = (int)((tiles + kXcds - 1) / kXcds);
+            hipLaunchKernelGGL((hessian_f16_kernel<kTile, kThreads, kKf16, kDepthf16>),
+                               dim3((unsigned)(per_xcd * kXcds)), dim3(kThreads), 0, s, H, n,
+                               static_cast<const half_t*>(X), ldx, ntok, nfull, (int)T, per_xcd);
+        }
     } else {
         TimedLaunch t(K_HESS_F32, s);
         const bool vec = (addr % 16 == 0) && (ldx % 4 == 0);
