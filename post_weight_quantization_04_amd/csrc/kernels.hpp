@@ -15,7 +15,6 @@ enum KernelId {
     K_HINV_LOAD,
     K_CHOL_STEP,
     K_HINV_STORE,
-    K_Q_ROWGRID,
     K_Q_CONVERT,
     K_Q_RDIAG,
     K_Q_GROUPGRID,

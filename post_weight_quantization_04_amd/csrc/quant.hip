@@ -56,39 +56,6 @@ __device__ __forceinline__ float to_f32(T v) {
     return (float)v;
 }
 
-// ---------------------------------------------------------------------------
-// Per-row grid from the input W (group_size == 0): one wave per row,
-// min/max by butterfly shuffles.
-// ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void row_grid_kernel(const T* __restrict__ W, int64_t d_out, int64_t d_in,
-                                                       float maxq, float* __restrict__ scales,
-                                                       int32_t* __restrict__ zeros, float* __restrict__ minmax) {
-    const int64_t R = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (R >= d_out) return;
-    float lo = INFINITY, hi = -INFINITY;
-    const T* row = W + R * d_in;
-    for (int64_t c = lane; c < d_in; c += 64) {
-        float x = to_f32(row[c]);
-        lo = fminf(lo, x);
-        hi = fmaxf(hi, x);
-    }
-    lo = wave_min(lo);
-    hi = wave_max(hi);
-    if (lane == 0) {
-        lo = fminf(lo, 0.0f);
-        hi = fmaxf(hi, 0.0f);
-        Grid g = make_grid(lo, hi, maxq);
-        scales[R] = g.s;
-        zeros[R] = (int32_t)g.z;
-        if (minmax) {
-            minmax[2 * R] = lo;
-            minmax[2 * R + 1] = hi;
-        }
-    }
-}
-
 // Group grid from the current working weights W[:, c0 : c0+g) (g > block).
 __global__ __launch_bounds__(256) void group_grid_kernel(const float* __restrict__ Wk, int64_t d_out, int64_t d_in,
                                                          int64_t c0, int64_t g, int64_t gi, int64_t ng, float maxq,
@@ -119,15 +86,88 @@ __global__ __launch_bounds__(256) void group_grid_kernel(const float* __restrict
     }
 }
 
-// Working copy in fp32 (exact for f16 inputs, subnormals included); dead
-// columns are zeroed.
-template <typename T>
-__global__ __launch_bounds__(256) void convert_kernel(const T* __restrict__ W, float* __restrict__ Wk, int64_t total,
-                                                      int64_t d_in, const uint8_t* __restrict__ dead) {
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
-        float x = to_f32(W[e]);
-        if (dead && dead[e % d_in]) x = 0.0f;
-        Wk[e] = x;
+// One pass over the input W, one wave per row: the fp32 working copy with
+// dead columns zeroed (exact for f16 inputs, subnormals included) and, with
+// kGrid, the row's grid from the input values (min/max by butterfly
+// shuffles).  kVec: rows of 16-byte aligned 8-element pieces (d_in % 8 == 0),
+// taken in batches of kBatch pieces per lane whose loads (and dead flags,
+// 8 at a time, with kDead) are all issued before any is used: pieces past
+// the row end load the lane's first piece again (harmless to the min/max)
+// and are not stored.
+template <typename T, bool kVec, bool kGrid, bool kDead>
+__global__ __launch_bounds__(256) void grid_convert_kernel(const T* __restrict__ W, float* __restrict__ Wk,
+                                                           int64_t d_out, int64_t d_in,
+                                                           const uint8_t* __restrict__ dead, float maxq,
+                                                           float* __restrict__ scales, int32_t* __restrict__ zeros,
+                                                           float* __restrict__ minmax) {
+    constexpr int kBatch = 8;
+    const int64_t R = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (R >= d_out) return;
+    const T* row = W + R * d_in;
+    float* out = Wk + R * d_in;
+    float lo = INFINITY, hi = -INFINITY;
+    if (kVec) {
+        for (int64_t base = 8 * lane; base < d_in; base += 8 * kWave * kBatch) {
+            float x[kBatch][8];
+            uint2 dd[kBatch];
+            int64_t cs[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                const int64_t c = base + (int64_t)8 * kWave * i;
+                cs[i] = c < d_in ? c : base;
+                if constexpr (sizeof(T) == 2) {
+                    const half8 h = *reinterpret_cast<const half8*>(row + cs[i]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[i][e] = (float)h[e];
+                } else {
+                    const float4v a = *reinterpret_cast<const float4v*>(row + cs[i]);
+                    const float4v b = *reinterpret_cast<const float4v*>(row + cs[i] + 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[i][e] = a[e];
+                        x[i][e + 4] = b[e];
+                    }
+                }
+                if (kDead) dd[i] = *reinterpret_cast<const uint2*>(dead + cs[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    lo = fminf(lo, x[i][e]);
+                    hi = fmaxf(hi, x[i][e]);
+                    if (kDead && ((((e < 4) ? dd[i].x : dd[i].y) >> (8 * (e & 3))) & 0xffu)) x[i][e] = 0.0f;
+                }
+                if (base + (int64_t)8 * kWave * i < d_in) {
+                    *reinterpret_cast<float4v*>(out + cs[i]) = (float4v){x[i][0], x[i][1], x[i][2], x[i][3]};
+                    *reinterpret_cast<float4v*>(out + cs[i] + 4) = (float4v){x[i][4], x[i][5], x[i][6], x[i][7]};
+                }
+            }
+        }
+    } else {
+        for (int64_t c = lane; c < d_in; c += kWave) {
+            float x = to_f32(row[c]);
+            lo = fminf(lo, x);
+            hi = fmaxf(hi, x);
+            if (kDead && dead[c]) x = 0.0f;
+            out[c] = x;
+        }
+    }
+    if (kGrid) {
+        lo = wave_min(lo);
+        hi = wave_max(hi);
+        if (lane == 0) {
+            lo = fminf(lo, 0.0f);
+            hi = fmaxf(hi, 0.0f);
+            Grid g = make_grid(lo, hi, maxq);
+            scales[R] = g.s;
+            zeros[R] = (int32_t)g.z;
+            if (minmax) {
+                minmax[2 * R] = lo;
+                minmax[2 * R + 1] = hi;
+            }
+        }
     }
 }
 
@@ -939,25 +979,39 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
     const int64_t ng = group ? d_in / group : 1;
     const float maxq = (float)((1 << bits) - 1);
     const unsigned rows4 = (unsigned)((d_out + 3) / 4);
-    if (group == 0) {
-        TimedLaunch t(K_Q_ROWGRID, s);
-        if (w_is_f16)
-            hipLaunchKernelGGL(row_grid_kernel<half_t>, dim3(rows4), dim3(256), 0, s, static_cast<const half_t*>(W),
-                               d_out, d_in, maxq, scales, zeros, minmax);
-        else
-            hipLaunchKernelGGL(row_grid_kernel<float>, dim3(rows4), dim3(256), 0, s, static_cast<const float*>(W),
-                               d_out, d_in, maxq, scales, zeros, minmax);
-    }
     {
+        // the working copy, and for per-row grids the grid, in one pass over W
         TimedLaunch t(K_Q_CONVERT, s);
-        const int64_t total = d_out * d_in;
-        const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 65536);
-        if (w_is_f16)
-            hipLaunchKernelGGL(convert_kernel<half_t>, dim3(blocks), dim3(256), 0, s, static_cast<const half_t*>(W),
-                               w.Wk, total, d_in, dead);
-        else
-            hipLaunchKernelGGL(convert_kernel<float>, dim3(blocks), dim3(256), 0, s, static_cast<const float*>(W),
-                               w.Wk, total, d_in, dead);
+        const uintptr_t wa = reinterpret_cast<uintptr_t>(W), da = reinterpret_cast<uintptr_t>(dead);
+        const bool vec = (d_in % 8 == 0) && (wa % 16 == 0) && (da % 8 == 0);
+        const dim3 grid(rows4), blk(256);
+#define GC_LAUNCH(T, V, G)                                                                                    \
+    do {                                                                                                      \
+        if (dead)                                                                                             \
+            hipLaunchKernelGGL((grid_convert_kernel<T, V, G, true>), grid, blk, 0, s, static_cast<const T*>(W), \
+                               w.Wk, d_out, d_in, dead, maxq, scales, zeros, minmax);                           \
+        else                                                                                                  \
+            hipLaunchKernelGGL((grid_convert_kernel<T, V, G, false>), grid, blk, 0, s, static_cast<const T*>(W), \
+                               w.Wk, d_out, d_in, dead, maxq, scales, zeros, minmax);                           \
+    } while (0)
+        if (w_is_f16) {
+            if (group == 0) {
+                if (vec) GC_LAUNCH(half_t, true, true);
+                else GC_LAUNCH(half_t, false, true);
+            } else {
+                if (vec) GC_LAUNCH(half_t, true, false);
+                else GC_LAUNCH(half_t, false, false);
+            }
+        } else {
+            if (group == 0) {
+                if (vec) GC_LAUNCH(float, true, true);
+                else GC_LAUNCH(float, false, true);
+            } else {
+                if (vec) GC_LAUNCH(float, true, false);
+                else GC_LAUNCH(float, false, false);
+            }
+        }
+#undef GC_LAUNCH
     }
     {
         TimedLaunch t(K_Q_RDIAG, s);
