@@ -16,7 +16,6 @@ enum KernelId {
     K_CHOL_STEP,
     K_HINV_STORE,
     K_Q_CONVERT,
-    K_Q_RDIAG,
     K_Q_GROUPGRID,
     K_Q_STEP,
     K_Q_TRAIL,

@@ -93,17 +93,22 @@ __global__ __launch_bounds__(256) void group_grid_kernel(const float* __restrict
 // taken in batches of kBatch pieces per lane whose loads (and dead flags,
 // 8 at a time, with kDead) are all issued before any is used: pieces past
 // the row end load the lane's first piece again (harmless to the min/max)
-// and are not stored.
+// and are not stored.  The same launch writes 1/U_jj (grid-stride over
+// all threads) and clears the per-row error sums.
 template <typename T, bool kVec, bool kGrid, bool kDead>
 __global__ __launch_bounds__(256) void grid_convert_kernel(const T* __restrict__ W, float* __restrict__ Wk,
                                                            int64_t d_out, int64_t d_in,
                                                            const uint8_t* __restrict__ dead, float maxq,
                                                            float* __restrict__ scales, int32_t* __restrict__ zeros,
-                                                           float* __restrict__ minmax) {
+                                                           float* __restrict__ minmax, const float* __restrict__ U,
+                                                           float* __restrict__ rdiag, float* __restrict__ err_row) {
     constexpr int kBatch = 8;
+    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < d_in; j += (int64_t)gridDim.x * blockDim.x)
+        rdiag[j] = 1.0f / U[j * d_in + j];
     const int64_t R = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (R >= d_out) return;
+    if (err_row && lane == 0) err_row[R] = 0.0f;
     const T* row = W + R * d_in;
     float* out = Wk + R * d_in;
     float lo = INFINITY, hi = -INFINITY;
@@ -171,15 +176,6 @@ __global__ __launch_bounds__(256) void grid_convert_kernel(const T* __restrict__
     }
 }
 
-__global__ __launch_bounds__(256) void rdiag_kernel(const float* __restrict__ U, int64_t n, float* __restrict__ rdiag) {
-    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (j < n) rdiag[j] = 1.0f / U[j * n + j];
-}
-
-__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
-    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (j < n) p[j] = 0.0f;
-}
 
 // ---------------------------------------------------------------------------
 // In-block sweep.  Dynamic LDS: Up, the upper block triangle of the U block
@@ -981,6 +977,7 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
     const unsigned rows4 = (unsigned)((d_out + 3) / 4);
     {
         // the working copy, and for per-row grids the grid, in one pass over W
+        // (with 1/U_jj and the cleared error sums)
         TimedLaunch t(K_Q_CONVERT, s);
         const uintptr_t wa = reinterpret_cast<uintptr_t>(W), da = reinterpret_cast<uintptr_t>(dead);
         const bool vec = (d_in % 8 == 0) && (wa % 16 == 0) && (da % 8 == 0);
@@ -989,10 +986,10 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
     do {                                                                                                      \
         if (dead)                                                                                             \
             hipLaunchKernelGGL((grid_convert_kernel<T, V, G, true>), grid, blk, 0, s, static_cast<const T*>(W), \
-                               w.Wk, d_out, d_in, dead, maxq, scales, zeros, minmax);                           \
+                               w.Wk, d_out, d_in, dead, maxq, scales, zeros, minmax, U, w.rdiag, err_row);      \
         else                                                                                                  \
             hipLaunchKernelGGL((grid_convert_kernel<T, V, G, false>), grid, blk, 0, s, static_cast<const T*>(W), \
-                               w.Wk, d_out, d_in, dead, maxq, scales, zeros, minmax);                           \
+                               w.Wk, d_out, d_in, dead, maxq, scales, zeros, minmax, U, w.rdiag, err_row);      \
     } while (0)
         if (w_is_f16) {
             if (group == 0) {
@@ -1013,12 +1010,6 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
         }
 #undef GC_LAUNCH
     }
-    {
-        TimedLaunch t(K_Q_RDIAG, s);
-        hipLaunchKernelGGL(rdiag_kernel, dim3((unsigned)((d_in + 255) / 256)), dim3(256), 0, s, U, d_in, w.rdiag);
-    }
-    if (err_row)
-        hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((d_out + 255) / 256)), dim3(256), 0, s, err_row, d_out);
     const bool vec = (reinterpret_cast<uintptr_t>(U) % 16 == 0) && (d_in % 4 == 0) && (block % 4 == 0);  // E rows are 16-byte aligned when block % 4 == 0
     const int bmax = (int)std::min(block, d_in);
     const size_t near_bytes = (size_t)((bmax + 3) & ~3) * kEtl * 4;
