@@ -81,10 +81,24 @@ __global__ __launch_bounds__(1024) void diag_stats_kernel(const float* __restric
                                                           int* __restrict__ fail) {
     __shared__ double part[16];
     double s = 0.0;
-    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
-        float h = H[i * n + i];
-        s += (double)h;
-        if (dead) dead[i] = (h == 0.0f) ? 1 : 0;
+    // every diagonal entry sits on its own cache line: a thread's loads are
+    // issued eight at a time before any is used (the sum keeps its order)
+    constexpr int kB = 8;
+    for (int64_t i0 = threadIdx.x; i0 < n; i0 += (int64_t)kB * blockDim.x) {
+        float h[kB];
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+            const int64_t i = i0 + (int64_t)b * blockDim.x;
+            h[b] = (i < n) ? H[i * n + i] : 0.0f;
+        }
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+            const int64_t i = i0 + (int64_t)b * blockDim.x;
+            if (i < n) {
+                s += (double)h[b];
+                if (dead) dead[i] = (h[b] == 0.0f) ? 1 : 0;
+            }
+        }
     }
     s = wave_sum(s);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
@@ -113,13 +127,23 @@ __global__ __launch_bounds__(256) void load_reversed_kernel(const float* __restr
     tri_index(blockIdx.x, TI, TJ);
     const double lam = scal[0];
     const int tid = threadIdx.x;
-    // stage: T[jj][ii] = H[n-1-(64TJ+jj)][n-1-(64TI+ii)], reading H rows contiguously
-    for (int e = tid; e < 64 * 64; e += 256) {
-        int jj = e >> 6, ii = e & 63;
-        int64_t i = TI * 64 + ii, j = TJ * 64 + jj;
-        float v = 0.0f;
-        if (i < n && j < n && i >= j) v = H[(n - 1 - j) * n + (n - 1 - i)];
-        T[jj][ii] = v;
+    // stage: T[jj][ii] = H[n-1-(64TJ+jj)][n-1-(64TI+ii)], reading H rows
+    // contiguously; a thread's 16 loads are issued before any is used
+    // (entries outside the triangle load H[0] and are replaced by zero)
+    float v[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const int e = tid + 256 * m;
+        const int jj = e >> 6, ii = e & 63;
+        const int64_t i = TI * 64 + ii, j = TJ * 64 + jj;
+        const bool ok = i < n && j < n && i >= j;
+        v[m] = H[ok ? (n - 1 - j) * n + (n - 1 - i) : 0];
+        if (!ok) v[m] = 0.0f;
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const int e = tid + 256 * m;
+        T[e >> 6][e & 63] = v[m];
     }
     __syncthreads();
     for (int e = tid; e < 64 * 64; e += 256) {
@@ -1096,9 +1120,23 @@ __global__ __launch_bounds__(256) void store_u_kernel(const double* __restrict__
     const int64_t r = n - 1 - i;
     const double* grow = G + gt(np, r / NB, 0) + (r % NB) * NB;  // row r of tile column 0
     float* urow = U + i * n;
-    for (int64_t j = threadIdx.x; j < n; j += blockDim.x) {
-        const int64_t c = n - 1 - j;
-        urow[j] = (j >= i) ? (float)grow[(c / NB) * NB * NB + (c % NB)] : 0.0f;
+    // eight loads per thread in flight before any store (entries below the
+    // diagonal load grow[0] and are written as zero)
+    constexpr int kB = 8;
+    for (int64_t j0 = threadIdx.x; j0 < n; j0 += (int64_t)kB * blockDim.x) {
+        double g[kB];
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+            const int64_t j = j0 + (int64_t)b * blockDim.x;
+            const int64_t c = n - 1 - j;
+            const bool ok = j < n && j >= i;
+            g[b] = grow[ok ? (c / NB) * NB * NB + (c % NB) : 0];
+        }
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+            const int64_t j = j0 + (int64_t)b * blockDim.x;
+            if (j < n) urow[j] = (j >= i) ? (float)g[b] : 0.0f;
+        }
     }
 }
 
