@@ -3,10 +3,10 @@
 //
 // One workgroup per lower-triangle tile (I >= J) of H, 128x128 on four waves
 // or, for wide layers, 256x256 on sixteen; each wave owns a 64x64 quarter as
-// 2x2 MFMA 32x32 accumulators.  Token slabs
-// of X rows I and J are staged through LDS; products run on MFMA with fp32
-// accumulation (f16 inputs: 32x32x16 f16, exact products; f32 inputs:
-// 32x32x2 f32).  Each call adds its token range into H once at the end.
+// 2x2 MFMA 32x32 accumulators.  Token slabs of X rows I and J are staged
+// through LDS; products run on MFMA with fp32 accumulation (f16 inputs:
+// 32x32x16 f16, exact products; f32 inputs: 32x32x2 f32).  Each call adds
+// its token range into H once at the end.
 // The MFMA instruction sequence over the tokens is the same for every slab
 // size, so the sums are the same bits whatever the slab and prefetch depth.
 #include "common.hpp"
@@ -48,13 +48,13 @@ __device__ __forceinline__ void store_quarter(float* __restrict__ H, int64_t n, 
 // ---------------------------------------------------------------------------
 // float16 inputs
 //
-// The products of one 128x128 tile over a 2048-token chunk take ~14 us of
-// MFMA time per CU pair, while a load from the memory-side cache takes a
-// large fraction of a microsecond under this load; with only the next slab in
-// flight the loop waits on every slab.  Here each thread keeps kDepth slabs
-// of kK tokens in flight in registers (static register sets, the slab loop
-// unrolled by kDepth), while the MFMAs consume the current slab from one of
-// two LDS buffers.  Tiles are dealt out so that each XCD (workgroups are
+// Each thread keeps kDepth slabs of kK tokens in flight in registers
+// (static register sets, the slab loop unrolled by kDepth) while the MFMAs
+// consume the current slab from one of two LDS buffers.  The loads of a full
+// slab are unconditional and every tile issues the same ones, so that before
+// each LDS stash the compiler waits only for the oldest set in flight (with
+// per-piece bounds branches it drained every load and the prefetch bought
+// nothing).  Tiles are dealt out so that each XCD (workgroups are
 // dispatched round-robin over the 8 XCDs) takes a contiguous run of a
 // super-tile order of the lower triangle, keeping the X panels it reads
 // few and resident in its own L2.
