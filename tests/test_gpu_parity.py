@@ -150,6 +150,23 @@ def test_quantize(lib, d_out, d_in, bits, group, block, dead):
     parity.check_codes(W.astype(np.float64), U32, dmask, q, bits, group, block)
 
 
+@pytest.mark.parametrize("d_out,d_in,bits,group,block,dead", [
+    (70, 300, 4, 0, 128, (3, 150)),   # f16 rows not a multiple of 8: element path of the working copy
+    (64, 200, 4, 0, 64, (7,)),        # f16, 16-byte pieces with dead flags
+])
+def test_quantize_fp16_weights(lib, d_out, d_in, bits, group, block, dead):
+    from post_weight_quantization_04_amd import layer
+    say("quantize f16", d_out, d_in, bits, group, block, dead)
+    W, X = _problem(d_out, d_in, 3 * d_in, seed=d_out * 37 + d_in, dead=dead, wdtype=np.float16)
+    U_ref, dmask, _ = oracle.prepare(oracle.hessian([X]))
+    U32 = U_ref.astype(F32)
+    fac = layer.Factor(dev(U32), dev(dmask.astype(np.uint8)), None, None)
+    qz = layer.quantize(dev(W), fac, bits, group, block)
+    _torch().cuda.synchronize()
+    q = _quant_dict(qz)
+    parity.check_codes(W.astype(np.float64), U32, dmask, q, bits, group, block)
+
+
 def test_quantize_fp16_weights_exact_conversion(lib):
     """All finite f16 values (subnormals included) survive the working copy:
     with U = I every column rounds independently, so the per-row grid and the
