@@ -7,7 +7,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 Pinned functions (see ``tests/test_oracle_pins.py``): ``hessian``, ``damp``,
 ``hinv_cholesky_upper``, ``grid``, ``quantize_values``, ``quantize``,
 ``dequantize``, ``output_error``, ``pack_codes``, ``unpack_codes``,
-``output_error_from_errors``, ``obq_quantize``.  No function here is
+``output_error_from_errors``, ``obq_quantize``, ``propagate``.  No function here is
 "parity unpinned".
 """
 from .gptq import (  # noqa: F401
@@ -22,6 +22,7 @@ from .gptq import (  # noqa: F401
     layer,
     obq_quantize,
     output_error,
+    propagate,
     output_error_from_errors,
     pack_codes,
     prepare,

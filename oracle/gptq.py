@@ -513,6 +513,26 @@ def obq_quantize(W: np.ndarray, Hinv: np.ndarray, bits: int, dead: Optional[np.n
     return ObqResult(codes, s.astype(F32), z.astype(np.int32), order, w_hat, loss, ties, hard)
 
 
+def propagate(W_hat: np.ndarray, X: np.ndarray, activation: str = "none") -> np.ndarray:
+    """The next layer's input from a quantized layer: ``Y = act(What X)`` in
+    fp64, ``What: [d_out, d_in]``, ``X: [d_in, N]``.
+
+    The pages quantize a network one linear layer at a time, each layer
+    against its own input activations (math4ai "GPTQ Hessian", opening
+    paragraph; aicassindra "Post-training quantization and the per-layer
+    objective", X the layer's calibration inputs).  Reading for a chain of
+    layers: the next layer's X is the already-quantized layer's output.  The
+    pages name no nonlinearity; ``activation`` is "none" or "relu"
+    (``max(0, .)``), the plainest stand-in.
+    """
+    Y = np.asarray(W_hat, dtype=np.float64) @ np.asarray(X, dtype=np.float64)
+    if activation == "relu":
+        Y = np.maximum(Y, 0.0)
+    elif activation != "none":
+        raise ValueError(f"activation {activation!r}")
+    return Y
+
+
 def layer(W: np.ndarray, x_chunks: Iterable[np.ndarray], bits: int, group_size: int, block_size: int,
           damp_frac: float = 0.01):
     """The whole path on one layer: returns ``(H, U, dead, lam, QuantResult)``."""

@@ -575,3 +575,39 @@ def test_obq_replay_counts():
     bad[0, [0, -1]] = bad[0, [-1, 0]]  # the last pick first: not a near-tie
     rep = oracle.obq_quantize(W, Hinv, 4, order_hint=bad)
     assert rep.hard >= 1 and list(rep.order[0]) == list(bad[0][:1]) + list(rep.order[0][1:])
+
+
+# ---------------------------------------------------------------------------
+# Propagation to the next layer (Y = act(What X))
+# ---------------------------------------------------------------------------
+def test_propagate_permutation_selects_rows():
+    """A permutation matrix as What picks rows of X exactly (a transposed
+    operand would pick by the inverse permutation)."""
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((7, 11))
+    perm = np.array([3, 0, 6, 1, 5, 2, 4])
+    P = np.zeros((7, 7))
+    P[np.arange(7), perm] = 1.0
+    Y = oracle.propagate(P, X)
+    np.testing.assert_array_equal(Y, X[perm])
+    inv = np.argsort(perm)
+    assert not np.array_equal(Y, X[inv])
+
+
+def test_propagate_relu_signs_and_scaling():
+    X = np.array([[1.0, -2.0, 3.0], [0.5, 0.5, -4.0]])
+    W = np.array([[1.0, 0.0], [0.0, -1.0], [2.0, 1.0]])
+    Y = oracle.propagate(W, X, "relu")
+    np.testing.assert_array_equal(Y, [[1.0, 0.0, 3.0], [0.0, 0.0, 4.0], [2.5, 0.0, 2.0]])
+    np.testing.assert_array_equal(oracle.propagate(3.0 * W, X, "relu"), 3.0 * Y)  # positive homogeneity
+    with pytest.raises(ValueError):
+        oracle.propagate(W, X, "tanh")
+
+
+def test_propagate_chain_with_identity_layers():
+    """Two identity layers hand X through unchanged; a layer of ones sums
+    the channels token by token."""
+    rng = np.random.default_rng(6)
+    X = rng.standard_normal((5, 9))
+    np.testing.assert_array_equal(oracle.propagate(np.eye(5), oracle.propagate(np.eye(5), X)), X)
+    np.testing.assert_allclose(oracle.propagate(np.ones((1, 5)), X)[0], X.sum(axis=0), rtol=1e-15)
