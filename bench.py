@@ -371,14 +371,21 @@ def main(argv=None) -> int:
         wh = torch.empty((d_out, d_in), dtype=torch.float16, device=dev)
         oe = torch.empty((d_out,), dtype=torch.float32, device=dev)
         sz = d_out * ng * 8
-        return {
+        jobs = {
             "pack_codes": (lambda: _lib.pack_codes(qout.codes, bits, packed), d_out * d_in + d_out * nw * 4),
             "dequantize_f16": (lambda: _lib.dequantize(packed, bits, d_in, qout.scales, qout.zeros, g, wh),
                                d_out * nw * 4 + sz + d_out * d_in * 2),
             "output_error": (lambda: _lib.output_error(Wd, fac.dead, packed, bits, qout.scales, qout.zeros, g,
                                                        qout.err_row, fac.lam, oe),
                              d_out * d_in * Wd.element_size() + d_out * nw * 4 + sz + d_out * 8 + d_in),
-        }, oe
+        }
+        if Xd.dtype == torch.float16:
+            # the next layer's input from this quantized layer, Y = relu(What X)
+            y = torch.empty((d_out, Xd.shape[1]), dtype=torch.float16, device=dev)
+            w_hat = layer.dequantize(packed, bits, d_in, qout.scales, qout.zeros, g, dtype=torch.float16)
+            jobs["propagate_relu"] = (lambda: _lib.propagate(w_hat, Xd, y, 1),
+                                      d_out * d_in * 2 + d_in * Xd.shape[1] * 2 + d_out * Xd.shape[1] * 2)
+        return jobs, oe
 
     if args.counter_pass:
         for _ in range(2):
@@ -513,6 +520,13 @@ def main(argv=None) -> int:
             cls = {"dequantize_f16": "dequantize"}.get(name, name)
             after[name] = {"ms": round(ms, 4), "bytes": int(nbytes), "GB/s": round(gbs, 1),
                            "frac_hbm": round(gbs / PEAK_HBM_GBS, 3), "traffic": recorded_traffic(cls)}
+            if name == "propagate_relu":
+                # a dense f16 contraction: reported against the f16 MFMA peak
+                fl = 2.0 * d_out * d_in * Xd.shape[1]
+                tf = fl / (ms * 1e-3) / 1e12
+                after[name] = {"ms": round(ms, 4), "flops": fl, "achieved": round(tf, 1), "peak": PEAK_TFLOPS["f16"],
+                               "unit": "TFLOP/s", "frac": round(tf / PEAK_TFLOPS["f16"], 4),
+                               "shape": f"Y[{d_out}x{Xd.shape[1]}] = relu(What[{d_out}x{d_in}] X)"}
         after["output_error_sum"] = float(oe.sum().item())
 
     greedy = None

@@ -11,7 +11,8 @@
  *                                                 (gptq_quantize_layer)
  * and, after the path, few-bit storage of the codes, dequantization and the
  * per-row output error (gptq_pack_codes, gptq_dequantize,
- * gptq_output_error).
+ * gptq_output_error), and the propagation of a quantized layer's output to
+ * the next layer of a chain (gptq_propagate).
  *
  * Conventions shared by every entry point
  *   - Tensor arguments are DEVICE pointers allocated and owned by the caller;
@@ -225,6 +226,29 @@ int gptq_dequantize(const uint32_t* packed, int bits, int64_t d_out, int64_t d_i
 int gptq_output_error(const void* W, int w_dtype, const uint8_t* dead, const uint32_t* packed, int bits,
                       const float* scales, const int32_t* zeros, int64_t group_size, int64_t d_out, int64_t d_in,
                       const float* err_row, const double* lambda, float* out_row, void* stream);
+
+/*
+ * Propagation to the next layer: Y = act(What X).  The pages quantize a
+ * network one linear layer at a time, each layer against its own input
+ * activations (math4ai "GPTQ Hessian", opening paragraph; aicassindra
+ * "Post-training quantization and the per-layer objective"); in a chain the
+ * next layer's X is the already-quantized layer's output.  The f16
+ * products are exact and summed in float32; each output is rounded once to
+ * f16 after the activation.
+ *   W_hat     [d_out, d_in] f16, row-major (row stride d_in): the
+ *             dequantized layer (gptq_dequantize with GPTQ_F16 output).
+ *   X         [d_in, n_tokens] f16 with row stride ldx (elements).
+ *   Y         [d_out, n_tokens] f16 output with row stride ldy (elements);
+ *             it must not overlap W_hat or X.
+ *   activation 0: none; 1: max(0, .) (the pages name no nonlinearity).
+ * d_in = 0 gives Y = act(0).  All pointers are device pointers owned by the
+ * caller; the call is asynchronous on `stream`.
+ * Errors: GPTQ_EINVAL (negative sizes, ldx or ldy below n_tokens, unknown
+ * dtype or activation, null pointer), GPTQ_EUNSUPPORTED (a dtype other than
+ * GPTQ_F16, d_out above 2^24 or n_tokens above 2^31).
+ */
+int gptq_propagate(const void* W_hat, int w_dtype, int64_t d_out, int64_t d_in, const void* X, int x_dtype,
+                   int64_t n_tokens, int64_t ldx, void* Y, int64_t ldy, int activation, void* stream);
 
 /*
  * Greedy-order quantization of small layers (OBQ), the variant the fixed

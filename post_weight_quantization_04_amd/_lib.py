@@ -28,6 +28,7 @@ EXPORTS = (
     "gptq_pack_codes",
     "gptq_dequantize",
     "gptq_output_error",
+    "gptq_propagate",
     "gptq_obq_workspace",
     "gptq_obq_quantize",
     "gptq_kernel_count",
@@ -69,6 +70,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "gptq_pack_codes": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp]),
         "gptq_dequantize": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i64, _vp, _i32, _vp]),
         "gptq_output_error": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
+        "gptq_propagate": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _i64, _i32, _vp]),
         "gptq_obq_workspace": (_sz, [_i64]),
         "gptq_obq_quantize": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _sz, _vp]),
@@ -193,6 +195,22 @@ def output_error(W, dead, packed, bits: int, scales, zeros, group_size: int, err
                                   _ptr(zeros), int(group_size), d_out, d_in, _ptr(err_row), _ptr(lam),
                                   _ptr(out_row), _stream(stream))
     _check("gptq_output_error", rc)
+
+
+def propagate(W_hat, X, Y, activation: int = 0, stream=None) -> None:
+    """``Y = act(W_hat X)``: ``W_hat [d_out, d_in]`` f16 contiguous, ``X
+    [d_in, n]`` and ``Y [d_out, n]`` f16 2-D views with unit column stride
+    (row strides ``X.stride(0)``, ``Y.stride(0)``); activation 0 none, 1 ReLU."""
+    for t in (X, Y):
+        if t.dim() != 2 or t.stride(1) != 1 or not t.is_cuda:
+            raise ValueError("X and Y must be 2-D device views with unit column stride")
+    d_out, d_in = W_hat.shape
+    n = X.shape[1]
+    if X.shape[0] != d_in or Y.shape != (d_out, n):
+        raise ValueError("shapes")
+    rc = load().gptq_propagate(_ptr(W_hat), _dtype_code(W_hat), d_out, d_in, X.data_ptr(), _dtype_code(X), n,
+                               X.stride(0), Y.data_ptr(), Y.stride(0), int(activation), _stream(stream))
+    _check("gptq_propagate", rc)
 
 
 def obq_workspace(d_in: int) -> int:

@@ -18,7 +18,7 @@ namespace {
 const char* const kNames[K_COUNT] = {
     "hessian_f16", "hessian_f32", "hinv_diag_stats", "hinv_load_reversed", "chol_step", "hinv_store_u",
     "q_grid_convert",         "q_group_grid",       "q_step",    "q_trail",
-    "pack_codes",  "dequantize",  "output_error", "obq_hinv", "obq_rows",
+    "pack_codes",  "dequantize",  "output_error", "obq_hinv", "obq_rows", "propagate",
 };
 int g_timed = -1;
 struct EventPair {
@@ -220,6 +220,20 @@ int gptq_output_error(const void* W, int w_dtype, const uint8_t* dead, const uin
     if (d_in > ((int64_t)1 << 24) || d_out > ((int64_t)1 << 24)) return GPTQ_EUNSUPPORTED;
     return hip_status(launch_output_error(W, w_dtype == GPTQ_F16, dead, packed, bits, scales, zeros, group_size,
                                           d_out, d_in, err_row, lambda, out_row, as_stream(stream)));
+}
+
+int gptq_propagate(const void* W_hat, int w_dtype, int64_t d_out, int64_t d_in, const void* X, int x_dtype,
+                   int64_t n_tokens, int64_t ldx, void* Y, int64_t ldy, int activation, void* stream) {
+    if (d_out < 0 || d_in < 0 || n_tokens < 0) return GPTQ_EINVAL;
+    if (activation != 0 && activation != 1) return GPTQ_EINVAL;
+    if ((w_dtype != GPTQ_F16 && w_dtype != GPTQ_F32) || (x_dtype != GPTQ_F16 && x_dtype != GPTQ_F32))
+        return GPTQ_EINVAL;
+    if (d_out == 0 || n_tokens == 0) return GPTQ_OK;
+    if (ldx < n_tokens || ldy < n_tokens) return GPTQ_EINVAL;
+    if (!Y || (d_in > 0 && (!W_hat || !X))) return GPTQ_EINVAL;
+    if (w_dtype != GPTQ_F16 || x_dtype != GPTQ_F16) return GPTQ_EUNSUPPORTED;
+    if (d_out > ((int64_t)1 << 24) || n_tokens > ((int64_t)1 << 31)) return GPTQ_EUNSUPPORTED;
+    return hip_status(launch_propagate(W_hat, d_out, d_in, X, n_tokens, ldx, Y, ldy, activation, as_stream(stream)));
 }
 
 }  // extern "C"

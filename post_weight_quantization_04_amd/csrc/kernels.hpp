@@ -24,6 +24,7 @@ enum KernelId {
     K_OUTERR,
     K_OBQ_HINV,
     K_OBQ_ROWS,
+    K_PROPAGATE,
     K_COUNT
 };
 
@@ -69,5 +70,9 @@ size_t obq_workspace_bytes(int64_t d_in);
 hipError_t launch_obq(const void* W, int w_is_f16, int64_t d_out, int64_t d_in, const float* U, const uint8_t* dead,
                       int bits, uint8_t* codes, float* scales, int32_t* zeros, int32_t* order, double* loss,
                       void* ws, hipStream_t s);
+
+// ---- propagation to the next layer ------------------------------------------
+hipError_t launch_propagate(const void* W, int64_t d_out, int64_t d_in, const void* X, int64_t ntok, int64_t ldx,
+                            void* Y, int64_t ldy, int relu, hipStream_t s);
 
 }  // namespace gptq

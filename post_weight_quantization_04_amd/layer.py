@@ -119,6 +119,16 @@ def dequantize(packed, bits: int, d_in: int, scales, zeros, group_size: int, dty
     return out
 
 
+def propagate(W_hat, X, relu: bool = False, out=None, stream=None):
+    """The next layer's input from a quantized layer: ``Y = act(W_hat X)``
+    in f16 (``gptq_propagate``); ``W_hat`` is the f16 dequantized layer."""
+    import torch
+    if out is None:
+        out = torch.empty((W_hat.shape[0], X.shape[1]), dtype=torch.float16, device=X.device)
+    _lib.propagate(W_hat, X, out, 1 if relu else 0, stream=stream)
+    return out
+
+
 def output_error(W, factor: Factor, q: Quantized, packed, bits: int, group_size: int, stream=None):
     """Per-row ``||dw X||^2`` from the loss identity (``gptq_output_error``)."""
     import torch

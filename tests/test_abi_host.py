@@ -155,3 +155,17 @@ def test_greedy_variant_argument_errors(clib):
     assert obq(ws=None) == 4 and obq(wsb=64 * 64 * 8 - 1) == 4
     assert obq(ws=ctypes.c_void_p(256 + 8)) == 4    # not 256-byte aligned
     assert obq(d_out=0) == 0 and obq(d_in=0) == 0
+
+
+def test_propagate_argument_errors(clib):
+    p = ctypes.c_void_p(256)
+
+    def prop(d_out=8, d_in=64, n=32, ldx=32, ldy=32, act=0, wd=0, xd=0, W=p, X=p, Y=p):
+        return clib.gptq_propagate(W, wd, d_out, d_in, X, xd, n, ldx, Y, ldy, act, None)
+
+    assert prop(d_out=-1) == 1 and prop(d_in=-1) == 1 and prop(n=-1) == 1
+    assert prop(act=2) == 1 and prop(wd=5) == 1 and prop(xd=5) == 1
+    assert prop(ldx=31) == 1 and prop(ldy=31) == 1
+    assert prop(W=None) == 1 and prop(X=None) == 1 and prop(Y=None) == 1
+    assert prop(wd=1) == 2 and prop(xd=1) == 2  # float32 operands are valid but not handled
+    assert prop(d_out=0) == 0 and prop(n=0) == 0  # nothing to do, nothing launched
