@@ -48,6 +48,7 @@ KERNEL_SOURCE = {
     "dequantize": ("pack.hip", "dequant_kernel"),
     "output_error": ("pack.hip", "output_error_kernel"),
     "obq_rows": ("obq.hip", "obq_row_kernel"),
+    "propagate_relu": ("propagate.hip", "propagate_kernel"),
 }
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "attn_proj_4096x4096_traffic.json")
 
@@ -526,6 +527,7 @@ def main(argv=None) -> int:
                 tf = fl / (ms * 1e-3) / 1e12
                 after[name] = {"ms": round(ms, 4), "flops": fl, "achieved": round(tf, 1), "peak": PEAK_TFLOPS["f16"],
                                "unit": "TFLOP/s", "frac": round(tf / PEAK_TFLOPS["f16"], 4),
+                               "traffic": recorded_traffic(name),
                                "shape": f"Y[{d_out}x{Xd.shape[1]}] = relu(What[{d_out}x{d_in}] X)"}
         after["output_error_sum"] = float(oe.sum().item())
 

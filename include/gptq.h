@@ -245,7 +245,8 @@ int gptq_output_error(const void* W, int w_dtype, const uint8_t* dead, const uin
  * caller; the call is asynchronous on `stream`.
  * Errors: GPTQ_EINVAL (negative sizes, ldx or ldy below n_tokens, unknown
  * dtype or activation, null pointer), GPTQ_EUNSUPPORTED (a dtype other than
- * GPTQ_F16, d_out above 2^24 or n_tokens above 2^31).
+ * GPTQ_F16, d_out above 2^24, d_in above 2^22, ldx above 2^23, or 2^31 or
+ * more 128 x 128 tiles of Y).
  */
 int gptq_propagate(const void* W_hat, int w_dtype, int64_t d_out, int64_t d_in, const void* X, int x_dtype,
                    int64_t n_tokens, int64_t ldx, void* Y, int64_t ldy, int activation, void* stream);

@@ -232,7 +232,8 @@ int gptq_propagate(const void* W_hat, int w_dtype, int64_t d_out, int64_t d_in, 
     if (ldx < n_tokens || ldy < n_tokens) return GPTQ_EINVAL;
     if (!Y || (d_in > 0 && (!W_hat || !X))) return GPTQ_EINVAL;
     if (w_dtype != GPTQ_F16 || x_dtype != GPTQ_F16) return GPTQ_EUNSUPPORTED;
-    if (d_out > ((int64_t)1 << 24) || n_tokens > ((int64_t)1 << 31)) return GPTQ_EUNSUPPORTED;
+    if (d_out > ((int64_t)1 << 24) || d_in > ((int64_t)1 << 22) || ldx > ((int64_t)1 << 23)) return GPTQ_EUNSUPPORTED;
+    if (((d_out + 127) / 128) * ((n_tokens + 127) / 128) > (int64_t)INT32_MAX) return GPTQ_EUNSUPPORTED;
     return hip_status(launch_propagate(W_hat, d_out, d_in, X, n_tokens, ldx, Y, ldy, activation, as_stream(stream)));
 }
 

@@ -8,12 +8,17 @@
 // One workgroup per 128 x 128 tile of Y (rows of What x tokens), four waves
 // in 2 x 2, each a 64 x 64 quarter as 2 x 2 MFMA 32x32x16 f16 accumulators
 // (exact f16 products, fp32 accumulation), rounded once to f16 at the end.
-// K runs in slabs of 32 through two LDS buffers, the next slab fetched into
+// K runs in slabs of 64 through two LDS buffers, the next slab fetched into
 // registers while the MFMAs consume the current one.  Both operands are
-// staged k-contiguous (What rows as they are, X transposed on the way in:
-// X is token-contiguous, so each thread gathers one token's 16 k values, a
-// 64-byte run across 32 lanes per k), so that every MFMA operand is one
-// 16-byte LDS read.
+// staged k-contiguous, so that every MFMA operand is one 16-byte LDS read:
+// What rows as they are; X (token-contiguous) transposed on the way in, each
+// thread loading four k rows of eight tokens with 16-byte loads and writing
+// each token's four k values with one 8-byte LDS store.
+//
+// Every load is a buffer load issued unconditionally: a lane whose element
+// lies outside the operand gets an offset past the end of the buffer, for
+// which the hardware returns zero.  No load is under a condition, so the
+// loads of a slab are in flight together.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -22,77 +27,106 @@ namespace gptq {
 namespace {
 
 constexpr int kPT = 128;          // tile edge
-constexpr int kPK = 32;           // K per slab
-constexpr int kPLd = kPK + 8;     // padded LDS row (halves): 16-byte reads of 16 rows hit distinct banks
+constexpr int kPK = 64;           // K per slab
+constexpr int kPLd = kPK + 8;     // LDS row (halves): 36 dwords, so 16-byte reads of 8 rows and
+                                  // 8-byte transposing stores of 16 lanes hit distinct banks
 constexpr int kPThreads = 256;
+constexpr uint32_t kPOut = 0x80000000u;  // an offset past every buffer: the load returns zero
 
-// Thread t stages row (or token) t/2 of a slab, k run (t % 2) * 16 .. +16.
-// Every load is issued unconditionally at a clamped address (rows, tokens
-// and k past the ends read a valid element) and replaced by zero after, so
-// that a thread's loads are in flight together.
-struct PropRegs {
-    half8 a[2];
-    half_t b[16];
-};
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
-template <bool kVecA>
-__device__ __forceinline__ void prop_fetch(PropRegs& r, const half_t* __restrict__ W, int64_t M, int64_t K,
-                                           const half_t* __restrict__ X, int64_t N, int64_t ldx, int64_t m0,
-                                           int64_t n0, int64_t k0, int tid) {
-    const int sr = tid >> 1, kh = (tid & 1) * 16;
-    const int64_t k = k0 + kh;
-    {
-        const int64_t row = m0 + sr;
-        const int64_t rc = min(row, M - 1);
-        if (kVecA && k + 16 <= K) {
-            r.a[0] = *reinterpret_cast<const half8*>(W + rc * K + k);
-            r.a[1] = *reinterpret_cast<const half8*>(W + rc * K + k + 8);
-            if (row >= M) r.a[0] = r.a[1] = (half8){};
+// buffer descriptor of a raw (unstrided) byte range; word 3 as for every gfx9 part
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t prop_rsrc(const half_t* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ half8 prop_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(half8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ half_t prop_load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(half_t, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+
+// What: thread t holds rows t/8 + 32 i (i < 4) of the tile, k run 8 (t % 8) .. +8
+// of the slab.  rw covers the tile's valid rows, rows x K halves from its first.
+template <bool kVec>
+__device__ __forceinline__ void prop_fetch_w(half8 (&a)[4], __amdgpu_buffer_rsrc_t rw, int64_t rows, int64_t K,
+                                             int64_t k0, int tid) {
+    const int64_t k = k0 + 8 * (tid % 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t r = tid / 8 + 32 * i;
+        if (kVec) {
+            // K % 8 == 0: a run is wholly inside or wholly past the row
+            const bool ok = r < rows && k < K;
+            a[i] = prop_load8(rw, ok ? (uint32_t)((r * K + k) * 2) : kPOut);
         } else {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t kk = min(k + e, K - 1);
-                const half_t v = W[rc * K + kk];
-                r.a[e >> 3][e & 7] = (row < M && k + e < K) ? v : (half_t)0;
+            for (int e = 0; e < 8; ++e) {
+                const bool ok = r < rows && k + e < K;
+                a[i][e] = prop_load1(rw, ok ? (uint32_t)((r * K + k + e) * 2) : kPOut);
             }
         }
     }
-    {
-        const int64_t tok = n0 + sr;
-        const int64_t tc = min(tok, N - 1);
+}
+
+// X: thread t holds k rows 4 (t % 16) + i (i < 4) of the slab, tokens
+// 8 (t / 16) .. +8 of the tile.  rx covers the slab from (k0, n0): krows rows
+// of ldx halves, the last ncols long.
+template <bool kVec>
+__device__ __forceinline__ void prop_fetch_x(half8 (&b)[4], __amdgpu_buffer_rsrc_t rx, int64_t krows, int64_t ncols,
+                                             int64_t ldx, int tid) {
+    const int64_t t = 8 * (tid / 16);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int64_t kk = min(k + e, K - 1);
-            const half_t v = X[kk * ldx + tc];
-            r.b[e] = (tok < N && k + e < K) ? v : (half_t)0;
+    for (int i = 0; i < 4; ++i) {
+        const int64_t kr = 4 * (tid % 16) + i;
+        if (kVec) {
+            // ncols % 8 == 0: a run of eight tokens is wholly valid or wholly past the end
+            const bool ok = kr < krows && t < ncols;
+            b[i] = prop_load8(rx, ok ? (uint32_t)((kr * ldx + t) * 2) : kPOut);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const bool ok = kr < krows && t + e < ncols;
+                b[i][e] = prop_load1(rx, ok ? (uint32_t)((kr * ldx + t + e) * 2) : kPOut);
+            }
         }
     }
 }
 
-__device__ __forceinline__ void prop_stash(const PropRegs& r, half_t* __restrict__ As, half_t* __restrict__ Bt,
-                                           int tid) {
-    const int sr = tid >> 1, kh = (tid & 1) * 16;
-    *reinterpret_cast<half8*>(&As[sr * kPLd + kh]) = r.a[0];
-    *reinterpret_cast<half8*>(&As[sr * kPLd + kh + 8]) = r.a[1];
-    half8 b0, b1;
+__device__ __forceinline__ void prop_stash(const half8 (&a)[4], const half8 (&b)[4], half_t* __restrict__ As,
+                                           half_t* __restrict__ Bt, int tid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<half8*>(&As[(tid / 8 + 32 * i) * kPLd + 8 * (tid % 8)]) = a[i];
+    // token 8 (t/16) + e takes k values 4 (t%16) .. +4
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        b0[e] = r.b[e];
-        b1[e] = r.b[e + 8];
+        const half4 v = {b[0][e], b[1][e], b[2][e], b[3][e]};
+        *reinterpret_cast<half4*>(&Bt[(8 * (tid / 16) + e) * kPLd + 4 * (tid % 16)]) = v;
     }
-    *reinterpret_cast<half8*>(&Bt[sr * kPLd + kh]) = b0;
-    *reinterpret_cast<half8*>(&Bt[sr * kPLd + kh + 8]) = b1;
 }
 
-template <bool kVecA, bool kRelu>
+// Tiles are numbered token-fastest; workgroups are dealt to the eight XCDs in
+// turn, so workgroup id is given tile (id % 8) * (tiles / 8) + id / 8: each XCD
+// works on a band of What rows against every token and keeps that band in
+// its own L2.
+template <bool kVecA, bool kVecB, bool kRelu>
 __global__ __launch_bounds__(kPThreads, 2) void propagate_kernel(const half_t* __restrict__ W, int64_t M, int64_t K,
                                                                const half_t* __restrict__ X, int64_t N,
-                                                               int64_t ldx, half_t* __restrict__ Y, int64_t ldy) {
+                                                               int64_t ldx, half_t* __restrict__ Y, int64_t ldy,
+                                                               int64_t ntn) {
     __shared__ half_t As[2][kPT * kPLd];
     __shared__ half_t Bt[2][kPT * kPLd];
-    const int64_t n0 = (int64_t)blockIdx.x * kPT, m0 = (int64_t)blockIdx.y * kPT;
+    const int64_t tiles = (int64_t)gridDim.x;
+    int64_t id = blockIdx.x;
+    if (tiles % 8 == 0) id = (id % 8) * (tiles / 8) + id / 8;
+    const int64_t n0 = (id % ntn) * kPT, m0 = (id / ntn) * kPT;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wi = w >> 1, wj = w & 1;
+    const int64_t rows = min(M - m0, (int64_t)kPT), ncols = min(N - n0, (int64_t)kPT);
+    const __amdgpu_buffer_rsrc_t rw = prop_rsrc(W + m0 * K, (uint32_t)(rows * K * 2));
 
     float16v acc[2][2];
 #pragma unroll
@@ -100,30 +134,53 @@ __global__ __launch_bounds__(kPThreads, 2) void propagate_kernel(const half_t* _
 #pragma unroll
         for (int q = 0; q < 2; ++q) acc[m][q] = (float16v){};
 
+    // Slab k0 into registers.  A slab past the end (k0 >= K) is fetched with
+    // every offset out of range and a zero-length X descriptor: zeros, no
+    // memory read, so that every iteration issues the same loads.
+    auto fetch = [&](half8 (&a)[4], half8 (&b)[4], int64_t k0) {
+        const int64_t krows = max((int64_t)0, min(K - k0, (int64_t)kPK));
+        prop_fetch_w<kVecA>(a, rw, rows, K, k0, tid);
+        const bool live = krows > 0;
+        const __amdgpu_buffer_rsrc_t rx = prop_rsrc(X + (live ? k0 * ldx + n0 : 0),
+                                                    live ? (uint32_t)(((krows - 1) * ldx + ncols) * 2) : 0u);
+        prop_fetch_x<kVecB>(b, rx, krows, ncols, ldx, tid);
+    };
+    // MFMA operands of step ks of a slab: one 16-byte LDS read each
+    auto operands = [&](half8 (&a)[2], half8 (&b)[2], int buf, int ks) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+            a[m] = *reinterpret_cast<const half8*>(&As[buf][(wi * 64 + 32 * m + (lane & 31)) * kPLd + ks + 8 * (lane >> 5)]);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            b[q] = *reinterpret_cast<const half8*>(&Bt[buf][(wj * 64 + 32 * q + (lane & 31)) * kPLd + ks + 8 * (lane >> 5)]);
+    };
+    auto mfmas = [&](const half8 (&a)[2], const half8 (&b)[2]) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) acc[m][q] = mfma32x32x16_f16(a[m], b[q], acc[m][q]);
+    };
+
+    // One slab in flight in registers, two LDS buffers; within a slab the
+    // operands of the next 16-deep step are read while the MFMAs of the
+    // current one run.
     const int64_t nslab = (K + kPK - 1) / kPK;
-    PropRegs r;
-    if (nslab > 0) prop_fetch<kVecA>(r, W, M, K, X, N, ldx, m0, n0, 0, tid);  // K = 0 gives Y = act(0)
+    half8 ra[4], rb[4];
+    if (nslab > 0) fetch(ra, rb, 0);  // K = 0 gives Y = act(0)
     for (int64_t sl = 0; sl < nslab; ++sl) {
         const int buf = (int)(sl & 1);
         // buffer buf was last read by slab sl-2, finished before the previous barrier
-        prop_stash(r, As[buf], Bt[buf], tid);
+        prop_stash(ra, rb, As[buf], Bt[buf], tid);
         __syncthreads();
-        if (sl + 1 < nslab) prop_fetch<kVecA>(r, W, M, K, X, N, ldx, m0, n0, (sl + 1) * kPK, tid);
-        const half_t* Ap = As[buf];
-        const half_t* Bp = Bt[buf];
+        fetch(ra, rb, (sl + 1) * kPK);  // past the end on the last slab: zeros, never stashed
+        half8 a0[2], b0[2], a1[2], b1[2];
+        operands(a0, b0, buf, 0);
 #pragma unroll
-        for (int ks = 0; ks < kPK; ks += 16) {
-            half8 a[2], b[2];
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-                a[m] = *reinterpret_cast<const half8*>(&Ap[(wi * 64 + 32 * m + (lane & 31)) * kPLd + ks + 8 * (lane >> 5)]);
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-                b[q] = *reinterpret_cast<const half8*>(&Bp[(wj * 64 + 32 * q + (lane & 31)) * kPLd + ks + 8 * (lane >> 5)]);
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int q = 0; q < 2; ++q) acc[m][q] = mfma32x32x16_f16(a[m], b[q], acc[m][q]);
+        for (int ks = 0; ks < kPK; ks += 32) {
+            operands(a1, b1, buf, ks + 16);
+            mfmas(a0, b0);
+            if (ks + 32 < kPK) operands(a0, b0, buf, ks + 32);
+            mfmas(a1, b1);
         }
     }
 #pragma unroll
@@ -142,24 +199,31 @@ __global__ __launch_bounds__(kPThreads, 2) void propagate_kernel(const half_t* _
 
 }  // namespace
 
+// Offsets inside one tile's rows of What and one slab of X stay below 2^31
+// bytes for d_in <= 2^22 and ldx <= 2^23, which the entry point enforces.
 hipError_t launch_propagate(const void* W, int64_t d_out, int64_t d_in, const void* X, int64_t ntok, int64_t ldx,
                             void* Y, int64_t ldy, int relu, hipStream_t s) {
     if (d_out == 0 || ntok == 0) return hipSuccess;
-    const dim3 grid((unsigned)((ntok + kPT - 1) / kPT), (unsigned)((d_out + kPT - 1) / kPT));
-    const bool vec = (reinterpret_cast<uintptr_t>(W) % 16 == 0) && (d_in % 8 == 0);
+    const int64_t ntn = (ntok + kPT - 1) / kPT, ntm = (d_out + kPT - 1) / kPT;
+    const dim3 grid((unsigned)(ntn * ntm));
+    const bool va = (reinterpret_cast<uintptr_t>(W) % 16 == 0) && (d_in % 8 == 0);
+    const bool vb = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && (ldx % 8 == 0) && (ntok % 8 == 0);
     const half_t* w = static_cast<const half_t*>(W);
     const half_t* x = static_cast<const half_t*>(X);
     half_t* y = static_cast<half_t*>(Y);
     TimedLaunch t(K_PROPAGATE, s);
-#define PROP_LAUNCH(V, R) \
-    hipLaunchKernelGGL((propagate_kernel<V, R>), grid, dim3(kPThreads), 0, s, w, d_out, d_in, x, ntok, ldx, y, ldy)
-    if (vec) {
-        if (relu) PROP_LAUNCH(true, true);
-        else PROP_LAUNCH(true, false);
-    } else {
-        if (relu) PROP_LAUNCH(false, true);
-        else PROP_LAUNCH(false, false);
-    }
+#define PROP_LAUNCH(A, B, R) \
+    hipLaunchKernelGGL((propagate_kernel<A, B, R>), grid, dim3(kPThreads), 0, s, w, d_out, d_in, x, ntok, ldx, y, ldy, ntn)
+#define PROP_RELU(A, B) \
+    do {                \
+        if (relu) PROP_LAUNCH(A, B, true); \
+        else PROP_LAUNCH(A, B, false);     \
+    } while (0)
+    if (va && vb) PROP_RELU(true, true);
+    else if (va) PROP_RELU(true, false);
+    else if (vb) PROP_RELU(false, true);
+    else PROP_RELU(false, false);
+#undef PROP_RELU
 #undef PROP_LAUNCH
     return hipGetLastError();
 }

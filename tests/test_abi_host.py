@@ -168,4 +168,8 @@ def test_propagate_argument_errors(clib):
     assert prop(ldx=31) == 1 and prop(ldy=31) == 1
     assert prop(W=None) == 1 and prop(X=None) == 1 and prop(Y=None) == 1
     assert prop(wd=1) == 2 and prop(xd=1) == 2  # float32 operands are valid but not handled
+    # beyond the 32-bit buffer offsets of one tile's rows of What and one slab of X
+    assert prop(d_in=(1 << 22) + 1) == 2 and prop(n=32, ldx=(1 << 23) + 1) == 2
+    assert prop(d_out=(1 << 24) + 1) == 2
+    assert prop(d_out=1 << 24, n=1 << 23, ldx=1 << 23, ldy=1 << 23) == 2  # 2^33 tiles
     assert prop(d_out=0) == 0 and prop(n=0) == 0  # nothing to do, nothing launched
