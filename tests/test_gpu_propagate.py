@@ -40,7 +40,8 @@ def bound(W, X, Y_ref):
     (257, 300, 129, False, 0, 3),     # ragged everywhere, X and Y at an unaligned offset
     (128, 1000, 256, True, 64, 0),
     (96, 256, 100, False, 0, 0),      # 16-byte What runs, element loads of X (tokens not a multiple of 8)
-    (384, 200, 1024, True, 0, 0),     # 24 tiles: the XCD-banded tile order
+    (384, 200, 1024, True, 0, 0),     # 24 tiles: the XCD-banded tile order (bands of rows)
+    (512, 72, 512, False, 0, 0),      # 16 tiles in a 4 x 4 grid, K one ragged slab
     (5, 0, 7, True, 0, 0),            # d_in = 0: Y = act(0)
 ])
 def test_propagate_matches_oracle(lib, M, K, N, relu, ld_pad, offset):
