@@ -64,15 +64,19 @@ def kernel_source_sha(name: str) -> str:
     return h.hexdigest()
 
 
-def recorded_traffic(name: str):
+def recorded_traffic(name: str, workload: str):
     """HBM bytes per launch of a kernel class from the committed counter
-    record, or None when there is none or the kernel's source has changed
-    since the counters were taken."""
+    record, or None when there is none, when the record was taken on another
+    workload, or when the kernel's source has changed since the counters were
+    taken."""
     import json
     if name not in KERNEL_SOURCE or not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as fh:
-        rec = json.load(fh).get("kernels", {}).get(name)
+        data = json.load(fh)
+    if data.get("workload", "").split(":")[0].strip() != workload:
+        return None
+    rec = data.get("kernels", {}).get(name)
     if not rec or rec.get("source_sha256") != kernel_source_sha(name):
         return None
     return rec["bytes_per_launch"]
@@ -479,7 +483,7 @@ def main(argv=None) -> int:
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        "traffic": recorded_traffic(dominant),
+        "traffic": recorded_traffic(dominant, args.workload),
         "avg_launch_ms": round(dom_ms / max(dom_launches, 1), 5),
         "launches_per_step": dom_launches // max(args.steps, 1),
     }
@@ -497,7 +501,7 @@ def main(argv=None) -> int:
         ach = fl / (ms * 1e-3) / 1e12
         mfma_kernels[name] = {"ms_per_step": round(ms, 4), "flops": fl, "achieved": round(ach, 2),
                               "peak": PEAK_TFLOPS[cls_], "unit": "TFLOP/s", "frac": round(ach / PEAK_TFLOPS[cls_], 4),
-                              "traffic": recorded_traffic(name)}
+                              "traffic": recorded_traffic(name, args.workload)}
 
     # after the path (not part of a step): few-bit storage, dequantization to
     # fp16 and the identity-based output error of the layer just quantized;
@@ -520,14 +524,14 @@ def main(argv=None) -> int:
             gbs = nbytes / (ms * 1e-3) / 1e9
             cls = {"dequantize_f16": "dequantize"}.get(name, name)
             after[name] = {"ms": round(ms, 4), "bytes": int(nbytes), "GB/s": round(gbs, 1),
-                           "frac_hbm": round(gbs / PEAK_HBM_GBS, 3), "traffic": recorded_traffic(cls)}
+                           "frac_hbm": round(gbs / PEAK_HBM_GBS, 3), "traffic": recorded_traffic(cls, args.workload)}
             if name == "propagate_relu":
                 # a dense f16 contraction: reported against the f16 MFMA peak
                 fl = 2.0 * d_out * d_in * Xd.shape[1]
                 tf = fl / (ms * 1e-3) / 1e12
                 after[name] = {"ms": round(ms, 4), "flops": fl, "achieved": round(tf, 1), "peak": PEAK_TFLOPS["f16"],
                                "unit": "TFLOP/s", "frac": round(tf / PEAK_TFLOPS["f16"], 4),
-                               "traffic": recorded_traffic(name),
+                               "traffic": recorded_traffic(name, args.workload),
                                "shape": f"Y[{d_out}x{Xd.shape[1]}] = relu(What[{d_out}x{d_in}] X)"}
         after["output_error_sum"] = float(oe.sum().item())
 

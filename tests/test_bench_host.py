@@ -62,17 +62,25 @@ def test_factorization_flops_leading_order():
     assert ratios[0] > ratios[1] > ratios[2]  # lower-order terms fade as d grows
 
 
-def test_recorded_traffic_needs_a_matching_source_hash(tmp_path, monkeypatch):
-    rec = {"kernels": {"chol_step": {"bytes_per_launch": 12345,
+def test_recorded_traffic_needs_a_matching_source_hash_and_workload(tmp_path, monkeypatch):
+    rec = {"workload": "attn_proj: 4096x4096 layer",
+           "kernels": {"chol_step": {"bytes_per_launch": 12345,
                                      "source_sha256": bench.kernel_source_sha("chol_step")}}}
     f = tmp_path / "traffic.json"
     f.write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
-    assert bench.recorded_traffic("chol_step") == 12345
-    assert bench.recorded_traffic("q_step") is None          # not in the record
-    assert bench.recorded_traffic("no_such_kernel") is None  # not a known class
+    assert bench.recorded_traffic("chol_step", "attn_proj") == 12345
+    assert bench.recorded_traffic("chol_step", "mlp_down") is None         # taken on another workload
+    assert bench.recorded_traffic("q_step", "attn_proj") is None           # not in the record
+    assert bench.recorded_traffic("no_such_kernel", "attn_proj") is None   # not a known class
     monkeypatch.setattr(bench, "kernel_source_sha", lambda name: "0" * 64)
-    assert bench.recorded_traffic("chol_step") is None       # source changed since the counters
+    assert bench.recorded_traffic("chol_step", "attn_proj") is None        # source changed since the counters
+
+
+def test_committed_traffic_record_names_its_workload():
+    with open(bench.TRAFFIC_FILE) as fh:
+        rec = json.load(fh)
+    assert rec["workload"].split(":")[0].strip() == "attn_proj"
 
 
 def test_every_traffic_class_names_an_existing_kernel():
