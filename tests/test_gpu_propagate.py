@@ -42,6 +42,7 @@ def bound(W, X, Y_ref):
     (96, 256, 100, False, 0, 0),      # 16-byte What runs, element loads of X (tokens not a multiple of 8)
     (384, 200, 1024, True, 0, 0),     # 24 tiles: the XCD-banded tile order (bands of rows)
     (512, 72, 512, False, 0, 0),      # 16 tiles in a 4 x 4 grid, K one ragged slab
+    (1000, 136, 4088, True, 0, 0),    # 256 tiles, ragged rows, tokens and last slab
     (5, 0, 7, True, 0, 0),            # d_in = 0: Y = act(0)
 ])
 def test_propagate_matches_oracle(lib, M, K, N, relu, ld_pad, offset):
