@@ -130,3 +130,28 @@ def test_two_layer_chain(lib):
     q = {"codes": qB.codes.cpu().numpy(), "scales": qB.scales.cpu().numpy(), "zeros": qB.zeros.cpu().numpy(),
          "err_row": qB.err_row.cpu().numpy(), "minmax": qB.minmax.cpu().numpy()}
     parity.check_codes(WB.astype(np.float64), UB.astype(np.float32), deadB, q, bits, 0, block)
+
+
+def test_propagate_full_size_sampled(lib):
+    """The 4096 x 4096 layer by 2048 tokens, the shape the benchmark times,
+    in the launch configuration it uses (16-byte loads, XCD-banded tiles):
+    sampled 32 x 32 blocks of Y against the oracle on the same rows of What
+    and columns of X, within the bound of the arithmetic."""
+    from post_weight_quantization_04_amd import layer
+    torch = _torch()
+    M, K, N = 4096, 4096, 2048
+    say("full size", M, K, N)
+    rng = np.random.default_rng(2048)
+    W = (rng.standard_normal((M, K), dtype=np.float32) * 0.02).astype(np.float16)
+    X = rng.standard_normal((K, N), dtype=np.float32).astype(np.float16)
+    Yd = layer.propagate(torch.from_numpy(W).cuda(), torch.from_numpy(X).cuda(), relu=True)
+    torch.cuda.synchronize()
+    Y = Yd.cpu().numpy().astype(np.float64)
+    for trial in range(4):
+        rows = np.sort(rng.choice(M, 32, replace=False))
+        cols = np.sort(rng.choice(N, 32, replace=False))
+        Wr, Xc = W[rows], X[:, cols]
+        ref = oracle.propagate(Wr, Xc, "relu")
+        got = Y[np.ix_(rows, cols)]
+        assert np.all(np.abs(got - ref) <= bound(Wr, Xc, ref)), trial
+    assert np.all(Y >= 0.0) and np.isfinite(Y).all()
