@@ -167,8 +167,9 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in,
 
 /*
  * Few-bit storage of the codes (aicassindra.com "tm_gptq_math",
- * "Post-training quantization in one paragraph": the quantized weights are
- * kept as few-bit integers; the pages fix no bit layout).  Layout: each
+ * "Post-training quantization and the per-layer objective": weights go from
+ * 16-bit floats to low-bit integers, 4-bit being the example given; the
+ * pages fix no bit layout).  Layout: each
  * row's codes form one little-endian bit stream, code j in bits
  * [j bits, (j+1) bits), least significant bit first, cut into 32-bit words;
  * a row holds gptq_packed_words(d_in, bits) = ceil(d_in bits / 32) words,
@@ -188,7 +189,7 @@ int gptq_pack_codes(const uint8_t* codes, int64_t d_out, int64_t d_in, int bits,
 
 /*
  * Dequantization What = s (q - z) from packed codes (aicassindra
- * "Post-training quantization in one paragraph", the grid of "A worked
+ * "Post-training quantization and the per-layer objective", the grid of "A worked
  * two-weight example").  The exact product of the scale and the integer
  * q - z is rounded once to the output type, to nearest even (one fp32
  * multiply, or one mixed-precision multiply with an fp16 result).

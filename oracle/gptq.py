@@ -222,9 +222,14 @@ def quantize(W: np.ndarray, U: np.ndarray, bits: int, group_size: int = 0, block
 
     Grid (reading): ``group_size == 0`` builds one grid per row from the
     input W before any change; ``group_size > 0`` rebuilds it at every
-    ``j % group_size == 0`` from the current ``W[:, j:j+group_size]`` as
-    stored at that moment.  Dead columns are zeroed after the per-row grid,
-    so they round to ``z`` with zero error and move nothing.
+    ``j % group_size == 0`` from the current weights ``W[:, j:j+group_size]``,
+    i.e. with the compensation of every column before j applied, which is
+    what an unblocked sweep (B = 1) holds there.  Lazy batching only delays
+    when updates are written ("same math"), so the grid does not depend on
+    B: where a group reaches past the current block, its columns there get
+    the block's pending compensation before the min/max is taken.  Dead
+    columns are zeroed after the per-row grid, so they round to ``z`` with
+    zero error and move nothing.
 
     ``hint`` (tie-aware replay): where the hint code differs from the own
     code, the hint is adopted and the difference is counted as a tie when
@@ -283,7 +288,13 @@ def quantize(W: np.ndarray, U: np.ndarray, bits: int, group_size: int = 0, block
         b1 = min(b0 + block_size, d_in)
         for j in range(b0, b1):
             if group_size and fixed_grid is None and j % group_size == 0:
-                gcols = W[:, j:j + group_size]
+                gcols = W[:, j:j + group_size].copy()
+                # columns past this block still lack the compensation from
+                # columns b0..j-1 (it is deferred to the block's end); the
+                # grid sees them with it applied, as an unblocked sweep would
+                lo = max(b1, j)
+                if j > b0 and j + group_size > lo:
+                    gcols[:, lo - j:] -= E[:, b0:j] @ U[b0:j, lo:j + group_size]
                 mn = gcols.min(axis=1).astype(F32)
                 mx = gcols.max(axis=1).astype(F32)
                 s, z = grid(mn, mx, bits)
@@ -350,9 +361,10 @@ def output_error(W: np.ndarray, W_hat: np.ndarray, x_chunks: Iterable[np.ndarray
 def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
     """Few-bit storage of the codes: ``[d_out, ceil(d_in bits / 32)]`` uint32.
 
-    The pages keep the quantized weights as few-bit integers (aicassindra
-    "Post-training quantization in one paragraph": weights stored as 3- or
-    4-bit integers) and fix no bit layout.  Reading used here: each row's
+    The pages keep the quantized weights as low-bit integers (aicassindra
+    "Post-training quantization and the per-layer objective": from 16-bit
+    floats to 4-bit integers, 4 being the example given) and fix no bit
+    layout.  Reading used here: each row's
     codes form one little-endian bit stream, code j in bits
     ``[j bits, (j+1) bits)``, least significant bit first, cut into 32-bit
     words; the last word of a row is zero-padded.  Written bit by bit.

@@ -1,6 +1,7 @@
 // Few-bit storage of the codes, dequantization, and the per-row output error
 // from the loss identity (aicassindra.com "tm_gptq_math", "Post-training
-// quantization in one paragraph": weights kept as few-bit integers; "The
+// quantization and the per-layer objective": weights lowered to low-bit
+// integers, 4-bit the example given; "The
 // reconstruction objective, written out" with the damped Hessian of "The
 // Cholesky trick for the inverse Hessian").
 //

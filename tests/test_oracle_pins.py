@@ -228,13 +228,17 @@ def test_sweep_matches_explicit_obs_reinversion(d_in, block):
 # ---------------------------------------------------------------------------
 # P3: lazy batches are exact (aicassindra "GPTQ's speedups": same math)
 # ---------------------------------------------------------------------------
-def test_lazy_batch_invariance():
-    W, X = _spd_problem(24, 200, 400, 21)
+@pytest.mark.parametrize("g", [0, 8, 16, 40])
+def test_lazy_batch_invariance(g):
+    W, X = _spd_problem(24, 240, 480, 21)
     U, dead, _ = oracle.prepare(oracle.hessian([X]))
-    ref = oracle.quantize(W, U, 4, 0, 1)
-    for B in (3, 32, 128, 200, 1000):
-        r = oracle.quantize(W, U, 4, 0, B)
+    ref = oracle.quantize(W, U, 4, g, 1)
+    for B in (3, 16, 24, 32, 48, 128, 200, 1000):
+        r = oracle.quantize(W, U, 4, g, B)
         np.testing.assert_array_equal(r.codes, ref.codes)
+        np.testing.assert_array_equal(r.scales, ref.scales)
+        np.testing.assert_array_equal(r.zeros, ref.zeros)
+        np.testing.assert_array_equal(r.minmax, ref.minmax)
         np.testing.assert_allclose(r.w_hat, ref.w_hat, rtol=0, atol=1e-14)
         np.testing.assert_allclose(r.E, ref.E, rtol=1e-10, atol=1e-14)
 
@@ -343,19 +347,48 @@ def test_dead_channel_removal_equivalence():
 # ---------------------------------------------------------------------------
 # group grids: rebuilt from the current weights at each group start
 # ---------------------------------------------------------------------------
-def test_group_grid_from_current_weights():
+@pytest.mark.parametrize("d_in,g,B", [
+    (32, 8, 16),    # groups start inside a block (g < B, g | B)
+    (32, 8, 8),     # group starts are block starts (g = B)
+    (48, 16, 4),    # a group spans several blocks (g > B, B | g)
+    (36, 12, 8),    # unaligned: a group reaches past the block it starts in
+    (30, 6, 1),     # unblocked
+])
+def test_group_grids_equal_explicit_obs_state(d_in, g, B):
+    """At every group start the grid is built from the weights with every
+    earlier column's compensation applied.  The reference state here comes
+    from explicit OBS steps with the inverse of H restricted to the free
+    columns, re-inverted at every step (no U, no lazy blocks), and the grid
+    of that state must equal the oracle's bit for bit."""
+    W, X = _spd_problem(5, d_in, 3 * d_in, 100 + d_in + g + B)
+    Hd, _, _ = oracle.damp(oracle.hessian([X]))
+    U = oracle.hinv_cholesky_upper(Hd)
+    bits = 4
+    r = oracle.quantize(W, U, bits, g, B)
+    for row in range(W.shape[0]):
+        w = W[row].astype(np.float64).copy()
+        s = z = None
+        for q in range(d_in):
+            if q % g == 0:
+                cols = w[q:q + g]
+                mn, mx = F32(cols.min()), F32(cols.max())
+                s1, z1 = oracle.grid(np.array([mn]), np.array([mx]), bits)
+                s, z = s1[0], z1[0]
+                k = q // g
+                assert r.minmax[row, k, 0] == min(mn, F32(0)), (row, q)
+                assert r.minmax[row, k, 1] == max(mx, F32(0)), (row, q)
+                assert r.scales[row, k] == s and r.zeros[row, k] == int(z), (row, q)
+            qv, _ = oracle.quantize_values(w[q:q + 1], np.array([s]), np.array([z]), bits)
+            wq = float(s) * (float(qv[0]) - float(z))
+            Finv = np.linalg.inv(Hd[q:, q:])
+            w[q:] += -((w[q] - wq) / Finv[0, 0]) * Finv[:, 0]
+            assert r.codes[row, q] == int(qv[0]), (row, q)
+        np.testing.assert_allclose(r.w_hat[row], w, rtol=1e-10, atol=1e-13)
+
+
+def test_group_grid_spanning_the_row_is_the_row_grid():
     W, X = _spd_problem(6, 32, 90, 71)
     U, _, _ = oracle.prepare(oracle.hessian([X]))
-    trace = []
-    r = oracle.quantize(W, U, 4, 8, 16, trace=trace)
-    T = np.stack(trace, axis=1)
-    for g in range(4):
-        j = 8 * g
-        # at the group start, columns j..j+7 as stored; column j is current
-        # (the in-block and deferred updates before j are applied)
-        mn = np.minimum(T[:, j], 0)
-        assert np.all(r.minmax[:, g, 0] <= mn.astype(F32) + 1e-7)
-    # a single group spanning the row equals the per-row grid
     r1 = oracle.quantize(W, U, 4, 32, 16)
     r0 = oracle.quantize(W, U, 4, 0, 16)
     np.testing.assert_array_equal(r1.scales, r0.scales)
