@@ -46,7 +46,8 @@ typedef enum {
     GPTQ_EINVAL = 1,       /* invalid argument (null pointer, negative size, bits out of [2,8], ...) */
     GPTQ_EUNSUPPORTED = 2, /* valid request these kernels do not handle (documented per call) */
     GPTQ_EHIP = 3,         /* a HIP runtime call or kernel launch failed */
-    GPTQ_EWORKSPACE = 4    /* workspace pointer null or smaller than the *_workspace() size */
+    GPTQ_EWORKSPACE = 4,   /* workspace pointer null or smaller than the *_workspace() size */
+    GPTQ_ESCRATCH = 5      /* problem larger than the fixed scratch of a no-allocation entry point */
 } gptq_status;
 
 typedef enum {
@@ -112,6 +113,30 @@ size_t gptq_prepare_hinv_workspace(int64_t d_in);
 int gptq_prepare_hinv(const float* H, int64_t d_in, double damp_frac, float* U, uint8_t* dead,
                       int32_t* info, double* lambda_out, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/*
+ * gptq_prepare_hinv without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight loops, harnesses that forbid hipMalloc).  Same operation,
+ * arguments, kernels and results as gptq_prepare_hinv; the workspace is a
+ * fixed device array inside the library instead, sized for
+ * d_in <= gptq_prepare_hinv_noalloc_max_din() (4096: about 134 MiB, held on
+ * every device the library runs on until the process ends).  Its device
+ * address is looked up once per device on the first call there (with that
+ * device current).  The call makes no hipMalloc, hipFree or other
+ * allocating call and records no timing events.
+ * Every call on one device shares that device's array: calls that overlap
+ * on one device (concurrent streams, or host threads) race and give
+ * undefined results; calls in order on one stream are safe.  Nothing in the
+ * array needs clearing between calls (every byte read is written first by
+ * the same call).
+ * Errors: as gptq_prepare_hinv, except that GPTQ_EWORKSPACE cannot occur;
+ * GPTQ_ESCRATCH for d_in above gptq_prepare_hinv_noalloc_max_din();
+ * GPTQ_EHIP if the array's address cannot be obtained.
+ */
+int gptq_prepare_hinv_noalloc(const float* H, int64_t d_in, double damp_frac, float* U, uint8_t* dead,
+                              int32_t* info, double* lambda_out, void* stream);
+int64_t gptq_prepare_hinv_noalloc_max_din(void);
 
 /*
  * Stage 4 -- the quantize-and-compensate sweep.

@@ -14,13 +14,15 @@ from typing import Optional, Tuple
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgptq_mi355x.so")
 
-GPTQ_OK, GPTQ_EINVAL, GPTQ_EUNSUPPORTED, GPTQ_EHIP, GPTQ_EWORKSPACE = 0, 1, 2, 3, 4
+GPTQ_OK, GPTQ_EINVAL, GPTQ_EUNSUPPORTED, GPTQ_EHIP, GPTQ_EWORKSPACE, GPTQ_ESCRATCH = 0, 1, 2, 3, 4, 5
 GPTQ_F16, GPTQ_F32 = 0, 1
 
 EXPORTS = (
     "gptq_hessian_accumulate",
     "gptq_prepare_hinv_workspace",
     "gptq_prepare_hinv",
+    "gptq_prepare_hinv_noalloc",
+    "gptq_prepare_hinv_noalloc_max_din",
     "gptq_quantize_layer_workspace",
     "gptq_quantize_layer",
     "gptq_status_string",
@@ -62,6 +64,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "gptq_hessian_accumulate": (_i32, [_vp, _i64, _vp, _i32, _i64, _i64, _vp]),
         "gptq_prepare_hinv_workspace": (_sz, [_i64]),
         "gptq_prepare_hinv": (_i32, [_vp, _i64, ctypes.c_double, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "gptq_prepare_hinv_noalloc": (_i32, [_vp, _i64, ctypes.c_double, _vp, _vp, _vp, _vp, _vp]),
+        "gptq_prepare_hinv_noalloc_max_din": (_i64, []),
         "gptq_quantize_layer_workspace": (_sz, [_i64, _i64, _i64]),
         "gptq_quantize_layer": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _sz, _vp]),
@@ -151,6 +155,18 @@ def prepare_hinv(H, damp_frac: float, U, dead=None, info=None, lambda_out=None, 
                                   workspace.numel() * workspace.element_size() if workspace is not None else 0,
                                   _stream(stream))
     _check("gptq_prepare_hinv", rc)
+
+
+def prepare_hinv_noalloc(H, damp_frac: float, U, dead=None, info=None, lambda_out=None, stream=None) -> None:
+    """``gptq_prepare_hinv`` on the library's fixed device scratch (no workspace, no allocation)."""
+    d_in = H.shape[0]
+    rc = load().gptq_prepare_hinv_noalloc(_ptr(H), d_in, float(damp_frac), _ptr(U), _ptr(dead), _ptr(info),
+                                          _ptr(lambda_out), _stream(stream))
+    _check("gptq_prepare_hinv_noalloc", rc)
+
+
+def prepare_hinv_noalloc_max_din() -> int:
+    return int(load().gptq_prepare_hinv_noalloc_max_din())
 
 
 def quantize_layer_workspace(d_out: int, d_in: int, block_size: int) -> int:

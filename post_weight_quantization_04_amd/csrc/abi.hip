@@ -4,6 +4,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/gptq.h"
@@ -20,15 +21,24 @@ const char* const kNames[K_COUNT] = {
     "q_grid_convert",         "q_group_grid",       "q_step",    "q_trail",
     "pack_codes",  "dequantize",  "output_error", "obq_hinv", "obq_rows", "propagate",
 };
+// The timing state is process-wide; the mutex makes concurrent entry-point
+// calls from several host threads safe, though the events then interleave.
+std::mutex g_mu;
 int g_timed = -1;
 struct EventPair {
     hipEvent_t a, b;
 };
 std::vector<EventPair> g_pending;
 std::vector<EventPair> g_free;
+thread_local bool t_timing_off = false;
 }  // namespace
 
+TimingOff::TimingOff() : prev(t_timing_off) { t_timing_off = true; }
+TimingOff::~TimingOff() { t_timing_off = prev; }
+
 TimedLaunch::TimedLaunch(int id, hipStream_t s) : slot(-1), stream(s) {
+    if (t_timing_off) return;
+    std::lock_guard<std::mutex> lock(g_mu);
     if (id != g_timed) return;
     EventPair ep;
     if (!g_free.empty()) {
@@ -50,7 +60,9 @@ TimedLaunch::TimedLaunch(int id, hipStream_t s) : slot(-1), stream(s) {
 }
 
 TimedLaunch::~TimedLaunch() {
-    if (slot >= 0) (void)hipEventRecord(g_pending[slot].b, stream);
+    if (slot < 0) return;
+    std::lock_guard<std::mutex> lock(g_mu);
+    (void)hipEventRecord(g_pending[slot].b, stream);
 }
 
 }  // namespace gptq
@@ -71,6 +83,9 @@ const char* gptq_status_string(int status) {
         case GPTQ_EUNSUPPORTED: return "GPTQ_EUNSUPPORTED: valid request not handled by these kernels";
         case GPTQ_EHIP: return "GPTQ_EHIP: HIP runtime or launch failure";
         case GPTQ_EWORKSPACE: return "GPTQ_EWORKSPACE: workspace missing or too small";
+        case GPTQ_ESCRATCH:
+            return "GPTQ_ESCRATCH: problem larger than the fixed scratch of the no-allocation entry point "
+                   "(d_in above gptq_prepare_hinv_noalloc_max_din())";
         default: return "GPTQ: unknown status";
     }
 }
@@ -81,12 +96,14 @@ const char* gptq_kernel_name(int id) { return (id >= 0 && id < K_COUNT) ? kNames
 
 int gptq_timing_enable(int id) {
     if (id >= K_COUNT) return GPTQ_EINVAL;
+    std::lock_guard<std::mutex> lock(g_mu);
     g_timed = id < 0 ? -1 : id;
     return GPTQ_OK;
 }
 
 int gptq_timing_read(double* total_ms, int64_t* launches) {
     if (!total_ms || !launches) return GPTQ_EINVAL;
+    std::lock_guard<std::mutex> lock(g_mu);
     double tot = 0.0;
     int64_t cnt = 0;
     int rc = GPTQ_OK;
@@ -134,6 +151,22 @@ int gptq_prepare_hinv(const float* H, int64_t d_in, double damp_frac, float* U, 
     return hip_status(
         launch_prepare_hinv(H, d_in, damp_frac, U, dead, info, lambda_out, workspace, as_stream(stream)));
 }
+
+int gptq_prepare_hinv_noalloc(const float* H, int64_t d_in, double damp_frac, float* U, uint8_t* dead,
+                              int32_t* info, double* lambda_out, void* stream) {
+    if (d_in < 0 || !(damp_frac >= 0.0) || !isfinite(damp_frac)) return GPTQ_EINVAL;
+    if (d_in == 0) return GPTQ_OK;
+    if (!H || !U || !info) return GPTQ_EINVAL;
+    if (d_in > kNoAllocMaxDin) return GPTQ_ESCRATCH;
+    void* ws = nullptr;
+    const hipError_t e = hinv_noalloc_scratch(&ws);
+    if (e != hipSuccess) return GPTQ_EHIP;
+    if (hinv_noalloc_scratch_bytes() < hinv_workspace_bytes(d_in)) return GPTQ_ESCRATCH;
+    TimingOff no_events;
+    return hip_status(launch_prepare_hinv(H, d_in, damp_frac, U, dead, info, lambda_out, ws, as_stream(stream)));
+}
+
+int64_t gptq_prepare_hinv_noalloc_max_din(void) { return kNoAllocMaxDin; }
 
 size_t gptq_quantize_layer_workspace(int64_t d_out, int64_t d_in, int64_t block_size) {
     if (d_out <= 0 || d_in <= 0 || block_size <= 0) return 0;

@@ -18,6 +18,8 @@
 // off it reversed and rounded to float32.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -26,6 +28,7 @@ namespace gptq {
 namespace {
 
 constexpr int NB = kCholNB;  // 64
+constexpr int kMaxDevices = 64;
 constexpr int kGemmThreads = 256;
 // Steps are paired (every other update of the rest deferred, then applied
 // with the next step's as one 128-deep product) from this many 64-wide tiles
@@ -43,7 +46,19 @@ struct HinvWs {
     int* fail;      // device flag: set once a pivot fails
 };
 
-__host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+__host__ __device__ constexpr int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// Bytes of the factorization workspace for order n (layout in carve()).
+constexpr size_t ws_bytes(int64_t n) {
+    return (size_t)(round_up(round_up(n, NB) * round_up(n, NB) * 8, 256) + 3 * round_up(round_up(n, NB) * NB * 8, 256) +
+                    256 + 256);
+}
+
+// Fixed device scratch of gptq_prepare_hinv_noalloc, for callers that cannot
+// allocate: the workspace of the largest order it takes.  In host code the
+// name is only a stand-in; the device address comes from
+// hinv_noalloc_scratch() below.
+static __device__ __align__(256) unsigned char scratch[ws_bytes(kNoAllocMaxDin)];
 
 // G is stored by 64x64 tiles: tile (I, J) of the n_pad x n_pad matrix is
 // NB*NB contiguous doubles, row-major inside (row stride NB), so that every
@@ -1142,9 +1157,29 @@ __global__ __launch_bounds__(256) void store_u_kernel(const double* __restrict__
 
 }  // namespace
 
-size_t hinv_workspace_bytes(int64_t n) {
-    const int64_t np = round_up(n, NB);
-    return (size_t)(round_up(np * np * 8, 256) + 3 * round_up(np * NB * 8, 256) + 256 + 256);
+size_t hinv_workspace_bytes(int64_t n) { return ws_bytes(n); }
+
+size_t hinv_noalloc_scratch_bytes() { return sizeof(scratch); }
+
+// Device address of `scratch` on the current device, looked up once per
+// device (each device holds its own copy of the array at its own address).
+hipError_t hinv_noalloc_scratch(void** out) {
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
 }
 
 

@@ -37,6 +37,14 @@ struct TimedLaunch {
     hipStream_t stream;
 };
 
+// While alive, TimedLaunch records nothing on this thread (the timing hook
+// creates HIP events, which entry points that must not allocate avoid).
+struct TimingOff {
+    TimingOff();
+    ~TimingOff();
+    bool prev;
+};
+
 // ---- stage 1 ---------------------------------------------------------------
 hipError_t launch_hessian(float* H, int64_t n, const void* X, int x_is_f16, int64_t ntok,
                           int64_t ldx, hipStream_t s);
@@ -46,6 +54,11 @@ constexpr int kCholNB = 64;  // panel width of the blocked factorization
 size_t hinv_workspace_bytes(int64_t n);
 hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, float* U, uint8_t* dead,
                                int32_t* info, double* lambda_out, void* ws, hipStream_t s);
+// Largest order the no-allocation entry point takes, its fixed scratch size,
+// and the scratch's device address on the current device.
+constexpr int64_t kNoAllocMaxDin = 4096;
+size_t hinv_noalloc_scratch_bytes();
+hipError_t hinv_noalloc_scratch(void** out);
 
 // ---- stage 4 ---------------------------------------------------------------
 size_t quant_workspace_bytes(int64_t d_out, int64_t d_in, int64_t block);
