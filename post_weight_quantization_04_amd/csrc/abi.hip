@@ -65,6 +65,21 @@ TimedLaunch::~TimedLaunch() {
     (void)hipEventRecord(g_pending[slot].b, stream);
 }
 
+int device_cu_count() {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static int count[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (count[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        count[dev] = n;
+    }
+    return count[dev];
+}
+
 }  // namespace gptq
 
 using namespace gptq;

@@ -17,11 +17,13 @@
 // After the last step the lower triangle of G holds M = L^-1 and U is read
 // off it reversed and rounded to float32.
 #include <math.h>
+#include <stdlib.h>
 
 #include <mutex>
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "sched.hpp"
 
 namespace gptq {
 
@@ -31,12 +33,11 @@ constexpr int NB = kCholNB;  // 64
 constexpr int kMaxDevices = 64;
 constexpr int kGemmThreads = 256;
 // Steps are paired (every other update of the rest deferred, then applied
-// with the next step's as one 128-deep product) from this many 64-wide tiles
-// on.  Measured on MI355X: at d_in = 11008 (172 tiles) the factorization
-// takes 25.5 ms paired against 29.0 ms unpaired (its trailing-matrix traffic
-// dominates); at 4096 (64 tiles) 2.46 against 2.21 ms (the odd steps'
-// longer critical part dominates).
-constexpr int kPairMinTiles = 128;
+// with the next step's as one 128-deep product) from sched::kPairMinTiles
+// 64-wide tiles on.  Measured on MI355X: at d_in = 11008 (172 tiles) the
+// factorization takes 25.5 ms paired against 29.0 ms unpaired (its
+// trailing-matrix traffic dominates); at 4096 (64 tiles) 2.46 against
+// 2.21 ms (the odd steps' longer critical part dominates).
 constexpr int kLdsLd = NB + 8;   // padded LDS row (doubles)
 
 struct HinvWs {
@@ -1020,25 +1021,7 @@ __device__ __forceinline__ void diag_panel_next_body(DiagPanelNextLds& u, double
 
 // The rest of the update of step k: the blocks (i, j), j <= i, with
 // i > k+1 and j != k+1 (column and row block k+1 are updated inside the
-// diagonal-block workgroups of step k+1).  Of the T(T+1)/2 - (k+1)(k+2)/2
-// blocks below row k, T - k - 1 lie in column block k+1 and k + 1 in row
-// block k+1.
-__host__ __device__ inline int64_t rest_tiles(int k, int T) {
-    const int64_t all = (int64_t)T * (T + 1) / 2 - (int64_t)(k + 1) * (k + 2) / 2;
-    return (k + 1 < T) ? all - T : all;
-}
-
-__device__ __forceinline__ void rest_tile(int k, int64_t b, int64_t& i, int64_t& j) {
-    // rows i >= k+2 hold i blocks each (j in 0..i without k+1); rows before
-    // i contribute i(i-1)/2 - (k+1)(k+2)/2 blocks
-    const int64_t c0 = (int64_t)(k + 1) * (k + 2) / 2;
-    int64_t r = (int64_t)((1.0 + sqrt(1.0 + 8.0 * (double)(b + c0))) * 0.5);
-    while (r * (r - 1) / 2 - c0 > b) --r;
-    while ((r + 1) * r / 2 - c0 <= b) ++r;
-    i = r;
-    const int64_t jj = b - (r * (r - 1) / 2 - c0);
-    j = (jj < k + 1) ? jj : jj + 1;
-}
+// diagonal-block workgroups of step k+1), enumerated by sched::rest_tile.
 
 // Diagonal block and panel of step 0 (later steps run inside chol_step_kernel).
 __global__ __launch_bounds__(kGemmThreads, 2) void chol_diag_panel_kernel(double* __restrict__ G, int64_t np,
@@ -1121,7 +1104,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void chol_step_kernel(double* __re
         }
     } else {
         int64_t i, j;
-        rest_tile(k, (int64_t)(b - npan - 1), i, j);
+        sched::rest_tile(k, (int64_t)(b - npan - 1), i, j);
         if (kPair) trail_body2(u.gemm, G, np, Pk, Pkm, k, i, j);
         else trail_body(u.gemm, G, np, Pk, k, i, j);
     }
@@ -1207,7 +1190,7 @@ hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, floa
         hipLaunchKernelGGL(load_reversed_kernel, dim3((unsigned)((int64_t)T * (T + 1) / 2)), dim3(256), 0, s, H, n,
                            np, (const double*)w.scal, w.G);
     }
-    const int npan = std::max(T - 1, 1);  // workgroups of a diagonal-block + panel launch
+    const int npan = std::max(T - 1, 1);  // workgroups of the diagonal-block + panel launch of step 0
     {
         TimedLaunch t(K_CHOL_STEP, s);
         hipLaunchKernelGGL(chol_diag_panel_kernel, dim3((unsigned)npan), dim3(kGemmThreads), 0, s, w.G, np, Pbuf[0], T,
@@ -1215,12 +1198,15 @@ hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, floa
     }
     // wide layers pair the steps: an even step's update of the rest is
     // deferred and applied with the next step's as one 128-deep product
-    const bool paired = T >= kPairMinTiles;
+    // (GPTQ_SCHED_PAIR=1 pairs them at any width: a test override, never
+    // needed for correctness)
+    bool paired = sched::chol_paired(T);
+    if (const char* e = getenv("GPTQ_SCHED_PAIR")) paired = paired || atoi(e) == 1;
     for (int k = 0; k < T; ++k) {
-        const int np1 = (k + 1 < T) ? npan : 0;
+        const sched::CholLaunch g = sched::chol_launch(k, T, paired);
+        const int np1 = g.nchain;
         const bool odd = (k & 1) != 0;
-        const int64_t n_rest = (paired && !odd) ? 0 : rest_tiles(k, T);
-        const dim3 grid((unsigned)(np1 + 1 + n_rest));
+        const dim3 grid((unsigned)g.grid);
         double* pk1 = Pbuf[(k + 1) % 3];
         const double* pk = Pbuf[k % 3];
         const double* pkm = Pbuf[(k + 2) % 3];  // step k-1

@@ -45,6 +45,9 @@ struct TimingOff {
     bool prev;
 };
 
+// Compute units of the current device, queried once per device (0 on error).
+int device_cu_count();
+
 // ---- stage 1 ---------------------------------------------------------------
 hipError_t launch_hessian(float* H, int64_t n, const void* X, int x_is_f16, int64_t ntok,
                           int64_t ldx, hipStream_t s);

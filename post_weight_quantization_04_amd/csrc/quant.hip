@@ -3,23 +3,35 @@
 // compensation" and "GPTQ's speedups: fixed order and lazy batches"; math4ai
 // "GPTQ Hessian", column-sweep paragraph).
 //
-// Per lazy block [b0, b1):
-//   sweep_kernel   one workgroup per 64 rows (lane = row); wave q owns the 16
-//                  block columns b0+16q.. in registers.  In phase p wave p
+// One launch of step_kernel per lazy block [b0, b1), on the caller's stream:
+//   sweep part     workgroups 0 .. ceil(d_out/64)-1, 64 rows each (lane =
+//                  row), 512 threads; wave q owns the 16 block columns
+//                  b0+16q.. in registers.  The previous block's scaled errors
+//                  first reach these columns in registers (MFMA 16x16x4 f32
+//                  against that block's rows of U), then in phase p wave p
 //                  rounds its columns one by one and compensates the rest of
-//                  its sub-block at once; its scaled errors go to LDS and the
-//                  waves owning later columns fold them in at the start of
-//                  phase p+1 (the same OBS updates, grouped by sub-block).
-//                  U entries are uniform across the wave and come in through
-//                  scalar loads.
-//   trail_kernel   W[:, b1:] -= E U[b0:b1, b1:], 128x128 tiles on MFMA
-//                  32x32x2 f32 with fp32 accumulation.
+//                  its 16 at once; its scaled errors go to LDS and the waves
+//                  owning later columns fold them in on MFMA 16x16x4 f32 (the
+//                  same OBS updates, grouped by sub-block).  The block's rows
+//                  of U are staged in LDS as packed 16x16 upper sub-blocks.
+//   far part       the previous block's update of every column from b1 on,
+//                  W[:, b1:] -= E_prev U[prev block, b1:] on MFMA 32x32x2 f32
+//                  with fp32 accumulation, cut into 128-row x 64-column
+//                  units dealt to every CU as contiguous ranges
+//                  (sched::far_split); the sweeping workgroups take a smaller
+//                  share after their sweep.
+// trail_kernel runs only at the start of a group wider than the block: the
+// previous block's update of every column from the group on, so that the
+// group's grid sees the updated weights.
 #include <math.h>
 
 #include <algorithm>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
+#include "sched.hpp"
 
 namespace gptq {
 
@@ -746,9 +758,9 @@ __global__ __launch_bounds__(256) void trail_kernel(float* __restrict__ Wk, int6
 // ahead of the products.  The launch is one workgroup per CU (its LDS), so
 // the per-wave work is large and the registers plentiful.
 // ---------------------------------------------------------------------------
-constexpr int kRestRows = 128;
-constexpr int kRestCols = 256;
-constexpr int kStrip = 64;           // unit of the far-update partition: 128 rows x 64 columns
+constexpr int kRestRows = sched::kFarRows;
+constexpr int kRestCols = sched::kFarCols;
+constexpr int kStrip = sched::kFarStrip;  // unit of the far-update partition: 128 rows x 64 columns
 constexpr int kRUs = kRestCols + 4;  // U stage row stride
 
 __host__ __device__ inline size_t rest_lds_bytes() {
@@ -881,27 +893,17 @@ __device__ __forceinline__ void rest_body(unsigned char* smem, int64_t r0, int64
 // take `per_sweep` units each after their sweep, the far-only workgroups
 // share the rest evenly.  With one workgroup per CU every range starts at
 // once, so the launch ends when the longest range does.
-struct FarSplit {
-    int64_t c_begin;
-    int64_t n_units;
-    int nstrip;      // strips per row tile
-    int per_sweep;   // units of each sweeping workgroup
-    int q, r;        // far-only workgroups: q units each, the first r one more
-};
+using sched::FarSplit;
 
-__device__ __forceinline__ void far_range(unsigned char* smem, int64_t u0, int64_t u1, int64_t c_begin, int nstrip,
+__device__ __forceinline__ void far_range(unsigned char* smem, int64_t u0, int64_t u1, const FarSplit& fs,
                                           float* __restrict__ Wk, int64_t d_out, int64_t d_in,
                                           const float* __restrict__ E, int64_t ldE, const float* __restrict__ U,
                                           int64_t bp0, int kp, bool vec) {
     for (int64_t u = u0; u < u1;) {
-        const int64_t rt = u / nstrip;
-        const int st = (int)(u - rt * nstrip);
-        const int ns = (int)std::min<int64_t>(std::min(kRestCols / kStrip, nstrip - st), u1 - u);
-        const int64_t c0 = c_begin + (int64_t)st * kStrip;
-        const int64_t c_end = std::min<int64_t>(d_in, c0 + (int64_t)ns * kStrip);
+        const sched::FarSub t = sched::far_sub(fs, u, u1, d_in);
         __syncthreads();  // the LDS stages of the previous sub-tile (or the sweep) are free again
-        rest_body(smem, rt * kRestRows, c0, c_end, Wk, d_out, d_in, E, ldE, U, bp0, kp, vec);
-        u += ns;
+        rest_body(smem, t.rt * kRestRows, t.c0, t.c_end, Wk, d_out, d_in, E, ldE, U, bp0, kp, vec);
+        u += t.ns;
     }
 }
 
@@ -922,45 +924,37 @@ __global__ __launch_bounds__(512) void step_kernel(float* __restrict__ Wk, int64
                                                    FarSplit fs, int vec_rest) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int b = (int)blockIdx.x;
-    int64_t u0, u1;
-    if (b < row_tiles) {
+    if (b < row_tiles)
         sweep_body<kAllFull>(smem, b, Wk, d_out, d_in, U, rdiag, b0, b1, bits, group, ng, scales, zeros, minmax,
                              codes, E, ldE, err_row, Ep, bp0, kp);
-        u0 = std::min<int64_t>((int64_t)b * fs.per_sweep, fs.n_units);
-        u1 = std::min<int64_t>(u0 + fs.per_sweep, fs.n_units);
-    } else {
-        const int f = b - row_tiles;
-        u0 = (int64_t)row_tiles * fs.per_sweep + (int64_t)f * fs.q + std::min(f, fs.r);
-        u1 = u0 + fs.q + (f < fs.r ? 1 : 0);
-    }
-    if (u1 > u0) far_range(smem, u0, u1, fs.c_begin, fs.nstrip, Wk, d_out, d_in, Ep, ldE, U, bp0, kp, vec_rest != 0);
+    int64_t u0, u1;
+    sched::far_units(fs, b, row_tiles, u0, u1);
+    if (u1 > u0) far_range(smem, u0, u1, fs, Wk, d_out, d_in, Ep, ldE, U, bp0, kp, vec_rest != 0);
 }
 
-// Deal the far update's units (n_units in all) to the launch: every CU
-// holds one workgroup; the sweeping workgroups (n_sweep of them) are busy
-// for about kSweepUnits units' time first, so they take that much less.
-constexpr double kSweepUnits = 3.0;
+}  // namespace
 
-int far_split(int64_t n_units, int n_sweep, int n_cu, FarSplit& fs) {
-    fs.per_sweep = 0;
-    fs.q = fs.r = 0;
-    if (n_units <= 0) return 0;
-    const int n_far = std::max(0, n_cu - n_sweep);
-    if (n_far == 0) {  // more sweeping workgroups than CUs: they do it all
-        fs.per_sweep = (int)((n_units + n_sweep - 1) / n_sweep);
-        return 0;
-    }
-    const double t = ((double)n_units + n_sweep * kSweepUnits) / (double)(n_sweep + n_far);
-    fs.per_sweep = (int)std::max(0.0, std::floor(t - kSweepUnits));
-    const int64_t rest = n_units - (int64_t)n_sweep * fs.per_sweep;
-    const int nf = (int)std::min<int64_t>(n_far, rest);
-    if (nf > 0) {
-        fs.q = (int)(rest / nf);
-        fs.r = (int)(rest % nf);
-    }
-    return nf;
+namespace {
+// The step kernel's dynamic LDS limit, raised once per device to the largest
+// size asked for so far (the attribute is per device).
+hipError_t allow_step_lds(size_t bytes) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static size_t allowed[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (allowed[dev] >= bytes) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel<true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel<false>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) allowed[dev] = bytes;
+    return e;
 }
-
 }  // namespace
 
 size_t quant_workspace_bytes(int64_t d_out, int64_t d_in, int64_t block) {
@@ -1015,23 +1009,13 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
     const size_t near_bytes = (size_t)((bmax + 3) & ~3) * kEtl * 4;
     const size_t ldsmax = std::max(sweep_lds_bytes(bmax) + near_bytes, rest_lds_bytes());
     if (ldsmax > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel<true>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsmax);
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel<false>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)ldsmax);
+        hipError_t e = allow_step_lds(ldsmax);
         if (e != hipSuccess) return e;
     }
     const int row_tiles = (int)((d_out + kRowsPerWg - 1) / kRowsPerWg);
     const int rest_rows = (int)((d_out + kRestRows - 1) / kRestRows);
-    int n_cu = 0;
-    {
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        n_cu = std::max(n_cu, 1);
-    }
+    const int n_cu = device_cu_count();
+    if (n_cu <= 0) return hipErrorInvalidDevice;
     hipError_t err = hipSuccess;
     // One launch per lazy block on the caller's stream: the sweep of block b
     // (its columns first receive block b-1's update, in registers) and, in
@@ -1068,8 +1052,7 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
         fs.c_begin = b1;
         fs.nstrip = (int)((d_in - b1 + kStrip - 1) / kStrip);
         const int64_t n_units = (kp > 0 && b1 < d_in) ? (int64_t)rest_rows * fs.nstrip : 0;
-        fs.n_units = n_units;
-        const int n_far = far_split(n_units, row_tiles, n_cu, fs);
+        const int n_far = sched::far_split(n_units, row_tiles, n_cu, fs);
         size_t lds = sweep_lds_bytes(bw) + (kp > 0 ? (size_t)((kp + 3) & ~3) * kEtl * 4 : 0);
         if (n_units > 0) lds = std::max(lds, rest_lds_bytes());
         TimedLaunch t(K_Q_STEP, s);

@@ -10,7 +10,10 @@ those other blocks is deferred and applied in the next launch together with
 the odd step's, and the odd launch's diagonal-block workgroups apply both
 steps.  Step s's panel lives in buffer s % 3.
 
-This replays that schedule block by block in numpy (every launch reads the
+Who does what in each launch comes from the schedule code the kernels and
+the launcher use (csrc/sched.hpp, built for the host by tests/sched_lib.py):
+the launch geometry and the tile of each rest workgroup.  This replays that
+schedule block by block in numpy (every launch reads the
 state as it was when the launch started, as the device's workgroups do) with
 small blocks, and checks the result against the inverse of numpy's Cholesky
 factor: a block missed, applied twice, read from the wrong panel buffer or
@@ -21,6 +24,8 @@ U = J L^-1 J.
 """
 import numpy as np
 import pytest
+
+import sched_lib
 
 
 def _inv_chol(D):
@@ -78,11 +83,16 @@ def replay(Gfull, nb, paired):
                 else:
                     Pk1[t + 1] = c2[t] @ Mk1.T
         writes[k, k] = Pk[0].copy()
-        if not (paired and not odd):
-            for i in range(k + 2, T):
-                for j in range(i + 1):
-                    if j == k1:
-                        continue
+        g = sched_lib.chol_geom(k, T, paired)
+        assert g["nchain"] == (max(T - 1, 1) if k1 < T else 0)
+        assert g["grid"] == g["nchain"] + 1 + g["n_rest"]
+        assert g["n_rest"] == (0 if (paired and not odd) else sched_lib.chol_rest_tiles(k, T))
+        rest = [sched_lib.chol_rest_tile(k, b) for b in range(g["n_rest"])]
+        assert len(set(rest)) == len(rest)
+        for i, j in rest:
+            assert k + 2 <= i < T and 0 <= j <= i and j != k1
+            if True:
+                if True:
                     if not pair:
                         if j < k:
                             writes[i, j] = old[i, j] - Pk[i] @ old[k, j]
@@ -107,7 +117,7 @@ def replay(Gfull, nb, paired):
 
 
 @pytest.mark.parametrize("paired", [False, True])
-@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8, 9])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8, 9, 13])
 def test_schedule_builds_inverse_cholesky_factor(T, paired):
     nb = 3
     n = T * nb
@@ -131,3 +141,32 @@ def test_schedule_gives_u_of_the_inverse():
     U = J @ Minv @ J
     assert np.allclose(np.tril(U, -1), 0.0)
     assert np.allclose(U.T @ U, np.linalg.inv(H), rtol=1e-9, atol=1e-12)
+
+
+@pytest.mark.parametrize("T", [64, 172, 129, 2048])
+def test_launch_geometry_at_layer_widths(T):
+    """Every launch at the widths the layers use: the rest items of step k
+    are exactly the lower tiles below row k+1 outside column and row block
+    k+1 (or none, for a deferred even step), in the row-major order."""
+    paired = bool(sched_lib.load().chol_paired_default(T))
+    assert paired == (T >= 128)
+    for k in range(T):
+        g = sched_lib.chol_geom(k, T, paired)
+        n = g["n_rest"]
+        if paired and k % 2 == 0:
+            assert n == 0
+            continue
+        # row i >= k+2 holds i items (columns 0..i without k+1)
+        assert n == sum(range(k + 2, T))
+        for b in {0, n // 3, n // 2, n - 1} if n else ():
+            i, j = sched_lib.chol_rest_tile(k, b)
+            assert k + 2 <= i < T and 0 <= j <= i and j != k + 1
+            assert b == sum(range(k + 2, i)) + (j if j < k + 1 else j - 1)
+
+
+def test_rest_tile_enumeration_is_row_major():
+    for T in (5, 17, 64):
+        for k in range(T):
+            want = [(i, j) for i in range(k + 2, T) for j in range(i + 1) if j != k + 1]
+            got = [sched_lib.chol_rest_tile(k, b) for b in range(sched_lib.chol_rest_tiles(k, T))]
+            assert got == want

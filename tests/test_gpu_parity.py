@@ -107,6 +107,28 @@ def test_prepare(lib, n, N, dead):
     assert host(f.lam)[0] == pytest.approx(lam_ref, rel=1e-12)
 
 
+@pytest.mark.parametrize("n,N,dead", [
+    (333, 700, (5, 6, 300)),     # 6 tiles, ragged last tile
+    (640, 1200, (7,)),           # 10 tiles
+    (200, 150, ()),              # 4 tiles, rank-deficient X
+])
+def test_prepare_paired_steps(lib, monkeypatch, n, N, dead):
+    """Steps paired at widths that would not pair them (GPTQ_SCHED_PAIR=1):
+    every even step's update of the rest deferred into the next launch, the
+    odd launches' diagonal-block workgroups applying both steps; U the same
+    within the bar."""
+    from post_weight_quantization_04_amd import layer
+    say("prepare paired steps", n, N, dead)
+    monkeypatch.setenv("GPTQ_SCHED_PAIR", "1")
+    _, X = _problem(1, n, N, seed=7 * n + N, dead=dead)
+    H32 = np.tril(oracle.hessian([X])).astype(F32)
+    f = layer.prepare(dev(H32), 0.01)
+    _torch().cuda.synchronize()
+    assert int(host(f.info)[0]) == 0
+    e, U_ref, dead_ref, lam_ref = parity.check_u(host(f.U), H32, 0.01)
+    np.testing.assert_array_equal(host(f.dead).astype(bool), dead_ref)
+
+
 def test_prepare_not_positive_definite(lib):
     from post_weight_quantization_04_amd import layer
     say("prepare non-PD")
