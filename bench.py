@@ -23,7 +23,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "ms per 4096×4096 4-bit GPTQ layer (XXᵀ+Cholesky+sweep); % MFMA/HBM peak"
-PEAK_TFLOPS = {"f16": 2500.0, "f32": 157.3, "f64": 78.6}
+# bf16x3: an fp32 product formed from six bf16 piece products on the 2.5 PF
+# bf16 MFMA peak, i.e. 2500 / 6 TFLOP/s of fp32-equivalent products
+PEAK_TFLOPS = {"f16": 2500.0, "f32": 157.3, "f64": 78.6, "bf16x3": 2500.0 / 6}
 PEAK_HBM_GBS = 8000.0
 PEAK_FP64_VALU = 78.6  # TFLOP/s, MI355X fp64 vector (256 CUs at 2.4 GHz)
 NB = 64  # panel width of the blocked factorization (kCholNB in the library)
@@ -226,7 +228,8 @@ def block_bench(args, wl, torch, wlm, _lib, layer) -> int:
         fac[xs.key] = layer.prepare(H[xs.key].fill_diagonal_(1.0), wl.damp, ws=ws[xs.key])
     Ws = [torch.from_numpy(wlm.make_weight(wl, li)).to(dev) for li in range(len(wl.layers))]
     wsq = layer.Workspace(dev)
-    outs = [layer.quantize(Ws[li], fac[sp.x_key], wl.bits, wl.group_size, wl.block_size, ws=wsq)
+    split = args.trailing == "split"
+    outs = [layer.quantize(Ws[li], fac[sp.x_key], wl.bits, wl.group_size, wl.block_size, ws=wsq, split=split)
             for li, sp in enumerate(wl.layers)]
     stream = torch.cuda.current_stream()
     chunk = {xs.key: xs.chunk for xs in wl.xs}
@@ -247,7 +250,8 @@ def block_bench(args, wl, torch, wlm, _lib, layer) -> int:
         for li, sp in enumerate(wl.layers):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            layer.quantize(Ws[li], fac[sp.x_key], wl.bits, wl.group_size, wl.block_size, ws=wsq, out=outs[li])
+            layer.quantize(Ws[li], fac[sp.x_key], wl.bits, wl.group_size, wl.block_size, ws=wsq, out=outs[li],
+                           split=split)
             b.record(stream)
             lev.append((sp.name, a, b))
         if times is not None:
@@ -285,7 +289,8 @@ def block_bench(args, wl, torch, wlm, _lib, layer) -> int:
                   f"activation set)",
         "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": steps, "warmup": 1, "ms_per_step": round(ms, 3),
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f16-mfma H / f64-mfma U / f32 sweep", "data": "synthetic (seeded; see workloads/)",
+        "dtype": "f16-mfma H / f64-mfma U / f32 sweep" + (" / bf16x3-mfma trailing update" if split else ""),
+        "data": "synthetic (seeded; see workloads/)",
         "config": {"workload": wl.name, "bits": wl.bits, "group_size": wl.group_size, "block_size": wl.block_size,
                    "damp": wl.damp},
         "activation_sets": per_set, "layers": per_layer,
@@ -300,6 +305,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="attn_proj")
+    ap.add_argument("--trailing", choices=("split", "fp32"), default="split",
+                    help="products of the lazy trailing update: bf16 pieces (gptq_quantize_layer_split) or fp32 MFMA")
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-breakdown", action="store_true")
@@ -331,6 +338,9 @@ def main(argv=None) -> int:
         return 2
 
     wl = wlm.get(args.workload)
+    split = args.trailing == "split"
+    if split:
+        KERNEL_CLASS["q_step"] = ("bf16x3", "mfma")
     if len(wl.layers) != 1:
         return block_bench(args, wl, torch, wlm, _lib, layer)
     spec = wl.layers[0]
@@ -346,7 +356,7 @@ def main(argv=None) -> int:
     H = torch.zeros((d_in, d_in), dtype=torch.float32, device=dev)
     ws1, ws2 = layer.Workspace(dev), layer.Workspace(dev)
     fac = layer.prepare(H.fill_(0).fill_diagonal_(1.0), wl.damp, ws=ws1)
-    qout = layer.quantize(Wd, fac, wl.bits, wl.group_size, wl.block_size, ws=ws2)
+    qout = layer.quantize(Wd, fac, wl.bits, wl.group_size, wl.block_size, ws=ws2, split=split)
     chunk = xs.chunk
     stream = torch.cuda.current_stream()
 
@@ -358,8 +368,8 @@ def main(argv=None) -> int:
     def stage_u():
         layer.prepare(H, wl.damp, ws=ws1, out=fac)
 
-    def stage_q():
-        layer.quantize(Wd, fac, wl.bits, wl.group_size, wl.block_size, ws=ws2, out=qout)
+    def stage_q(split=split):
+        layer.quantize(Wd, fac, wl.bits, wl.group_size, wl.block_size, ws=ws2, out=qout, split=split)
 
     def step():
         stage_h()
@@ -535,6 +545,21 @@ def main(argv=None) -> int:
                                "shape": f"Y[{d_out}x{Xd.shape[1]}] = relu(What[{d_out}x{d_in}] X)"}
         after["output_error_sum"] = float(oe.sum().item())
 
+    # the quantize stage with the other precision of the trailing update, for
+    # comparison (after the timed region)
+    other = {}
+    stage_q(split=not split)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(5):
+        stage_q(split=not split)
+    b.record(stream)
+    torch.cuda.synchronize()
+    other["quantize_layer_" + ("fp32" if split else "split") + "_ms"] = round(a.elapsed_time(b) / 5, 4)
+    stage_q()
+    torch.cuda.synchronize()
+
     greedy = None
     if not args.no_greedy:
         greedy = greedy_variant(torch, wlm, _lib, layer)
@@ -556,11 +581,13 @@ def main(argv=None) -> int:
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16-mfma H / f64-mfma U / f32 sweep",
+        "dtype": "f16-mfma H / f64-mfma U / f32 sweep" + (" / bf16x3-mfma trailing update" if split else ""),
         "data": "synthetic (seeded; see workloads/)",
         "config": {"workload": wl.name, "d_out": d_out, "d_in": d_in, "n_tokens": n_tok, "bits": wl.bits,
                    "group_size": wl.group_size, "block_size": wl.block_size, "damp": wl.damp,
-                   "w_dtype": spec.dtype, "x_dtype": xs.dtype, "token_chunk": chunk},
+                   "w_dtype": spec.dtype, "x_dtype": xs.dtype, "token_chunk": chunk,
+                   "trailing_update": "bf16x3" if split else "fp32"},
+        "other_precision": other,
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "kernels_ms_per_step": {k: round(v, 4) for k, v in sorted(kernel_ms.items(), key=lambda kv: -kv[1])},
         "kernel_launches_per_step": kernel_launches,

@@ -191,6 +191,29 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in,
                         float* minmax, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gptq_quantize_layer with the lazy trailing update's products in split
+ * precision (aicassindra "GPTQ's speedups: fixed order and lazy batches":
+ * the batched update is the dense product that carries the arithmetic).
+ * For W[:, b1:] -= E U[b0:b1, b1:] each fp32 operand is written as the sum
+ * of three bf16 pieces, x = x0 + x1 + x2 (x0 the nearest bf16 to x, x1 that
+ * of x - x0, x2 that of x - x0 - x1), and the product is formed from the six
+ * piece products with i + j <= 2 on bf16 MFMA with fp32 accumulation: every
+ * piece product is exact in fp32 and the three left out are below 2^-26 of
+ * |e u|, so the update carries fp32-level error at the bf16 MFMA rate.  The
+ * in-block sweep, the grids and everything else are as in
+ * gptq_quantize_layer; arguments, outputs and errors are the same, except
+ * that the workspace must hold gptq_quantize_layer_split_workspace() bytes:
+ * it also keeps the bf16 pieces of U, written once per call,
+ * 6 ceil(d_in/block_size) d_in ceil(block_size/16)*16 bytes (100 MB at
+ * d_in = 4096, block 128).
+ */
+size_t gptq_quantize_layer_split_workspace(int64_t d_out, int64_t d_in, int64_t block_size);
+int gptq_quantize_layer_split(const void* W, int w_dtype, int64_t d_out, int64_t d_in, const float* U,
+                              const uint8_t* dead, int bits, int64_t group_size, int64_t block_size,
+                              uint8_t* codes, float* scales, int32_t* zeros, float* err_row, float* minmax,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Few-bit storage of the codes (aicassindra.com "tm_gptq_math",
  * "Post-training quantization and the per-layer objective": weights go from
  * 16-bit floats to low-bit integers, 4-bit being the example given; the

@@ -24,7 +24,9 @@ EXPORTS = (
     "gptq_prepare_hinv_noalloc",
     "gptq_prepare_hinv_noalloc_max_din",
     "gptq_quantize_layer_workspace",
+    "gptq_quantize_layer_split_workspace",
     "gptq_quantize_layer",
+    "gptq_quantize_layer_split",
     "gptq_status_string",
     "gptq_packed_words",
     "gptq_pack_codes",
@@ -67,8 +69,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "gptq_prepare_hinv_noalloc": (_i32, [_vp, _i64, ctypes.c_double, _vp, _vp, _vp, _vp, _vp]),
         "gptq_prepare_hinv_noalloc_max_din": (_i64, []),
         "gptq_quantize_layer_workspace": (_sz, [_i64, _i64, _i64]),
+        "gptq_quantize_layer_split_workspace": (_sz, [_i64, _i64, _i64]),
         "gptq_quantize_layer": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _sz, _vp]),
+        "gptq_quantize_layer_split": (_i32, [_vp, _i32, _i64, _i64, _vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp,
+                                             _vp, _vp, _sz, _vp]),
         "gptq_status_string": (ctypes.c_char_p, [_i32]),
         "gptq_packed_words": (_i64, [_i64, _i32]),
         "gptq_pack_codes": (_i32, [_vp, _i64, _i64, _i32, _vp, _vp]),
@@ -169,19 +174,23 @@ def prepare_hinv_noalloc_max_din() -> int:
     return int(load().gptq_prepare_hinv_noalloc_max_din())
 
 
-def quantize_layer_workspace(d_out: int, d_in: int, block_size: int) -> int:
-    return int(load().gptq_quantize_layer_workspace(d_out, d_in, block_size))
+def quantize_layer_workspace(d_out: int, d_in: int, block_size: int, split: bool = False) -> int:
+    name = "gptq_quantize_layer_split_workspace" if split else "gptq_quantize_layer_workspace"
+    return int(getattr(load(), name)(d_out, d_in, block_size))
 
 
 def quantize_layer(W, U, dead, bits: int, group_size: int, block_size: int, codes, scales, zeros,
-                   err_row=None, minmax=None, workspace=None, stream=None) -> None:
+                   err_row=None, minmax=None, workspace=None, stream=None, split: bool = False) -> None:
+    """``gptq_quantize_layer``, or ``gptq_quantize_layer_split`` (the lazy
+    trailing update on split-precision bf16 products) with ``split``."""
     d_out, d_in = W.shape
-    rc = load().gptq_quantize_layer(_ptr(W), _dtype_code(W), d_out, d_in, _ptr(U), _ptr(dead), int(bits),
-                                    int(group_size), int(block_size), _ptr(codes), _ptr(scales), _ptr(zeros),
-                                    _ptr(err_row), _ptr(minmax), _ptr(workspace),
-                                    workspace.numel() * workspace.element_size() if workspace is not None else 0,
-                                    _stream(stream))
-    _check("gptq_quantize_layer", rc)
+    name = "gptq_quantize_layer_split" if split else "gptq_quantize_layer"
+    rc = getattr(load(), name)(_ptr(W), _dtype_code(W), d_out, d_in, _ptr(U), _ptr(dead), int(bits),
+                               int(group_size), int(block_size), _ptr(codes), _ptr(scales), _ptr(zeros),
+                               _ptr(err_row), _ptr(minmax), _ptr(workspace),
+                               workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                               _stream(stream))
+    _check(name, rc)
 
 
 # ---------------------------------------------------------------------------

@@ -18,7 +18,7 @@ namespace gptq {
 namespace {
 const char* const kNames[K_COUNT] = {
     "hessian_f16", "hessian_f32", "hinv_diag_stats", "hinv_load_reversed", "chol_step", "hinv_store_u",
-    "q_grid_convert",         "q_group_grid",       "q_step",    "q_trail",
+    "q_grid_convert",         "q_group_grid",       "q_step",    "q_trail",  "q_split_u",
     "pack_codes",  "dequantize",  "output_error", "obq_hinv", "obq_rows", "propagate",
 };
 // The timing state is process-wide; the mutex makes concurrent entry-point
@@ -185,13 +185,18 @@ int64_t gptq_prepare_hinv_noalloc_max_din(void) { return kNoAllocMaxDin; }
 
 size_t gptq_quantize_layer_workspace(int64_t d_out, int64_t d_in, int64_t block_size) {
     if (d_out <= 0 || d_in <= 0 || block_size <= 0) return 0;
-    return quant_workspace_bytes(d_out, d_in, block_size);
+    return quant_workspace_bytes(d_out, d_in, block_size, 0);
 }
 
-int gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in, const float* U,
-                        const uint8_t* dead, int bits, int64_t group_size, int64_t block_size, uint8_t* codes,
-                        float* scales, int32_t* zeros, float* err_row, float* minmax, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+size_t gptq_quantize_layer_split_workspace(int64_t d_out, int64_t d_in, int64_t block_size) {
+    if (d_out <= 0 || d_in <= 0 || block_size <= 0) return 0;
+    return quant_workspace_bytes(d_out, d_in, block_size, 1);
+}
+
+namespace {
+int quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in, const float* U, const uint8_t* dead,
+                   int bits, int64_t group_size, int64_t block_size, uint8_t* codes, float* scales, int32_t* zeros,
+                   float* err_row, float* minmax, void* workspace, size_t workspace_bytes, int split, void* stream) {
     if (d_out < 0 || d_in < 0) return GPTQ_EINVAL;
     if (w_dtype != GPTQ_F16 && w_dtype != GPTQ_F32) return GPTQ_EINVAL;
     if (bits < 2 || bits > 8) return GPTQ_EINVAL;
@@ -205,11 +210,29 @@ int gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in,
     if (d_out == 0 || d_in == 0) return GPTQ_OK;
     if (!W || !U || !codes || !scales || !zeros) return GPTQ_EINVAL;
     if (d_out > ((int64_t)1 << 24) || d_in > ((int64_t)1 << 20)) return GPTQ_EUNSUPPORTED;
-    if (!workspace || workspace_bytes < quant_workspace_bytes(d_out, d_in, block_size) ||
+    if (!workspace || workspace_bytes < quant_workspace_bytes(d_out, d_in, block_size, split) ||
         reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
         return GPTQ_EWORKSPACE;
     return hip_status(launch_quantize(W, w_dtype == GPTQ_F16, d_out, d_in, U, dead, bits, group_size, block_size,
-                                      codes, scales, zeros, err_row, minmax, workspace, as_stream(stream)));
+                                      codes, scales, zeros, err_row, minmax, workspace, split,
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+int gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in, const float* U,
+                        const uint8_t* dead, int bits, int64_t group_size, int64_t block_size, uint8_t* codes,
+                        float* scales, int32_t* zeros, float* err_row, float* minmax, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    return quantize_layer(W, w_dtype, d_out, d_in, U, dead, bits, group_size, block_size, codes, scales, zeros,
+                          err_row, minmax, workspace, workspace_bytes, 0, stream);
+}
+
+int gptq_quantize_layer_split(const void* W, int w_dtype, int64_t d_out, int64_t d_in, const float* U,
+                              const uint8_t* dead, int bits, int64_t group_size, int64_t block_size, uint8_t* codes,
+                              float* scales, int32_t* zeros, float* err_row, float* minmax, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    return quantize_layer(W, w_dtype, d_out, d_in, U, dead, bits, group_size, block_size, codes, scales, zeros,
+                          err_row, minmax, workspace, workspace_bytes, 1, stream);
 }
 
 size_t gptq_obq_workspace(int64_t d_in) {

@@ -19,6 +19,7 @@ enum KernelId {
     K_Q_GROUPGRID,
     K_Q_STEP,
     K_Q_TRAIL,
+    K_Q_SPLITU,
     K_PACK,
     K_DEQUANT,
     K_OUTERR,
@@ -64,11 +65,11 @@ size_t hinv_noalloc_scratch_bytes();
 hipError_t hinv_noalloc_scratch(void** out);
 
 // ---- stage 4 ---------------------------------------------------------------
-size_t quant_workspace_bytes(int64_t d_out, int64_t d_in, int64_t block);
+size_t quant_workspace_bytes(int64_t d_out, int64_t d_in, int64_t block, int split);
 hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d_in, const float* U,
                            const uint8_t* dead, int bits, int64_t group, int64_t block,
                            uint8_t* codes, float* scales, int32_t* zeros, float* err_row,
-                           float* minmax, void* ws, hipStream_t s);
+                           float* minmax, void* ws, int split, hipStream_t s);
 
 // ---- few-bit storage, dequantization, output error ---------------------------
 int64_t packed_words(int64_t d_in, int bits);

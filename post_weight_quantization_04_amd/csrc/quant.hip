@@ -48,7 +48,14 @@ struct QuantWs {
     float* Wk;     // [d_out, d_in] working weights
     float* E[2];   // [d_out, block] scaled errors, alternating between blocks
     float* rdiag;  // [d_in] 1 / U_jj
+    __bf16* U3;    // split path: bf16 pieces of U by lazy block, [nb][3][d_in][ldk]
 };
+
+// k extent of one block's U pieces (whole 16-deep chunks)
+__host__ __device__ inline int64_t split_ldk(int64_t block) { return (block + 15) / 16 * 16; }
+__host__ __device__ inline int64_t split_u_elems(int64_t d_in, int64_t block) {
+    return ((d_in + block - 1) / block) * 3 * d_in * split_ldk(block);
+}
 
 QuantWs carve(void* ws, int64_t d_out, int64_t d_in, int64_t block) {
     char* p = static_cast<char*>(ws);
@@ -60,7 +67,73 @@ QuantWs carve(void* ws, int64_t d_out, int64_t d_in, int64_t block) {
         p += rup(d_out * block * 4, 256);
     }
     w.rdiag = reinterpret_cast<float*>(p);
+    p += rup(d_in * 4, 256);
+    w.U3 = reinterpret_cast<__bf16*>(p);
     return w;
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __bf16 bf16_rne(float x) {
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return __builtin_bit_cast(__bf16, (uint16_t)(u >> 16));
+}
+__device__ __forceinline__ float bf16_f(__bf16 h) {
+    return __builtin_bit_cast(float, (uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+// x = p0 + p1 + p2 to within 2^-27 |x|: p0 the nearest bf16 to x, p1 that of
+// x - p0, p2 that of x - p0 - p1 (both differences exact in fp32)
+__device__ __forceinline__ void split3(float x, __bf16& p0, __bf16& p1, __bf16& p2) {
+    p0 = bf16_rne(x);
+    const float r1 = x - bf16_f(p0);
+    p1 = bf16_rne(r1);
+    p2 = bf16_rne(r1 - bf16_f(p1));
+}
+
+// The bf16 pieces of U for the split trailing update, written once per
+// layer: U3[b][p][c][kk] = piece p of U[b*block + kk][c] (kk < ldk, zero
+// past the block), so that a block's rows of U reach the MFMA B operand as
+// 16-byte reads along k.  Block b's rows are read only by the update after
+// block b+1, for the columns from (b+2)*block on, so only those are written
+// (the rest of U3 is never read).  One workgroup per (64 columns, block):
+// the 64-column slab of the block's rows is read along rows and transposed
+// through LDS.
+__global__ __launch_bounds__(256) void split_u_kernel(const float* __restrict__ U, int64_t d_in, int64_t block,
+                                                      int64_t ldk, __bf16* __restrict__ U3) {
+    __shared__ float T[128][65];
+    const int64_t b = blockIdx.y;
+    const int64_t c0 = (int64_t)blockIdx.x * 64;
+    if (c0 + 64 <= (b + 2) * block) return;  // columns this block's pieces are never read for
+    const int64_t k0 = b * block;
+    const int kb = (int)min(block, d_in - k0);
+    const int tid = threadIdx.x;
+    for (int e = tid; e < 128 * 64; e += 256) {
+        const int kk = e >> 6, cc = e & 63;
+        const int64_t c = c0 + cc;
+        T[kk][cc] = (kk < kb && c < d_in) ? U[(k0 + kk) * d_in + c] : 0.0f;
+    }
+    __syncthreads();
+    __bf16* out = U3 + b * 3 * d_in * ldk;
+    const int groups = (int)(ldk / 8);
+    for (int e = tid; e < 64 * groups; e += 256) {
+        const int cc = e / groups, g = e % groups;
+        const int64_t c = c0 + cc;
+        if (c >= d_in) continue;
+        bf16x8 p[3];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            __bf16 h0, h1, h2;
+            split3(T[8 * g + x][cc], h0, h1, h2);
+            p[0][x] = h0;
+            p[1][x] = h1;
+            p[2][x] = h2;
+        }
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            *reinterpret_cast<bf16x8*>(&out[(q * d_in + c) * ldk + 8 * g]) = p[q];
+    }
 }
 
 template <typename T>
@@ -887,6 +960,175 @@ __device__ __forceinline__ void rest_body(unsigned char* smem, int64_t r0, int64
         }
 }
 
+// ---------------------------------------------------------------------------
+// The same far update with split-precision products: each fp32 operand is
+// the sum of three bf16 pieces, x = x0 + x1 + x2 (x0 = bf16(x) to nearest
+// even, x1 = bf16(x - x0), x2 = bf16(x - x0 - x1); both differences are
+// exact in fp32), and E U is formed from the six piece products with
+// i + j <= 2 on MFMA 32x32x16 bf16 (each product exact in fp32, fp32
+// accumulation).  The three dropped products are below 2^-26 of |e u|; the
+// piece products take 6 bf16 MFMAs (192 cycles) where fp32 MFMA 32x32x2
+// takes 8 (512 cycles) per 16-deep step.  K in chunks of 16 through two LDS
+// buffers: E pieces row-major by k, U pieces transposed (column-major by k)
+// so that both MFMA operands are 16-byte reads along k.
+// ---------------------------------------------------------------------------
+constexpr int kSK = 16;           // K per chunk
+constexpr int kSLd = kSK + 8;     // padded LDS row of a piece stage (bf16)
+constexpr int kSEPiece = kRestRows * kSLd;  // one E piece of one buffer (bf16)
+constexpr int kSUPiece = kRestCols * kSLd;  // one U piece of one buffer (bf16)
+constexpr int kSBuf = 3 * (kSEPiece + kSUPiece);
+
+__host__ __device__ inline size_t rest_split_lds_bytes() { return (size_t)2 * kSBuf * 2; }
+
+
+// chunk operands: E rows r0 + tid/4, k kc + 4(tid%4) .. +4 (split here);
+// the U pieces of column c0 + tid%256, k kc + 8(tid/256) .. +8, already
+// split (U3b: the previous block's pieces, [3][d_in][ldk]).  Columns past
+// c_end load column c0 (their products are never stored).
+__device__ __forceinline__ void rest_split_fetch(float (&e)[4], bf16x8 (&u)[3], const float* __restrict__ E,
+                                                 int64_t ldE, const __bf16* __restrict__ U3b, int64_t ldk,
+                                                 int64_t d_out, int64_t d_in, int64_t r0, int64_t c0, int64_t c_end,
+                                                 int kp, int kc, int tid, bool vec) {
+    {
+        const int64_t R = r0 + (tid >> 2);
+        const int k = kc + (tid & 3) * 4;
+        const float* src = E + R * ldE + k;
+        if (vec && R < d_out && k + 4 <= kp) {
+            *reinterpret_cast<float4v*>(&e[0]) = *reinterpret_cast<const float4v*>(src);
+        } else {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) e[x] = (R < d_out && k + x < kp) ? src[x] : 0.0f;
+        }
+    }
+    {
+        int64_t col = c0 + (tid & 255);
+        if (col >= c_end) col = c0;
+        const int k = kc + (tid >> 8) * 8;
+        const __bf16* src = U3b + col * ldk + k;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) u[q] = *reinterpret_cast<const bf16x8*>(src + q * d_in * ldk);
+    }
+}
+
+__device__ __forceinline__ void rest_split_stash(const float (&e)[4], const bf16x8 (&u)[3], __bf16* __restrict__ S,
+                                                 int tid) {
+    {
+        bf16x4 p[3];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            __bf16 h0, h1, h2;
+            split3(e[x], h0, h1, h2);
+            p[0][x] = h0;
+            p[1][x] = h1;
+            p[2][x] = h2;
+        }
+        const int off = (tid >> 2) * kSLd + (tid & 3) * 4;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) *reinterpret_cast<bf16x4*>(&S[q * kSEPiece + off]) = p[q];
+    }
+    {
+        const int off = 3 * kSEPiece + (tid & 255) * kSLd + (tid >> 8) * 8;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) *reinterpret_cast<bf16x8*>(&S[off + q * kSUPiece]) = u[q];
+    }
+}
+
+__device__ __forceinline__ float16v mfma32x32x16_bf16(bf16x8 a, bf16x8 b, float16v c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int NQ>
+__device__ __forceinline__ void rest_split_chunk(const __bf16* S, int wi, int colw, int lane, float16v (&acc)[4]) {
+    const int kk = 8 * (lane >> 5);
+    bf16x8 a[3], b[3][NQ];
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+        a[p] = *reinterpret_cast<const bf16x8*>(&S[p * kSEPiece + (wi * 32 + (lane & 31)) * kSLd + kk]);
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            b[p][q] = *reinterpret_cast<const bf16x8*>(
+                &S[3 * kSEPiece + p * kSUPiece + (colw + 32 * q + (lane & 31)) * kSLd + kk]);
+    // the smaller piece products first
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) acc[q] = mfma32x32x16_bf16(a[2], b[0][q], acc[q]);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) acc[q] = mfma32x32x16_bf16(a[1], b[1][q], acc[q]);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) acc[q] = mfma32x32x16_bf16(a[0], b[2][q], acc[q]);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) acc[q] = mfma32x32x16_bf16(a[1], b[0][q], acc[q]);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) acc[q] = mfma32x32x16_bf16(a[0], b[1][q], acc[q]);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) acc[q] = mfma32x32x16_bf16(a[0], b[0][q], acc[q]);
+}
+
+__device__ __forceinline__ void rest_split_body(unsigned char* smem, int64_t r0, int64_t c0, int64_t c_end,
+                                                float* __restrict__ Wk, int64_t d_out, int64_t d_in,
+                                                const float* __restrict__ E, int64_t ldE,
+                                                const __bf16* __restrict__ U3b, int64_t ldk, int kp, bool vec) {
+    __bf16* S0 = reinterpret_cast<__bf16*>(smem);  // [2][kSBuf]
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wi = w >> 1, wj = w & 1;
+    const int nchunks = (kp + kSK - 1) / kSK;
+    const int ns = (int)((c_end - c0 + kStrip - 1) / kStrip);
+    const int colw = wj * ns * 32;
+    const int64_t cw = c0 + colw;
+    const int nq = (int)std::min<int64_t>(ns, std::max<int64_t>(0, (c_end - cw + 31) / 32));
+    const bool inner = (r0 + kRestRows <= d_out) && (cw + 32 * nq <= c_end);
+
+    float16v acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = (float16v){};
+    float e[4];
+    bf16x8 u[3];
+    rest_split_fetch(e, u, E, ldE, U3b, ldk, d_out, d_in, r0, c0, c_end, kp, 0, tid, vec);
+    float wold[4][16];
+    for (int c = 0; c < nchunks; ++c) {
+        __bf16* S = S0 + (c & 1) * kSBuf;
+        rest_split_stash(e, u, S, tid);
+        __syncthreads();
+        if (c + 1 < nchunks)
+            rest_split_fetch(e, u, E, ldE, U3b, ldk, d_out, d_in, r0, c0, c_end, kp, (c + 1) * kSK, tid, vec);
+        if (c == 0) {
+            // the old W tile, behind the next chunk's operands; addresses
+            // outside the sub-tile are clamped to its first element (never
+            // stored)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (q < nq) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int64_t row = r0 + wi * 32 + acc32_row(v, lane);
+                        const int64_t col = cw + 32 * q + (lane & 31);
+                        const bool ok = row < d_out && col < c_end;
+                        wold[q][v] = Wk[ok ? row * d_in + col : r0 * d_in + c0];
+                    }
+                }
+        }
+        switch (nq) {
+            case 4: rest_split_chunk<4>(S, wi, colw, lane, acc); break;
+            case 3: rest_split_chunk<3>(S, wi, colw, lane, acc); break;
+            case 2: rest_split_chunk<2>(S, wi, colw, lane, acc); break;
+            case 1: rest_split_chunk<1>(S, wi, colw, lane, acc); break;
+            default: break;
+        }
+    }
+    if (nchunks == 0) return;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        if (q < nq) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = r0 + wi * 32 + acc32_row(v, lane);
+                const int64_t col = cw + 32 * q + (lane & 31);
+                if (inner || (row < d_out && col < c_end)) Wk[row * d_in + col] = wold[q][v] - acc[q][v];
+            }
+        }
+}
+
 // The far update of one launch is split into units of 128 rows x 64
 // columns (unit u: row tile u / nstrip, strip u % nstrip of the columns
 // [c_begin, d_in)), dealt out as contiguous ranges: the sweeping workgroups
@@ -895,14 +1137,19 @@ __device__ __forceinline__ void rest_body(unsigned char* smem, int64_t r0, int64
 // once, so the launch ends when the longest range does.
 using sched::FarSplit;
 
+template <bool kSplit>
 __device__ __forceinline__ void far_range(unsigned char* smem, int64_t u0, int64_t u1, const FarSplit& fs,
                                           float* __restrict__ Wk, int64_t d_out, int64_t d_in,
                                           const float* __restrict__ E, int64_t ldE, const float* __restrict__ U,
-                                          int64_t bp0, int kp, bool vec) {
+                                          const __bf16* __restrict__ U3b, int64_t ldk, int64_t bp0, int kp,
+                                          bool vec) {
     for (int64_t u = u0; u < u1;) {
         const sched::FarSub t = sched::far_sub(fs, u, u1, d_in);
         __syncthreads();  // the LDS stages of the previous sub-tile (or the sweep) are free again
-        rest_body(smem, t.rt * kRestRows, t.c0, t.c_end, Wk, d_out, d_in, E, ldE, U, bp0, kp, vec);
+        if (kSplit)
+            rest_split_body(smem, t.rt * kRestRows, t.c0, t.c_end, Wk, d_out, d_in, E, ldE, U3b, ldk, kp, vec);
+        else
+            rest_body(smem, t.rt * kRestRows, t.c0, t.c_end, Wk, d_out, d_in, E, ldE, U, bp0, kp, vec);
         u += t.ns;
     }
 }
@@ -913,7 +1160,7 @@ __device__ __forceinline__ void far_range(unsigned char* smem, int64_t u0, int64
 // b1 on; the other workgroups do only that update.  The two parts touch
 // disjoint columns of W and different error buffers, so nothing but the
 // launch order separates the blocks.
-template <bool kAllFull>
+template <bool kAllFull, bool kSplit>
 __global__ __launch_bounds__(512) void step_kernel(float* __restrict__ Wk, int64_t d_out, int64_t d_in,
                                                    const float* __restrict__ U, const float* __restrict__ rdiag,
                                                    int64_t b0, int64_t b1, int bits, int64_t group, int64_t ng,
@@ -921,7 +1168,8 @@ __global__ __launch_bounds__(512) void step_kernel(float* __restrict__ Wk, int64
                                                    float* __restrict__ minmax, uint8_t* __restrict__ codes,
                                                    float* __restrict__ E, int64_t ldE, float* __restrict__ err_row,
                                                    const float* __restrict__ Ep, int64_t bp0, int kp, int row_tiles,
-                                                   FarSplit fs, int vec_rest) {
+                                                   FarSplit fs, int vec_rest, const __bf16* __restrict__ U3b,
+                                                   int64_t ldk) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int b = (int)blockIdx.x;
     if (b < row_tiles)
@@ -929,7 +1177,7 @@ __global__ __launch_bounds__(512) void step_kernel(float* __restrict__ Wk, int64
                              codes, E, ldE, err_row, Ep, bp0, kp);
     int64_t u0, u1;
     sched::far_units(fs, b, row_tiles, u0, u1);
-    if (u1 > u0) far_range(smem, u0, u1, fs, Wk, d_out, d_in, Ep, ldE, U, bp0, kp, vec_rest != 0);
+    if (u1 > u0) far_range<kSplit>(smem, u0, u1, fs, Wk, d_out, d_in, Ep, ldE, U, U3b, ldk, bp0, kp, vec_rest != 0);
 }
 
 }  // namespace
@@ -947,23 +1195,28 @@ hipError_t allow_step_lds(size_t bytes) {
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
     std::lock_guard<std::mutex> lock(mu);
     if (allowed[dev] >= bytes) return hipSuccess;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel<true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e == hipSuccess)
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&step_kernel<false>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e == hipSuccess) allowed[dev] = bytes;
+    const void* fns[4] = {reinterpret_cast<const void*>(&step_kernel<true, false>),
+                          reinterpret_cast<const void*>(&step_kernel<false, false>),
+                          reinterpret_cast<const void*>(&step_kernel<true, true>),
+                          reinterpret_cast<const void*>(&step_kernel<false, true>)};
+    for (const void* f : fns) {
+        e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+        if (e != hipSuccess) return e;
+    }
+    allowed[dev] = bytes;
     return e;
 }
 }  // namespace
 
-size_t quant_workspace_bytes(int64_t d_out, int64_t d_in, int64_t block) {
-    return (size_t)(rup(d_out * d_in * 4, 256) + 2 * rup(d_out * block * 4, 256) + rup(d_in * 4, 256));
+size_t quant_workspace_bytes(int64_t d_out, int64_t d_in, int64_t block, int split) {
+    return (size_t)(rup(d_out * d_in * 4, 256) + 2 * rup(d_out * block * 4, 256) + rup(d_in * 4, 256) +
+                    (split ? rup(split_u_elems(d_in, block) * 2, 256) : 0));
 }
 
 hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d_in, const float* U,
                            const uint8_t* dead, int bits, int64_t group, int64_t block, uint8_t* codes,
-                           float* scales, int32_t* zeros, float* err_row, float* minmax, void* ws, hipStream_t s) {
+                           float* scales, int32_t* zeros, float* err_row, float* minmax, void* ws, int split,
+                           hipStream_t s) {
     if (d_out == 0 || d_in == 0) return hipSuccess;
     QuantWs w = carve(ws, d_out, d_in, block);
     const int64_t ng = group ? d_in / group : 1;
@@ -1005,9 +1258,18 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
 #undef GC_LAUNCH
     }
     const bool vec = (reinterpret_cast<uintptr_t>(U) % 16 == 0) && (d_in % 4 == 0) && (block % 4 == 0);  // E rows are 16-byte aligned when block % 4 == 0
+    const int64_t ldk = split_ldk(block);
+    if (split && d_in > block) {
+        // the bf16 pieces of every block's rows of U, once per layer
+        TimedLaunch t(K_Q_SPLITU, s);
+        // the last block's pieces are never read (no update follows it)
+        const dim3 grid((unsigned)((d_in + 63) / 64), (unsigned)((d_in + block - 1) / block - 1));
+        hipLaunchKernelGGL(split_u_kernel, grid, dim3(256), 0, s, U, d_in, block, ldk, w.U3);
+    }
     const int bmax = (int)std::min(block, d_in);
     const size_t near_bytes = (size_t)((bmax + 3) & ~3) * kEtl * 4;
-    const size_t ldsmax = std::max(sweep_lds_bytes(bmax) + near_bytes, rest_lds_bytes());
+    const size_t rest_bytes = split ? rest_split_lds_bytes() : rest_lds_bytes();
+    const size_t ldsmax = std::max(sweep_lds_bytes(bmax) + near_bytes, rest_bytes);
     if (ldsmax > 64 * 1024) {
         hipError_t e = allow_step_lds(ldsmax);
         if (e != hipSuccess) return e;
@@ -1032,6 +1294,8 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
         const float* Ep = bi > 0 ? w.E[(bi - 1) & 1] : nullptr;
         const int64_t bp0 = b0 - block;
         int kp = bi > 0 ? (int)block : 0;
+        // the previous block's U pieces (split path only)
+        const __bf16* U3b = (split && bi > 0) ? w.U3 + (int64_t)(bi - 1) * 3 * d_in * ldk : nullptr;
         if (group > block && b0 % group == 0) {
             if (kp > 0) {
                 TimedLaunch t(K_Q_TRAIL, s);
@@ -1054,17 +1318,21 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
         const int64_t n_units = (kp > 0 && b1 < d_in) ? (int64_t)rest_rows * fs.nstrip : 0;
         const int n_far = sched::far_split(n_units, row_tiles, n_cu, fs);
         size_t lds = sweep_lds_bytes(bw) + (kp > 0 ? (size_t)((kp + 3) & ~3) * kEtl * 4 : 0);
-        if (n_units > 0) lds = std::max(lds, rest_lds_bytes());
+        if (n_units > 0) lds = std::max(lds, rest_bytes);
         TimedLaunch t(K_Q_STEP, s);
         const dim3 grid((unsigned)(row_tiles + n_far));
-        if (bw % kSub == 0)
-            hipLaunchKernelGGL(step_kernel<true>, grid, dim3(512), lds, s, w.Wk, d_out, d_in, U,
-                               (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes, Eb, block,
-                               err_row, Ep, bp0, kp, row_tiles, fs, (int)vec);
-        else
-            hipLaunchKernelGGL(step_kernel<false>, grid, dim3(512), lds, s, w.Wk, d_out, d_in, U,
-                               (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes, Eb, block,
-                               err_row, Ep, bp0, kp, row_tiles, fs, (int)vec);
+#define STEP_LAUNCH(FULL, SPLIT)                                                                             \
+    hipLaunchKernelGGL((step_kernel<FULL, SPLIT>), grid, dim3(512), lds, s, w.Wk, d_out, d_in, U,              \
+                       (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes, Eb, block, \
+                       err_row, Ep, bp0, kp, row_tiles, fs, (int)vec, U3b, ldk)
+        if (bw % kSub == 0) {
+            if (split) STEP_LAUNCH(true, true);
+            else STEP_LAUNCH(true, false);
+        } else {
+            if (split) STEP_LAUNCH(false, true);
+            else STEP_LAUNCH(false, false);
+        }
+#undef STEP_LAUNCH
     }
     (void)err;
     return hipGetLastError();

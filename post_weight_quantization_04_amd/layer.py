@@ -83,7 +83,7 @@ def prepare(H, damp_frac: float = 0.01, ws: Optional[Workspace] = None, out: Opt
 
 
 def quantize(W, factor: Factor, bits: int, group_size: int, block_size: int, ws: Optional[Workspace] = None,
-             out: Optional[Quantized] = None, use_dead: bool = True, stream=None) -> Quantized:
+             out: Optional[Quantized] = None, use_dead: bool = True, stream=None, split: bool = False) -> Quantized:
     import torch
     d_out, d_in = W.shape
     dev = W.device
@@ -95,9 +95,9 @@ def quantize(W, factor: Factor, bits: int, group_size: int, block_size: int, ws:
                         torch.empty((d_out,), dtype=torch.float32, device=dev),
                         torch.empty((d_out, ng, 2), dtype=torch.float32, device=dev))
     ws = ws or Workspace(dev)
-    buf = ws.get(_lib.quantize_layer_workspace(d_out, d_in, block_size))
+    buf = ws.get(_lib.quantize_layer_workspace(d_out, d_in, block_size, split=split))
     _lib.quantize_layer(W, factor.U, factor.dead if use_dead else None, bits, group_size, block_size, out.codes,
-                        out.scales, out.zeros, out.err_row, out.minmax, buf, stream=stream)
+                        out.scales, out.zeros, out.err_row, out.minmax, buf, stream=stream, split=split)
     return out
 
 
