@@ -45,6 +45,7 @@ KERNEL_SOURCE = {
     "chol_step": ("hinv.hip", "chol_step_kernel"),
     "q_trail": ("quant.hip", "trail_kernel"),
     "q_step": ("quant.hip", "step_kernel"),
+    "q_split_u": ("quant.hip", "split_u_kernel"),
     "hessian_f16": ("hessian.hip", "hessian_f16_kernel"),
     "pack_codes": ("pack.hip", "pack_codes_kernel"),
     "dequantize": ("pack.hip", "dequant_kernel"),
@@ -60,7 +61,7 @@ def kernel_source_sha(name: str) -> str:
     import hashlib
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "post_weight_quantization_04_amd", "csrc")
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCE[name][0], "common.hpp", "kernels.hpp"):
+    for f in (KERNEL_SOURCE[name][0], "common.hpp", "kernels.hpp", "sched.hpp"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
