@@ -9,6 +9,8 @@
 // its token range into H once at the end.
 // The MFMA instruction sequence over the tokens is the same for every slab
 // size, so the sums are the same bits whatever the slab and prefetch depth.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -156,6 +158,11 @@ constexpr int kDepthf16 = 2;  // slabs in flight per thread
 // such tiles per side (d_in <= 3840) too few tiles remain to fill the chip,
 // and the 128x128 tiles of four waves (41 KB of LDS) are used.
 constexpr int kWideTile = 256, kWideThreads = 1024, kWideMinT = 16;
+// Mid-size layers whose 256-wide tiles would leave many CUs idle take
+// 192x192 tiles: twelve waves load the slabs (one 16-byte piece of each
+// operand per thread and slab), nine of them compute a 64x64 quarter each.
+// At d_in = 4096 that is 253 tiles for 256 CUs instead of 136.
+constexpr int kMidTile = 192, kMidThreads = 768;
 
 // Slabs below nfull take the unconditional path; the rest (at most the last
 // one, or all when X is unaligned) the element path.  Diagonal tiles load
@@ -169,7 +176,7 @@ __global__ __launch_bounds__(kThr, kThr == kThreads ? 2 : 1) void hessian_f16_ke
                                                                  int64_t ntok, int64_t nfull, int T,
                                                                  int per_xcd) {
     using S = Slab<kTl, kThr, kK>;
-    constexpr int kWg = kTl / 64;  // waves per tile dimension
+    constexpr int kWg = kTl / 64;  // computing waves per tile dimension (further waves only load)
     __shared__ half_t As[2][kTl * S::kLd];
     __shared__ half_t Bs[2][kTl * S::kLd];
     const int t = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
@@ -178,7 +185,9 @@ __global__ __launch_bounds__(kThr, kThr == kThreads ? 2 : 1) void hessian_f16_ke
     tile_of_super(t, T, I, J);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wi = w / kWg, wj = w % kWg;
-    const bool active = !(I == J && wi < wj);  // above the diagonal of a diagonal tile
+    // waves past kWg^2 only load; on a diagonal tile the quarters above the
+    // diagonal are skipped
+    const bool active = w < kWg * kWg && !(I == J && wi < wj);
     const int rA = I * kTl, rB = J * kTl;
 
     float16v acc[2][2];
@@ -354,7 +363,20 @@ hipError_t launch_hessian(float* H, int64_t n, const void* X, int x_is_f16, int6
         const bool vec = (addr % 16 == 0) && (ldx % 8 == 0);
         const int64_t nfull = vec ? ntok / kKf16 : 0;
         const int64_t Tw = (n + kWideTile - 1) / kWideTile;
-        if (Tw >= kWideMinT) {
+        const int64_t Tm = (n + kMidTile - 1) / kMidTile;
+        const int n_cu = device_cu_count();
+        // rounds of one-workgroup-per-CU tiles, weighted by tile area; the
+        // 192-wide tile takes a quarter more per unit of area (nine
+        // computing waves put three on one SIMD and two on the others)
+        const int64_t tw_all = Tw * (Tw + 1) / 2, tm_all = Tm * (Tm + 1) / 2;
+        const double cost_w = (double)((tw_all + n_cu - 1) / std::max(n_cu, 1)) * 256.0 * 256.0;
+        const double cost_m = 1.25 * (double)((tm_all + n_cu - 1) / std::max(n_cu, 1)) * 192.0 * 192.0;
+        if (Tw >= kWideMinT && n_cu > 0 && cost_m < cost_w) {
+            const int per_xcd = (int)((tm_all + kXcds - 1) / kXcds);
+            hipLaunchKernelGGL((hessian_f16_kernel<kMidTile, kMidThreads, kKf16, kDepthf16>),
+                               dim3((unsigned)(per_xcd * kXcds)), dim3(kMidThreads), 0, s, H, n,
+                               static_cast<const half_t*>(X), ldx, ntok, nfull, (int)Tm, per_xcd);
+        } else if (Tw >= kWideMinT) {
             const int64_t tw = Tw * (Tw + 1) / 2;
             const int per_xcd = (int)((tw + kXcds - 1) / kXcds);
             hipLaunchKernelGGL((hessian_f16_kernel<kWideTile, kWideThreads, kKf16, kDepthf16>),
