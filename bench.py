@@ -35,6 +35,7 @@ KERNEL_CLASS = {
     "hessian_f16": ("f16", "mfma"),
     "hessian_f32": ("f32", "mfma"),
     "chol_step": ("f64", "mfma"),
+    "chol32_step": ("f32", "mfma"),
     "q_step": ("f32", "mfma"),
     "q_trail": ("f32", "mfma"),
 }
@@ -43,6 +44,7 @@ KERNEL_CLASS = {
 # kernel class -> (source file, kernel symbol) for the HBM traffic record
 KERNEL_SOURCE = {
     "chol_step": ("hinv.hip", "chol_step_kernel"),
+    "chol32_step": ("hinv32.hip", "chol32_step_kernel"),
     "q_trail": ("quant.hip", "trail_kernel"),
     "q_step": ("quant.hip", "step_kernel"),
     "q_split_u": ("quant.hip", "split_u_kernel"),
@@ -61,7 +63,7 @@ def kernel_source_sha(name: str) -> str:
     import hashlib
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "post_weight_quantization_04_amd", "csrc")
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCE[name][0], "common.hpp", "kernels.hpp", "sched.hpp"):
+    for f in (KERNEL_SOURCE[name][0], "common.hpp", "kernels.hpp", "sched.hpp", "prep_common.hpp"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -90,7 +92,7 @@ def algorithmic_flops(name: str, d_out: int, d_in: int, n_tok: int, block: int, 
     n = d_in
     if name.startswith("hessian"):
         return float(n) * (n + 1) * n_tok
-    if name == "chol_step":
+    if name in ("chol_step", "chol32_step"):
         # blocked Cholesky of the reversed H with the inverse factor built
         # alongside; per step k, with m = n - 64(k+1) trailing rows and
         # c = 64(k+1) inverse columns, the update costs m(m+1)·64 (lower
@@ -213,7 +215,12 @@ def greedy_variant(torch, wlm, _lib, layer, reps: int = 10) -> dict:
     }
 
 
-def block_bench(args, wl, torch, wlm, _lib, layer) -> int:
+def path_dtype(split: bool, fp32: bool) -> str:
+    return ("f16-mfma H / " + ("f32" if fp32 else "f64") + "-mfma U / f32 sweep"
+            + (" / bf16x3-mfma trailing update" if split else " / f32-mfma trailing update"))
+
+
+def block_bench(args, wl, torch, wlm, _lib, layer, split: bool, fp32: bool) -> int:
     """A multi-layer workload quantized one layer after another: per step,
     H and U once for every distinct set of input activations (layers that
     read the same activations share them), then every layer's sweep with
@@ -226,10 +233,9 @@ def block_bench(args, wl, torch, wlm, _lib, layer) -> int:
         Xd[xs.key] = torch.from_numpy(wlm.x_full(wl, xs.key)).to(dev)
         H[xs.key] = torch.zeros((xs.d_in, xs.d_in), dtype=torch.float32, device=dev)
         ws[xs.key] = layer.Workspace(dev)
-        fac[xs.key] = layer.prepare(H[xs.key].fill_diagonal_(1.0), wl.damp, ws=ws[xs.key])
+        fac[xs.key] = layer.prepare(H[xs.key].fill_diagonal_(1.0), wl.damp, ws=ws[xs.key], fp32=fp32)
     Ws = [torch.from_numpy(wlm.make_weight(wl, li)).to(dev) for li in range(len(wl.layers))]
     wsq = layer.Workspace(dev)
-    split = args.trailing == "split"
     outs = [layer.quantize(Ws[li], fac[sp.x_key], wl.bits, wl.group_size, wl.block_size, ws=wsq, split=split)
             for li, sp in enumerate(wl.layers)]
     stream = torch.cuda.current_stream()
@@ -244,7 +250,7 @@ def block_bench(args, wl, torch, wlm, _lib, layer) -> int:
             for t0 in range(0, xs.n_tokens, chunk[xs.key]):
                 _lib.hessian_accumulate(H[xs.key], Xd[xs.key][:, t0:t0 + chunk[xs.key]])
             b.record(stream)
-            layer.prepare(H[xs.key], wl.damp, ws=ws[xs.key], out=fac[xs.key])
+            layer.prepare(H[xs.key], wl.damp, ws=ws[xs.key], out=fac[xs.key], fp32=fp32)
             c.record(stream)
             ev.append((xs.key, a, b, c))
         lev = []
@@ -290,10 +296,11 @@ def block_bench(args, wl, torch, wlm, _lib, layer) -> int:
                   f"activation set)",
         "value": round(ms, 3), "unit": "ms", "n_gpus": 1, "steps": steps, "warmup": 1, "ms_per_step": round(ms, 3),
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f16-mfma H / f64-mfma U / f32 sweep" + (" / bf16x3-mfma trailing update" if split else ""),
+        "dtype": path_dtype(split, fp32),
         "data": "synthetic (seeded; see workloads/)",
         "config": {"workload": wl.name, "bits": wl.bits, "group_size": wl.group_size, "block_size": wl.block_size,
-                   "damp": wl.damp},
+                   "damp": wl.damp, "factorization": "fp32" if fp32 else "fp64",
+                   "trailing_update": "bf16x3" if split else "fp32"},
         "activation_sets": per_set, "layers": per_layer,
     }
     print(json.dumps(out), flush=True)
@@ -308,6 +315,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="attn_proj")
     ap.add_argument("--trailing", choices=("split", "fp32"), default="split",
                     help="products of the lazy trailing update: bf16 pieces (gptq_quantize_layer_split) or fp32 MFMA")
+    ap.add_argument("--factor", choices=("fp32", "fp64"), default="fp32",
+                    help="precision of the blocked factorization: gptq_prepare_hinv_fp32 or gptq_prepare_hinv")
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-breakdown", action="store_true")
@@ -340,10 +349,11 @@ def main(argv=None) -> int:
 
     wl = wlm.get(args.workload)
     split = args.trailing == "split"
+    fp32 = args.factor == "fp32"
     if split:
         KERNEL_CLASS["q_step"] = ("bf16x3", "mfma")
     if len(wl.layers) != 1:
-        return block_bench(args, wl, torch, wlm, _lib, layer)
+        return block_bench(args, wl, torch, wlm, _lib, layer, split, fp32)
     spec = wl.layers[0]
     xs = wl.x(spec.x_key)
     d_out, d_in, n_tok = spec.d_out, spec.d_in, xs.n_tokens
@@ -356,7 +366,7 @@ def main(argv=None) -> int:
     Xd = torch.from_numpy(X).to(dev)
     H = torch.zeros((d_in, d_in), dtype=torch.float32, device=dev)
     ws1, ws2 = layer.Workspace(dev), layer.Workspace(dev)
-    fac = layer.prepare(H.fill_(0).fill_diagonal_(1.0), wl.damp, ws=ws1)
+    fac = layer.prepare(H.fill_(0).fill_diagonal_(1.0), wl.damp, ws=ws1, fp32=fp32)
     qout = layer.quantize(Wd, fac, wl.bits, wl.group_size, wl.block_size, ws=ws2, split=split)
     chunk = xs.chunk
     stream = torch.cuda.current_stream()
@@ -366,8 +376,8 @@ def main(argv=None) -> int:
         for t0 in range(0, n_tok, chunk):
             _lib.hessian_accumulate(H, Xd[:, t0:t0 + chunk])
 
-    def stage_u():
-        layer.prepare(H, wl.damp, ws=ws1, out=fac)
+    def stage_u(fp32=fp32):
+        layer.prepare(H, wl.damp, ws=ws1, out=fac, fp32=fp32)
 
     def stage_q(split=split):
         layer.quantize(Wd, fac, wl.bits, wl.group_size, wl.block_size, ws=ws2, out=qout, split=split)
@@ -462,7 +472,8 @@ def main(argv=None) -> int:
             if cnt:
                 kernel_ms[name] = ms
                 kernel_launches[name] = cnt
-    dominant = max((k for k in kernel_ms if k in KERNEL_CLASS), key=lambda k: kernel_ms[k], default="chol_step")
+    dominant = max((k for k in kernel_ms if k in KERNEL_CLASS), key=lambda k: kernel_ms[k],
+                   default="chol32_step" if fp32 else "chol_step")
 
     # timed region: K steps, with the dominant kernel's launches bracketed by events
     _lib.timing_enable(dominant)
@@ -560,6 +571,17 @@ def main(argv=None) -> int:
     other["quantize_layer_" + ("fp32" if split else "split") + "_ms"] = round(a.elapsed_time(b) / 5, 4)
     stage_q()
     torch.cuda.synchronize()
+    # ... and the factorization in the other precision
+    stage_u(fp32=not fp32)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(5):
+        stage_u(fp32=not fp32)
+    b.record(stream)
+    torch.cuda.synchronize()
+    other["prepare_hinv_" + ("fp64" if fp32 else "fp32") + "_ms"] = round(a.elapsed_time(b) / 5, 4)
+    stage_u()
+    torch.cuda.synchronize()
 
     greedy = None
     if not args.no_greedy:
@@ -582,11 +604,12 @@ def main(argv=None) -> int:
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16-mfma H / f64-mfma U / f32 sweep" + (" / bf16x3-mfma trailing update" if split else ""),
+        "dtype": path_dtype(split, fp32),
         "data": "synthetic (seeded; see workloads/)",
         "config": {"workload": wl.name, "d_out": d_out, "d_in": d_in, "n_tokens": n_tok, "bits": wl.bits,
                    "group_size": wl.group_size, "block_size": wl.block_size, "damp": wl.damp,
                    "w_dtype": spec.dtype, "x_dtype": xs.dtype, "token_chunk": chunk,
+                   "factorization": "fp32" if fp32 else "fp64",
                    "trailing_update": "bf16x3" if split else "fp32"},
         "other_precision": other,
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},

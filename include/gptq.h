@@ -115,6 +115,27 @@ int gptq_prepare_hinv(const float* H, int64_t d_in, double damp_frac, float* U, 
                       void* stream);
 
 /*
+ * gptq_prepare_hinv with the factorization in float32: the same operation,
+ * route, arguments, outputs and errors, but G = J H J is held in float32
+ * and every product of the blocked factorization runs on MFMA f32 with
+ * float32 accumulation (the pages run the Cholesky of the damped H in the
+ * working precision; aicassindra "The Cholesky trick for the inverse
+ * Hessian").  Rounding grows with the condition number of the damped H:
+ * with damp_frac = 0.01 the relative Frobenius error of U against a float64
+ * factorization stays near 1e-6 on Hessians whose damped condition number
+ * is up to about 1e5; inputs worse conditioned than that belong on
+ * gptq_prepare_hinv.  The damping statistics (lambda, dead flags) are
+ * computed in float64 as there.  info reports a failed pivot in the same
+ * way, judged on the float32 pivots.
+ *   workspace  at least gptq_prepare_hinv_fp32_workspace(d_in) bytes,
+ *              256-byte aligned; clobbered.
+ */
+size_t gptq_prepare_hinv_fp32_workspace(int64_t d_in);
+int gptq_prepare_hinv_fp32(const float* H, int64_t d_in, double damp_frac, float* U, uint8_t* dead,
+                           int32_t* info, double* lambda_out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
  * gptq_prepare_hinv without a workspace argument and without any allocation,
  * for callers that cannot allocate device memory (code under HIP graph
  * capture, tight loops, harnesses that forbid hipMalloc).  Same operation,

@@ -21,6 +21,8 @@ EXPORTS = (
     "gptq_hessian_accumulate",
     "gptq_prepare_hinv_workspace",
     "gptq_prepare_hinv",
+    "gptq_prepare_hinv_fp32_workspace",
+    "gptq_prepare_hinv_fp32",
     "gptq_prepare_hinv_noalloc",
     "gptq_prepare_hinv_noalloc_max_din",
     "gptq_quantize_layer_workspace",
@@ -66,6 +68,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "gptq_hessian_accumulate": (_i32, [_vp, _i64, _vp, _i32, _i64, _i64, _vp]),
         "gptq_prepare_hinv_workspace": (_sz, [_i64]),
         "gptq_prepare_hinv": (_i32, [_vp, _i64, ctypes.c_double, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+        "gptq_prepare_hinv_fp32_workspace": (_sz, [_i64]),
+        "gptq_prepare_hinv_fp32": (_i32, [_vp, _i64, ctypes.c_double, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
         "gptq_prepare_hinv_noalloc": (_i32, [_vp, _i64, ctypes.c_double, _vp, _vp, _vp, _vp, _vp]),
         "gptq_prepare_hinv_noalloc_max_din": (_i64, []),
         "gptq_quantize_layer_workspace": (_sz, [_i64, _i64, _i64]),
@@ -148,18 +152,22 @@ def hessian_accumulate(H, X, stream=None) -> None:
     _check("gptq_hessian_accumulate", rc)
 
 
-def prepare_hinv_workspace(d_in: int) -> int:
-    return int(load().gptq_prepare_hinv_workspace(d_in))
+def prepare_hinv_workspace(d_in: int, fp32: bool = False) -> int:
+    lib = load()
+    return int(lib.gptq_prepare_hinv_fp32_workspace(d_in) if fp32 else lib.gptq_prepare_hinv_workspace(d_in))
 
 
 def prepare_hinv(H, damp_frac: float, U, dead=None, info=None, lambda_out=None, workspace=None,
-                 stream=None) -> None:
+                 stream=None, fp32: bool = False) -> None:
+    """``gptq_prepare_hinv`` (float64 factorization) or, with ``fp32``,
+    ``gptq_prepare_hinv_fp32``."""
     d_in = H.shape[0]
-    rc = load().gptq_prepare_hinv(_ptr(H), d_in, float(damp_frac), _ptr(U), _ptr(dead), _ptr(info),
-                                  _ptr(lambda_out), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size() if workspace is not None else 0,
-                                  _stream(stream))
-    _check("gptq_prepare_hinv", rc)
+    name = "gptq_prepare_hinv_fp32" if fp32 else "gptq_prepare_hinv"
+    rc = getattr(load(), name)(_ptr(H), d_in, float(damp_frac), _ptr(U), _ptr(dead), _ptr(info),
+                               _ptr(lambda_out), _ptr(workspace),
+                               workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                               _stream(stream))
+    _check(name, rc)
 
 
 def prepare_hinv_noalloc(H, damp_frac: float, U, dead=None, info=None, lambda_out=None, stream=None) -> None:

@@ -20,6 +20,7 @@ const char* const kNames[K_COUNT] = {
     "hessian_f16", "hessian_f32", "hinv_diag_stats", "hinv_load_reversed", "chol_step", "hinv_store_u",
     "q_grid_convert",         "q_group_grid",       "q_step",    "q_trail",  "q_split_u",
     "pack_codes",  "dequantize",  "output_error", "obq_hinv", "obq_rows", "propagate",
+    "hinv32_load_reversed", "chol32_step", "hinv32_store_u",
 };
 // The timing state is process-wide; the mutex makes concurrent entry-point
 // calls from several host threads safe, though the events then interleave.
@@ -165,6 +166,21 @@ int gptq_prepare_hinv(const float* H, int64_t d_in, double damp_frac, float* U, 
         return GPTQ_EWORKSPACE;
     return hip_status(
         launch_prepare_hinv(H, d_in, damp_frac, U, dead, info, lambda_out, workspace, as_stream(stream)));
+}
+
+size_t gptq_prepare_hinv_fp32_workspace(int64_t d_in) { return d_in > 0 ? hinv32_workspace_bytes(d_in) : 0; }
+
+int gptq_prepare_hinv_fp32(const float* H, int64_t d_in, double damp_frac, float* U, uint8_t* dead, int32_t* info,
+                           double* lambda_out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (d_in < 0 || !(damp_frac >= 0.0) || !isfinite(damp_frac)) return GPTQ_EINVAL;
+    if (d_in == 0) return GPTQ_OK;
+    if (!H || !U || !info) return GPTQ_EINVAL;
+    if (d_in > (int64_t)1 << 17) return GPTQ_EUNSUPPORTED;
+    if (!workspace || workspace_bytes < hinv32_workspace_bytes(d_in) ||
+        reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return GPTQ_EWORKSPACE;
+    return hip_status(
+        launch_prepare_hinv32(H, d_in, damp_frac, U, dead, info, lambda_out, workspace, as_stream(stream)));
 }
 
 int gptq_prepare_hinv_noalloc(const float* H, int64_t d_in, double damp_frac, float* U, uint8_t* dead,

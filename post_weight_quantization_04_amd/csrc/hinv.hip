@@ -23,6 +23,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "prep_common.hpp"
 #include "sched.hpp"
 
 namespace gptq {
@@ -47,8 +48,6 @@ struct HinvWs {
     int* fail;      // device flag: set once a pivot fails
 };
 
-__host__ __device__ constexpr int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
-
 // Bytes of the factorization workspace for order n (layout in carve()).
 constexpr size_t ws_bytes(int64_t n) {
     return (size_t)(round_up(round_up(n, NB) * round_up(n, NB) * 8, 256) + 3 * round_up(round_up(n, NB) * NB * 8, 256) +
@@ -60,11 +59,6 @@ constexpr size_t ws_bytes(int64_t n) {
 // name is only a stand-in; the device address comes from
 // hinv_noalloc_scratch() below.
 static __device__ __align__(256) unsigned char scratch[ws_bytes(kNoAllocMaxDin)];
-
-// G is stored by 64x64 tiles: tile (I, J) of the n_pad x n_pad matrix is
-// NB*NB contiguous doubles, row-major inside (row stride NB), so that every
-// tile the factorization reads or writes is one contiguous 32 KB block.
-__host__ __device__ inline int64_t gt(int64_t np, int64_t I, int64_t J) { return (I * (np / NB) + J) * NB * NB; }
 
 HinvWs carve(void* ws, int64_t n) {
     const int64_t np = round_up(n, NB);
@@ -78,106 +72,6 @@ HinvWs carve(void* ws, int64_t n) {
     p += 256;
     w.fail = reinterpret_cast<int*>(p);
     return w;
-}
-
-__device__ __forceinline__ void tri_index(int64_t b, int64_t& I, int64_t& J) {
-    int64_t i = (int64_t)((sqrt(8.0 * (double)b + 1.0) - 1.0) * 0.5);
-    while ((i + 1) * (i + 2) / 2 <= b) ++i;
-    while (i * (i + 1) / 2 > b) --i;
-    I = i;
-    J = b - i * (i + 1) / 2;
-}
-
-// ---------------------------------------------------------------------------
-// S2: lambda = damp * mean(diag H), dead flags, status words cleared
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void diag_stats_kernel(const float* __restrict__ H, int64_t n, double damp,
-                                                          uint8_t* __restrict__ dead, double* __restrict__ scal,
-                                                          double* __restrict__ lambda_out, int32_t* __restrict__ info,
-                                                          int* __restrict__ fail) {
-    __shared__ double part[16];
-    double s = 0.0;
-    // every diagonal entry sits on its own cache line: a thread's loads are
-    // issued eight at a time before any is used (the sum keeps its order)
-    constexpr int kB = 8;
-    for (int64_t i0 = threadIdx.x; i0 < n; i0 += (int64_t)kB * blockDim.x) {
-        float h[kB];
-#pragma unroll
-        for (int b = 0; b < kB; ++b) {
-            const int64_t i = i0 + (int64_t)b * blockDim.x;
-            h[b] = (i < n) ? H[i * n + i] : 0.0f;
-        }
-#pragma unroll
-        for (int b = 0; b < kB; ++b) {
-            const int64_t i = i0 + (int64_t)b * blockDim.x;
-            if (i < n) {
-                s += (double)h[b];
-                if (dead) dead[i] = (h[b] == 0.0f) ? 1 : 0;
-            }
-        }
-    }
-    s = wave_sum(s);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        double t = 0.0;
-        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += part[w];
-        double lam = damp * (t / (double)n);
-        scal[0] = lam;
-        if (lambda_out) *lambda_out = lam;
-        *info = 0;
-        *fail = 0;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// G = J (H + damping) J in float64, lower triangle, padded with identity.
-// G[i][j] = H[n-1-j][n-1-i] (a lower-triangle element of H for i >= j).
-// One 64x64 lower tile of G per workgroup, transposed through LDS.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void load_reversed_kernel(const float* __restrict__ H, int64_t n, int64_t np,
-                                                            const double* __restrict__ scal,
-                                                            double* __restrict__ G) {
-    __shared__ float T[64][65];
-    int64_t TI, TJ;
-    tri_index(blockIdx.x, TI, TJ);
-    const double lam = scal[0];
-    const int tid = threadIdx.x;
-    // stage: T[jj][ii] = H[n-1-(64TJ+jj)][n-1-(64TI+ii)], reading H rows
-    // contiguously; a thread's 16 loads are issued before any is used
-    // (entries outside the triangle load H[0] and are replaced by zero)
-    float v[16];
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const int e = tid + 256 * m;
-        const int jj = e >> 6, ii = e & 63;
-        const int64_t i = TI * 64 + ii, j = TJ * 64 + jj;
-        const bool ok = i < n && j < n && i >= j;
-        v[m] = H[ok ? (n - 1 - j) * n + (n - 1 - i) : 0];
-        if (!ok) v[m] = 0.0f;
-    }
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const int e = tid + 256 * m;
-        T[e >> 6][e & 63] = v[m];
-    }
-    __syncthreads();
-    for (int e = tid; e < 64 * 64; e += 256) {
-        int ii = e >> 6, jj = e & 63;
-        int64_t i = TI * 64 + ii, j = TJ * 64 + jj;
-        double g;
-        if (i >= n || j >= n) {
-            g = (i == j) ? 1.0 : 0.0;
-        } else if (i == j) {
-            double h = (double)T[jj][ii];
-            g = (h == 0.0 ? 1.0 : h) + lam;
-        } else if (i > j) {
-            g = (double)T[jj][ii];
-        } else {
-            g = 0.0;
-        }
-        G[gt(np, TI, TJ) + e] = g;
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1110,34 +1004,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void chol_step_kernel(double* __re
     }
 }
 
-// U[i][j] = M[n-1-i][n-1-j] for j >= i, 0 below the diagonal; one row per block.
-__global__ __launch_bounds__(256) void store_u_kernel(const double* __restrict__ G, int64_t np, int64_t n,
-                                                      float* __restrict__ U, const int* __restrict__ fail) {
-    if (*fail) return;
-    const int64_t i = blockIdx.x;
-    const int64_t r = n - 1 - i;
-    const double* grow = G + gt(np, r / NB, 0) + (r % NB) * NB;  // row r of tile column 0
-    float* urow = U + i * n;
-    // eight loads per thread in flight before any store (entries below the
-    // diagonal load grow[0] and are written as zero)
-    constexpr int kB = 8;
-    for (int64_t j0 = threadIdx.x; j0 < n; j0 += (int64_t)kB * blockDim.x) {
-        double g[kB];
-#pragma unroll
-        for (int b = 0; b < kB; ++b) {
-            const int64_t j = j0 + (int64_t)b * blockDim.x;
-            const int64_t c = n - 1 - j;
-            const bool ok = j < n && j >= i;
-            g[b] = grow[ok ? (c / NB) * NB * NB + (c % NB) : 0];
-        }
-#pragma unroll
-        for (int b = 0; b < kB; ++b) {
-            const int64_t j = j0 + (int64_t)b * blockDim.x;
-            if (j < n) urow[j] = (j >= i) ? (float)g[b] : 0.0f;
-        }
-    }
-}
-
 }  // namespace
 
 size_t hinv_workspace_bytes(int64_t n) { return ws_bytes(n); }
@@ -1187,7 +1053,7 @@ hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, floa
     }
     {
         TimedLaunch t(K_HINV_LOAD, s);
-        hipLaunchKernelGGL(load_reversed_kernel, dim3((unsigned)((int64_t)T * (T + 1) / 2)), dim3(256), 0, s, H, n,
+        hipLaunchKernelGGL(load_reversed_kernel<double>, dim3((unsigned)((int64_t)T * (T + 1) / 2)), dim3(256), 0, s, H, n,
                            np, (const double*)w.scal, w.G);
     }
     const int npan = std::max(T - 1, 1);  // workgroups of the diagonal-block + panel launch of step 0
@@ -1220,7 +1086,7 @@ hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, floa
     }
     {
         TimedLaunch t(K_HINV_STORE, s);
-        hipLaunchKernelGGL(store_u_kernel, dim3((unsigned)n), dim3(256), 0, s, (const double*)w.G, np, n, U,
+        hipLaunchKernelGGL(store_u_kernel<double>, dim3((unsigned)n), dim3(256), 0, s, (const double*)w.G, np, n, U,
                            (const int*)w.fail);
     }
     return hipGetLastError();

@@ -26,6 +26,9 @@ enum KernelId {
     K_OBQ_HINV,
     K_OBQ_ROWS,
     K_PROPAGATE,
+    K_HINV32_LOAD,
+    K_CHOL32_STEP,
+    K_HINV32_STORE,
     K_COUNT
 };
 
@@ -63,6 +66,11 @@ hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, floa
 constexpr int64_t kNoAllocMaxDin = 4096;
 size_t hinv_noalloc_scratch_bytes();
 hipError_t hinv_noalloc_scratch(void** out);
+
+// The same stages with float32 tiles and MFMA f32 products.
+size_t hinv32_workspace_bytes(int64_t n);
+hipError_t launch_prepare_hinv32(const float* H, int64_t n, double damp_frac, float* U, uint8_t* dead,
+                                 int32_t* info, double* lambda_out, void* ws, hipStream_t s);
 
 // ---- stage 4 ---------------------------------------------------------------
 size_t quant_workspace_bytes(int64_t d_out, int64_t d_in, int64_t block, int split);

@@ -67,7 +67,7 @@ def hessian_chunks(chunks: Iterable, d_in: int, device="cuda", H=None, stream=No
 
 
 def prepare(H, damp_frac: float = 0.01, ws: Optional[Workspace] = None, out: Optional[Factor] = None,
-            stream=None) -> Factor:
+            stream=None, fp32: bool = False) -> Factor:
     import torch
     d_in = H.shape[0]
     dev = H.device
@@ -77,8 +77,8 @@ def prepare(H, damp_frac: float = 0.01, ws: Optional[Workspace] = None, out: Opt
                      torch.empty((1,), dtype=torch.int32, device=dev),
                      torch.empty((1,), dtype=torch.float64, device=dev))
     ws = ws or Workspace(dev)
-    buf = ws.get(_lib.prepare_hinv_workspace(d_in))
-    _lib.prepare_hinv(H, damp_frac, out.U, out.dead, out.info, out.lam, buf, stream=stream)
+    buf = ws.get(_lib.prepare_hinv_workspace(d_in, fp32=fp32))
+    _lib.prepare_hinv(H, damp_frac, out.U, out.dead, out.info, out.lam, buf, stream=stream, fp32=fp32)
     return out
 
 

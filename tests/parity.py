@@ -52,6 +52,14 @@ def check_u(U_dev: np.ndarray, H_dev: np.ndarray, damp: float):
     return e, U_ref, dead_ref, lam_ref
 
 
+def check_u_ref(U_dev: np.ndarray, U_ref: np.ndarray):
+    """U against an oracle factor already computed from the device's H."""
+    e = rel_fro(np.triu(U_dev), U_ref)
+    assert np.all(np.tril(U_dev, -1) == 0)
+    assert e <= U_TOL, f"U rel err {e:.3g}"
+    return e
+
+
 def check_codes(W, U_dev, dead, q, bits, group, block, rows=None):
     """Tie-aware replay on (a sample of) rows; returns the replay result."""
     codes = q["codes"]

@@ -4,8 +4,10 @@ At these sizes the oracle checks what it can compute one by one, or
 properties that hold at any size:
   H      the whole diagonal plus 4000 sampled lower entries, each 2 x_i . x_j
          in fp64 over all tokens (relative error of the sampled set <= 1e-5)
-  U      in full, the oracle factoring the device's own H (<= 1e-4)
-  codes  tie-aware replay on sampled rows (rows decouple), for the fp32 and
+  U      in full, the oracle factoring the device's own H (<= 1e-4), for the
+         float64 and the float32 factorization
+  codes  tie-aware replay on sampled rows (rows decouple), for the float64
+         factor with the fp32 trailing update and the float32 factor with
          the split-precision trailing update
   error  ||W X - What X||^2 on the sampled rows over all tokens, against the
          oracle's own sweep with the factor of the device H, within 0.5%;
@@ -73,15 +75,20 @@ def rows_output_error(W_rows, What_rows, X, chunk=2048):
 
 
 def run_key(Xd, d_in, chunk, damp):
-    """Device H over token chunks, then U."""
+    """Device H over token chunks, then U in both factorization precisions."""
     import torch
     from post_weight_quantization_04_amd import _lib, layer
     H = torch.zeros((d_in, d_in), dtype=torch.float32, device="cuda")
     for t0 in range(0, Xd.shape[1], chunk):
         _lib.hessian_accumulate(H, Xd[:, t0:t0 + chunk])
     f = layer.prepare(H, damp)
+    f32 = layer.prepare(H, damp, fp32=True)
     torch.cuda.synchronize()
-    return H, f
+    return H, f, f32
+
+
+# (factorization precision, trailing-update precision) pairs checked end to end
+PATHS = (("fp64", False), ("fp32", True))
 
 
 def check_layer(name, W, fac_host, Ud, dead, bits, group, block, X, nrows, seed, split=False, U_e2e=None):
@@ -129,20 +136,22 @@ def test_attn_proj_g128_131072_tokens(lib):
     W = wl.make_weight(w)
     X = wl.x_full(w)
     Xd = _dev(X)
-    H, f = run_key(Xd, 4096, w.x("x").chunk, w.damp)
+    H, f, f32 = run_key(Xd, 4096, w.x("x").chunk, w.damp)
     del Xd
     Hd = _host(H)
-    assert int(_host(f.info)[0]) == 0
+    assert int(_host(f.info)[0]) == 0 and int(_host(f32.info)[0]) == 0
     sampled_h_check(Hd, X)
     U = _host(f.U)
     _, U_ref, dead_ref, _ = parity.check_u(U, Hd, w.damp)
+    U32 = _host(f32.U)
+    say(f"attn_proj_g128: fp32 factor U rel err {parity.check_u_ref(U32, U_ref):.3g}")
     assert not dead_ref.any()
     say("attn_proj_g128: oracle H and U from X (4.4e12 flop)")
     e2e = oracle_factor_from_x(w)
-    for split in (False, True):
-        ties, e_dev, e_ref = check_layer("attn_proj_g128", W, (U, U_ref), f.U, dead_ref, w.bits, w.group_size,
+    for (prec, split), (Uh, fac) in zip(PATHS, ((U, f), (U32, f32))):
+        ties, e_dev, e_ref = check_layer("attn_proj_g128", W, (Uh, U_ref), fac.U, dead_ref, w.bits, w.group_size,
                                          w.block_size, X, 256, 1, split=split, U_e2e=e2e)
-        say(f"attn_proj_g128 split={split}: ties {ties}, out err {e_dev:.6g} vs {e_ref:.6g}")
+        say(f"attn_proj_g128 {prec} factor, split={split}: ties {ties}, out err {e_dev:.6g} vs {e_ref:.6g}")
     say(f"attn_proj_g128 ok in {time.time() - t0:.0f}s")
 
 
@@ -154,10 +163,10 @@ def test_mlp_down_11008(lib):
     W = wl.make_weight(w)
     X = wl.x_full(w)
     Xd = _dev(X)
-    H, f = run_key(Xd, 11008, w.x("x").chunk, w.damp)
+    H, f, f32 = run_key(Xd, 11008, w.x("x").chunk, w.damp)
     del Xd
     Hd = _host(H)
-    assert int(_host(f.info)[0]) == 0
+    assert int(_host(f.info)[0]) == 0 and int(_host(f32.info)[0]) == 0
     sampled_h_check(Hd, X)
     dead_dev = _host(f.dead).astype(bool)
     gen_dead = wl.dead_channels(w)
@@ -166,12 +175,15 @@ def test_mlp_down_11008(lib):
     _, U_ref, dead_ref, lam_ref = parity.check_u(U, Hd, w.damp)
     np.testing.assert_array_equal(dead_dev, dead_ref)
     assert _host(f.lam)[0] == pytest.approx(lam_ref, rel=1e-12)
+    np.testing.assert_array_equal(_host(f32.dead).astype(bool), dead_ref)
+    U32 = _host(f32.U)
+    say(f"mlp_down: fp32 factor U rel err {parity.check_u_ref(U32, U_ref):.3g}")
     say("mlp_down: oracle H and U from X (4.0e12 flop)")
     e2e = oracle_factor_from_x(w)
-    for split in (False, True):
-        ties, e_dev, e_ref = check_layer("mlp_down", W, (U, U_ref), f.U, dead_ref, w.bits, w.group_size,
+    for (prec, split), (Uh, fac) in zip(PATHS, ((U, f), (U32, f32))):
+        ties, e_dev, e_ref = check_layer("mlp_down", W, (Uh, U_ref), fac.U, dead_ref, w.bits, w.group_size,
                                          w.block_size, X, 256, 2, split=split, U_e2e=e2e)
-        say(f"mlp_down split={split}: ties {ties}, out err {e_dev:.6g} vs {e_ref:.6g}")
+        say(f"mlp_down {prec} factor, split={split}: ties {ties}, out err {e_dev:.6g} vs {e_ref:.6g}")
     say(f"mlp_down ok in {time.time() - t0:.0f}s")
 
 
@@ -185,27 +197,31 @@ def decoder_factors(lib):
         say("decoder_block H+U", xs.key, xs.d_in)
         X = wl.x_full(w, xs.key)
         Xd = _dev(X)
-        H, f = run_key(Xd, xs.d_in, xs.chunk, w.damp)
+        H, f, f32 = run_key(Xd, xs.d_in, xs.chunk, w.damp)
         del Xd
         Hd = _host(H)
-        assert int(_host(f.info)[0]) == 0
+        assert int(_host(f.info)[0]) == 0 and int(_host(f32.info)[0]) == 0
         sampled_h_check(Hd, X, n_pairs=2000, seed=len(xs.key))
         U = _host(f.U)
         _, U_ref, dead_ref, _ = parity.check_u(U, Hd, w.damp)
-        factors[xs.key] = (U, U_ref, f, dead_ref)
+        U32 = _host(f32.U)
+        say(f"decoder_block {xs.key}: fp32 factor U rel err {parity.check_u_ref(U32, U_ref):.3g}")
+        factors[xs.key] = {"fp64": (U, f), "fp32": (U32, f32), "U_ref": U_ref, "dead": dead_ref}
         Xs[xs.key] = X
     return w, factors, Xs
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("split", [False, True])
+@pytest.mark.parametrize("prec,split", PATHS)
 @pytest.mark.parametrize("li", range(7))
-def test_decoder_block_layer(decoder_factors, li, split):
+def test_decoder_block_layer(decoder_factors, li, prec, split):
     """Layer li of the 7-layer decoder block (q, k, v, o, gate, up, down;
-    65536 Student-t tokens; 4-bit g128), 256 sampled rows."""
+    65536 Student-t tokens; 4-bit g128), 256 sampled rows, for each pair of
+    factorization and trailing-update precisions."""
     w, factors, Xs = decoder_factors
     spec = w.layers[li]
     W = wl.make_weight(w, li)
-    U, U_ref, f, dead_ref = factors[spec.x_key]
-    check_layer(f"decoder_block.{spec.name}", W, (U, U_ref), f.U, dead_ref, w.bits, w.group_size, w.block_size,
-                Xs[spec.x_key], 256, 10 + li, split=split)
+    fk = factors[spec.x_key]
+    U, f = fk[prec]
+    check_layer(f"decoder_block.{spec.name}", W, (U, fk["U_ref"]), f.U, fk["dead"], w.bits, w.group_size,
+                w.block_size, Xs[spec.x_key], 256, 10 + li, split=split)
