@@ -117,37 +117,38 @@ __device__ __forceinline__ float bcast_row(float x) {
 }
 
 // Pivot C of the symmetric elimination of a 16x16 block A = L D L^T, kept
-// in one array per lane.  With u_r = A_rC / p (p the pivot), every row r
-// below C takes A_rj -= u_r A_Cj; column C of row r then keeps A_rC, which
+// in one array per lane.  With y_j = A_Cj / p (p the pivot), every row r
+// below C takes A_rj -= A_rC y_j; column C of row r then keeps A_rC, which
 // is -p times the entry (r, C) of L_unit^-1 (row operations applied to the
 // identity).  That scaling is the same in every row, so the later pivots
 // update those entries in place like the rest.  The pivot row is cleared
-// from column C on after it has been broadcast (the broadcast copy carries
-// a zero at C, which leaves column C as it is), so that no later pivot
-// touches a row above it.  Lane (g = lane/16, j = lane%16) holds rows
-// 4g .. 4g+3 of column j; pj collects the pivot of column j.  `first`
-// records 1 + the first pivot that is not positive.
+// from column C on after it has been broadcast (y carries a zero at C,
+// which leaves column C as it is), so that no later pivot touches a row
+// above it.  Lane (g = lane/16, j = lane%16) holds rows 4g .. 4g+3 of
+// column j; pj collects the pivot of column j.
+// One pivot is a single wave's in-order instruction stream, so it is kept
+// short: the pivot comes from the broadcast row by a DPP read (no
+// round trip through a scalar register), the reciprocal is the hardware's
+// (within 1 ulp; the sums of the blocked products round far more), and the
+// row is scaled once so that each row update is one fused multiply-add
+// whose broadcast operand the compiler reads through DPP.
 template <int C>
-__device__ __forceinline__ void gj_step(int g, int j, float (&x)[4], float& pj, int& first) {
+__device__ __forceinline__ void gj_step(int g, int j, float (&x)[4], float& pj) {
     constexpr int R = C >> 2, S = C & 3;
-    const float p = bitsf(__builtin_amdgcn_readlane(fbits(x[S]), kSb * R + C));
-    if (!(p > 0.0f) && first == 0) first = C + 1;
-    const float inv = rcp32(p);
-    const float yrow = bcast_row<R>((j == C) ? 0.0f : x[S]);  // A[C][j], zero at j = C
+    const float row = bcast_row<R>(x[S]);  // A[C][j] in every row group
+    const float p = bcast_in_row<C>(row);  // A[C][C] in every lane
+    const float ny = (j == C) ? 0.0f : -(row * __builtin_amdgcn_rcpf(p));
     if (g == R && j >= C) x[S] = 0.0f;
     if (j == C) pj = p;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float u = bcast_in_row<C>(x[e]) * inv;  // A[4g+e][C] / p, zero for rows <= C
-        x[e] = fmaf(-u, yrow, x[e]);
-    }
+    for (int e = 0; e < 4; ++e) x[e] = fmaf(bcast_in_row<C>(x[e]), ny, x[e]);  // A[4g+e][C] y_j, zero for rows <= C
 }
 
 // Sub-block s of L.g (one wave): Ls = inverse of its Cholesky factor,
 // written in place (exact zeros above the diagonal).  After the pivots,
 // entry (r, j < r) is -p_j (L_unit^-1)_rj and Ls = D^-1/2 L_unit^-1.
 // Returns 0, or 1 + the local column of the first pivot that is not
-// positive (wave-uniform).
+// positive (wave-uniform; the pivots after it are then meaningless).
 __device__ __forceinline__ int gj16(Diag32& L, int s, int lane) {
     const int g = lane >> 4, j = lane & 15;
     const int o = kSb * s;
@@ -158,23 +159,25 @@ __device__ __forceinline__ int gj16(Diag32& L, int s, int lane) {
         x[e] = (r >= j) ? L.g[o + r][o + j] : L.g[o + j][o + r];  // symmetric from the lower triangle
     }
     float pj = 1.0f;
-    int first = 0;
-    gj_step<0>(g, j, x, pj, first);
-    gj_step<1>(g, j, x, pj, first);
-    gj_step<2>(g, j, x, pj, first);
-    gj_step<3>(g, j, x, pj, first);
-    gj_step<4>(g, j, x, pj, first);
-    gj_step<5>(g, j, x, pj, first);
-    gj_step<6>(g, j, x, pj, first);
-    gj_step<7>(g, j, x, pj, first);
-    gj_step<8>(g, j, x, pj, first);
-    gj_step<9>(g, j, x, pj, first);
-    gj_step<10>(g, j, x, pj, first);
-    gj_step<11>(g, j, x, pj, first);
-    gj_step<12>(g, j, x, pj, first);
-    gj_step<13>(g, j, x, pj, first);
-    gj_step<14>(g, j, x, pj, first);
-    gj_step<15>(g, j, x, pj, first);
+    gj_step<0>(g, j, x, pj);
+    gj_step<1>(g, j, x, pj);
+    gj_step<2>(g, j, x, pj);
+    gj_step<3>(g, j, x, pj);
+    gj_step<4>(g, j, x, pj);
+    gj_step<5>(g, j, x, pj);
+    gj_step<6>(g, j, x, pj);
+    gj_step<7>(g, j, x, pj);
+    gj_step<8>(g, j, x, pj);
+    gj_step<9>(g, j, x, pj);
+    gj_step<10>(g, j, x, pj);
+    gj_step<11>(g, j, x, pj);
+    gj_step<12>(g, j, x, pj);
+    gj_step<13>(g, j, x, pj);
+    gj_step<14>(g, j, x, pj);
+    gj_step<15>(g, j, x, pj);
+    // lanes 0..15 hold the pivots of columns 0..15
+    const uint64_t bad = __ballot(!(pj > 0.0f)) & 0xFFFFull;
+    const int first = bad ? __builtin_ctzll(bad) + 1 : 0;
     const float nrj = -rcp32(pj);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
