@@ -211,6 +211,15 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Workgroup barrier that orders LDS accesses only (the diagonal block and
+// the chain's product stages exchange data through LDS alone), so that
+// global loads still in flight are not waited for, as __syncthreads would.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Factor and invert the block held in L.g (256 threads).  Returns 0 or
 // 1 + the local column of the first pivot that is not positive
 // (block-uniform).  One sub-step of lookahead: while wave 0 forms P_{s+1},
@@ -220,16 +229,24 @@ __device__ __forceinline__ void wave_lds_sync() {
 //            and M_sj = Ls A_sj (j < s), in place;
 //   phase 2  wave 0: A_{s+1,s+1} -= P_{s+1} P_{s+1}^T, pivots of s+1;
 //            waves 1..3: the other tiles (i, j), i > s, j <= i.
-__device__ __forceinline__ int diag64(Diag32& L) {
+// hook(0) runs on waves 1..3 while wave 0 pivots the first sub-block, hook(1)
+// on the same waves right after that (before their first update work), and
+// hook(2) on them after their update tiles of sub-step 2 (where wave 0's
+// pivots of sub-block 3 leave them idle).
+template <typename Hook>
+__device__ __forceinline__ int diag64(Diag32& L, Hook&& hook) {
     const int lane = threadIdx.x & 63, w = wave_id();
     const int crow = 4 * (lane >> 4);  // first result row of this lane
     constexpr int S = NB / kSb;
     if (w == 0) {
         const int st = gj16(L, 0, lane);
         if (lane == 0) L.status = st;
+    } else {
+        hook(0);
     }
-    __syncthreads();
+    lds_barrier();
     if (L.status) return L.status;
+    if (w != 0) hook(1);
     for (int s = 0; s < S; ++s) {
         const int o = kSb * s;
         auto panel_p = [&](int i, int slot) {  // P_i = A_is Ls^T
@@ -255,7 +272,7 @@ __device__ __forceinline__ int diag64(Diag32& L) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         // phase 2
         if (w == 0) {
             if (s + 1 < S) {
@@ -294,11 +311,16 @@ __device__ __forceinline__ int diag64(Diag32& L) {
                     }
                 }
             }
+            if (s == 2) hook(2);
         }
-        __syncthreads();
+        lds_barrier();
         if (s + 1 < S && L.status) return kSb * (s + 1) + L.status;
     }
     return 0;
+}
+
+__device__ __forceinline__ int diag64(Diag32& L) {
+    return diag64(L, [](int) {});
 }
 
 // ---------------------------------------------------------------------------
@@ -666,6 +688,164 @@ __device__ __forceinline__ void diag_panel_next_body(Chain32Lds& u, float* __res
 }
 
 // ---------------------------------------------------------------------------
+// The same step without pairing, with the panel operand's update taken off
+// the critical chain: its operands are staged right after the D product and
+// waves 1..3 form it as 16x16 tiles in the diagonal block's idle time (four
+// tiles while wave 0 pivots the first sub-block, the rest after their update
+// tiles of sub-step 2); after the diagonal block they write it into the
+// stage as the panel product's operand: A = X for t >= k1, a direct B = X
+// for t < k1.  Wave w takes row band w-1 (four tiles) and on row band 3 the
+// tiles (3,0), (3,1) (w = 1), (3,2) (w = 2) or (3,3) (w = 3).
+// ---------------------------------------------------------------------------
+constexpr int kOpMax = 6;  // op tiles of one wave
+
+__device__ __forceinline__ bool op_tile_of(int w, int j, int& mt, int& nt) {
+    if (j < 4) {
+        mt = w - 1;
+        nt = j;
+        return true;
+    }
+    mt = 3;
+    if (w == 1) {
+        nt = j - 4;
+        return j < 6;
+    }
+    nt = (w == 2) ? 2 : 3;
+    return j == 4;
+}
+
+// 16x16 tile (mt, nt) of A B from the stage; lane l gets C[16 mt + 4 (l/16) + v][16 nt + l%16].
+template <bool kBT>
+__device__ __forceinline__ float4v op_tile(const Gemm32& s, int mt, int nt, int lane) {
+    const int i = lane & 15, g = lane >> 4;
+    float4v acc = {};
+#pragma unroll
+    for (int ks = 0; ks < NB; ks += 4) {
+        const int k = ks + g;
+        const float a = s.A[(16 * mt + i) * kAs + k];
+        const float b = kBT ? s.B[(16 * nt + i) * kAs + k] : s.B[k * kBd + 16 * nt + i];
+        acc = mfma16x16x4_f32(a, b, acc);
+    }
+    return acc;
+}
+
+// Panel tile from an operand already in the stage (A for t >= kd, direct B
+// for t < kd) and M from L.g.
+__device__ __forceinline__ void panel_product_staged(Chain32Lds& u, bool inv_row, float* __restrict__ dst) {
+    Gemm32& s = u.gemm;
+    if (inv_row) stash_m(u.diag, s.A);
+    else stash_m(u.diag, s.B);
+    lds_barrier();
+    float4v acc[2][2];
+    zero_acc(acc);
+    if (inv_row) gemm_compute<false>(s, acc);
+    else gemm_compute<true>(s, acc);
+    const float none[2][2][4] = {};
+    tile_store<0>(dst, acc, none);
+}
+
+__device__ __forceinline__ void diag_panel_next_overlap(Chain32Lds& u, float* __restrict__ G, int64_t np,
+                                                        float* __restrict__ Pk1, const float* __restrict__ Pk, int k,
+                                                        int T, int t, int32_t* __restrict__ info,
+                                                        int* __restrict__ fail) {
+    const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+    const int k1 = k + 1;
+    const bool has_tile = t < T - 1;
+    const bool inv_row = t < k1;
+    const bool neg = inv_row && t == k;  // G_{k1,k} holds nothing yet: X = -P_k1 M_kk
+    Gemm32& s = u.gemm;
+    Diag32& L = u.diag;
+    float pd[16];
+    tile_fetch(pd, Pk + (int64_t)k1 * NB * NB, tid);
+    float xo[16];
+    float cold[kOpMax][4];  // old values of the operand, op-tile layout (waves 1..3)
+    if (has_tile) {
+        if (!inv_row) tile_fetch(xo, Pk + (int64_t)(t + 1) * NB * NB, tid);
+        else if (t == k) tile_fetch(xo, Pk, tid);  // M_kk (zeros above the diagonal)
+        else tile_fetch(xo, G + gt(np, k, t), tid);
+    }
+    load_block(L, G + gt(np, k1, k1));
+    // D = G_k1k1 - P_k1 P_k1^T
+    float4v acc[2][2];
+    zero_acc(acc);
+    stash_a(pd, s, tid);
+    stash_b<true>(pd, s, tid);
+    __syncthreads();
+    gemm_compute<true>(s, acc);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) L.g[acc_row(m, v)][acc_col(q)] -= acc[m][q][v];
+    // the old values are needed only after the op tiles: loaded now, they
+    // do not delay the D product's operands
+    if (has_tile && w != 0 && !neg) {
+        const float* ct = !inv_row ? G + gt(np, t + 1, k1) : G + gt(np, k1, t);
+#pragma unroll
+        for (int j = 0; j < kOpMax; ++j) {
+            int mt, nt;
+            if (op_tile_of(w, j, mt, nt)) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    cold[j][v] = ct[(16 * mt + 4 * (lane >> 4) + v) * NB + 16 * nt + (lane & 15)];
+            }
+        }
+    }
+    if (has_tile) {
+        lds_barrier();  // every wave is done with the D product's stage
+        if (!inv_row) {
+            stash_a(xo, s, tid);
+            stash_b<true>(pd, s, tid);
+        } else {
+            stash_a(pd, s, tid);
+            stash_b<false>(xo, s, tid);
+        }
+    }
+    lds_barrier();
+    float4v oacc[kOpMax];
+    // stage 0: the four tiles of the wave's row band; stage 2: its tiles on
+    // row band 3.  The tiles stay in registers until the diagonal block is
+    // done (other waves read the operands until then).
+    auto hook = [&](int stage) {
+        if (!has_tile || stage == 1) return;
+#pragma unroll
+        for (int j = 0; j < kOpMax; ++j) {
+            int mt, nt;
+            if ((j < 4) != (stage == 0) || !op_tile_of(w, j, mt, nt)) continue;
+            oacc[j] = inv_row ? op_tile<false>(s, mt, nt, lane) : op_tile<true>(s, mt, nt, lane);
+        }
+    };
+    const int st = diag64(L, hook);
+    if (st) {
+        if (t == 0 && tid == 0) {
+            *info = k1 * NB + st;
+            *fail = 1;
+        }
+        return;
+    }
+    if (t == 0) store_m(L, Pk1);
+    if (!has_tile) return;
+    // X into the stage as the panel product's operand (every wave is past
+    // the diagonal block's last barrier, so the op operands are dead)
+    if (w != 0) {
+#pragma unroll
+        for (int j = 0; j < kOpMax; ++j) {
+            int mt, nt;
+            if (!op_tile_of(w, j, mt, nt)) continue;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = 16 * mt + 4 * (lane >> 4) + v, col = 16 * nt + (lane & 15);
+                const float x = neg ? -oacc[j][v] : cold[j][v] - oacc[j][v];
+                if (inv_row) s.B[row * kBd + col] = x;
+                else s.A[row * kAs + col] = x;
+            }
+        }
+    }
+    panel_product_staged(u, inv_row, inv_row ? G + gt(np, k1, t) : Pk1 + (int64_t)(t + 1) * NB * NB);
+}
+
+// ---------------------------------------------------------------------------
 // The rest of the update of step k: the blocks (i, j), j <= i, with
 // i > k+1 and j != k+1 (column and row block k+1 are updated inside the
 // diagonal-block workgroups of step k+1), enumerated by sched::rest_tile.
@@ -763,7 +943,8 @@ __global__ __launch_bounds__(kThreads, 2) void chol32_step_kernel(float* __restr
     if (*fail) return;
     const int b = (int)blockIdx.x;
     if (b < npan) {
-        diag_panel_next_body<kPair>(u, G, np, Pk1, Pk, Pkm, k, T, b, info, fail);
+        if (kPair) diag_panel_next_body<true>(u, G, np, Pk1, Pk, Pkm, k, T, b, info, fail);
+        else diag_panel_next_overlap(u, G, np, Pk1, Pk, k, T, b, info, fail);
     } else if (b == npan) {
         float* Gkk = G + gt(np, k, k);
 #pragma unroll
