@@ -1,14 +1,17 @@
 // Stage 1: H += 2 X X^T on the lower triangle (aicassindra.com
 // "tm_gptq_math", "Why it is second-order: the Hessian").
 //
-// One workgroup per lower-triangle tile (I >= J) of H, 128x128 on four waves
-// or, for wide layers, 256x256 on sixteen; each wave owns a 64x64 quarter as
-// 2x2 MFMA 32x32 accumulators.  Token slabs of X rows I and J are staged
-// through LDS; products run on MFMA with fp32 accumulation (f16 inputs:
-// 32x32x16 f16, exact products; f32 inputs: 32x32x2 f32).  Each call adds
-// its token range into H once at the end.
-// The MFMA instruction sequence over the tokens is the same for every slab
-// size, so the sums are the same bits whatever the slab and prefetch depth.
+// One workgroup per lower-triangle tile (I >= J) of H: 128x128 on four
+// waves for narrow layers; for wide ones 256x256 on sixteen waves, or
+// 192x192 on twelve (nine compute waves, three loader waves) where 256-wide
+// tiles would leave CUs idle.  Every computing wave keeps one 64x64 quarter
+// as 2x2 MFMA 32x32 accumulators.  Token slabs of X rows I
+// and J are staged through LDS; products run on MFMA with fp32 accumulation
+// (f16 inputs: 32x32x16 f16, exact products; f32 inputs: 32x32x2 f32).  Each
+// call adds its token range into H once at the end.
+// The MFMA instruction sequence over the tokens is the same for every tile,
+// slab size and prefetch depth (zero-padded tails add exact zeros), so the
+// sums are the same bits whichever kernel a shape takes.
 #include <algorithm>
 
 #include "common.hpp"
@@ -29,22 +32,39 @@ __device__ __forceinline__ void tile_of(int b, int& I, int& J) {
     J = b - i * (i + 1) / 2;
 }
 
-// Adds 2*acc into the lower triangle of H for one wave's 64x64 quarter.
+// Adds 2*acc into the lower triangle of H for one wave's 64x64 quarter.  The
+// old values of a 32-row half are all loaded before any of them is stored,
+// so a wave waits for memory twice rather than once per element.  Entries
+// past n or above the diagonal load from a clamped, always valid address
+// (measured faster than skipping their loads) and are not stored.  Addresses
+// are a wave-uniform row base plus an unsigned 32-bit offset (at most
+// 64 n < 2^31 for any width whose H fits in memory).
 __device__ __forceinline__ void store_quarter(float* __restrict__ H, int64_t n, int r0, int c0,
                                               const float16v (&acc)[2][2], int lane) {
+    const int ni = (int)n;
+    const int rb = min(r0, ni - 1);
+    float* __restrict__ base = H + (int64_t)rb * n;
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < 2; ++m) {
+        float old[2][16];
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                int row = r0 + 32 * m + acc32_row(v, lane);
-                int col = c0 + 32 * q + (lane & 31);
-                if (row < n && col <= row) {
-                    float* p = H + (int64_t)row * n + col;
-                    *p = *p + 2.0f * acc[m][q][v];
-                }
+                const int row = r0 + 32 * m + acc32_row(v, lane);
+                const int col = c0 + 32 * q + (lane & 31);
+                const int rr = min(row, ni - 1), cc = min(col, rr);
+                old[q][v] = base[(unsigned)((rr - rb) * ni + cc)];
             }
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = r0 + 32 * m + acc32_row(v, lane);
+                const int col = c0 + 32 * q + (lane & 31);
+                if (row < ni && col <= row) base[(unsigned)((row - rb) * ni + col)] = old[q][v] + 2.0f * acc[m][q][v];
+            }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -151,18 +171,16 @@ __device__ __forceinline__ void stash_slab(const SlabRegs<kTl, kThr, kK>& v, hal
 
 constexpr int kKf16 = 32;    // tokens per slab
 constexpr int kDepthf16 = 2;  // slabs in flight per thread
-// Wide layers take 256x256 tiles on 16 waves (each wave still a 64x64
-// quarter): half the X bytes per product of 128x128 tiles, four waves per
-// SIMD to hide their latency, 80 KB of LDS.  Measured per 2048-token chunk:
-// 471 against 571 us at d_in = 11008, 82 against 85 us at 4096; below 16
-// such tiles per side (d_in <= 3840) too few tiles remain to fill the chip,
-// and the 128x128 tiles of four waves (41 KB of LDS) are used.
-constexpr int kWideTile = 256, kWideThreads = 1024, kWideMinT = 16;
-// Mid-size layers whose 256-wide tiles would leave many CUs idle take
-// 192x192 tiles: twelve waves load the slabs (one 16-byte piece of each
-// operand per thread and slab), nine of them compute a 64x64 quarter each.
-// At d_in = 4096 that is 253 tiles for 256 CUs instead of 136.
-constexpr int kMidTile = 192, kMidThreads = 768;
+// Layers with at least 16 tiles of 256 per side (d_in > 3840) take wide
+// tiles; narrower ones the 128x128 tiles of four waves (41 KB of LDS, two
+// workgroups per CU).  Among wide layers, those with at least two rounds of
+// 256x256 tiles per CU take those, on 16 waves of one 64x64 quarter each
+// (half the X bytes per product of 128x128 tiles, four waves per SIMD, 80 KB
+// of LDS); the others the warp-specialised 192x192 kernel below, whose 253
+// tiles at d_in = 4096 fill the chip where 136 tiles of 256 would not.
+// Measured per 2048-token chunk: d_in = 4096, 54 against 75 us; d_in =
+// 11008, 371 against 525 us.
+constexpr int kWideTile = 256, kWideThreads = 1024, kWideMinT = 16, kWideMinRounds = 2;
 
 // Slabs below nfull take the unconditional path; the rest (at most the last
 // one, or all when X is unaligned) the element path.  Diagonal tiles load
@@ -281,6 +299,183 @@ __global__ __launch_bounds__(kThr, kThr == kThreads ? 2 : 1) void hessian_f16_ke
 }
 
 // ---------------------------------------------------------------------------
+// float16 inputs, wide layers: 192x192 tiles, warp-specialised.
+//
+// Waves 0..8 each own a 64x64 quarter and only read LDS and issue MFMAs;
+// waves 9..11 only load X and write the slabs into LDS, one slab ahead of
+// the compute waves, so that the LDS writes of slab s+1 overlap the products
+// of slab s (measured at d_in = 4096, 2048 tokens: 41.7 against 47.5 us for
+// the loop when every wave both loads and computes).  64-token slabs, two LDS
+// buffers, one barrier per slab: buffer (s+1)&1 is written after the barrier
+// that ends slab s-1, whose readers have all finished with it by then.  The
+// loaders hold one slab in registers beyond the one they write (a second
+// measured no faster at 64 tokens per slab).
+// ---------------------------------------------------------------------------
+constexpr int kWsTile = 192, kWsK = 64, kWsDepth = 1;
+constexpr int kWsCompute = 9, kWsLoaders = 3, kWsThreads = (kWsCompute + kWsLoaders) * 64;
+
+// Loader side: thread lt of the 192 loader threads moves kWsPieces 16-byte
+// pieces of the 384 x 64 slab (rows 0..191 of panel I, then 192..383 of
+// panel J): piece i is row lt / 8 + 24 i, tokens (lt % 8) * 8 .. + 8.
+constexpr int kWsChunks = kWsK / 8;
+constexpr int kWsPieces = 2 * kWsTile * kWsChunks / (kWsLoaders * 64);
+constexpr int kWsRowsPerPass = kWsLoaders * 64 / kWsChunks;
+constexpr int kWsLd = kWsK + 8;  // padded LDS row (halves): conflict-free 16-byte MFMA operand reads
+static_assert(kWsPieces * kWsRowsPerPass == 2 * kWsTile && kWsPieces % 2 == 0, "loader pieces cover both panels");
+
+__global__ __launch_bounds__(kWsThreads, 1) void hessian_f16_ws_kernel(float* __restrict__ H, int64_t n,
+                                                                       const half_t* __restrict__ X, int64_t ldx,
+                                                                       int64_t ntok, int64_t nfull, int T,
+                                                                       int per_xcd) {
+    __shared__ half_t As[2][kWsTile * kWsLd];
+    __shared__ half_t Bs[2][kWsTile * kWsLd];
+    const int t = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+    if (t >= T * (T + 1) / 2) return;
+    int I, J;
+    tile_of_super(t, T, I, J);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int rA = I * kWsTile, rB = J * kWsTile;
+    const int64_t nslab = (ntok + kWsK - 1) / kWsK;
+
+    if (w >= kWsCompute) {
+        const int lt = tid - kWsCompute * 64;
+        const int chunk = lt % kWsChunks;
+        // pieces 0..kWsPieces/2-1 lie in panel I, the rest in panel J (row
+        // lt / 8 + 24 i < 192 exactly for i < 8)
+        constexpr int kHalf = kWsPieces / 2;
+        // clamped row of each piece; its address is formed at each use
+        // (kept as a pointer per piece, the sixteen 64-bit addresses and their
+        // per-slab increments outgrew the register budget)
+        int prow[kWsPieces];
+        const int dst0 = (lt / kWsChunks) * kWsLd + chunk * 8;
+#pragma unroll
+        for (int i = 0; i < kWsPieces; ++i) {
+            const int rr = lt / kWsChunks + kWsRowsPerPass * (i % kHalf);
+            // rows past n are clamped to row n-1: they feed only accumulator
+            // entries that are never stored
+            prow[i] = (int)min((int64_t)((i < kHalf ? rA : rB) + rr), n - 1);
+        }
+        auto rowp = [&](int i) {
+            int r = prow[i];
+            asm volatile("" : "+v"(r));  // formed here, not hoisted out of the slab loop
+            return X + (int64_t)r * ldx;
+        };
+        half8 v[kWsDepth][kWsPieces];
+        // a full slab: one unconditional 16-byte load per piece
+        auto fetch_full_ws = [&](half8(&x)[kWsPieces], int64_t f) {
+#pragma unroll
+            for (int i = 0; i < kWsPieces; ++i)
+                x[i] = *reinterpret_cast<const half8*>(rowp(i) + f * kWsK + chunk * 8);
+        };
+        // any slab: full ones as above, the partial last one (or every slab of
+        // an unaligned X) by element loads with tokens past ntok read as zero;
+        // slabs past the last are not loaded
+        auto fetch = [&](half8(&x)[kWsPieces], int64_t f) {
+            if (f < nfull) {
+                fetch_full_ws(x, f);
+            } else if (f < nslab) {
+                // every element load is unconditional, from a token index
+                // clamped to ntok-1, and the value past ntok replaced by zero
+                // afterwards (a load under a branch would be waited for there)
+                const int64_t k = f * kWsK + chunk * 8;
+#pragma unroll
+                for (int i = 0; i < kWsPieces; ++i) {
+                    const half_t* p = rowp(i);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const half_t h = p[min(k + e, ntok - 1)];
+                        x[i][e] = (k + e < ntok) ? h : (half_t)0;
+                    }
+                }
+            }
+        };
+        auto put = [&](const half8(&x)[kWsPieces], int b) {
+#pragma unroll
+            for (int i = 0; i < kWsPieces; ++i)
+                *reinterpret_cast<half8*>(&(i < kHalf ? As[b] : Bs[b])[dst0 + kWsRowsPerPass * (i % kHalf) * kWsLd]) = x[i];
+        };
+        // steady part: iterations whose refetch (slab sl + 1 + depth) is full,
+        // entered with exactly kWsDepth full sets in flight so that each LDS
+        // write waits only for the oldest set
+        const int64_t lim = nfull - 1 - kWsDepth;
+        const int64_t nsteady = lim > 0 ? (lim / kWsDepth) * kWsDepth : 0;
+        if (nsteady > 0) {
+#pragma unroll
+            for (int d = 0; d < kWsDepth; ++d) {
+                fetch_full_ws(v[d], d);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            put(v[0], 0);
+            fetch_full_ws(v[0], kWsDepth);
+        } else {
+#pragma unroll
+            for (int d = 0; d < kWsDepth; ++d) fetch(v[d], d);
+            put(v[0], 0);
+            fetch(v[0], kWsDepth);
+        }
+        __syncthreads();
+        // iteration sl writes slab sl+1 (held in set (sl+1) % depth) and
+        // refills that set with slab sl+1+depth; one barrier per iteration
+        int64_t s0 = 0;
+        for (; s0 < nsteady; s0 += kWsDepth) {
+#pragma unroll
+            for (int d = 0; d < kWsDepth; ++d) {
+                const int64_t sl = s0 + d;
+                const int dn = (d + 1) % kWsDepth;
+                put(v[dn], (int)((sl + 1) & 1));
+                fetch_full_ws(v[dn], sl + 1 + kWsDepth);
+                __syncthreads();
+            }
+        }
+        for (; s0 < nslab; s0 += kWsDepth) {
+#pragma unroll
+            for (int d = 0; d < kWsDepth; ++d) {
+                const int64_t sl = s0 + d;
+                if (sl >= nslab) break;
+                const int dn = (d + 1) % kWsDepth;
+                if (sl + 1 < nslab) put(v[dn], (int)((sl + 1) & 1));
+                fetch(v[dn], sl + 1 + kWsDepth);
+                __syncthreads();
+            }
+        }
+        return;
+    }
+
+    // compute waves: quarter (wi, wj) of the tile; on a diagonal tile the
+    // quarters above the diagonal are skipped (their waves still take every
+    // barrier)
+    const int wi = w / 3, wj = w % 3;
+    const bool active = !(I == J && wi < wj);
+    float16v acc[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) acc[m][q] = (float16v){};
+    const int offA = (wi * 64 + (lane & 31)) * kWsLd + 8 * (lane >> 5);
+    const int offB = (wj * 64 + (lane & 31)) * kWsLd + 8 * (lane >> 5);
+    __syncthreads();
+    for (int64_t sl = 0; sl < nslab; ++sl) {
+        if (active) {
+            const half_t* Ap = As[sl & 1] + offA;
+            const half_t* Bp = Bs[sl & 1] + offB;
+#pragma unroll
+            for (int ks = 0; ks < kWsK / 16; ++ks) {
+                const half8 a0 = *reinterpret_cast<const half8*>(Ap + 16 * ks);
+                const half8 a1 = *reinterpret_cast<const half8*>(Ap + 32 * kWsLd + 16 * ks);
+                const half8 b0 = *reinterpret_cast<const half8*>(Bp + 16 * ks);
+                const half8 b1 = *reinterpret_cast<const half8*>(Bp + 32 * kWsLd + 16 * ks);
+                acc[0][0] = mfma32x32x16_f16(a0, b0, acc[0][0]);
+                acc[0][1] = mfma32x32x16_f16(a0, b1, acc[0][1]);
+                acc[1][0] = mfma32x32x16_f16(a1, b0, acc[1][0]);
+                acc[1][1] = mfma32x32x16_f16(a1, b1, acc[1][1]);
+            }
+        }
+        __syncthreads();
+    }
+    if (active) store_quarter(H, n, rA + wi * 64, rB + wj * 64, acc, lane);
+}
+
+// ---------------------------------------------------------------------------
 // float32 inputs
 // ---------------------------------------------------------------------------
 constexpr int kK32 = 32;
@@ -307,7 +502,7 @@ __device__ __forceinline__ void load_slab_f32(float (*S)[kLd32], const float* __
 }
 
 template <bool kVec>
-__global__ __launch_bounds__(kThreads) void hessian_f32_kernel(float* __restrict__ H, int64_t n,
+__global__ __launch_bounds__(kThreads, 2) void hessian_f32_kernel(float* __restrict__ H, int64_t n,
                                                               const float* __restrict__ X, int64_t ldx,
                                                               int64_t ntok) {
     __shared__ float As[kTile][kLd32];
@@ -363,25 +558,19 @@ hipError_t launch_hessian(float* H, int64_t n, const void* X, int x_is_f16, int6
         const bool vec = (addr % 16 == 0) && (ldx % 8 == 0);
         const int64_t nfull = vec ? ntok / kKf16 : 0;
         const int64_t Tw = (n + kWideTile - 1) / kWideTile;
-        const int64_t Tm = (n + kMidTile - 1) / kMidTile;
+        const int64_t tw_all = Tw * (Tw + 1) / 2;
         const int n_cu = device_cu_count();
-        // rounds of one-workgroup-per-CU tiles, weighted by tile area; the
-        // 192-wide tile takes a quarter more per unit of area (nine
-        // computing waves put three on one SIMD and two on the others)
-        const int64_t tw_all = Tw * (Tw + 1) / 2, tm_all = Tm * (Tm + 1) / 2;
-        const double cost_w = (double)((tw_all + n_cu - 1) / std::max(n_cu, 1)) * 256.0 * 256.0;
-        const double cost_m = 1.25 * (double)((tm_all + n_cu - 1) / std::max(n_cu, 1)) * 192.0 * 192.0;
-        if (Tw >= kWideMinT && n_cu > 0 && cost_m < cost_w) {
-            const int per_xcd = (int)((tm_all + kXcds - 1) / kXcds);
-            hipLaunchKernelGGL((hessian_f16_kernel<kMidTile, kMidThreads, kKf16, kDepthf16>),
-                               dim3((unsigned)(per_xcd * kXcds)), dim3(kMidThreads), 0, s, H, n,
-                               static_cast<const half_t*>(X), ldx, ntok, nfull, (int)Tm, per_xcd);
-        } else if (Tw >= kWideMinT) {
-            const int64_t tw = Tw * (Tw + 1) / 2;
-            const int per_xcd = (int)((tw + kXcds - 1) / kXcds);
+        if (Tw >= kWideMinT && n_cu > 0 && tw_all >= (int64_t)kWideMinRounds * n_cu) {
+            const int per_xcd = (int)((tw_all + kXcds - 1) / kXcds);
             hipLaunchKernelGGL((hessian_f16_kernel<kWideTile, kWideThreads, kKf16, kDepthf16>),
                                dim3((unsigned)(per_xcd * kXcds)), dim3(kWideThreads), 0, s, H, n,
                                static_cast<const half_t*>(X), ldx, ntok, nfull, (int)Tw, per_xcd);
+        } else if (Tw >= kWideMinT) {
+            const int64_t Tm = (n + kWsTile - 1) / kWsTile;
+            const int64_t nfull_ws = vec ? ntok / kWsK : 0;
+            const int per_xcd = (int)((Tm * (Tm + 1) / 2 + kXcds - 1) / kXcds);
+            hipLaunchKernelGGL(hessian_f16_ws_kernel, dim3((unsigned)(per_xcd * kXcds)), dim3(kWsThreads), 0, s, H, n,
+                               static_cast<const half_t*>(X), ldx, ntok, nfull_ws, (int)Tm, per_xcd);
         } else {
             const int per_xcd = (int)((tiles + kXcds - 1) / kXcds);
             hipLaunchKernelGGL((hessian_f16_kernel<kTile, kThreads, kKf16, kDepthf16>),

@@ -57,10 +57,12 @@ def _quant_dict(qz):
     (130, 1000, np.float16, 300),     # chunk views at unaligned offsets
     (256, 2048, np.float16, 1024),
     (1, 5, np.float16, None),
-    (4000, 333, np.float16, None),    # 192-wide tiles (21 per side): ragged tiles and token tail
+    (4000, 333, np.float16, None),    # 192-wide tiles (21 per side): ragged tiles, unaligned rows
+    (4000, 1000, np.float16, None),   # 192-wide tiles: 13 steady slabs, then the generic part and a ragged tail
     (4096, 700, np.float16, 300),     # 192-wide tiles, ragged last tile row, unaligned chunk views
-    (4500, 96, np.float16, None),     # 256-wide tiles (18 per side), ragged
+    (4500, 96, np.float16, None),     # 192-wide tiles (24 per side), one full slab and a tail
     (3904, 700, np.float16, 300),     # 192-wide tiles: chunk views at unaligned offsets
+    (8000, 200, np.float16, None),    # 256-wide tiles (32 per side: two rounds on 256 CUs), ragged
 ])
 def test_hessian(lib, n, N, xdtype, chunk):
     from post_weight_quantization_04_amd import layer
