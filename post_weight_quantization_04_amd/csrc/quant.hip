@@ -1065,6 +1065,66 @@ __device__ __forceinline__ void rest_split_chunk(const __bf16* S, int wi, int co
     for (int q = 0; q < NQ; ++q) acc[q] = mfma32x32x16_bf16(a[0], b[0][q], acc[q]);
 }
 
+// A full sub-tile (128 x 256 inside W, K = 128: eight chunks, four 32-column
+// pieces per wave): the chunk loop unrolled, the operands of chunk c+2
+// fetched while chunk c is multiplied (two register sets), and the old W
+// tile read during the last two chunks, behind every operand fetch.  Loads
+// complete in issue order, so no operand wait includes the W tile.
+__device__ __forceinline__ void rest_split_body_full(unsigned char* smem, int64_t r0, int64_t c0,
+                                                     float* __restrict__ Wk, int64_t d_out, int64_t d_in,
+                                                     const float* __restrict__ E, int64_t ldE,
+                                                     const __bf16* __restrict__ U3b, int64_t ldk, bool vec) {
+    constexpr int kChunks = kMaxBlock / kSK;
+    __bf16* S0 = reinterpret_cast<__bf16*>(smem);  // [2][kSBuf]
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wi = w >> 1, wj = w & 1;
+    const int colw = wj * 4 * 32;
+    const int64_t cw = c0 + colw;
+    const int64_t c_end = c0 + kRestCols;
+    // wave-uniform base and 32-bit element offsets (at most 31 d_in + 127)
+    float* __restrict__ wbase = Wk + (r0 + wi * 32) * d_in + cw;
+    const int di = (int)d_in;
+    // offsets formed at each use from an opaque copy of the lane index, so
+    // that the 64 addresses are not kept live from the loads to the stores
+    auto woff = [&](int q, int v) {
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        return (unsigned)(acc32_row(v, l) * di + 32 * q + (l & 31));
+    };
+
+    float16v acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = (float16v){};
+    float e[2][4];
+    bf16x8 u[2][3];
+    rest_split_fetch(e[0], u[0], E, ldE, U3b, ldk, d_out, d_in, r0, c0, c_end, kMaxBlock, 0, tid, vec);
+    __builtin_amdgcn_sched_barrier(0);
+    rest_split_fetch(e[1], u[1], E, ldE, U3b, ldk, d_out, d_in, r0, c0, c_end, kMaxBlock, kSK, tid, vec);
+    float wold[4][16];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        __bf16* S = S0 + (c & 1) * kSBuf;
+        rest_split_stash(e[c & 1], u[c & 1], S, tid);
+        __syncthreads();
+        if (c + 2 < kChunks)
+            rest_split_fetch(e[c & 1], u[c & 1], E, ldE, U3b, ldk, d_out, d_in, r0, c0, c_end, kMaxBlock,
+                             (c + 2) * kSK, tid, vec);
+        if (c >= kChunks - 2) {
+            // half of the old W tile: pieces 2 (c - 6) and 2 (c - 6) + 1
+#pragma unroll
+            for (int q = 2 * (c - (kChunks - 2)); q < 2 * (c - (kChunks - 2)) + 2; ++q)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) wold[q][v] = wbase[woff(q, v)];
+        }
+        rest_split_chunk<4>(S, wi, colw, lane, acc);
+        __builtin_amdgcn_sched_barrier(0);  // keep each chunk's work inside its own iteration
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) wbase[woff(q, v)] = wold[q][v] - acc[q][v];
+}
+
 __device__ __forceinline__ void rest_split_body(unsigned char* smem, int64_t r0, int64_t c0, int64_t c_end,
                                                 float* __restrict__ Wk, int64_t d_out, int64_t d_in,
                                                 const float* __restrict__ E, int64_t ldE,
@@ -1078,6 +1138,10 @@ __device__ __forceinline__ void rest_split_body(unsigned char* smem, int64_t r0,
     const int64_t cw = c0 + colw;
     const int nq = (int)std::min<int64_t>(ns, std::max<int64_t>(0, (c_end - cw + 31) / 32));
     const bool inner = (r0 + kRestRows <= d_out) && (cw + 32 * nq <= c_end);
+    if (kp == kMaxBlock && nq == 4 && inner && c_end - c0 == kRestCols) {
+        rest_split_body_full(smem, r0, c0, Wk, d_out, d_in, E, ldE, U3b, ldk, vec);
+        return;
+    }
 
     float16v acc[4];
 #pragma unroll
