@@ -13,7 +13,8 @@
 namespace gptq {
 
 // ---------------------------------------------------------------------------
-// Kernel timing: host-side list of event pairs for the selected kernel id.
+// Kernel timing: host-side list of event pairs for the selected kernel id,
+// one pair per launch, stamped by the dispatch (GPTQ_LAUNCH).
 // ---------------------------------------------------------------------------
 namespace {
 const char* const kNames[K_COUNT] = {
@@ -37,7 +38,7 @@ thread_local bool t_timing_off = false;
 TimingOff::TimingOff() : prev(t_timing_off) { t_timing_off = true; }
 TimingOff::~TimingOff() { t_timing_off = prev; }
 
-TimedLaunch::TimedLaunch(int id, hipStream_t s) : slot(-1), stream(s) {
+LaunchEvents::LaunchEvents(int id) {
     if (t_timing_off) return;
     std::lock_guard<std::mutex> lock(g_mu);
     if (id != g_timed) return;
@@ -52,18 +53,9 @@ TimedLaunch::TimedLaunch(int id, hipStream_t s) : slot(-1), stream(s) {
             return;
         }
     }
-    if (hipEventRecord(ep.a, s) != hipSuccess) {
-        g_free.push_back(ep);
-        return;
-    }
     g_pending.push_back(ep);
-    slot = (int)g_pending.size() - 1;
-}
-
-TimedLaunch::~TimedLaunch() {
-    if (slot < 0) return;
-    std::lock_guard<std::mutex> lock(g_mu);
-    (void)hipEventRecord(g_pending[slot].b, stream);
+    a = ep.a;
+    b = ep.b;
 }
 
 int device_cu_count() {

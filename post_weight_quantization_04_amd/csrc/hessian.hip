@@ -562,18 +562,18 @@ hipError_t launch_hessian(float* H, int64_t n, const void* X, int x_is_f16, int6
         const int n_cu = device_cu_count();
         if (Tw >= kWideMinT && n_cu > 0 && tw_all >= (int64_t)kWideMinRounds * n_cu) {
             const int per_xcd = (int)((tw_all + kXcds - 1) / kXcds);
-            hipLaunchKernelGGL((hessian_f16_kernel<kWideTile, kWideThreads, kKf16, kDepthf16>),
+            GPTQ_LAUNCH(t, (hessian_f16_kernel<kWideTile, kWideThreads, kKf16, kDepthf16>),
                                dim3((unsigned)(per_xcd * kXcds)), dim3(kWideThreads), 0, s, H, n,
                                static_cast<const half_t*>(X), ldx, ntok, nfull, (int)Tw, per_xcd);
         } else if (Tw >= kWideMinT) {
             const int64_t Tm = (n + kWsTile - 1) / kWsTile;
             const int64_t nfull_ws = vec ? ntok / kWsK : 0;
             const int per_xcd = (int)((Tm * (Tm + 1) / 2 + kXcds - 1) / kXcds);
-            hipLaunchKernelGGL(hessian_f16_ws_kernel, dim3((unsigned)(per_xcd * kXcds)), dim3(kWsThreads), 0, s, H, n,
+            GPTQ_LAUNCH(t, hessian_f16_ws_kernel, dim3((unsigned)(per_xcd * kXcds)), dim3(kWsThreads), 0, s, H, n,
                                static_cast<const half_t*>(X), ldx, ntok, nfull_ws, (int)Tm, per_xcd);
         } else {
             const int per_xcd = (int)((tiles + kXcds - 1) / kXcds);
-            hipLaunchKernelGGL((hessian_f16_kernel<kTile, kThreads, kKf16, kDepthf16>),
+            GPTQ_LAUNCH(t, (hessian_f16_kernel<kTile, kThreads, kKf16, kDepthf16>),
                                dim3((unsigned)(per_xcd * kXcds)), dim3(kThreads), 0, s, H, n,
                                static_cast<const half_t*>(X), ldx, ntok, nfull, (int)T, per_xcd);
         }
@@ -581,10 +581,10 @@ hipError_t launch_hessian(float* H, int64_t n, const void* X, int x_is_f16, int6
         TimedLaunch t(K_HESS_F32, s);
         const bool vec = (addr % 16 == 0) && (ldx % 4 == 0);
         if (vec)
-            hipLaunchKernelGGL(hessian_f32_kernel<true>, dim3((unsigned)tiles), dim3(kThreads), 0, s, H, n,
+            GPTQ_LAUNCH(t, hessian_f32_kernel<true>, dim3((unsigned)tiles), dim3(kThreads), 0, s, H, n,
                                static_cast<const float*>(X), ldx, ntok);
         else
-            hipLaunchKernelGGL(hessian_f32_kernel<false>, dim3((unsigned)tiles), dim3(kThreads), 0, s, H, n,
+            GPTQ_LAUNCH(t, hessian_f32_kernel<false>, dim3((unsigned)tiles), dim3(kThreads), 0, s, H, n,
                                static_cast<const float*>(X), ldx, ntok);
     }
     return hipGetLastError();

@@ -1048,18 +1048,18 @@ hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, floa
     hipError_t e = hipSuccess;
     {
         TimedLaunch t(K_HINV_DIAGSUM, s);
-        hipLaunchKernelGGL(diag_stats_kernel, dim3(1), dim3(1024), 0, s, H, n, damp_frac, dead, w.scal, lambda_out,
+        GPTQ_LAUNCH(t, diag_stats_kernel, dim3(1), dim3(1024), 0, s, H, n, damp_frac, dead, w.scal, lambda_out,
                            info, w.fail);
     }
     {
         TimedLaunch t(K_HINV_LOAD, s);
-        hipLaunchKernelGGL(load_reversed_kernel<double>, dim3((unsigned)((int64_t)T * (T + 1) / 2)), dim3(256), 0, s, H, n,
+        GPTQ_LAUNCH(t, load_reversed_kernel<double>, dim3((unsigned)((int64_t)T * (T + 1) / 2)), dim3(256), 0, s, H, n,
                            np, (const double*)w.scal, w.G);
     }
     const int npan = std::max(T - 1, 1);  // workgroups of the diagonal-block + panel launch of step 0
     {
         TimedLaunch t(K_CHOL_STEP, s);
-        hipLaunchKernelGGL(chol_diag_panel_kernel, dim3((unsigned)npan), dim3(kGemmThreads), 0, s, w.G, np, Pbuf[0], T,
+        GPTQ_LAUNCH(t, chol_diag_panel_kernel, dim3((unsigned)npan), dim3(kGemmThreads), 0, s, w.G, np, Pbuf[0], T,
                            info, w.fail);
     }
     // wide layers pair the steps: an even step's update of the rest is
@@ -1078,15 +1078,15 @@ hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, floa
         const double* pkm = Pbuf[(k + 2) % 3];  // step k-1
         TimedLaunch t(K_CHOL_STEP, s);
         if (paired && odd)
-            hipLaunchKernelGGL(chol_step_kernel<true>, grid, dim3(kGemmThreads), 0, s, w.G, np, pk1, pk, pkm, k, T,
+            GPTQ_LAUNCH(t, chol_step_kernel<true>, grid, dim3(kGemmThreads), 0, s, w.G, np, pk1, pk, pkm, k, T,
                                np1, info, w.fail);
         else
-            hipLaunchKernelGGL(chol_step_kernel<false>, grid, dim3(kGemmThreads), 0, s, w.G, np, pk1, pk, pkm, k, T,
+            GPTQ_LAUNCH(t, chol_step_kernel<false>, grid, dim3(kGemmThreads), 0, s, w.G, np, pk1, pk, pkm, k, T,
                                np1, info, w.fail);
     }
     {
         TimedLaunch t(K_HINV_STORE, s);
-        hipLaunchKernelGGL(store_u_kernel<double>, dim3((unsigned)n), dim3(256), 0, s, (const double*)w.G, np, n, U,
+        GPTQ_LAUNCH(t, store_u_kernel<double>, dim3((unsigned)n), dim3(256), 0, s, (const double*)w.G, np, n, U,
                            (const int*)w.fail);
     }
     return hipGetLastError();

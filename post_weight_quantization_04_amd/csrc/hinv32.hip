@@ -978,18 +978,18 @@ hipError_t launch_prepare_hinv32(const float* H, int64_t n, double damp_frac, fl
     float* Pbuf[3] = {w.P, w.P + pstride, w.P + 2 * pstride};  // step s: buffer s % 3
     {
         TimedLaunch t(K_HINV_DIAGSUM, s);
-        hipLaunchKernelGGL(diag_stats_kernel, dim3(1), dim3(1024), 0, s, H, n, damp_frac, dead, w.scal, lambda_out,
+        GPTQ_LAUNCH(t, diag_stats_kernel, dim3(1), dim3(1024), 0, s, H, n, damp_frac, dead, w.scal, lambda_out,
                            info, w.fail);
     }
     {
         TimedLaunch t(K_HINV32_LOAD, s);
-        hipLaunchKernelGGL(load_reversed_kernel<float>, dim3((unsigned)((int64_t)T * (T + 1) / 2)), dim3(256), 0, s,
+        GPTQ_LAUNCH(t, load_reversed_kernel<float>, dim3((unsigned)((int64_t)T * (T + 1) / 2)), dim3(256), 0, s,
                            H, n, np, (const double*)w.scal, w.G);
     }
     const int npan = T - 1 > 1 ? T - 1 : 1;  // workgroups of the step-0 launch
     {
         TimedLaunch t(K_CHOL32_STEP, s);
-        hipLaunchKernelGGL(chol32_diag_panel_kernel, dim3((unsigned)npan), dim3(kThreads), 0, s, w.G, np, Pbuf[0], T,
+        GPTQ_LAUNCH(t, chol32_diag_panel_kernel, dim3((unsigned)npan), dim3(kThreads), 0, s, w.G, np, Pbuf[0], T,
                            info, w.fail);
     }
     bool paired = sched::chol_paired(T);
@@ -1003,15 +1003,15 @@ hipError_t launch_prepare_hinv32(const float* H, int64_t n, double damp_frac, fl
         const float* pkm = Pbuf[(k + 2) % 3];  // step k-1
         TimedLaunch t(K_CHOL32_STEP, s);
         if (paired && odd)
-            hipLaunchKernelGGL(chol32_step_kernel<true>, grid, dim3(kThreads), 0, s, w.G, np, pk1, pk, pkm, k, T,
+            GPTQ_LAUNCH(t, chol32_step_kernel<true>, grid, dim3(kThreads), 0, s, w.G, np, pk1, pk, pkm, k, T,
                                g.nchain, info, w.fail);
         else
-            hipLaunchKernelGGL(chol32_step_kernel<false>, grid, dim3(kThreads), 0, s, w.G, np, pk1, pk, pkm, k, T,
+            GPTQ_LAUNCH(t, chol32_step_kernel<false>, grid, dim3(kThreads), 0, s, w.G, np, pk1, pk, pkm, k, T,
                                g.nchain, info, w.fail);
     }
     {
         TimedLaunch t(K_HINV32_STORE, s);
-        hipLaunchKernelGGL(store_u_kernel<float>, dim3((unsigned)n), dim3(256), 0, s, (const float*)w.G, np, n, U,
+        GPTQ_LAUNCH(t, store_u_kernel<float>, dim3((unsigned)n), dim3(256), 0, s, (const float*)w.G, np, n, U,
                            (const int*)w.fail);
     }
     return hipGetLastError();

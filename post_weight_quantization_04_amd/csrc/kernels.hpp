@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -32,16 +33,26 @@ enum KernelId {
     K_COUNT
 };
 
-// Records a HIP event pair around the launches made while it is alive when
-// timing is enabled for `id` (see gptq_timing_enable); a no-op otherwise.
+// Kernel id of the launches in its scope, for the timing hook (see
+// gptq_timing_enable).  Every launch goes through GPTQ_LAUNCH, which, while
+// timing is enabled for that id, has the dispatch itself stamp a fresh HIP
+// event pair with the kernel's start and end (no marker packets between the
+// launches, so timed launches keep their spacing); a plain launch otherwise.
 struct TimedLaunch {
-    TimedLaunch(int id, hipStream_t s);
-    ~TimedLaunch();
-    int slot;
-    hipStream_t stream;
+    TimedLaunch(int kernel_id, hipStream_t) : id(kernel_id) {}
+    int id;
 };
+struct LaunchEvents {
+    explicit LaunchEvents(int id);
+    hipEvent_t a = nullptr, b = nullptr;
+};
+#define GPTQ_LAUNCH(t, kernel, grid, block, shmem, stream, ...)                                        \
+    do {                                                                                             \
+        const ::gptq::LaunchEvents gptq_ev_((t).id);                                                 \
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, gptq_ev_.a, gptq_ev_.b, 0u, __VA_ARGS__); \
+    } while (0)
 
-// While alive, TimedLaunch records nothing on this thread (the timing hook
+// While alive, launches record no events on this thread (the timing hook
 // creates HIP events, which entry points that must not allocate avoid).
 struct TimingOff {
     TimingOff();

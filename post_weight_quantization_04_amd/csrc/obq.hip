@@ -207,15 +207,15 @@ hipError_t launch_obq(const void* W, int w_is_f16, int64_t d_out, int64_t d_in, 
     {
         TimedLaunch t(K_OBQ_HINV, s);
         const int64_t n2 = d_in * d_in;
-        hipLaunchKernelGGL(obq_hinv_kernel, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, s, U, (int)d_in, Hinv);
+        GPTQ_LAUNCH(t, obq_hinv_kernel, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, s, U, (int)d_in, Hinv);
     }
     TimedLaunch t(K_OBQ_ROWS, s);
     if (w_is_f16)
-        hipLaunchKernelGGL(obq_row_kernel<half_t>, dim3((unsigned)d_out), dim3(256), 0, s,
+        GPTQ_LAUNCH(t, obq_row_kernel<half_t>, dim3((unsigned)d_out), dim3(256), 0, s,
                            static_cast<const half_t*>(W), (int)d_in, (const double*)Hinv, dead, bits, codes, scales,
                            zeros, order, loss);
     else
-        hipLaunchKernelGGL(obq_row_kernel<float>, dim3((unsigned)d_out), dim3(256), 0, s,
+        GPTQ_LAUNCH(t, obq_row_kernel<float>, dim3((unsigned)d_out), dim3(256), 0, s,
                            static_cast<const float*>(W), (int)d_in, (const double*)Hinv, dead, bits, codes, scales,
                            zeros, order, loss);
     return hipGetLastError();

@@ -189,7 +189,7 @@ hipError_t launch_pack(const uint8_t* codes, int64_t d_out, int64_t d_in, int bi
     TimedLaunch t(K_PACK, s);
     for (int64_t r0 = 0; r0 < d_out; r0 += 65535) {  // grid y is at most 65535 rows per launch
         const unsigned rows = (unsigned)std::min<int64_t>(65535, d_out - r0);
-        hipLaunchKernelGGL(pack_codes_kernel, dim3((unsigned)((nw + 255) / 256), rows), dim3(256), 0, s,
+        GPTQ_LAUNCH(t, pack_codes_kernel, dim3((unsigned)((nw + 255) / 256), rows), dim3(256), 0, s,
                            codes + r0 * d_in, (int)d_in, bits, (int)nw, packed + r0 * nw);
     }
     return hipGetLastError();
@@ -204,11 +204,11 @@ hipError_t launch_dequant(const uint32_t* packed, int bits, int64_t d_out, int64
     for (int64_t r0 = 0; r0 < d_out; r0 += 65535) {
         const unsigned rows = (unsigned)std::min<int64_t>(65535, d_out - r0);
         if (out_is_f16)
-            hipLaunchKernelGGL(dequant_kernel<half_t>, dim3(gx, rows), dim3(256), 0, s, packed + r0 * nw, bits,
+            GPTQ_LAUNCH(t, dequant_kernel<half_t>, dim3(gx, rows), dim3(256), 0, s, packed + r0 * nw, bits,
                                (int)nw, (int)d_in, scales + r0 * ng, zeros + r0 * ng, (int)group, (int)ng,
                                static_cast<half_t*>(out) + r0 * d_in);
         else
-            hipLaunchKernelGGL(dequant_kernel<float>, dim3(gx, rows), dim3(256), 0, s, packed + r0 * nw, bits,
+            GPTQ_LAUNCH(t, dequant_kernel<float>, dim3(gx, rows), dim3(256), 0, s, packed + r0 * nw, bits,
                                (int)nw, (int)d_in, scales + r0 * ng, zeros + r0 * ng, (int)group, (int)ng,
                                static_cast<float*>(out) + r0 * d_in);
     }
@@ -223,11 +223,11 @@ hipError_t launch_output_error(const void* W, int w_is_f16, const uint8_t* dead,
     const int64_t ng = group ? d_in / group : 1;
     TimedLaunch t(K_OUTERR, s);
     if (w_is_f16)
-        hipLaunchKernelGGL(output_error_kernel<half_t>, dim3((unsigned)d_out), dim3(256), 0, s,
+        GPTQ_LAUNCH(t, output_error_kernel<half_t>, dim3((unsigned)d_out), dim3(256), 0, s,
                            static_cast<const half_t*>(W), dead, packed, bits, (int)nw, (int)d_in, scales, zeros,
                            (int)group, (int)ng, err_row, lambda, out);
     else
-        hipLaunchKernelGGL(output_error_kernel<float>, dim3((unsigned)d_out), dim3(256), 0, s,
+        GPTQ_LAUNCH(t, output_error_kernel<float>, dim3((unsigned)d_out), dim3(256), 0, s,
                            static_cast<const float*>(W), dead, packed, bits, (int)nw, (int)d_in, scales, zeros,
                            (int)group, (int)ng, err_row, lambda, out);
     return hipGetLastError();

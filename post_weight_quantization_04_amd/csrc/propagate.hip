@@ -213,7 +213,7 @@ hipError_t launch_propagate(const void* W, int64_t d_out, int64_t d_in, const vo
     half_t* y = static_cast<half_t*>(Y);
     TimedLaunch t(K_PROPAGATE, s);
 #define PROP_LAUNCH(A, B, R) \
-    hipLaunchKernelGGL((propagate_kernel<A, B, R>), grid, dim3(kPThreads), 0, s, w, d_out, d_in, x, ntok, ldx, y, ldy, ntn)
+    GPTQ_LAUNCH(t, (propagate_kernel<A, B, R>), grid, dim3(kPThreads), 0, s, w, d_out, d_in, x, ntok, ldx, y, ldy, ntn)
 #define PROP_RELU(A, B) \
     do {                \
         if (relu) PROP_LAUNCH(A, B, true); \

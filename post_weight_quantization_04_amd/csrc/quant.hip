@@ -1296,10 +1296,10 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
 #define GC_LAUNCH(T, V, G)                                                                                    \
     do {                                                                                                      \
         if (dead)                                                                                             \
-            hipLaunchKernelGGL((grid_convert_kernel<T, V, G, true>), grid, blk, 0, s, static_cast<const T*>(W), \
+            GPTQ_LAUNCH(t, (grid_convert_kernel<T, V, G, true>), grid, blk, 0, s, static_cast<const T*>(W), \
                                w.Wk, d_out, d_in, dead, maxq, scales, zeros, minmax, U, w.rdiag, err_row);      \
         else                                                                                                  \
-            hipLaunchKernelGGL((grid_convert_kernel<T, V, G, false>), grid, blk, 0, s, static_cast<const T*>(W), \
+            GPTQ_LAUNCH(t, (grid_convert_kernel<T, V, G, false>), grid, blk, 0, s, static_cast<const T*>(W), \
                                w.Wk, d_out, d_in, dead, maxq, scales, zeros, minmax, U, w.rdiag, err_row);      \
     } while (0)
         if (w_is_f16) {
@@ -1328,7 +1328,7 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
         TimedLaunch t(K_Q_SPLITU, s);
         // the last block's pieces are never read (no update follows it)
         const dim3 grid((unsigned)((d_in + 63) / 64), (unsigned)((d_in + block - 1) / block - 1));
-        hipLaunchKernelGGL(split_u_kernel, grid, dim3(256), 0, s, U, d_in, block, ldk, w.U3);
+        GPTQ_LAUNCH(t, split_u_kernel, grid, dim3(256), 0, s, U, d_in, block, ldk, w.U3);
     }
     const int bmax = (int)std::min(block, d_in);
     const size_t near_bytes = (size_t)((bmax + 3) & ~3) * kEtl * 4;
@@ -1365,15 +1365,15 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
                 TimedLaunch t(K_Q_TRAIL, s);
                 dim3 grid((unsigned)((d_in - b0 + kTT - 1) / kTT), (unsigned)((d_out + kTrailRows - 1) / kTrailRows));
                 if (vec)
-                    hipLaunchKernelGGL((trail_kernel<true, kTrailRows>), grid, dim3(256), 0, s, w.Wk, d_out, d_in, Ep,
+                    GPTQ_LAUNCH(t, (trail_kernel<true, kTrailRows>), grid, dim3(256), 0, s, w.Wk, d_out, d_in, Ep,
                                        block, U, bp0, b0, b0, d_in);
                 else
-                    hipLaunchKernelGGL((trail_kernel<false, kTrailRows>), grid, dim3(256), 0, s, w.Wk, d_out, d_in, Ep,
+                    GPTQ_LAUNCH(t, (trail_kernel<false, kTrailRows>), grid, dim3(256), 0, s, w.Wk, d_out, d_in, Ep,
                                        block, U, bp0, b0, b0, d_in);
                 kp = 0;
             }
             TimedLaunch t(K_Q_GROUPGRID, s);
-            hipLaunchKernelGGL(group_grid_kernel, dim3(rows4), dim3(256), 0, s, (const float*)w.Wk, d_out, d_in, b0,
+            GPTQ_LAUNCH(t, group_grid_kernel, dim3(rows4), dim3(256), 0, s, (const float*)w.Wk, d_out, d_in, b0,
                                group, b0 / group, ng, maxq, scales, zeros, minmax);
         }
         FarSplit fs;
@@ -1386,7 +1386,7 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
         TimedLaunch t(K_Q_STEP, s);
         const dim3 grid((unsigned)(row_tiles + n_far));
 #define STEP_LAUNCH(FULL, SPLIT)                                                                             \
-    hipLaunchKernelGGL((step_kernel<FULL, SPLIT>), grid, dim3(512), lds, s, w.Wk, d_out, d_in, U,              \
+    GPTQ_LAUNCH(t, (step_kernel<FULL, SPLIT>), grid, dim3(512), lds, s, w.Wk, d_out, d_in, U,              \
                        (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes, Eb, block, \
                        err_row, Ep, bp0, kp, row_tiles, fs, (int)vec, U3b, ldk)
         if (bw % kSub == 0) {
