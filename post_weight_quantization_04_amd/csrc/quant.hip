@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void split_u_kernel(const float* __restrict__ 
     __shared__ float T[128][65];
     const int64_t b = blockIdx.y;
     const int64_t c0 = (int64_t)blockIdx.x * 64;
-    if (c0 + 64 <= (b + 2) * block) return;  // columns this block's pieces are never read for
+    if (c0 + 64 <= (b + 1) * block) return;  // columns this block's pieces are never read for
     const int64_t k0 = b * block;
     const int kb = (int)min(block, d_in - k0);
     const int tid = threadIdx.x;
@@ -389,6 +389,67 @@ __device__ __forceinline__ void near_update(float (&wv)[kSub], const float (&ua)
     sub_row_deltas(wv, acc);
 }
 
+// The same near update with split-precision products (the split path): the
+// scaled errors E_prev and U are each the sum of three bf16 pieces, and the
+// update is formed from the six piece products with i + j <= 2 on MFMA
+// 16x16x32 bf16 (each product exact in fp32, fp32 accumulation), as in the
+// far update.  The U operand U_blk^T (16 columns x kp) is read as 16-byte
+// runs along k from the pieces split once per layer (U3p: the previous
+// block's, [3][d_in][ldk], column-major by k; zero past the block); the E
+// operand from its pieces staged in LDS by row (ets[p][row][k], zero past kp).
+// The result has the layout of near_update's, so the same row transpose
+// applies it.
+constexpr int kEtsLd = kMaxBlock + 8;                 // LDS row of a staged E piece (bf16)
+constexpr int kEtsPiece = kRowsPerWg * kEtsLd;       // one E piece (bf16)
+
+__device__ __forceinline__ float4v mfma16x16x32_bf16(bf16x8 a, bf16x8 b, float4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void near_update_split(float (&wv)[kSub], const __bf16* __restrict__ U3p, int64_t d_in,
+                                                  int64_t ldk, int64_t c0q, int cq, const __bf16* __restrict__ ets,
+                                                  int kp, int lane) {
+    const int i = lane & 15, g = lane >> 4;
+    float4v acc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m] = (float4v){};
+    const __bf16* ucol = U3p + (c0q + i) * ldk;
+#pragma unroll
+    for (int c = 0; c < kMaxBlock / 32; ++c) {
+        if (32 * c < kp) {
+            const int k0 = 32 * c + 8 * g;
+            bf16x8 a[3];
+#pragma unroll
+            for (int q = 0; q < 3; ++q)
+                a[q] = (i < cq && k0 < ldk) ? *reinterpret_cast<const bf16x8*>(ucol + q * d_in * ldk + k0)
+                                            : (bf16x8){};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                bf16x8 b[3];
+#pragma unroll
+                for (int q = 0; q < 3; ++q)
+                    b[q] = *reinterpret_cast<const bf16x8*>(&ets[q * kEtsPiece + (16 * m + i) * kEtsLd + k0]);
+                // the smaller piece products first
+                acc[m] = mfma16x16x32_bf16(a[2], b[0], acc[m]);
+                acc[m] = mfma16x16x32_bf16(a[1], b[1], acc[m]);
+                acc[m] = mfma16x16x32_bf16(a[0], b[2], acc[m]);
+                acc[m] = mfma16x16x32_bf16(a[1], b[0], acc[m]);
+                acc[m] = mfma16x16x32_bf16(a[0], b[1], acc[m]);
+                acc[m] = mfma16x16x32_bf16(a[0], b[0], acc[m]);
+            }
+        }
+    }
+    sub_row_deltas(wv, acc);
+}
+
+// LDS of the staged E_prev: transposed fp32 (near_update) or three bf16
+// pieces by row (near_update_split), after the sweep's own regions; 16 bytes
+// of slack let the pieces start 16-byte aligned.
+__host__ __device__ inline size_t near_lds_bytes(int kp, bool split) {
+    if (kp <= 0) return 0;
+    return split ? (size_t)3 * kEtsPiece * 2 + 16 : (size_t)((kp + 3) & ~3) * kEtl * 4;
+}
+
 // Rounds this wave's columns in order, compensating the later columns of
 // the sub-block at once.  U rows of the sub-block and 1/U_jj are read into
 // registers before the dependent chain starts.
@@ -446,9 +507,9 @@ __device__ __forceinline__ void sweep_sub(float (&wv)[kSub], float s, float sinv
 // width is a multiple of 16, so every wave owns 16 columns and the unguarded
 // code paths are the only ones compiled.  With kp > 0 the scaled errors Ep
 // of the previous block [bp0, bp0 + kp) are applied to this block's columns
-// first (near_update); the LDS then holds E_prev^T after the sweep's own
-// regions.
-template <bool kAllFull>
+// first (near_update, or near_update_split with kSplit); the LDS then holds
+// E_prev^T (or its bf16 pieces) after the sweep's own regions.
+template <bool kAllFull, bool kSplit>
 __device__ __forceinline__ void sweep_body(unsigned char* smem, int rt, const float* __restrict__ Wk, int64_t d_out,
                                            int64_t d_in, const float* __restrict__ U,
                                            const float* __restrict__ rdiag, int64_t b0, int64_t b1, int bits,
@@ -456,7 +517,7 @@ __device__ __forceinline__ void sweep_body(unsigned char* smem, int rt, const fl
                                            int32_t* __restrict__ zeros, float* __restrict__ minmax,
                                            uint8_t* __restrict__ codes, float* __restrict__ E, int64_t ldE,
                                            float* __restrict__ err_row, const float* __restrict__ Ep, int64_t bp0,
-                                           int kp) {
+                                           int kp, const __bf16* __restrict__ U3p, int64_t ldk) {
     const int bw = (int)(b1 - b0);
     const int nw = (bw + kSub - 1) / kSub;
     const int uld = kUld;
@@ -466,6 +527,8 @@ __device__ __forceinline__ void sweep_body(unsigned char* smem, int rt, const fl
     float* red = Ebuf + 2 * kSub * kEld;                                  // nw*64*2
     float* errs = red + nw * 64 * 2;                                      // nw*64
     float* et = errs + nw * 64;                                           // [kp rounded up to 4][kEtl]
+    // split path: [3][kRowsPerWg][kEtsLd] bf16 pieces, 16-byte aligned
+    __bf16* ets = reinterpret_cast<__bf16*>(smem + ((reinterpret_cast<uintptr_t>(et) - reinterpret_cast<uintptr_t>(smem) + 15) & ~(uintptr_t)15));
 
     const int lane = threadIdx.x & 63;
     const int q = wave_id();
@@ -512,10 +575,12 @@ __device__ __forceinline__ void sweep_body(unsigned char* smem, int rt, const fl
     const int er = threadIdx.x >> 3, ek = (threadIdx.x & 7) * 16;
     if (kp > 0) {
         const int i = lane & 15, g = lane >> 4;
+        if (!kSplit) {
 #pragma unroll
-        for (int j = 0; j < kMaxBlock / 4; ++j) {
-            const int k = 4 * j + g;
-            ua[j] = (k < kp && i < cq) ? U[(bp0 + k) * d_in + c0q + i] : 0.0f;
+            for (int j = 0; j < kMaxBlock / 4; ++j) {
+                const int k = 4 * j + g;
+                ua[j] = (k < kp && i < cq) ? U[(bp0 + k) * d_in + c0q + i] : 0.0f;
+            }
         }
         const int64_t Re = (int64_t)rt * kRowsPerWg + er;
         const float* src = Ep + Re * ldE + ek;
@@ -567,16 +632,38 @@ __device__ __forceinline__ void sweep_body(unsigned char* smem, int rt, const fl
     }
     for (int e = threadIdx.x; e < bw; e += nth) rdg[e] = rdiag[b0 + e];
     if (kp > 0) {
-        const int kp4 = (kp + 3) & ~3;
+        if (kSplit) {
+            // the three bf16 pieces of E_prev row er, k = ek .. ek + 15 (zero
+            // past kp: ep holds zeros there)
+            bf16x8 p[3][2];
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            if (ek + e < kp4) et[(ek + e) * kEtl + er] = ep[e];
+            for (int e = 0; e < 16; ++e) {
+                __bf16 h0, h1, h2;
+                split3(ep[e], h0, h1, h2);
+                p[0][e >> 3][e & 7] = h0;
+                p[1][e >> 3][e & 7] = h1;
+                p[2][e >> 3][e & 7] = h2;
+            }
+#pragma unroll
+            for (int q = 0; q < 3; ++q)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    *reinterpret_cast<bf16x8*>(&ets[q * kEtsPiece + er * kEtsLd + ek + 8 * h]) = p[q][h];
+        } else {
+            const int kp4 = (kp + 3) & ~3;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (ek + e < kp4) et[(ek + e) * kEtl + er] = ep[e];
+        }
     }
 
     float sinv = 1.0f / s;
     float errsq = 0.0f;
     __syncthreads();
-    if (kp > 0) near_update(wv, ua, et, kp, lane);
+    if (kp > 0) {
+        if (kSplit) near_update_split(wv, U3p, d_in, ldk, c0q, cq, ets, kp, lane);
+        else near_update(wv, ua, et, kp, lane);
+    }
 
     for (int p = 0; p < nw; ++p) {
         // wave p carries the dependent chain of this phase: it gets issue
@@ -1237,8 +1324,8 @@ __global__ __launch_bounds__(512) void step_kernel(float* __restrict__ Wk, int64
     extern __shared__ __align__(16) unsigned char smem[];
     const int b = (int)blockIdx.x;
     if (b < row_tiles)
-        sweep_body<kAllFull>(smem, b, Wk, d_out, d_in, U, rdiag, b0, b1, bits, group, ng, scales, zeros, minmax,
-                             codes, E, ldE, err_row, Ep, bp0, kp);
+        sweep_body<kAllFull, kSplit>(smem, b, Wk, d_out, d_in, U, rdiag, b0, b1, bits, group, ng, scales, zeros,
+                                     minmax, codes, E, ldE, err_row, Ep, bp0, kp, U3b, ldk);
     int64_t u0, u1;
     sched::far_units(fs, b, row_tiles, u0, u1);
     if (u1 > u0) far_range<kSplit>(smem, u0, u1, fs, Wk, d_out, d_in, Ep, ldE, U, U3b, ldk, bp0, kp, vec_rest != 0);
@@ -1331,7 +1418,7 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
         GPTQ_LAUNCH(t, split_u_kernel, grid, dim3(256), 0, s, U, d_in, block, ldk, w.U3);
     }
     const int bmax = (int)std::min(block, d_in);
-    const size_t near_bytes = (size_t)((bmax + 3) & ~3) * kEtl * 4;
+    const size_t near_bytes = near_lds_bytes(bmax, split);
     const size_t rest_bytes = split ? rest_split_lds_bytes() : rest_lds_bytes();
     const size_t ldsmax = std::max(sweep_lds_bytes(bmax) + near_bytes, rest_bytes);
     if (ldsmax > 64 * 1024) {
@@ -1381,7 +1468,7 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
         fs.nstrip = (int)((d_in - b1 + kStrip - 1) / kStrip);
         const int64_t n_units = (kp > 0 && b1 < d_in) ? (int64_t)rest_rows * fs.nstrip : 0;
         const int n_far = sched::far_split(n_units, row_tiles, n_cu, fs);
-        size_t lds = sweep_lds_bytes(bw) + (kp > 0 ? (size_t)((kp + 3) & ~3) * kEtl * 4 : 0);
+        size_t lds = sweep_lds_bytes(bw) + near_lds_bytes(kp, split);
         if (n_units > 0) lds = std::max(lds, rest_bytes);
         TimedLaunch t(K_Q_STEP, s);
         const dim3 grid((unsigned)(row_tiles + n_far));
