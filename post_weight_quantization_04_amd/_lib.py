@@ -63,6 +63,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise FileNotFoundError(
             f"{path} is missing: build it with `python -m post_weight_quantization_04_amd.build`")
+    # torch ships its own HIP runtime under the same soname.  Loading torch
+    # first makes the library bind to that one runtime, the one that owns the
+    # device memory and streams handed in; loaded the other way round, the
+    # process holds two runtimes and every launch on torch's buffers fails.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     sig = {
         "gptq_hessian_accumulate": (_i32, [_vp, _i64, _vp, _i32, _i64, _i64, _vp]),

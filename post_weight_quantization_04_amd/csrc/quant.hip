@@ -109,10 +109,28 @@ __global__ __launch_bounds__(256) void split_u_kernel(const float* __restrict__ 
     const int64_t k0 = b * block;
     const int kb = (int)min(block, d_in - k0);
     const int tid = threadIdx.x;
-    for (int e = tid; e < 128 * 64; e += 256) {
-        const int kk = e >> 6, cc = e & 63;
-        const int64_t c = c0 + cc;
-        T[kk][cc] = (kk < kb && c < d_in) ? U[(k0 + kk) * d_in + c] : 0.0f;
+    if (c0 + 64 <= d_in && (d_in & 3) == 0 && (reinterpret_cast<uintptr_t>(U) & 15) == 0) {
+        // every load of the slab in flight before the first LDS store:
+        // thread t reads 16 bytes of rows t/16 + 16 i, columns 4 (t%16) ..
+        float4v v[8];
+        const int cc = 4 * (tid & 15);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int kk = (tid >> 4) + 16 * i;
+            v[i] = (kk < kb) ? *reinterpret_cast<const float4v*>(U + (k0 + kk) * d_in + c0 + cc) : (float4v){};
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int kk = (tid >> 4) + 16 * i;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) T[kk][cc + x] = v[i][x];
+        }
+    } else {
+        for (int e = tid; e < 128 * 64; e += 256) {
+            const int kk = e >> 6, cc = e & 63;
+            const int64_t c = c0 + cc;
+            T[kk][cc] = (kk < kb && c < d_in) ? U[(k0 + kk) * d_in + c] : 0.0f;
+        }
     }
     __syncthreads();
     __bf16* out = U3 + b * 3 * d_in * ldk;
