@@ -46,13 +46,25 @@ __host__ __device__ inline int64_t rup(int64_t a, int64_t b) { return (a + b - 1
 
 struct QuantWs {
     float* Wk;     // [d_out, d_in] working weights
-    float* E[2];   // [d_out, block] scaled errors, alternating between blocks
+    float* E[2];   // scaled errors of a block at eoff, alternating between blocks
     float* rdiag;  // [d_in] 1 / U_jj
-    __bf16* U3;    // split path: bf16 pieces of U by lazy block, [nb][3][d_in][ldk]
+    __bf16* U3;    // split path: bf16 pieces of U by lazy block, [nb][3][ldk/16][d_in][16]
 };
 
 // k extent of one block's U pieces (whole 16-deep chunks)
 __host__ __device__ inline int64_t split_ldk(int64_t block) { return (block + 15) / 16 * 16; }
+// Offset of the scaled error of row r, block column k: runs of 16 columns,
+// each holding every row's 16 values together, so that a sub-block's errors
+// are written, and a K chunk's are read, as consecutive memory.
+__host__ __device__ inline int64_t eoff(int64_t d_out, int64_t r, int k) {
+    return ((int64_t)(k >> 4) * d_out + r) * 16 + (k & 15);
+}
+// Offset of piece p of U[k][c] inside one block's pieces: runs of 16 k, each
+// holding every column's 16 values together, so that the 16-byte operand
+// reads of one k run over consecutive columns are consecutive in memory.
+__host__ __device__ inline int64_t u3_offset(int64_t d_in, int64_t ldk, int p, int64_t k, int64_t c) {
+    return ((p * (ldk / 16) + k / 16) * d_in + c) * 16 + (k & 15);
+}
 __host__ __device__ inline int64_t split_u_elems(int64_t d_in, int64_t block) {
     return ((d_in + block - 1) / block) * 3 * d_in * split_ldk(block);
 }
@@ -64,7 +76,7 @@ QuantWs carve(void* ws, int64_t d_out, int64_t d_in, int64_t block) {
     p += rup(d_out * d_in * 4, 256);
     for (int i = 0; i < 2; ++i) {
         w.E[i] = reinterpret_cast<float*>(p);
-        p += rup(d_out * block * 4, 256);
+        p += rup(d_out * split_ldk(block) * 4, 256);
     }
     w.rdiag = reinterpret_cast<float*>(p);
     p += rup(d_in * 4, 256);
@@ -93,9 +105,9 @@ __device__ __forceinline__ void split3(float x, __bf16& p0, __bf16& p1, __bf16& 
 }
 
 // The bf16 pieces of U for the split trailing update, written once per
-// layer: U3[b][p][c][kk] = piece p of U[b*block + kk][c] (kk < ldk, zero
-// past the block), so that a block's rows of U reach the MFMA B operand as
-// 16-byte reads along k.  Block b's rows are read only by the update after
+// layer: piece p of U[b*block + kk][c] at U3 + b*3*d_in*ldk + u3_offset(p,
+// kk, c) (kk < ldk, zero past the block), so that a block's rows of U reach
+// the MFMA B operand as 16-byte reads along k.  Block b's rows are read only by the update after
 // block b+1, for the columns from (b+2)*block on, so only those are written
 // (the rest of U3 is never read).  One workgroup per (64 columns, block):
 // the 64-column slab of the block's rows is read along rows and transposed
@@ -135,8 +147,10 @@ __global__ __launch_bounds__(256) void split_u_kernel(const float* __restrict__ 
     __syncthreads();
     __bf16* out = U3 + b * 3 * d_in * ldk;
     const int groups = (int)(ldk / 8);
+    // consecutive threads: the two halves of one column's 16-k run, then the
+    // next column, so that the stores of a run are consecutive
     for (int e = tid; e < 64 * groups; e += 256) {
-        const int cc = e / groups, g = e % groups;
+        const int run = e >> 7, cc = (e & 127) >> 1, g = 2 * run + (e & 1);
         const int64_t c = c0 + cc;
         if (c >= d_in) continue;
         bf16x8 p[3];
@@ -150,7 +164,7 @@ __global__ __launch_bounds__(256) void split_u_kernel(const float* __restrict__ 
         }
 #pragma unroll
         for (int q = 0; q < 3; ++q)
-            *reinterpret_cast<bf16x8*>(&out[(q * d_in + c) * ldk + 8 * g]) = p[q];
+            *reinterpret_cast<bf16x8*>(&out[u3_offset(d_in, ldk, q, 8 * g, c)]) = p[q];
     }
 }
 
@@ -413,7 +427,7 @@ __device__ __forceinline__ void near_update(float (&wv)[kSub], const float (&ua)
 // 16x16x32 bf16 (each product exact in fp32, fp32 accumulation), as in the
 // far update.  The U operand U_blk^T (16 columns x kp) is read as 16-byte
 // runs along k from the pieces split once per layer (U3p: the previous
-// block's, [3][d_in][ldk], column-major by k; zero past the block); the E
+// block's, at u3_offset; zero past the block); the E
 // operand from its pieces staged in LDS by row (ets[p][row][k], zero past kp).
 // The result has the layout of near_update's, so the same row transpose
 // applies it.
@@ -431,7 +445,6 @@ __device__ __forceinline__ void near_update_split(float (&wv)[kSub], const __bf1
     float4v acc[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = (float4v){};
-    const __bf16* ucol = U3p + (c0q + i) * ldk;
 #pragma unroll
     for (int c = 0; c < kMaxBlock / 32; ++c) {
         if (32 * c < kp) {
@@ -439,8 +452,9 @@ __device__ __forceinline__ void near_update_split(float (&wv)[kSub], const __bf1
             bf16x8 a[3];
 #pragma unroll
             for (int q = 0; q < 3; ++q)
-                a[q] = (i < cq && k0 < ldk) ? *reinterpret_cast<const bf16x8*>(ucol + q * d_in * ldk + k0)
-                                            : (bf16x8){};
+                a[q] = (i < cq && k0 < ldk)
+                           ? *reinterpret_cast<const bf16x8*>(U3p + u3_offset(d_in, ldk, q, k0, c0q + i))
+                           : (bf16x8){};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 bf16x8 b[3];
@@ -533,7 +547,7 @@ __device__ __forceinline__ void sweep_body(unsigned char* smem, int rt, const fl
                                            const float* __restrict__ rdiag, int64_t b0, int64_t b1, int bits,
                                            int64_t group, int64_t ng, float* __restrict__ scales,
                                            int32_t* __restrict__ zeros, float* __restrict__ minmax,
-                                           uint8_t* __restrict__ codes, float* __restrict__ E, int64_t ldE,
+                                           uint8_t* __restrict__ codes, float* __restrict__ E,
                                            float* __restrict__ err_row, const float* __restrict__ Ep, int64_t bp0,
                                            int kp, const __bf16* __restrict__ U3p, int64_t ldk) {
     const int bw = (int)(b1 - b0);
@@ -587,10 +601,11 @@ __device__ __forceinline__ void sweep_body(unsigned char* smem, int rt, const fl
     }
 
     // near update operands: U rows of the previous block for this wave's
-    // columns, and 16 entries of E_prev per thread (row tid/8, k run 16 (tid%8))
+    // columns, and 16 entries of E_prev per thread (row tid%64, the k run
+    // 16 (tid/64): a wave reads one run of 64 rows, 4 KB in a row)
     float ua[kMaxBlock / 4];
     float ep[16];
-    const int er = threadIdx.x >> 3, ek = (threadIdx.x & 7) * 16;
+    const int er = threadIdx.x & 63, ek = (threadIdx.x >> 6) * 16;
     if (kp > 0) {
         const int i = lane & 15, g = lane >> 4;
         if (!kSplit) {
@@ -601,8 +616,8 @@ __device__ __forceinline__ void sweep_body(unsigned char* smem, int rt, const fl
             }
         }
         const int64_t Re = (int64_t)rt * kRowsPerWg + er;
-        const float* src = Ep + Re * ldE + ek;
-        if (Re < d_out && ek + 16 <= kp && (ldE & 3) == 0 && (reinterpret_cast<uintptr_t>(Ep) & 15) == 0) {
+        const float* src = Ep + eoff(d_out, Re, ek);
+        if (Re < d_out && ek + 16 <= kp && (reinterpret_cast<uintptr_t>(Ep) & 15) == 0) {
 #pragma unroll
             for (int e = 0; e < 16; e += 4) *reinterpret_cast<float4v*>(&ep[e]) = *reinterpret_cast<const float4v*>(src + e);
         } else {
@@ -748,18 +763,18 @@ __device__ __forceinline__ void sweep_body(unsigned char* smem, int rt, const fl
             // this sub-block's codes and scaled errors are final: store them
             // now so that the stores drain while the later sub-blocks run
             const int64_t ce = kSub * (int64_t)p;  // column of the block
-            const bool vec_out = vec_row && (ldE & 3) == 0 && (d_in & 15) == 0 && ((b0 + ce) & 15) == 0 &&
+            const bool vec_out = vec_row && (d_in & 15) == 0 && ((b0 + ce) & 15) == 0 &&
                                  ((reinterpret_cast<uintptr_t>(codes) | reinterpret_cast<uintptr_t>(E)) & 15) == 0;
             if (vec_out) {
                 *reinterpret_cast<uint4*>(codes + R * d_in + b0 + ce) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
 #pragma unroll
-                for (int t = 0; t < kSub; t += 4) *reinterpret_cast<float4v*>(E + R * ldE + ce + t) = *reinterpret_cast<const float4v*>(&ev[t]);
+                for (int t = 0; t < kSub; t += 4) *reinterpret_cast<float4v*>(E + eoff(d_out, R, (int)ce + t)) = *reinterpret_cast<const float4v*>(&ev[t]);
             } else if (rowok) {
 #pragma unroll
                 for (int t = 0; t < kSub; ++t)
                     if (t < cq) {
                         codes[R * d_in + b0 + ce + t] = (uint8_t)(cw[t >> 2] >> (8 * (t & 3)));
-                        E[R * ldE + ce + t] = ev[t];
+                        E[eoff(d_out, R, (int)ce + t)] = ev[t];
                     }
             }
         }
@@ -805,15 +820,15 @@ struct TrailRegs {
 };
 
 template <bool kVec, int kRT>
-__device__ __forceinline__ void trail_fetch(TrailRegs<kRT>& r, const float* __restrict__ E, int64_t ldE,
+__device__ __forceinline__ void trail_fetch(TrailRegs<kRT>& r, const float* __restrict__ E,
                                             const float* __restrict__ U, int64_t d_out, int64_t d_in, int64_t r0,
                                             int64_t c0, int64_t b0, int K, int kc, int tid, int64_t c_end) {
     constexpr int kE = TrailRegs<kRT>::kE;
     constexpr int kPerRow = kTK / kE;  // threads per E row
     {
         const int64_t R = r0 + tid / kPerRow;
-        const int k = kc + (tid % kPerRow) * kE;
-        const float* src = E + R * ldE + k;
+        const int k = kc + (tid % kPerRow) * kE;  // kE-aligned: its kE entries lie in one run
+        const float* src = E + eoff(d_out, R, k);
         if (kVec && R < d_out && k + kE <= K) {
 #pragma unroll
             for (int e = 0; e < kE; e += 4) *reinterpret_cast<float4v*>(&r.e[e]) = *reinterpret_cast<const float4v*>(src + e);
@@ -854,7 +869,7 @@ __device__ __forceinline__ void trail_stash(const TrailRegs<kRT>& r, TrailLds& s
 // chunks of 32 through two LDS buffers with a register prefetch.
 template <bool kVec, int kRT>
 __global__ __launch_bounds__(256) void trail_kernel(float* __restrict__ Wk, int64_t d_out, int64_t d_in,
-                                                    const float* __restrict__ E, int64_t ldE,
+                                                    const float* __restrict__ E,
                                                     const float* __restrict__ U, int64_t b0, int64_t b1,
                                                     int64_t c_begin, int64_t c_end) {
     static_assert(kRT <= kTrailRows, "the E stage is sized for kTrailRows rows");
@@ -874,7 +889,7 @@ __global__ __launch_bounds__(256) void trail_kernel(float* __restrict__ Wk, int6
         for (int q = 0; q < 2; ++q) acc[m][q] = (float16v){};
 
     TrailRegs<kRT> regs;
-    trail_fetch<kVec, kRT>(regs, E, ldE, U, d_out, d_in, r0, c0, b0, K, 0, tid, c_end);
+    trail_fetch<kVec, kRT>(regs, E, U, d_out, d_in, r0, c0, b0, K, 0, tid, c_end);
     // the 64-row tile reads its W tile early (a 128-row tile would need 64
     // more registers for it and lose occupancy)
     constexpr bool kPre = kRT == 64;
@@ -895,7 +910,7 @@ __global__ __launch_bounds__(256) void trail_kernel(float* __restrict__ Wk, int6
         const int buf = c & 1;
         trail_stash<kRT>(regs, s, buf, tid);
         __syncthreads();
-        if (c + 1 < nchunks) trail_fetch<kVec, kRT>(regs, E, ldE, U, d_out, d_in, r0, c0, b0, K, (c + 1) * kTK, tid, c_end);
+        if (c + 1 < nchunks) trail_fetch<kVec, kRT>(regs, E, U, d_out, d_in, r0, c0, b0, K, (c + 1) * kTK, tid, c_end);
         const float* Es = s.E[buf];
         const float* Us = s.U[buf];
 #pragma unroll
@@ -945,13 +960,13 @@ __host__ __device__ inline size_t rest_lds_bytes() {
     return (size_t)(2 * kRestRows * kEs + 2 * kTK * kRUs) * 4;
 }
 
-__device__ __forceinline__ void rest_fetch(float (&e)[8], float (&u)[16], const float* __restrict__ E, int64_t ldE,
+__device__ __forceinline__ void rest_fetch(float (&e)[8], float (&u)[16], const float* __restrict__ E,
                                            const float* __restrict__ U, int64_t d_out, int64_t d_in, int64_t r0,
                                            int64_t c0, int64_t c_end, int64_t bp0, int kp, int kc, int tid, bool vec) {
     {
         const int64_t R = r0 + (tid >> 2);
-        const int k = kc + (tid & 3) * 8;
-        const float* src = E + R * ldE + k;
+        const int k = kc + (tid & 3) * 8;  // 8-aligned: its 8 entries lie in one run
+        const float* src = E + eoff(d_out, R, k);
         if (vec && R < d_out && k + 8 <= kp) {
 #pragma unroll
             for (int x = 0; x < 8; x += 4) *reinterpret_cast<float4v*>(&e[x]) = *reinterpret_cast<const float4v*>(src + x);
@@ -991,7 +1006,7 @@ __device__ __forceinline__ void rest_chunk(const float* Eb, const float* Ub, int
 
 __device__ __forceinline__ void rest_body(unsigned char* smem, int64_t r0, int64_t c0, int64_t c_end,
                                           float* __restrict__ Wk, int64_t d_out, int64_t d_in,
-                                          const float* __restrict__ E, int64_t ldE, const float* __restrict__ U,
+                                          const float* __restrict__ E, const float* __restrict__ U,
                                           int64_t bp0, int kp, bool vec) {
     float* Es = reinterpret_cast<float*>(smem);  // [2][kRestRows * kEs]
     float* Us = Es + 2 * kRestRows * kEs;        // [2][kTK * kRUs]
@@ -1010,7 +1025,7 @@ __device__ __forceinline__ void rest_body(unsigned char* smem, int64_t r0, int64
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = (float16v){};
     float e[8], u[16];
-    rest_fetch(e, u, E, ldE, U, d_out, d_in, r0, c0, c_end, bp0, kp, 0, tid, vec);
+    rest_fetch(e, u, E, U, d_out, d_in, r0, c0, c_end, bp0, kp, 0, tid, vec);
     float wold[4][16];
     for (int c = 0; c < nchunks; ++c) {
         const int buf = c & 1;
@@ -1024,7 +1039,7 @@ __device__ __forceinline__ void rest_body(unsigned char* smem, int64_t r0, int64
         }
         __syncthreads();
         if (c + 1 < nchunks)
-            rest_fetch(e, u, E, ldE, U, d_out, d_in, r0, c0, c_end, bp0, kp, (c + 1) * kTK, tid, vec);
+            rest_fetch(e, u, E, U, d_out, d_in, r0, c0, c_end, bp0, kp, (c + 1) * kTK, tid, vec);
         if (c == 0) {
             // the old W tile, behind the next chunk's operands (so that their
             // wait does not include it); addresses outside the sub-tile are
@@ -1087,17 +1102,25 @@ __host__ __device__ inline size_t rest_split_lds_bytes() { return (size_t)2 * kS
 
 
 // chunk operands: E rows r0 + tid/4, k kc + 4(tid%4) .. +4 (split here);
-// the U pieces of column c0 + tid%256, k kc + 8(tid/256) .. +8, already
-// split (U3b: the previous block's pieces, [3][d_in][ldk]).  Columns past
+// the U pieces of column c0 + tid/2, k kc + 8(tid%2) .. +8, already
+// split (U3b: the previous block's pieces at u3_offset, so that a wave's
+// reads of one piece are 1 KB in a row).  Columns past
 // c_end load column c0 (their products are never stored).
 __device__ __forceinline__ void rest_split_fetch(float (&e)[4], bf16x8 (&u)[3], const float* __restrict__ E,
-                                                 int64_t ldE, const __bf16* __restrict__ U3b, int64_t ldk,
+                                                 const __bf16* __restrict__ U3b, int64_t ldk,
                                                  int64_t d_out, int64_t d_in, int64_t r0, int64_t c0, int64_t c_end,
                                                  int kp, int kc, int tid, bool vec) {
+    // addresses formed anew at each fetch from an opaque copy of the thread
+    // index: the run offsets of successive fetches are too far apart for an
+    // instruction offset, and addresses kept from one fetch to the next would
+    // cost registers
+    int t = tid;
+    asm volatile("" : "+v"(t));
     {
-        const int64_t R = r0 + (tid >> 2);
-        const int k = kc + (tid & 3) * 4;
-        const float* src = E + R * ldE + k;
+        const int64_t R = r0 + (t >> 2);
+        const int k = kc + (t & 3) * 4;
+        // eoff(R, k), its run part (kc / 16) uniform
+        const float* src = E + ((int64_t)(kc >> 4) * d_out + R) * 16 + (t & 3) * 4;
         if (vec && R < d_out && k + 4 <= kp) {
             *reinterpret_cast<float4v*>(&e[0]) = *reinterpret_cast<const float4v*>(src);
         } else {
@@ -1106,10 +1129,10 @@ __device__ __forceinline__ void rest_split_fetch(float (&e)[4], bf16x8 (&u)[3], 
         }
     }
     {
-        int64_t col = c0 + (tid & 255);
+        int64_t col = c0 + (t >> 1);
         if (col >= c_end) col = c0;
-        const int k = kc + (tid >> 8) * 8;
-        const __bf16* src = U3b + col * ldk + k;
+        // u3_offset(0, kc + 8 (t%2), col), its run part (kc / 16) uniform
+        const __bf16* src = U3b + (int64_t)(kc >> 4) * d_in * 16 + col * 16 + (t & 1) * 8;
 #pragma unroll
         for (int q = 0; q < 3; ++q) u[q] = *reinterpret_cast<const bf16x8*>(src + q * d_in * ldk);
     }
@@ -1132,7 +1155,7 @@ __device__ __forceinline__ void rest_split_stash(const float (&e)[4], const bf16
         for (int q = 0; q < 3; ++q) *reinterpret_cast<bf16x4*>(&S[q * kSEPiece + off]) = p[q];
     }
     {
-        const int off = 3 * kSEPiece + (tid & 255) * kSLd + (tid >> 8) * 8;
+        const int off = 3 * kSEPiece + (tid >> 1) * kSLd + (tid & 1) * 8;
 #pragma unroll
         for (int q = 0; q < 3; ++q) *reinterpret_cast<bf16x8*>(&S[off + q * kSUPiece]) = u[q];
     }
@@ -1177,7 +1200,7 @@ __device__ __forceinline__ void rest_split_chunk(const __bf16* S, int wi, int co
 // complete in issue order, so no operand wait includes the W tile.
 __device__ __forceinline__ void rest_split_body_full(unsigned char* smem, int64_t r0, int64_t c0,
                                                      float* __restrict__ Wk, int64_t d_out, int64_t d_in,
-                                                     const float* __restrict__ E, int64_t ldE,
+                                                     const float* __restrict__ E,
                                                      const __bf16* __restrict__ U3b, int64_t ldk, bool vec) {
     constexpr int kChunks = kMaxBlock / kSK;
     __bf16* S0 = reinterpret_cast<__bf16*>(smem);  // [2][kSBuf]
@@ -1202,9 +1225,9 @@ __device__ __forceinline__ void rest_split_body_full(unsigned char* smem, int64_
     for (int q = 0; q < 4; ++q) acc[q] = (float16v){};
     float e[2][4];
     bf16x8 u[2][3];
-    rest_split_fetch(e[0], u[0], E, ldE, U3b, ldk, d_out, d_in, r0, c0, c_end, kMaxBlock, 0, tid, vec);
+    rest_split_fetch(e[0], u[0], E, U3b, ldk, d_out, d_in, r0, c0, c_end, kMaxBlock, 0, tid, vec);
     __builtin_amdgcn_sched_barrier(0);
-    rest_split_fetch(e[1], u[1], E, ldE, U3b, ldk, d_out, d_in, r0, c0, c_end, kMaxBlock, kSK, tid, vec);
+    rest_split_fetch(e[1], u[1], E, U3b, ldk, d_out, d_in, r0, c0, c_end, kMaxBlock, kSK, tid, vec);
     float wold[4][16];
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
@@ -1212,7 +1235,7 @@ __device__ __forceinline__ void rest_split_body_full(unsigned char* smem, int64_
         rest_split_stash(e[c & 1], u[c & 1], S, tid);
         __syncthreads();
         if (c + 2 < kChunks)
-            rest_split_fetch(e[c & 1], u[c & 1], E, ldE, U3b, ldk, d_out, d_in, r0, c0, c_end, kMaxBlock,
+            rest_split_fetch(e[c & 1], u[c & 1], E, U3b, ldk, d_out, d_in, r0, c0, c_end, kMaxBlock,
                              (c + 2) * kSK, tid, vec);
         if (c >= kChunks - 2) {
             // half of the old W tile: pieces 2 (c - 6) and 2 (c - 6) + 1
@@ -1232,7 +1255,7 @@ __device__ __forceinline__ void rest_split_body_full(unsigned char* smem, int64_
 
 __device__ __forceinline__ void rest_split_body(unsigned char* smem, int64_t r0, int64_t c0, int64_t c_end,
                                                 float* __restrict__ Wk, int64_t d_out, int64_t d_in,
-                                                const float* __restrict__ E, int64_t ldE,
+                                                const float* __restrict__ E,
                                                 const __bf16* __restrict__ U3b, int64_t ldk, int kp, bool vec) {
     __bf16* S0 = reinterpret_cast<__bf16*>(smem);  // [2][kSBuf]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1244,7 +1267,7 @@ __device__ __forceinline__ void rest_split_body(unsigned char* smem, int64_t r0,
     const int nq = (int)std::min<int64_t>(ns, std::max<int64_t>(0, (c_end - cw + 31) / 32));
     const bool inner = (r0 + kRestRows <= d_out) && (cw + 32 * nq <= c_end);
     if (kp == kMaxBlock && nq == 4 && inner && c_end - c0 == kRestCols) {
-        rest_split_body_full(smem, r0, c0, Wk, d_out, d_in, E, ldE, U3b, ldk, vec);
+        rest_split_body_full(smem, r0, c0, Wk, d_out, d_in, E, U3b, ldk, vec);
         return;
     }
 
@@ -1253,14 +1276,14 @@ __device__ __forceinline__ void rest_split_body(unsigned char* smem, int64_t r0,
     for (int q = 0; q < 4; ++q) acc[q] = (float16v){};
     float e[4];
     bf16x8 u[3];
-    rest_split_fetch(e, u, E, ldE, U3b, ldk, d_out, d_in, r0, c0, c_end, kp, 0, tid, vec);
+    rest_split_fetch(e, u, E, U3b, ldk, d_out, d_in, r0, c0, c_end, kp, 0, tid, vec);
     float wold[4][16];
     for (int c = 0; c < nchunks; ++c) {
         __bf16* S = S0 + (c & 1) * kSBuf;
         rest_split_stash(e, u, S, tid);
         __syncthreads();
         if (c + 1 < nchunks)
-            rest_split_fetch(e, u, E, ldE, U3b, ldk, d_out, d_in, r0, c0, c_end, kp, (c + 1) * kSK, tid, vec);
+            rest_split_fetch(e, u, E, U3b, ldk, d_out, d_in, r0, c0, c_end, kp, (c + 1) * kSK, tid, vec);
         if (c == 0) {
             // the old W tile, behind the next chunk's operands; addresses
             // outside the sub-tile are clamped to its first element (never
@@ -1309,16 +1332,16 @@ using sched::FarSplit;
 template <bool kSplit>
 __device__ __forceinline__ void far_range(unsigned char* smem, int64_t u0, int64_t u1, const FarSplit& fs,
                                           float* __restrict__ Wk, int64_t d_out, int64_t d_in,
-                                          const float* __restrict__ E, int64_t ldE, const float* __restrict__ U,
+                                          const float* __restrict__ E, const float* __restrict__ U,
                                           const __bf16* __restrict__ U3b, int64_t ldk, int64_t bp0, int kp,
                                           bool vec) {
     for (int64_t u = u0; u < u1;) {
         const sched::FarSub t = sched::far_sub(fs, u, u1, d_in);
         __syncthreads();  // the LDS stages of the previous sub-tile (or the sweep) are free again
         if (kSplit)
-            rest_split_body(smem, t.rt * kRestRows, t.c0, t.c_end, Wk, d_out, d_in, E, ldE, U3b, ldk, kp, vec);
+            rest_split_body(smem, t.rt * kRestRows, t.c0, t.c_end, Wk, d_out, d_in, E, U3b, ldk, kp, vec);
         else
-            rest_body(smem, t.rt * kRestRows, t.c0, t.c_end, Wk, d_out, d_in, E, ldE, U, bp0, kp, vec);
+            rest_body(smem, t.rt * kRestRows, t.c0, t.c_end, Wk, d_out, d_in, E, U, bp0, kp, vec);
         u += t.ns;
     }
 }
@@ -1335,7 +1358,7 @@ __global__ __launch_bounds__(512) void step_kernel(float* __restrict__ Wk, int64
                                                    int64_t b0, int64_t b1, int bits, int64_t group, int64_t ng,
                                                    float* __restrict__ scales, int32_t* __restrict__ zeros,
                                                    float* __restrict__ minmax, uint8_t* __restrict__ codes,
-                                                   float* __restrict__ E, int64_t ldE, float* __restrict__ err_row,
+                                                   float* __restrict__ E, float* __restrict__ err_row,
                                                    const float* __restrict__ Ep, int64_t bp0, int kp, int row_tiles,
                                                    FarSplit fs, int vec_rest, const __bf16* __restrict__ U3b,
                                                    int64_t ldk) {
@@ -1343,10 +1366,10 @@ __global__ __launch_bounds__(512) void step_kernel(float* __restrict__ Wk, int64
     const int b = (int)blockIdx.x;
     if (b < row_tiles)
         sweep_body<kAllFull, kSplit>(smem, b, Wk, d_out, d_in, U, rdiag, b0, b1, bits, group, ng, scales, zeros,
-                                     minmax, codes, E, ldE, err_row, Ep, bp0, kp, U3b, ldk);
+                                     minmax, codes, E, err_row, Ep, bp0, kp, U3b, ldk);
     int64_t u0, u1;
     sched::far_units(fs, b, row_tiles, u0, u1);
-    if (u1 > u0) far_range<kSplit>(smem, u0, u1, fs, Wk, d_out, d_in, Ep, ldE, U, U3b, ldk, bp0, kp, vec_rest != 0);
+    if (u1 > u0) far_range<kSplit>(smem, u0, u1, fs, Wk, d_out, d_in, Ep, U, U3b, ldk, bp0, kp, vec_rest != 0);
 }
 
 }  // namespace
@@ -1378,7 +1401,7 @@ hipError_t allow_step_lds(size_t bytes) {
 }  // namespace
 
 size_t quant_workspace_bytes(int64_t d_out, int64_t d_in, int64_t block, int split) {
-    return (size_t)(rup(d_out * d_in * 4, 256) + 2 * rup(d_out * block * 4, 256) + rup(d_in * 4, 256) +
+    return (size_t)(rup(d_out * d_in * 4, 256) + 2 * rup(d_out * split_ldk(block) * 4, 256) + rup(d_in * 4, 256) +
                     (split ? rup(split_u_elems(d_in, block) * 2, 256) : 0));
 }
 
@@ -1471,10 +1494,10 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
                 dim3 grid((unsigned)((d_in - b0 + kTT - 1) / kTT), (unsigned)((d_out + kTrailRows - 1) / kTrailRows));
                 if (vec)
                     GPTQ_LAUNCH(t, (trail_kernel<true, kTrailRows>), grid, dim3(256), 0, s, w.Wk, d_out, d_in, Ep,
-                                       block, U, bp0, b0, b0, d_in);
+                                       U, bp0, b0, b0, d_in);
                 else
                     GPTQ_LAUNCH(t, (trail_kernel<false, kTrailRows>), grid, dim3(256), 0, s, w.Wk, d_out, d_in, Ep,
-                                       block, U, bp0, b0, b0, d_in);
+                                       U, bp0, b0, b0, d_in);
                 kp = 0;
             }
             TimedLaunch t(K_Q_GROUPGRID, s);
@@ -1492,7 +1515,7 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
         const dim3 grid((unsigned)(row_tiles + n_far));
 #define STEP_LAUNCH(FULL, SPLIT)                                                                             \
     GPTQ_LAUNCH(t, (step_kernel<FULL, SPLIT>), grid, dim3(512), lds, s, w.Wk, d_out, d_in, U,              \
-                       (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes, Eb, block, \
+                       (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes, Eb, \
                        err_row, Ep, bp0, kp, row_tiles, fs, (int)vec, U3b, ldk)
         if (bw % kSub == 0) {
             if (split) STEP_LAUNCH(true, true);
