@@ -438,9 +438,28 @@ __device__ __forceinline__ float4v mfma16x16x32_bf16(bf16x8 a, bf16x8 b, float4v
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ void near_update_split(float (&wv)[kSub], const __bf16* __restrict__ U3p, int64_t d_in,
-                                                  int64_t ldk, int64_t c0q, int cq, const __bf16* __restrict__ ets,
-                                                  int kp, int lane) {
+// The U operands of the near update (lane: column c0q + lane%16, k run
+// 32 c + 8 (lane/16) .. +8 of chunk c), loaded at the start of the sweep so
+// that their latency overlaps the staging; addresses are clamped to valid
+// ones and the values past the block's columns or k range set to zero.
+__device__ __forceinline__ void near_split_fetch(bf16x8 (&na)[kMaxBlock / 32][3], const __bf16* __restrict__ U3p,
+                                                 int64_t d_in, int64_t ldk, int64_t c0q, int cq, int kp, int lane) {
+    const int i = lane & 15, g = lane >> 4;
+    const int64_t col = c0q + (i < cq ? i : cq - 1);
+#pragma unroll
+    for (int c = 0; c < kMaxBlock / 32; ++c) {
+        if (32 * c < kp && cq > 0) {  // wave-uniform
+            const int k0 = 32 * c + 8 * g;
+            const int kk = k0 < ldk ? k0 : (int)ldk - 8;
+#pragma unroll
+            for (int q = 0; q < 3; ++q) na[c][q] = *reinterpret_cast<const bf16x8*>(U3p + u3_offset(d_in, ldk, q, kk, col));
+        }
+    }
+}
+
+__device__ __forceinline__ void near_update_split(float (&wv)[kSub], const bf16x8 (&na)[kMaxBlock / 32][3],
+                                                  int64_t ldk, int cq, const __bf16* __restrict__ ets, int kp,
+                                                  int lane) {
     const int i = lane & 15, g = lane >> 4;
     float4v acc[4];
 #pragma unroll
@@ -451,10 +470,7 @@ __device__ __forceinline__ void near_update_split(float (&wv)[kSub], const __bf1
             const int k0 = 32 * c + 8 * g;
             bf16x8 a[3];
 #pragma unroll
-            for (int q = 0; q < 3; ++q)
-                a[q] = (i < cq && k0 < ldk)
-                           ? *reinterpret_cast<const bf16x8*>(U3p + u3_offset(d_in, ldk, q, k0, c0q + i))
-                           : (bf16x8){};
+            for (int q = 0; q < 3; ++q) a[q] = (i < cq && k0 < ldk) ? na[c][q] : (bf16x8){};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 bf16x8 b[3];
@@ -584,6 +600,9 @@ __device__ __forceinline__ void sweep_body(unsigned char* smem, int rt, const fl
         for (int t = 0; t < kSub; ++t) wv[t] = (rowok && t < cq) ? Wk[R * d_in + c0q + t] : 0.0f;
     }
 
+    bf16x8 na[kMaxBlock / 32][3];
+    if (kSplit && kp > 0) near_split_fetch(na, U3p, d_in, ldk, c0q, cq, kp, lane);
+
     float s = 1.0f, zf = 0.0f;
     if (group == 0) {
         if (rowok) {
@@ -694,7 +713,7 @@ __device__ __forceinline__ void sweep_body(unsigned char* smem, int rt, const fl
     float errsq = 0.0f;
     __syncthreads();
     if (kp > 0) {
-        if (kSplit) near_update_split(wv, U3p, d_in, ldk, c0q, cq, ets, kp, lane);
+        if (kSplit) near_update_split(wv, na, ldk, cq, ets, kp, lane);
         else near_update(wv, ua, et, kp, lane);
     }
 

@@ -88,14 +88,16 @@ GPTQ_HD inline CholLaunch chol_launch(int k, int T, bool paired) {
 // [c_begin, d_in) in units of kFarRows rows x kFarStrip columns (unit u:
 // row tile u / nstrip, strip u % nstrip).  The units are dealt out as
 // contiguous ranges: each sweeping workgroup takes per_sweep units after its
-// sweep (which takes about kSweepUnits units' time), the far-only
-// workgroups share the rest evenly; a range is walked in sub-tiles of at
-// most kFarCols columns that stay inside one row tile.
+// sweep (which takes about kSweepUnits units' time: at 4096 x 4096 a sweep
+// of 64 rows by 128 columns lasts about 24 us, a unit about 3.9 us when
+// every CU updates), the far-only workgroups share the rest evenly; a range
+// is walked in sub-tiles of at most kFarCols columns that stay inside one
+// row tile.
 // ---------------------------------------------------------------------------
 constexpr int kFarRows = 128;
 constexpr int kFarCols = 256;
 constexpr int kFarStrip = 64;
-constexpr double kSweepUnits = 3.0;
+constexpr double kSweepUnits = 6.0;
 
 struct FarSplit {
     int64_t c_begin;
