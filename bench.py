@@ -47,7 +47,6 @@ KERNEL_SOURCE = {
     "chol32_step": ("hinv32.hip", "chol32_step_kernel"),
     "q_trail": ("quant.hip", "trail_kernel"),
     "q_step": ("quant.hip", "step_kernel"),
-    "q_split_u": ("quant.hip", "split_u_kernel"),
     "hessian_f16": ("hessian.hip", "hessian_f16"),  # hessian_f16_kernel and hessian_f16_ws_kernel
     "pack_codes": ("pack.hip", "pack_codes_kernel"),
     "dequantize": ("pack.hip", "dequant_kernel"),

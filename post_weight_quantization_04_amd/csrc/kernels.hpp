@@ -20,7 +20,6 @@ enum KernelId {
     K_Q_GROUPGRID,
     K_Q_STEP,
     K_Q_TRAIL,
-    K_Q_SPLITU,
     K_PACK,
     K_DEQUANT,
     K_OUTERR,

@@ -107,39 +107,50 @@ __device__ __forceinline__ void split3(float x, __bf16& p0, __bf16& p1, __bf16& 
 // The bf16 pieces of U for the split trailing update, written once per
 // layer: piece p of U[b*block + kk][c] at U3 + b*3*d_in*ldk + u3_offset(p,
 // kk, c) (kk < ldk, zero past the block), so that a block's rows of U reach
-// the MFMA B operand as 16-byte reads along k.  Block b's rows are read only by the update after
-// block b+1, for the columns from (b+2)*block on, so only those are written
-// (the rest of U3 is never read).  One workgroup per (64 columns, block):
-// the 64-column slab of the block's rows is read along rows and transposed
-// through LDS.
-__global__ __launch_bounds__(256) void split_u_kernel(const float* __restrict__ U, int64_t d_in, int64_t block,
-                                                      int64_t ldk, __bf16* __restrict__ U3) {
-    __shared__ float T[128][65];
-    const int64_t b = blockIdx.y;
-    const int64_t c0 = (int64_t)blockIdx.x * 64;
-    if (c0 + 64 <= (b + 1) * block) return;  // columns this block's pieces are never read for
+// the MFMA B operand as 16-byte reads along k.  Block b's rows are read by
+// the launch of block b+1 (near update, columns of block b+1) and by the
+// updates of the later columns, so only the columns from (b+1)*block on are
+// written (the rest of U3 is never read).  The work comes in items of 64
+// columns x one block, each read along rows and transposed through LDS
+// (T: 128 x 65 floats) by the kThreads threads of a workgroup; the items are
+// split by the workgroups of the first block's launch that do not sweep.
+constexpr int kSplitCols = 64;
+
+__host__ __device__ inline int64_t split_items(int64_t d_in, int64_t block) {
+    return ((d_in + kSplitCols - 1) / kSplitCols) * ((d_in + block - 1) / block - 1);
+}
+
+template <int kThreads>
+__device__ __forceinline__ void split_u_item(float (*T)[kSplitCols + 1], const float* __restrict__ U, int64_t d_in,
+                                             int64_t block, int64_t ldk, __bf16* __restrict__ U3, int64_t item) {
+    const int64_t nslab = (d_in + kSplitCols - 1) / kSplitCols;
+    const int64_t b = item / nslab;
+    const int64_t c0 = (item - b * nslab) * kSplitCols;
+    if (c0 + kSplitCols <= (b + 1) * block) return;  // columns this block's pieces are never read for
     const int64_t k0 = b * block;
     const int kb = (int)min(block, d_in - k0);
     const int tid = threadIdx.x;
-    if (c0 + 64 <= d_in && (d_in & 3) == 0 && (reinterpret_cast<uintptr_t>(U) & 15) == 0) {
+    if (c0 + kSplitCols <= d_in && (d_in & 3) == 0 && (reinterpret_cast<uintptr_t>(U) & 15) == 0) {
         // every load of the slab in flight before the first LDS store:
-        // thread t reads 16 bytes of rows t/16 + 16 i, columns 4 (t%16) ..
-        float4v v[8];
+        // thread t reads 16 bytes of rows t/16 + (kThreads/16) i, columns
+        // 4 (t%16) ..
+        constexpr int kPer = kMaxBlock * 16 / kThreads;
+        float4v v[kPer];
         const int cc = 4 * (tid & 15);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int kk = (tid >> 4) + 16 * i;
+        for (int i = 0; i < kPer; ++i) {
+            const int kk = (tid >> 4) + (kThreads / 16) * i;
             v[i] = (kk < kb) ? *reinterpret_cast<const float4v*>(U + (k0 + kk) * d_in + c0 + cc) : (float4v){};
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int kk = (tid >> 4) + 16 * i;
+        for (int i = 0; i < kPer; ++i) {
+            const int kk = (tid >> 4) + (kThreads / 16) * i;
 #pragma unroll
             for (int x = 0; x < 4; ++x) T[kk][cc + x] = v[i][x];
         }
     } else {
-        for (int e = tid; e < 128 * 64; e += 256) {
-            const int kk = e >> 6, cc = e & 63;
+        for (int e = tid; e < kMaxBlock * kSplitCols; e += kThreads) {
+            const int kk = e / kSplitCols, cc = e % kSplitCols;
             const int64_t c = c0 + cc;
             T[kk][cc] = (kk < kb && c < d_in) ? U[(k0 + kk) * d_in + c] : 0.0f;
         }
@@ -149,8 +160,8 @@ __global__ __launch_bounds__(256) void split_u_kernel(const float* __restrict__ 
     const int groups = (int)(ldk / 8);
     // consecutive threads: the two halves of one column's 16-k run, then the
     // next column, so that the stores of a run are consecutive
-    for (int e = tid; e < 64 * groups; e += 256) {
-        const int run = e >> 7, cc = (e & 127) >> 1, g = 2 * run + (e & 1);
+    for (int e = tid; e < kSplitCols * groups; e += kThreads) {
+        const int run = e / (2 * kSplitCols), cc = (e % (2 * kSplitCols)) >> 1, g = 2 * run + (e & 1);
         const int64_t c = c0 + cc;
         if (c >= d_in) continue;
         bf16x8 p[3];
@@ -166,6 +177,7 @@ __global__ __launch_bounds__(256) void split_u_kernel(const float* __restrict__ 
         for (int q = 0; q < 3; ++q)
             *reinterpret_cast<bf16x8*>(&out[u3_offset(d_in, ldk, q, 8 * g, c)]) = p[q];
     }
+    __syncthreads();  // T is free for the next item
 }
 
 template <typename T>
@@ -1370,7 +1382,10 @@ __device__ __forceinline__ void far_range(unsigned char* smem, int64_t u0, int64
 // then take their share of the previous block's update of the columns from
 // b1 on; the other workgroups do only that update.  The two parts touch
 // disjoint columns of W and different error buffers, so nothing but the
-// launch order separates the blocks.
+// launch order separates the blocks.  In the first block's launch of the
+// split path (split_wgs > 0), which has no update, split_wgs workgroups
+// after the sweeping ones form the bf16 pieces of U (U3w) instead; they are
+// first read by the next launch.
 template <bool kAllFull, bool kSplit>
 __global__ __launch_bounds__(512) void step_kernel(float* __restrict__ Wk, int64_t d_out, int64_t d_in,
                                                    const float* __restrict__ U, const float* __restrict__ rdiag,
@@ -1380,9 +1395,15 @@ __global__ __launch_bounds__(512) void step_kernel(float* __restrict__ Wk, int64
                                                    float* __restrict__ E, float* __restrict__ err_row,
                                                    const float* __restrict__ Ep, int64_t bp0, int kp, int row_tiles,
                                                    FarSplit fs, int vec_rest, const __bf16* __restrict__ U3b,
-                                                   int64_t ldk) {
+                                                   int64_t ldk, __bf16* __restrict__ U3w, int split_wgs) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int b = (int)blockIdx.x;
+    if (kSplit && split_wgs > 0 && b >= row_tiles) {
+        float(*T)[kSplitCols + 1] = reinterpret_cast<float(*)[kSplitCols + 1]>(smem);
+        const int64_t n = split_items(d_in, b1 - b0);
+        for (int64_t i = b - row_tiles; i < n; i += split_wgs) split_u_item<512>(T, U, d_in, b1 - b0, ldk, U3w, i);
+        return;
+    }
     if (b < row_tiles)
         sweep_body<kAllFull, kSplit>(smem, b, Wk, d_out, d_in, U, rdiag, b0, b1, bits, group, ng, scales, zeros,
                                      minmax, codes, E, err_row, Ep, bp0, kp, U3b, ldk);
@@ -1470,13 +1491,6 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
     }
     const bool vec = (reinterpret_cast<uintptr_t>(U) % 16 == 0) && (d_in % 4 == 0) && (block % 4 == 0);  // E rows are 16-byte aligned when block % 4 == 0
     const int64_t ldk = split_ldk(block);
-    if (split && d_in > block) {
-        // the bf16 pieces of every block's rows of U, once per layer
-        TimedLaunch t(K_Q_SPLITU, s);
-        // the last block's pieces are never read (no update follows it)
-        const dim3 grid((unsigned)((d_in + 63) / 64), (unsigned)((d_in + block - 1) / block - 1));
-        GPTQ_LAUNCH(t, split_u_kernel, grid, dim3(256), 0, s, U, d_in, block, ldk, w.U3);
-    }
     const int bmax = (int)std::min(block, d_in);
     const size_t near_bytes = near_lds_bytes(bmax, split);
     const size_t rest_bytes = split ? rest_split_lds_bytes() : rest_lds_bytes();
@@ -1530,12 +1544,16 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
         const int n_far = sched::far_split(n_units, row_tiles, n_cu, fs);
         size_t lds = sweep_lds_bytes(bw) + near_lds_bytes(kp, split);
         if (n_units > 0) lds = std::max(lds, rest_bytes);
+        // the bf16 pieces of every block's rows of U (split path), once per
+        // layer, by the CUs the first block's sweep leaves free
+        const int split_wgs = (split && bi == 0 && d_in > block) ? std::max(n_cu - row_tiles, 32) : 0;
+        if (split_wgs > 0) lds = std::max(lds, (size_t)kMaxBlock * (kSplitCols + 1) * 4);
         TimedLaunch t(K_Q_STEP, s);
-        const dim3 grid((unsigned)(row_tiles + n_far));
+        const dim3 grid((unsigned)(row_tiles + n_far + split_wgs));
 #define STEP_LAUNCH(FULL, SPLIT)                                                                             \
     GPTQ_LAUNCH(t, (step_kernel<FULL, SPLIT>), grid, dim3(512), lds, s, w.Wk, d_out, d_in, U,              \
                        (const float*)w.rdiag, b0, b1, bits, group, ng, scales, zeros, minmax, codes, Eb, \
-                       err_row, Ep, bp0, kp, row_tiles, fs, (int)vec, U3b, ldk)
+                       err_row, Ep, bp0, kp, row_tiles, fs, (int)vec, U3b, ldk, w.U3, split_wgs)
         if (bw % kSub == 0) {
             if (split) STEP_LAUNCH(true, true);
             else STEP_LAUNCH(true, false);
