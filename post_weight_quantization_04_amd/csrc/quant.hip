@@ -1541,7 +1541,8 @@ hipError_t launch_quantize(const void* W, int w_is_f16, int64_t d_out, int64_t d
         fs.c_begin = b1;
         fs.nstrip = (int)((d_in - b1 + kStrip - 1) / kStrip);
         const int64_t n_units = (kp > 0 && b1 < d_in) ? (int64_t)rest_rows * fs.nstrip : 0;
-        const int n_far = sched::far_split(n_units, row_tiles, n_cu, fs);
+        const int n_far =
+            sched::far_split(n_units, row_tiles, n_cu, fs, split ? sched::kSweepUnits : sched::kSweepUnitsF32);
         size_t lds = sweep_lds_bytes(bw) + near_lds_bytes(kp, split);
         if (n_units > 0) lds = std::max(lds, rest_bytes);
         // the bf16 pieces of every block's rows of U (split path), once per

@@ -88,16 +88,18 @@ GPTQ_HD inline CholLaunch chol_launch(int k, int T, bool paired) {
 // [c_begin, d_in) in units of kFarRows rows x kFarStrip columns (unit u:
 // row tile u / nstrip, strip u % nstrip).  The units are dealt out as
 // contiguous ranges: each sweeping workgroup takes per_sweep units after its
-// sweep (which takes about kSweepUnits units' time: at 4096 x 4096 a sweep
-// of 64 rows by 128 columns lasts about 24 us, a unit about 3.9 us when
-// every CU updates), the far-only workgroups share the rest evenly; a range
-// is walked in sub-tiles of at most kFarCols columns that stay inside one
-// row tile.
+// sweep (which takes about `sweep_units` units' time: at 4096 x 4096 a
+// sweep of 64 rows by 128 columns lasts about 24 us, a unit of the split
+// update about 3.9 us when every CU updates, kSweepUnits; one of the fp32
+// update about 5 us, kSweepUnitsF32), the far-only workgroups share the rest
+// evenly; a range is walked in sub-tiles of at most kFarCols columns that
+// stay inside one row tile.
 // ---------------------------------------------------------------------------
 constexpr int kFarRows = 128;
 constexpr int kFarCols = 256;
 constexpr int kFarStrip = 64;
 constexpr double kSweepUnits = 6.0;
+constexpr double kSweepUnitsF32 = 3.0;
 
 struct FarSplit {
     int64_t c_begin;
@@ -109,7 +111,8 @@ struct FarSplit {
 
 // Fills the split of n_units over n_sweep sweeping workgroups and the other
 // CUs (one workgroup per CU); returns the number of far-only workgroups.
-GPTQ_HD inline int far_split(int64_t n_units, int n_sweep, int n_cu, FarSplit& fs) {
+GPTQ_HD inline int far_split(int64_t n_units, int n_sweep, int n_cu, FarSplit& fs,
+                             double sweep_units = kSweepUnits) {
     fs.n_units = n_units;
     fs.per_sweep = 0;
     fs.q = fs.r = 0;
@@ -119,8 +122,8 @@ GPTQ_HD inline int far_split(int64_t n_units, int n_sweep, int n_cu, FarSplit& f
         fs.per_sweep = (int)((n_units + n_sweep - 1) / n_sweep);
         return 0;
     }
-    const double t = ((double)n_units + n_sweep * kSweepUnits) / (double)(n_sweep + n_far);
-    const double ps = t - kSweepUnits;
+    const double t = ((double)n_units + n_sweep * sweep_units) / (double)(n_sweep + n_far);
+    const double ps = t - sweep_units;
     fs.per_sweep = ps > 0.0 ? (int)ps : 0;  // floor of a non-negative value
     const int64_t rest = n_units - (int64_t)n_sweep * fs.per_sweep;
     const int nf = (int)min_of<int64_t>(n_far, rest);
