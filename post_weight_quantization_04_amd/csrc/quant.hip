@@ -15,11 +15,15 @@
 //                  same OBS updates, grouped by sub-block).  The block's rows
 //                  of U are staged in LDS as packed 16x16 upper sub-blocks.
 //   far part       the previous block's update of every column from b1 on,
-//                  W[:, b1:] -= E_prev U[prev block, b1:] on MFMA 32x32x2 f32
-//                  with fp32 accumulation, cut into 128-row x 64-column
-//                  units dealt to every CU as contiguous ranges
+//                  W[:, b1:] -= E_prev U[prev block, b1:], cut into 128-row x
+//                  64-column units dealt to every CU as contiguous ranges
 //                  (sched::far_split); the sweeping workgroups take a smaller
-//                  share after their sweep.
+//                  share after their sweep.  Products on MFMA 32x32x2 f32
+//                  with fp32 accumulation, or (split path) as six products
+//                  of bf16 pieces on MFMA 32x32x16 bf16.
+// On the split path the near update also runs on bf16 pieces, and the first
+// block's launch, which has no far part, forms the bf16 pieces of U for all
+// later launches on its non-sweeping workgroups.
 // trail_kernel runs only at the start of a group wider than the block: the
 // previous block's update of every column from the group on, so that the
 // group's grid sees the updated weights.
