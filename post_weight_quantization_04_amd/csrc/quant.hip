@@ -538,13 +538,29 @@ __device__ __forceinline__ void sweep_sub(float (&wv)[kSub], float s, float sinv
     float r[kSub];
 #pragma unroll
     for (int t = 0; t < kSub; ++t) r[t] = rd[t];
+    // kVecU: U rows in two register sets, row t+1 loaded at the start of
+    // column t, so that the loads are in flight through a whole column's
+    // dependent chain.  Only the entries used (columns after t) are loaded:
+    // 16-byte loads for whole quads, single ones before the first whole quad
+    // (a vector load with unused lanes lets the chain reuse its registers,
+    // which then waits for the load)
+    float ub[2][kSub];
+    auto load_row = [&](float (&u)[kSub], int t) {
+        const int q0 = 4 * ((t + 4) / 4);  // first whole quad after column t
+#pragma unroll
+        for (int c = t + 1; c < q0 && c < kSub; ++c) u[c] = ublk[t * uld + c];
+#pragma unroll
+        for (int c = q0; c < kSub; c += 4) *reinterpret_cast<float4v*>(&u[c]) = *reinterpret_cast<const float4v*>(ublk + t * uld + c);
+    };
+    if (kVecU) load_row(ub[0], 0);
 #pragma unroll
     for (int t = 0; t < kSub; ++t) {
         if (kFull || t < cq) {
             float u[kSub];
             if (kVecU) {
+                if (t + 1 < kSub) load_row(ub[(t + 1) & 1], t + 1);
 #pragma unroll
-                for (int c = 4 * ((t + 1) / 4); c < kSub; c += 4) *reinterpret_cast<float4v*>(&u[c]) = *reinterpret_cast<const float4v*>(ublk + t * uld + c);
+                for (int c = t + 1; c < kSub; ++c) u[c] = ub[t & 1][c];
             } else {
 #pragma unroll
                 for (int t2 = t + 1; t2 < kSub; ++t2) u[t2] = ublk[t * uld + t2];
