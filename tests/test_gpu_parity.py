@@ -162,6 +162,7 @@ def test_prepare_not_positive_definite(lib):
     (16, 96, 4, 16, 16, ()),
     (50, 128, 4, 0, 32, (2, 64, 127)),  # dead channels
     (130, 128, 3, 128, 128, (10,)),
+    (16448, 384, 4, 0, 128, ()),     # more sweeping workgroups than CUs: they take the whole update
 ])
 def test_quantize(lib, d_out, d_in, bits, group, block, dead):
     from post_weight_quantization_04_amd import layer

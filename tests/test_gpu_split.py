@@ -60,6 +60,8 @@ def _q(qz):
     (50, 128, 4, 0, 32, (2, 64, 127)),  # dead channels
     (300, 1000, 4, 0, 128, (5,)),      # several sub-tiles per launch, ragged row tile
     (257, 640, 3, 64, 128, ()),        # groups inside the block, ragged rows
+    (16448, 384, 4, 0, 128, ()),       # more sweeping workgroups (257) than CUs: no far-only workgroups,
+                                       # and the U pieces formed by the 32 extra workgroups of the first launch
 ])
 def test_quantize_split(lib, d_out, d_in, bits, group, block, dead):
     from post_weight_quantization_04_amd import layer
