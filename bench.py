@@ -245,9 +245,10 @@ def block_bench(args, wl, torch, wlm, _lib, layer, split: bool, fp32: bool) -> i
         for xs in wl.xs:
             a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
             a.record(stream)
-            H[xs.key].zero_()
-            for t0 in range(0, xs.n_tokens, chunk[xs.key]):
-                _lib.hessian_accumulate(H[xs.key], Xd[xs.key][:, t0:t0 + chunk[xs.key]])
+            ck = chunk[xs.key]
+            _lib.hessian_set(H[xs.key], Xd[xs.key][:, 0:ck])
+            for t0 in range(ck, xs.n_tokens, ck):
+                _lib.hessian_accumulate(H[xs.key], Xd[xs.key][:, t0:t0 + ck])
             b.record(stream)
             layer.prepare(H[xs.key], wl.damp, ws=ws[xs.key], out=fac[xs.key], fp32=fp32)
             c.record(stream)
@@ -371,8 +372,9 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream()
 
     def stage_h():
-        H.zero_()
-        for t0 in range(0, n_tok, chunk):
+        # the first chunk sets H's lower triangle, the others accumulate
+        _lib.hessian_set(H, Xd[:, 0:chunk])
+        for t0 in range(chunk, n_tok, chunk):
             _lib.hessian_accumulate(H, Xd[:, t0:t0 + chunk])
 
     def stage_u(fp32=fp32):

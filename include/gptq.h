@@ -4,7 +4,7 @@
  *
  * The path quantizes one linear layer W [d_out, d_in] against calibration
  * inputs X [d_in, N] in four stages:
- *   1. H = 2 X X^T                                (gptq_hessian_accumulate)
+ *   1. H = 2 X X^T             (gptq_hessian_set, gptq_hessian_accumulate)
  *   2. H <- H + lambda I, dead channels skipped   (gptq_prepare_hinv)
  *   3. U upper with H^-1 = U^T U                  (gptq_prepare_hinv)
  *   4. fixed-order, block-lazy quantize-and-compensate sweep
@@ -78,6 +78,24 @@ typedef enum {
  */
 int gptq_hessian_accumulate(float* H, int64_t d_in, const void* X, int x_dtype,
                             int64_t n_tokens, int64_t ldx, void* stream);
+
+/*
+ * Stage 1, first (or only) token chunk -- the same operation without the
+ * previous H (same sections of the same pages):
+ *     H = 2 * X * X^T
+ * on the lower triangle including the diagonal; the strictly upper triangle
+ * is not written.  The old values of H are neither read nor needed, so the
+ * caller does not zero H first; later chunks go through
+ * gptq_hessian_accumulate.  n_tokens = 0 writes zeros (an empty sum).  The
+ * products and the float32 accumulation are those of
+ * gptq_hessian_accumulate, so setting and then accumulating gives the same
+ * H, bit for bit, as accumulating every chunk into a zeroed H.
+ * Arguments as gptq_hessian_accumulate.
+ * Errors: GPTQ_EINVAL for H null (d_in > 0), X null with n_tokens > 0,
+ * d_in < 0, n_tokens < 0, ldx < n_tokens, unknown x_dtype.
+ */
+int gptq_hessian_set(float* H, int64_t d_in, const void* X, int x_dtype,
+                     int64_t n_tokens, int64_t ldx, void* stream);
 
 /*
  * Stages 2 and 3 -- damping, dead channels and the factor U.

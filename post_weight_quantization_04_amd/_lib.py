@@ -19,6 +19,7 @@ GPTQ_F16, GPTQ_F32 = 0, 1
 
 EXPORTS = (
     "gptq_hessian_accumulate",
+    "gptq_hessian_set",
     "gptq_prepare_hinv_workspace",
     "gptq_prepare_hinv",
     "gptq_prepare_hinv_fp32_workspace",
@@ -71,6 +72,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     sig = {
         "gptq_hessian_accumulate": (_i32, [_vp, _i64, _vp, _i32, _i64, _i64, _vp]),
+        "gptq_hessian_set": (_i32, [_vp, _i64, _vp, _i32, _i64, _i64, _vp]),
         "gptq_prepare_hinv_workspace": (_sz, [_i64]),
         "gptq_prepare_hinv": (_i32, [_vp, _i64, ctypes.c_double, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
         "gptq_prepare_hinv_fp32_workspace": (_sz, [_i64]),
@@ -142,9 +144,7 @@ def _dtype_code(t) -> int:
 # ---------------------------------------------------------------------------
 # the three entry points
 # ---------------------------------------------------------------------------
-def hessian_accumulate(H, X, stream=None) -> None:
-    """``H[lower] += 2 X X^T`` for ``X: [d_in, n]`` (a 2-D view with unit
-    column stride; row stride = ``X.stride(0)``)."""
+def _hessian_call(fn: str, H, X, stream) -> None:
     if X.dim() != 2 or X.stride(1) != 1:
         raise ValueError("X must be 2-D with unit column stride")
     d_in, n = X.shape
@@ -152,9 +152,20 @@ def hessian_accumulate(H, X, stream=None) -> None:
         raise ValueError("H shape")
     if not X.is_cuda:
         raise ValueError("device tensor expected")
-    rc = load().gptq_hessian_accumulate(_ptr(H), d_in, X.data_ptr(), _dtype_code(X), n, X.stride(0),
-                                        _stream(stream))
-    _check("gptq_hessian_accumulate", rc)
+    rc = getattr(load(), fn)(_ptr(H), d_in, X.data_ptr(), _dtype_code(X), n, X.stride(0), _stream(stream))
+    _check(fn, rc)
+
+
+def hessian_accumulate(H, X, stream=None) -> None:
+    """``H[lower] += 2 X X^T`` for ``X: [d_in, n]`` (a 2-D view with unit
+    column stride; row stride = ``X.stride(0)``)."""
+    _hessian_call("gptq_hessian_accumulate", H, X, stream)
+
+
+def hessian_set(H, X, stream=None) -> None:
+    """``H[lower] = 2 X X^T`` (the old values not read; the strictly upper
+    triangle not written), for the first token chunk."""
+    _hessian_call("gptq_hessian_set", H, X, stream)
 
 
 def prepare_hinv_workspace(d_in: int, fp32: bool = False) -> int:

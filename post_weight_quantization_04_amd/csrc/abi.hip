@@ -142,7 +142,17 @@ int gptq_hessian_accumulate(float* H, int64_t d_in, const void* X, int x_dtype, 
     if (d_in == 0 || n_tokens == 0) return GPTQ_OK;
     if (!H || !X) return GPTQ_EINVAL;
     if (d_in > (int64_t)1 << 20) return GPTQ_EUNSUPPORTED;
-    return hip_status(launch_hessian(H, d_in, X, x_dtype == GPTQ_F16, n_tokens, ldx, as_stream(stream)));
+    return hip_status(launch_hessian(H, d_in, X, x_dtype == GPTQ_F16, n_tokens, ldx, 0, as_stream(stream)));
+}
+
+int gptq_hessian_set(float* H, int64_t d_in, const void* X, int x_dtype, int64_t n_tokens, int64_t ldx,
+                     void* stream) {
+    if (d_in < 0 || n_tokens < 0 || ldx < n_tokens) return GPTQ_EINVAL;
+    if (x_dtype != GPTQ_F16 && x_dtype != GPTQ_F32) return GPTQ_EINVAL;
+    if (d_in == 0) return GPTQ_OK;
+    if (!H || (n_tokens > 0 && !X)) return GPTQ_EINVAL;
+    if (d_in > (int64_t)1 << 20) return GPTQ_EUNSUPPORTED;
+    return hip_status(launch_hessian(H, d_in, X, x_dtype == GPTQ_F16, n_tokens, ldx, 1, as_stream(stream)));
 }
 
 size_t gptq_prepare_hinv_workspace(int64_t d_in) { return d_in > 0 ? hinv_workspace_bytes(d_in) : 0; }

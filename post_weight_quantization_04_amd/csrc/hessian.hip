@@ -39,6 +39,7 @@ __device__ __forceinline__ void tile_of(int b, int& I, int& J) {
 // (measured faster than skipping their loads) and are not stored.  Addresses
 // are a wave-uniform row base plus an unsigned 32-bit offset (at most
 // 64 n < 2^31 for any width whose H fits in memory).
+template <bool kSet>
 __device__ __forceinline__ void store_quarter(float* __restrict__ H, int64_t n, int r0, int c0,
                                               const float16v (&acc)[2][2], int lane) {
     const int ni = (int)n;
@@ -46,23 +47,26 @@ __device__ __forceinline__ void store_quarter(float* __restrict__ H, int64_t n, 
     float* __restrict__ base = H + (int64_t)rb * n;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-        float old[2][16];
+        float old[2][16] = {};
+        if (!kSet) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = r0 + 32 * m + acc32_row(v, lane);
+                    const int col = c0 + 32 * q + (lane & 31);
+                    const int rr = min(row, ni - 1), cc = min(col, rr);
+                    old[q][v] = base[(unsigned)((rr - rb) * ni + cc)];
+                }
+        }
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int row = r0 + 32 * m + acc32_row(v, lane);
                 const int col = c0 + 32 * q + (lane & 31);
-                const int rr = min(row, ni - 1), cc = min(col, rr);
-                old[q][v] = base[(unsigned)((rr - rb) * ni + cc)];
-            }
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = r0 + 32 * m + acc32_row(v, lane);
-                const int col = c0 + 32 * q + (lane & 31);
-                if (row < ni && col <= row) base[(unsigned)((row - rb) * ni + col)] = old[q][v] + 2.0f * acc[m][q][v];
+                if (row < ni && col <= row)
+                    base[(unsigned)((row - rb) * ni + col)] = kSet ? 2.0f * acc[m][q][v] : old[q][v] + 2.0f * acc[m][q][v];
             }
     }
 }
@@ -192,7 +196,7 @@ template <int kTl, int kThr, int kK, int kDepth>
 __global__ __launch_bounds__(kThr, kThr == kThreads ? 2 : 1) void hessian_f16_kernel(float* __restrict__ H, int64_t n,
                                                                  const half_t* __restrict__ X, int64_t ldx,
                                                                  int64_t ntok, int64_t nfull, int T,
-                                                                 int per_xcd) {
+                                                                 int per_xcd, int set) {
     using S = Slab<kTl, kThr, kK>;
     constexpr int kWg = kTl / 64;  // computing waves per tile dimension (further waves only load)
     __shared__ half_t As[2][kTl * S::kLd];
@@ -295,7 +299,10 @@ __global__ __launch_bounds__(kThr, kThr == kThreads ? 2 : 1) void hessian_f16_ke
             compute(sl);
         }
     }
-    if (active) store_quarter(H, n, rA + wi * 64, rB + wj * 64, acc, lane);
+    if (active) {
+        if (set) store_quarter<true>(H, n, rA + wi * 64, rB + wj * 64, acc, lane);
+        else store_quarter<false>(H, n, rA + wi * 64, rB + wj * 64, acc, lane);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -326,7 +333,7 @@ static_assert(kWsPieces * kWsRowsPerPass == 2 * kWsTile && kWsPieces % 2 == 0, "
 __global__ __launch_bounds__(kWsThreads, 1) void hessian_f16_ws_kernel(float* __restrict__ H, int64_t n,
                                                                        const half_t* __restrict__ X, int64_t ldx,
                                                                        int64_t ntok, int64_t nfull, int T,
-                                                                       int per_xcd) {
+                                                                       int per_xcd, int set) {
     __shared__ half_t As[2][kWsTile * kWsLd];
     __shared__ half_t Bs[2][kWsTile * kWsLd];
     const int t = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
@@ -472,7 +479,10 @@ __global__ __launch_bounds__(kWsThreads, 1) void hessian_f16_ws_kernel(float* __
         }
         __syncthreads();
     }
-    if (active) store_quarter(H, n, rA + wi * 64, rB + wj * 64, acc, lane);
+    if (active) {
+        if (set) store_quarter<true>(H, n, rA + wi * 64, rB + wj * 64, acc, lane);
+        else store_quarter<false>(H, n, rA + wi * 64, rB + wj * 64, acc, lane);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -504,7 +514,7 @@ __device__ __forceinline__ void load_slab_f32(float (*S)[kLd32], const float* __
 template <bool kVec>
 __global__ __launch_bounds__(kThreads, 2) void hessian_f32_kernel(float* __restrict__ H, int64_t n,
                                                               const float* __restrict__ X, int64_t ldx,
-                                                              int64_t ntok) {
+                                                              int64_t ntok, int set) {
     __shared__ float As[kTile][kLd32];
     __shared__ float Bs[kTile][kLd32];
     int I, J;
@@ -541,16 +551,32 @@ __global__ __launch_bounds__(kThreads, 2) void hessian_f32_kernel(float* __restr
         }
         __syncthreads();
     }
-    if (active) store_quarter(H, n, I * kTile + wi * 64, J * kTile + wj * 64, acc, lane);
+    if (active) {
+        if (set) store_quarter<true>(H, n, I * kTile + wi * 64, J * kTile + wj * 64, acc, lane);
+        else store_quarter<false>(H, n, I * kTile + wi * 64, J * kTile + wj * 64, acc, lane);
+    }
+}
+
+// Row r of H: columns 0..r set to zero (the lower triangle of an empty sum).
+__global__ __launch_bounds__(256) void zero_lower_kernel(float* __restrict__ H, int64_t n) {
+    const int64_t r = blockIdx.x;
+    for (int64_t c = threadIdx.x; c <= r; c += blockDim.x) H[r * n + c] = 0.0f;
 }
 
 }  // namespace
 
-hipError_t launch_hessian(float* H, int64_t n, const void* X, int x_is_f16, int64_t ntok, int64_t ldx,
+hipError_t launch_hessian(float* H, int64_t n, const void* X, int x_is_f16, int64_t ntok, int64_t ldx, int set,
                           hipStream_t s) {
     const int64_t T = (n + kTile - 1) / kTile;
     const int64_t tiles = T * (T + 1) / 2;
-    if (tiles == 0 || ntok == 0) return hipSuccess;
+    if (tiles == 0) return hipSuccess;
+    if (ntok == 0) {
+        if (!set) return hipSuccess;
+        // H = 2 X X^T with no tokens: the lower triangle becomes zero
+        TimedLaunch t(x_is_f16 ? K_HESS_F16 : K_HESS_F32, s);
+        GPTQ_LAUNCH(t, zero_lower_kernel, dim3((unsigned)n), dim3(256), 0, s, H, n);
+        return hipGetLastError();
+    }
     const uintptr_t addr = reinterpret_cast<uintptr_t>(X);
     if (x_is_f16) {
         TimedLaunch t(K_HESS_F16, s);
@@ -564,28 +590,28 @@ hipError_t launch_hessian(float* H, int64_t n, const void* X, int x_is_f16, int6
             const int per_xcd = (int)((tw_all + kXcds - 1) / kXcds);
             GPTQ_LAUNCH(t, (hessian_f16_kernel<kWideTile, kWideThreads, kKf16, kDepthf16>),
                                dim3((unsigned)(per_xcd * kXcds)), dim3(kWideThreads), 0, s, H, n,
-                               static_cast<const half_t*>(X), ldx, ntok, nfull, (int)Tw, per_xcd);
+                               static_cast<const half_t*>(X), ldx, ntok, nfull, (int)Tw, per_xcd, set);
         } else if (Tw >= kWideMinT) {
             const int64_t Tm = (n + kWsTile - 1) / kWsTile;
             const int64_t nfull_ws = vec ? ntok / kWsK : 0;
             const int per_xcd = (int)((Tm * (Tm + 1) / 2 + kXcds - 1) / kXcds);
             GPTQ_LAUNCH(t, hessian_f16_ws_kernel, dim3((unsigned)(per_xcd * kXcds)), dim3(kWsThreads), 0, s, H, n,
-                               static_cast<const half_t*>(X), ldx, ntok, nfull_ws, (int)Tm, per_xcd);
+                               static_cast<const half_t*>(X), ldx, ntok, nfull_ws, (int)Tm, per_xcd, set);
         } else {
             const int per_xcd = (int)((tiles + kXcds - 1) / kXcds);
             GPTQ_LAUNCH(t, (hessian_f16_kernel<kTile, kThreads, kKf16, kDepthf16>),
                                dim3((unsigned)(per_xcd * kXcds)), dim3(kThreads), 0, s, H, n,
-                               static_cast<const half_t*>(X), ldx, ntok, nfull, (int)T, per_xcd);
+                               static_cast<const half_t*>(X), ldx, ntok, nfull, (int)T, per_xcd, set);
         }
     } else {
         TimedLaunch t(K_HESS_F32, s);
         const bool vec = (addr % 16 == 0) && (ldx % 4 == 0);
         if (vec)
             GPTQ_LAUNCH(t, hessian_f32_kernel<true>, dim3((unsigned)tiles), dim3(kThreads), 0, s, H, n,
-                               static_cast<const float*>(X), ldx, ntok);
+                               static_cast<const float*>(X), ldx, ntok, set);
         else
             GPTQ_LAUNCH(t, hessian_f32_kernel<false>, dim3((unsigned)tiles), dim3(kThreads), 0, s, H, n,
-                               static_cast<const float*>(X), ldx, ntok);
+                               static_cast<const float*>(X), ldx, ntok, set);
     }
     return hipGetLastError();
 }

@@ -64,7 +64,7 @@ int device_cu_count();
 
 // ---- stage 1 ---------------------------------------------------------------
 hipError_t launch_hessian(float* H, int64_t n, const void* X, int x_is_f16, int64_t ntok,
-                          int64_t ldx, hipStream_t s);
+                          int64_t ldx, int set, hipStream_t s);
 
 // ---- stages 2 + 3 ----------------------------------------------------------
 constexpr int kCholNB = 64;  // panel width of the blocked factorization

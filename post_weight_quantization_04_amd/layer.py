@@ -44,15 +44,16 @@ class Workspace:
 
 def hessian(X, chunk: Optional[int] = None, H=None, stream=None):
     """``H = 2 X X^T`` (lower triangle) from a device ``X [d_in, N]``,
-    streamed in token chunks of ``chunk`` (whole X if None)."""
+    streamed in token chunks of ``chunk`` (whole X if None): the first chunk
+    sets the lower triangle, the others accumulate into it.  A new H has a
+    zero upper triangle; that of a given H is left as it is."""
     import torch
     d_in, n = X.shape
     if H is None:
         H = torch.zeros((d_in, d_in), dtype=torch.float32, device=X.device)
-    else:
-        H.zero_()
     step = chunk or max(n, 1)
-    for t0 in range(0, n, step):
+    _lib.hessian_set(H, X[:, 0:min(step, n)], stream=stream)
+    for t0 in range(step, n, step):
         _lib.hessian_accumulate(H, X[:, t0:t0 + step], stream=stream)
     return H
 

@@ -70,6 +70,16 @@ def test_hessian_argument_errors(clib):
     assert f(None, 4, None, 1, 0, 0, None) == 0          # no tokens
 
 
+def test_hessian_set_argument_errors(clib):
+    f = clib.gptq_hessian_set
+    assert f(None, 4, None, 0, 8, 4, None) == 1          # ldx < n_tokens
+    assert f(None, -1, None, 0, 8, 8, None) == 1
+    assert f(None, 4, None, 7, 8, 8, None) == 1          # dtype
+    assert f(None, 4, None, 0, 8, 8, None) == 1          # null pointers
+    assert f(None, 0, None, 0, 8, 8, None) == 0          # empty
+    assert f(None, 4, None, 1, 0, 0, None) == 1          # no tokens still writes H: H null is an error
+
+
 def test_prepare_argument_errors(clib):
     f = clib.gptq_prepare_hinv
     fake = ctypes.c_void_p(256)  # never dereferenced: validation fails first

@@ -77,6 +77,50 @@ def test_hessian(lib, n, N, xdtype, chunk):
     assert np.all(np.triu(Hd, 1) == 0)  # upper triangle untouched (zeroed by the caller)
 
 
+@pytest.mark.parametrize("n,N,xdtype,chunk", [
+    (300, 200, np.float16, 64),       # 128-wide tiles: set, then three accumulating chunks
+    (4000, 333, np.float16, None),    # 192-wide tiles
+    (8000, 100, np.float16, 40),      # 256-wide tiles
+    (200, 150, np.float32, 50),       # float32 inputs
+])
+def test_hessian_set_then_accumulate(lib, n, N, xdtype, chunk):
+    """Setting H from the first chunk (old values neither read nor needed)
+    and accumulating the rest gives, bit for bit, the H of accumulating every
+    chunk into a zeroed H; the strictly upper triangle is not written."""
+    import torch
+    say("hessian set", n, N, xdtype.__name__, chunk)
+    _, X = _problem(1, n, N, seed=n + 7 * N, xdtype=xdtype)
+    Xd = dev(X)
+    step = chunk or N
+    H0 = torch.zeros((n, n), dtype=torch.float32, device=Xd.device)
+    for t0 in range(0, N, step):
+        _lib_mod().hessian_accumulate(H0, Xd[:, t0:t0 + step])
+    H1 = torch.full((n, n), 7.0, dtype=torch.float32, device=Xd.device)
+    _lib_mod().hessian_set(H1, Xd[:, 0:step])
+    for t0 in range(step, N, step):
+        _lib_mod().hessian_accumulate(H1, Xd[:, t0:t0 + step])
+    torch.cuda.synchronize()
+    a, b = host(H0), host(H1)
+    np.testing.assert_array_equal(np.tril(b), np.tril(a))
+    assert np.all(b[np.triu_indices(n, 1)] == 7.0)
+
+
+def test_hessian_set_empty_writes_zero(lib):
+    import torch
+    say("hessian set, no tokens")
+    H = torch.full((70, 70), 3.0, dtype=torch.float32, device="cuda")
+    X = torch.zeros((70, 0), dtype=torch.float16, device="cuda")
+    _lib_mod().hessian_set(H, X)
+    torch.cuda.synchronize()
+    h = host(H)
+    assert np.all(h[np.tril_indices(70)] == 0.0) and np.all(h[np.triu_indices(70, 1)] == 3.0)
+
+
+def _lib_mod():
+    from post_weight_quantization_04_amd import _lib
+    return _lib
+
+
 def test_hessian_fp16_products_exact(lib):
     """Each f16 x f16 product is exact in fp32: a single-token X gives
     H = 2 x x^T exactly."""
