@@ -67,7 +67,8 @@ typedef enum {
  *   H        [d_in, d_in] float32, leading dimension d_in.  Only the lower
  *            triangle including the diagonal (row >= col) is read and
  *            written; the strictly upper triangle is left untouched.  The
- *            caller zeroes H before the first chunk.
+ *            caller zeroes H before the first chunk, or writes the first
+ *            chunk with gptq_hessian_set.
  *   X        [d_in, n_tokens] of x_dtype, row stride ldx elements (>= n_tokens):
  *            row i holds channel i's value for each token, so a token chunk
  *            of a larger X is the pointer X + t0 with the same ldx.
