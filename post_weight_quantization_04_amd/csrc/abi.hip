@@ -18,7 +18,7 @@ namespace gptq {
 // ---------------------------------------------------------------------------
 namespace {
 const char* const kNames[K_COUNT] = {
-    "hessian_f16", "hessian_f32", "hinv_diag_stats", "hinv_load_reversed", "chol_step", "hinv_store_u",
+    "hessian_f16", "hessian_f32", "hinv_load_reversed", "chol_step", "hinv_store_u",
     "q_grid_convert",         "q_group_grid",       "q_step",    "q_trail",
     "pack_codes",  "dequantize",  "output_error", "obq_hinv", "obq_rows", "propagate",
     "hinv32_load_reversed", "chol32_step", "hinv32_store_u",

@@ -44,14 +44,13 @@ constexpr int kLdsLd = NB + 8;   // padded LDS row (doubles)
 struct HinvWs {
     double* G;      // n_pad x n_pad by 64x64 tiles (see gt)
     double* P;      // 3 x [n_pad / NB][NB][NB] (step s uses buffer s % 3)
-    double* scal;   // [0] = lambda
     int* fail;      // device flag: set once a pivot fails
 };
 
 // Bytes of the factorization workspace for order n (layout in carve()).
 constexpr size_t ws_bytes(int64_t n) {
     return (size_t)(round_up(round_up(n, NB) * round_up(n, NB) * 8, 256) + 3 * round_up(round_up(n, NB) * NB * 8, 256) +
-                    256 + 256);
+                    256);
 }
 
 // Fixed device scratch of gptq_prepare_hinv_noalloc, for callers that cannot
@@ -68,8 +67,6 @@ HinvWs carve(void* ws, int64_t n) {
     p += round_up(np * np * 8, 256);
     w.P = reinterpret_cast<double*>(p);  // three panel buffers
     p += 3 * round_up(np * NB * 8, 256);
-    w.scal = reinterpret_cast<double*>(p);
-    p += 256;
     w.fail = reinterpret_cast<int*>(p);
     return w;
 }
@@ -1047,14 +1044,11 @@ hipError_t launch_prepare_hinv(const float* H, int64_t n, double damp_frac, floa
     double* Pbuf[3] = {w.P, w.P + pstride, w.P + 2 * pstride};  // step s: buffer s % 3
     hipError_t e = hipSuccess;
     {
-        TimedLaunch t(K_HINV_DIAGSUM, s);
-        GPTQ_LAUNCH(t, diag_stats_kernel, dim3(1), dim3(1024), 0, s, H, n, damp_frac, dead, w.scal, lambda_out,
-                           info, w.fail);
-    }
-    {
+        // lambda, the dead flags and the status words come with the reversed
+        // load (its diagonal-tile workgroups)
         TimedLaunch t(K_HINV_LOAD, s);
-        GPTQ_LAUNCH(t, load_reversed_kernel<double>, dim3((unsigned)((int64_t)T * (T + 1) / 2)), dim3(256), 0, s, H, n,
-                           np, (const double*)w.scal, w.G);
+        GPTQ_LAUNCH(t, load_reversed_kernel<double>, dim3((unsigned)((int64_t)T * (T + 1) / 2)), dim3(256), 0, s,
+                           H, n, np, damp_frac, dead, lambda_out, info, w.fail, w.G);
     }
     const int npan = std::max(T - 1, 1);  // workgroups of the diagonal-block + panel launch of step 0
     {

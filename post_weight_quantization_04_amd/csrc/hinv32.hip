@@ -39,13 +39,12 @@ constexpr int kThreads = 256;
 struct Ws32 {
     float* G;      // n_pad x n_pad by 64x64 tiles (see gt)
     float* P;      // 3 x [n_pad / NB][NB][NB] (step s uses buffer s % 3)
-    double* scal;  // [0] = lambda
     int* fail;     // device flag: set once a pivot fails
 };
 
 constexpr size_t ws32_bytes(int64_t n) {
     return (size_t)(round_up(round_up(n, NB) * round_up(n, NB) * 4, 256) + 3 * round_up(round_up(n, NB) * NB * 4, 256) +
-                    256 + 256);
+                    256);
 }
 
 Ws32 carve32(void* ws, int64_t n) {
@@ -56,8 +55,6 @@ Ws32 carve32(void* ws, int64_t n) {
     p += round_up(np * np * 4, 256);
     w.P = reinterpret_cast<float*>(p);
     p += 3 * round_up(np * NB * 4, 256);
-    w.scal = reinterpret_cast<double*>(p);
-    p += 256;
     w.fail = reinterpret_cast<int*>(p);
     return w;
 }
@@ -977,14 +974,11 @@ hipError_t launch_prepare_hinv32(const float* H, int64_t n, double damp_frac, fl
     const int64_t pstride = round_up(np * NB * 4, 256) / 4;
     float* Pbuf[3] = {w.P, w.P + pstride, w.P + 2 * pstride};  // step s: buffer s % 3
     {
-        TimedLaunch t(K_HINV_DIAGSUM, s);
-        GPTQ_LAUNCH(t, diag_stats_kernel, dim3(1), dim3(1024), 0, s, H, n, damp_frac, dead, w.scal, lambda_out,
-                           info, w.fail);
-    }
-    {
+        // lambda, the dead flags and the status words come with the reversed
+        // load (its diagonal-tile workgroups)
         TimedLaunch t(K_HINV32_LOAD, s);
         GPTQ_LAUNCH(t, load_reversed_kernel<float>, dim3((unsigned)((int64_t)T * (T + 1) / 2)), dim3(256), 0, s,
-                           H, n, np, (const double*)w.scal, w.G);
+                           H, n, np, damp_frac, dead, lambda_out, info, w.fail, w.G);
     }
     const int npan = T - 1 > 1 ? T - 1 : 1;  // workgroups of the step-0 launch
     {

@@ -12,7 +12,6 @@ namespace gptq {
 enum KernelId {
     K_HESS_F16 = 0,
     K_HESS_F32,
-    K_HINV_DIAGSUM,
     K_HINV_LOAD,
     K_CHOL_STEP,
     K_HINV_STORE,

@@ -36,16 +36,13 @@ __device__ __forceinline__ void tri_index(int64_t b, int64_t& I, int64_t& J) {
     J = b - i * (i + 1) / 2;
 }
 
-// lambda = damp * mean(diag H) in float64, dead flags (zero diagonal), and
-// the status words cleared.  One workgroup of 1024 threads.
-__global__ __launch_bounds__(1024) void diag_stats_kernel(const float* __restrict__ H, int64_t n, double damp,
-                                                          uint8_t* __restrict__ dead, double* __restrict__ scal,
-                                                          double* __restrict__ lambda_out, int32_t* __restrict__ info,
-                                                          int* __restrict__ fail) {
-    __shared__ double part[16];
+// The statistics inside the reversed load: every workgroup of a diagonal
+// tile sums the whole diagonal of H itself, in float64 and in one fixed
+// order (so every copy of lambda is the same number), and marks the dead
+// channels of its own tile; workgroup 0 (tile (0, 0)) publishes lambda and
+// clears the status words.  This replaces diag_stats_kernel and its launch.
+__device__ __forceinline__ double diag_lambda(const float* __restrict__ H, int64_t n, double damp, double* red) {
     double s = 0.0;
-    // every diagonal entry sits on its own cache line: a thread's loads are
-    // issued eight at a time before any is used (the sum keeps its order)
     constexpr int kB = 8;
     for (int64_t i0 = threadIdx.x; i0 < n; i0 += (int64_t)kB * blockDim.x) {
         float h[kB];
@@ -55,26 +52,14 @@ __global__ __launch_bounds__(1024) void diag_stats_kernel(const float* __restric
             h[b] = (i < n) ? H[i * n + i] : 0.0f;
         }
 #pragma unroll
-        for (int b = 0; b < kB; ++b) {
-            const int64_t i = i0 + (int64_t)b * blockDim.x;
-            if (i < n) {
-                s += (double)h[b];
-                if (dead) dead[i] = (h[b] == 0.0f) ? 1 : 0;
-            }
-        }
+        for (int b = 0; b < kB; ++b) s += (double)h[b];
     }
     s = wave_sum(s);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        double t = 0.0;
-        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += part[w];
-        double lam = damp * (t / (double)n);
-        scal[0] = lam;
-        if (lambda_out) *lambda_out = lam;
-        *info = 0;
-        *fail = 0;
-    }
+    double t = 0.0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
+    return damp * (t / (double)n);
 }
 
 // G = J (H + damping) J, lower triangle, padded with identity, in the tile
@@ -85,12 +70,29 @@ __global__ __launch_bounds__(1024) void diag_stats_kernel(const float* __restric
 // of G per workgroup, transposed through LDS.
 template <typename E>
 __global__ __launch_bounds__(256) void load_reversed_kernel(const float* __restrict__ H, int64_t n, int64_t np,
-                                                            const double* __restrict__ scal, E* __restrict__ G) {
+                                                            double damp, uint8_t* __restrict__ dead,
+                                                            double* __restrict__ lambda_out,
+                                                            int32_t* __restrict__ info, int* __restrict__ fail,
+                                                            E* __restrict__ G) {
     __shared__ float T[64][65];
+    __shared__ double red[4];
     int64_t TI, TJ;
     tri_index(blockIdx.x, TI, TJ);
-    const double lam = scal[0];
     const int tid = threadIdx.x;
+    double lam = 0.0;
+    if (TI == TJ) {  // block-uniform
+        lam = diag_lambda(H, n, damp, red);
+        // dead flags of this tile's channels: G index i is channel n-1-i
+        if (dead && tid < 64) {
+            const int64_t i = TI * 64 + tid;
+            if (i < n) dead[n - 1 - i] = (H[(n - 1 - i) * n + (n - 1 - i)] == 0.0f) ? 1 : 0;
+        }
+        if (blockIdx.x == 0 && tid == 0) {
+            if (lambda_out) *lambda_out = lam;
+            *info = 0;
+            *fail = 0;
+        }
+    }
     // stage: T[jj][ii] = H[n-1-(64TJ+jj)][n-1-(64TI+ii)], reading H rows
     // contiguously; a thread's 16 loads are issued before any is used
     // (entries outside the triangle load H[0] and are replaced by zero)
