@@ -350,29 +350,32 @@ __global__ __launch_bounds__(kWsThreads, 1) void hessian_f16_ws_kernel(float* __
         // pieces 0..kWsPieces/2-1 lie in panel I, the rest in panel J (row
         // lt / 8 + 24 i < 192 exactly for i < 8)
         constexpr int kHalf = kWsPieces / 2;
-        // clamped row of each piece; its address is formed at each use
-        // (kept as a pointer per piece, the sixteen 64-bit addresses and their
-        // per-slab increments outgrew the register budget)
-        int prow[kWsPieces];
+        // byte offset of each piece (clamped row, first token of the piece)
+        // from the first token of its slab: a full slab's loads take a
+        // wave-uniform base plus these 32-bit offsets, with no per-load
+        // 64-bit address arithmetic (the launcher checks that they fit)
+        unsigned voff[kWsPieces];
         const int dst0 = (lt / kWsChunks) * kWsLd + chunk * 8;
 #pragma unroll
         for (int i = 0; i < kWsPieces; ++i) {
             const int rr = lt / kWsChunks + kWsRowsPerPass * (i % kHalf);
             // rows past n are clamped to row n-1: they feed only accumulator
             // entries that are never stored
-            prow[i] = (int)min((int64_t)((i < kHalf ? rA : rB) + rr), n - 1);
+            const int64_t row = min((int64_t)((i < kHalf ? rA : rB) + rr), n - 1);
+            voff[i] = (unsigned)((row * ldx + chunk * 8) * 2);
         }
+        // first element of piece i's row
         auto rowp = [&](int i) {
-            int r = prow[i];
-            asm volatile("" : "+v"(r));  // formed here, not hoisted out of the slab loop
-            return X + (int64_t)r * ldx;
+            unsigned o = voff[i];
+            asm volatile("" : "+v"(o));  // formed at each use, not kept as sixteen 64-bit pointers
+            return reinterpret_cast<const half_t*>(reinterpret_cast<const char*>(X) + o) - chunk * 8;
         };
         half8 v[kWsDepth][kWsPieces];
         // a full slab: one unconditional 16-byte load per piece
         auto fetch_full_ws = [&](half8(&x)[kWsPieces], int64_t f) {
+            const char* base = reinterpret_cast<const char*>(X + f * kWsK);
 #pragma unroll
-            for (int i = 0; i < kWsPieces; ++i)
-                x[i] = *reinterpret_cast<const half8*>(rowp(i) + f * kWsK + chunk * 8);
+            for (int i = 0; i < kWsPieces; ++i) x[i] = *reinterpret_cast<const half8*>(base + voff[i]);
         };
         // any slab: full ones as above, the partial last one (or every slab of
         // an unaligned X) by element loads with tokens past ntok read as zero;
@@ -591,7 +594,9 @@ hipError_t launch_hessian(float* H, int64_t n, const void* X, int x_is_f16, int6
             GPTQ_LAUNCH(t, (hessian_f16_kernel<kWideTile, kWideThreads, kKf16, kDepthf16>),
                                dim3((unsigned)(per_xcd * kXcds)), dim3(kWideThreads), 0, s, H, n,
                                static_cast<const half_t*>(X), ldx, ntok, nfull, (int)Tw, per_xcd, set);
-        } else if (Tw >= kWideMinT) {
+        } else if (Tw >= kWideMinT && (n - 1) * ldx * 2 + 256 < ((int64_t)1 << 32)) {
+            // (the warp-specialised kernel addresses X by 32-bit byte offsets
+            // from each slab's first token)
             const int64_t Tm = (n + kWsTile - 1) / kWsTile;
             const int64_t nfull_ws = vec ? ntok / kWsK : 0;
             const int per_xcd = (int)((Tm * (Tm + 1) / 2 + kXcds - 1) / kXcds);
