@@ -105,6 +105,28 @@ def test_hessian_set_then_accumulate(lib, n, N, xdtype, chunk):
     assert np.all(b[np.triu_indices(n, 1)] == 7.0)
 
 
+@pytest.mark.parametrize("ldx", [530_000, 540_000])
+def test_hessian_large_row_stride(lib, ldx):
+    """A chunk of a very long X (rows 1 MB apart): with byte offsets below
+    4 GiB the 192-wide kernel takes d_in = 4000, above it the 128-wide one;
+    either gives, bit for bit, the H of the same chunk stored contiguously."""
+    import torch
+    n, N = 4000, 96
+    say("hessian large row stride", n, N, ldx)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    big = torch.empty((n, ldx), dtype=torch.float16, device="cuda")
+    big[:, :N] = torch.randn((n, N), generator=g, device="cuda").to(torch.float16)
+    Xv = big[:, :N]
+    Xc = Xv.contiguous()
+    H0 = torch.zeros((n, n), dtype=torch.float32, device="cuda")
+    H1 = torch.zeros((n, n), dtype=torch.float32, device="cuda")
+    _lib_mod().hessian_accumulate(H0, Xc)
+    _lib_mod().hessian_accumulate(H1, Xv)
+    torch.cuda.synchronize()
+    assert torch.equal(H0, H1)
+    del big, Xv
+
+
 def test_hessian_set_empty_writes_zero(lib):
     import torch
     say("hessian set, no tokens")
