@@ -240,15 +240,16 @@ def block_bench(args, wl, torch, wlm, _lib, layer, split: bool, fp32: bool) -> i
     stream = torch.cuda.current_stream()
     chunk = {xs.key: xs.chunk for xs in wl.xs}
 
+    # the token chunks of every activation set, as separate views
+    views = {xs.key: [Xd[xs.key][:, t0:t0 + chunk[xs.key]] for t0 in range(0, xs.n_tokens, chunk[xs.key])]
+             for xs in wl.xs}
+
     def run(times=None):
         ev = []
         for xs in wl.xs:
             a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
             a.record(stream)
-            ck = chunk[xs.key]
-            _lib.hessian_set(H[xs.key], Xd[xs.key][:, 0:ck])
-            for t0 in range(ck, xs.n_tokens, ck):
-                _lib.hessian_accumulate(H[xs.key], Xd[xs.key][:, t0:t0 + ck])
+            hessian_stage(_lib, H[xs.key], views[xs.key])
             b.record(stream)
             layer.prepare(H[xs.key], wl.damp, ws=ws[xs.key], out=fac[xs.key], fp32=fp32)
             c.record(stream)
@@ -305,6 +306,18 @@ def block_bench(args, wl, torch, wlm, _lib, layer, split: bool, fp32: bool) -> i
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+def hessian_stage(_lib, H, views):
+    """H from the token chunks of one activation set: one chunked call when
+    they share a shape (the first chunk sets H's lower triangle, the others
+    add), else the first set and the others added one call each."""
+    if len(views) > 1 and all(v.shape == views[0].shape for v in views):
+        _lib.hessian_chunks(H, views, set_first=True)
+        return
+    _lib.hessian_set(H, views[0])
+    for v in views[1:]:
+        _lib.hessian_accumulate(H, v)
 
 
 def main(argv=None) -> int:
@@ -371,11 +384,10 @@ def main(argv=None) -> int:
     chunk = xs.chunk
     stream = torch.cuda.current_stream()
 
+    views = [Xd[:, t0:t0 + chunk] for t0 in range(0, n_tok, chunk)]
+
     def stage_h():
-        # the first chunk sets H's lower triangle, the others accumulate
-        _lib.hessian_set(H, Xd[:, 0:chunk])
-        for t0 in range(chunk, n_tok, chunk):
-            _lib.hessian_accumulate(H, Xd[:, t0:t0 + chunk])
+        hessian_stage(_lib, H, views)
 
     def stage_u(fp32=fp32):
         layer.prepare(H, wl.damp, ws=ws1, out=fac, fp32=fp32)

@@ -4,7 +4,8 @@
  *
  * The path quantizes one linear layer W [d_out, d_in] against calibration
  * inputs X [d_in, N] in four stages:
- *   1. H = 2 X X^T             (gptq_hessian_set, gptq_hessian_accumulate)
+ *   1. H = 2 X X^T             (gptq_hessian_set, gptq_hessian_accumulate,
+ *                               gptq_hessian_accumulate_chunks)
  *   2. H <- H + lambda I, dead channels skipped   (gptq_prepare_hinv)
  *   3. U upper with H^-1 = U^T U                  (gptq_prepare_hinv)
  *   4. fixed-order, block-lazy quantize-and-compensate sweep
@@ -97,6 +98,34 @@ int gptq_hessian_accumulate(float* H, int64_t d_in, const void* X, int x_dtype,
  */
 int gptq_hessian_set(float* H, int64_t d_in, const void* X, int x_dtype,
                      int64_t n_tokens, int64_t ldx, void* stream);
+
+/*
+ * Stage 1 over several token chunks in one call (same sections of the same
+ * pages):
+ *     H = [H +] sum_c 2 * X_c * X_c^T,   c = 0 .. n_chunks-1
+ * on the lower triangle including the diagonal; the strictly upper triangle
+ * is not written.  For callers that hold several chunks at once (separate
+ * buffers, one shape): up to 32 float16 chunks whose rows start 16-byte
+ * aligned and whose n_tokens is a multiple of 64 are summed in one launch,
+ * with a single float32 add into H, instead of one read-modify-write of H
+ * per chunk.  Other chunks (float32, unaligned, ragged) are added one call
+ * per chunk, as by gptq_hessian_set / gptq_hessian_accumulate.  The sum
+ * over a group of chunks equals, bit for bit, one gptq_hessian_accumulate
+ * call over the same tokens stored contiguously; against one call per
+ * chunk it differs only by float32 rounding of the per-chunk adds.
+ *
+ *   X_chunks  HOST array of n_chunks DEVICE pointers; chunk c is
+ *             [d_in, n_tokens] of x_dtype with row stride ldx.
+ *   set       1: the first chunk writes H (old values neither read nor
+ *             needed; n_chunks = 0 or n_tokens = 0 writes zeros);
+ *             0: every chunk adds into H.
+ *   other arguments as gptq_hessian_accumulate.
+ * Errors: GPTQ_EINVAL for H null (when anything is written), X_chunks or a
+ * chunk pointer null with n_chunks, n_tokens > 0, d_in < 0, n_chunks < 0,
+ * n_tokens < 0, ldx < n_tokens, set not 0 or 1, unknown x_dtype.
+ */
+int gptq_hessian_accumulate_chunks(float* H, int64_t d_in, const void* const* X_chunks, int64_t n_chunks,
+                                   int x_dtype, int64_t n_tokens, int64_t ldx, int set, void* stream);
 
 /*
  * Stages 2 and 3 -- damping, dead channels and the factor U.

@@ -20,6 +20,7 @@ GPTQ_F16, GPTQ_F32 = 0, 1
 EXPORTS = (
     "gptq_hessian_accumulate",
     "gptq_hessian_set",
+    "gptq_hessian_accumulate_chunks",
     "gptq_prepare_hinv_workspace",
     "gptq_prepare_hinv",
     "gptq_prepare_hinv_fp32_workspace",
@@ -73,6 +74,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "gptq_hessian_accumulate": (_i32, [_vp, _i64, _vp, _i32, _i64, _i64, _vp]),
         "gptq_hessian_set": (_i32, [_vp, _i64, _vp, _i32, _i64, _i64, _vp]),
+        "gptq_hessian_accumulate_chunks": (_i32, [_vp, _i64, _vp, _i64, _i32, _i64, _i64, _i32, _vp]),
         "gptq_prepare_hinv_workspace": (_sz, [_i64]),
         "gptq_prepare_hinv": (_i32, [_vp, _i64, ctypes.c_double, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
         "gptq_prepare_hinv_fp32_workspace": (_sz, [_i64]),
@@ -166,6 +168,29 @@ def hessian_set(H, X, stream=None) -> None:
     """``H[lower] = 2 X X^T`` (the old values not read; the strictly upper
     triangle not written), for the first token chunk."""
     _hessian_call("gptq_hessian_set", H, X, stream)
+
+
+def hessian_chunks(H, Xs, set_first: bool = False, stream=None) -> None:
+    """``H[lower] (=|+=) sum_c 2 X_c X_c^T`` over a list of token chunks of
+    one shape, dtype and row stride (2-D views with unit column stride);
+    ``set_first`` writes H from the first chunk instead of adding."""
+    Xs = list(Xs)
+    if not Xs:
+        raise ValueError("no chunks")
+    X0 = Xs[0]
+    for X in Xs:
+        if X.dim() != 2 or X.stride(1) != 1 or not X.is_cuda:
+            raise ValueError("chunks must be 2-D device views with unit column stride")
+        if X.shape != X0.shape or X.stride(0) != X0.stride(0) or X.dtype != X0.dtype:
+            raise ValueError("chunks differ in shape, row stride or dtype")
+    d_in, n = X0.shape
+    if H.shape != (d_in, d_in):
+        raise ValueError("H shape")
+    ptrs = (ctypes.c_void_p * len(Xs))(*[X.data_ptr() for X in Xs])
+    rc = load().gptq_hessian_accumulate_chunks(_ptr(H), d_in, ctypes.cast(ptrs, ctypes.c_void_p), len(Xs),
+                                               _dtype_code(X0), n, X0.stride(0), int(bool(set_first)),
+                                               _stream(stream))
+    _check("gptq_hessian_accumulate_chunks", rc)
 
 
 def prepare_hinv_workspace(d_in: int, fp32: bool = False) -> int:

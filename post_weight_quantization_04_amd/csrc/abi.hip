@@ -142,7 +142,7 @@ int gptq_hessian_accumulate(float* H, int64_t d_in, const void* X, int x_dtype, 
     if (d_in == 0 || n_tokens == 0) return GPTQ_OK;
     if (!H || !X) return GPTQ_EINVAL;
     if (d_in > (int64_t)1 << 20) return GPTQ_EUNSUPPORTED;
-    return hip_status(launch_hessian(H, d_in, X, x_dtype == GPTQ_F16, n_tokens, ldx, 0, as_stream(stream)));
+    return hip_status(launch_hessian(H, d_in, &X, 1, x_dtype == GPTQ_F16, n_tokens, ldx, 0, as_stream(stream)));
 }
 
 int gptq_hessian_set(float* H, int64_t d_in, const void* X, int x_dtype, int64_t n_tokens, int64_t ldx,
@@ -152,7 +152,32 @@ int gptq_hessian_set(float* H, int64_t d_in, const void* X, int x_dtype, int64_t
     if (d_in == 0) return GPTQ_OK;
     if (!H || (n_tokens > 0 && !X)) return GPTQ_EINVAL;
     if (d_in > (int64_t)1 << 20) return GPTQ_EUNSUPPORTED;
-    return hip_status(launch_hessian(H, d_in, X, x_dtype == GPTQ_F16, n_tokens, ldx, 1, as_stream(stream)));
+    return hip_status(launch_hessian(H, d_in, &X, 1, x_dtype == GPTQ_F16, n_tokens, ldx, 1, as_stream(stream)));
+}
+
+int gptq_hessian_accumulate_chunks(float* H, int64_t d_in, const void* const* X_chunks, int64_t n_chunks,
+                                   int x_dtype, int64_t n_tokens, int64_t ldx, int set, void* stream) {
+    if (d_in < 0 || n_chunks < 0 || n_tokens < 0 || ldx < n_tokens) return GPTQ_EINVAL;
+    if (x_dtype != GPTQ_F16 && x_dtype != GPTQ_F32) return GPTQ_EINVAL;
+    if (set != 0 && set != 1) return GPTQ_EINVAL;
+    if (d_in == 0) return GPTQ_OK;
+    if (n_chunks > 0 && n_tokens > 0) {
+        if (!X_chunks) return GPTQ_EINVAL;
+        for (int64_t c = 0; c < n_chunks; ++c)
+            if (!X_chunks[c]) return GPTQ_EINVAL;
+    }
+    if (n_chunks == 0 || n_tokens == 0) {
+        if (!set) return GPTQ_OK;
+        if (!H) return GPTQ_EINVAL;
+        if (d_in > (int64_t)1 << 20) return GPTQ_EUNSUPPORTED;
+        // an empty sum: the lower triangle becomes zero
+        const void* none = nullptr;
+        return hip_status(launch_hessian(H, d_in, &none, 1, x_dtype == GPTQ_F16, 0, ldx, 1, as_stream(stream)));
+    }
+    if (!H) return GPTQ_EINVAL;
+    if (d_in > (int64_t)1 << 20) return GPTQ_EUNSUPPORTED;
+    return hip_status(launch_hessian(H, d_in, X_chunks, n_chunks, x_dtype == GPTQ_F16, n_tokens, ldx, set,
+                                     as_stream(stream)));
 }
 
 size_t gptq_prepare_hinv_workspace(int64_t d_in) { return d_in > 0 ? hinv_workspace_bytes(d_in) : 0; }

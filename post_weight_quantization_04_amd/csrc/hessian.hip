@@ -88,6 +88,15 @@ __device__ __forceinline__ void store_quarter(float* __restrict__ H, int64_t n, 
 constexpr int kXcds = 8;
 constexpr int kSuper = 4;  // super-tile edge, in tiles
 
+// The token chunks of one call: chunk c holds the call's tokens
+// [c * spc * slab, (c + 1) * spc * slab) at p[c] (every chunk the same row
+// stride), so that one launch sums several chunks before its single add into
+// H.  spc = 0: one chunk, at X.
+constexpr int kMaxChunks = 32;
+struct XChunks {
+    const half_t* p[kMaxChunks];
+};
+
 // Tile t of the super-tile order: super-rows P (kSuper tile rows each), in
 // each super-row the super-tiles Q <= P left to right, in each super-tile the
 // tiles row by row (only J <= I on the diagonal super-tile).
@@ -196,7 +205,7 @@ template <int kTl, int kThr, int kK, int kDepth>
 __global__ __launch_bounds__(kThr, kThr == kThreads ? 2 : 1) void hessian_f16_kernel(float* __restrict__ H, int64_t n,
                                                                  const half_t* __restrict__ X, int64_t ldx,
                                                                  int64_t ntok, int64_t nfull, int T,
-                                                                 int per_xcd, int set) {
+                                                                 int per_xcd, int set, const XChunks xc, int spc) {
     using S = Slab<kTl, kThr, kK>;
     constexpr int kWg = kTl / 64;  // computing waves per tile dimension (further waves only load)
     __shared__ half_t As[2][kTl * S::kLd];
@@ -221,10 +230,21 @@ __global__ __launch_bounds__(kThr, kThr == kThreads ? 2 : 1) void hessian_f16_ke
     const int64_t nslab = (ntok + kK - 1) / kK;
     SlabRegs<kTl, kThr, kK> ra[kDepth], rb[kDepth];
 
+    // full slab f: slab f % spc of chunk f / spc (with several chunks)
+    auto full = [&](SlabRegs<kTl, kThr, kK>& va, SlabRegs<kTl, kThr, kK>& vb, int64_t f) {
+        const half_t* Xc = X;
+        int64_t k0 = f * kK;
+        if (spc) {
+            const int c = (int)f / spc;
+            Xc = xc.p[c];
+            k0 = (f - (int64_t)c * spc) * kK;
+        }
+        fetch_full<kTl, kThr, kK>(va, Xc, n, ldx, rA, k0, tid);
+        fetch_full<kTl, kThr, kK>(vb, Xc, n, ldx, rB, k0, tid);
+    };
     auto fetch = [&](SlabRegs<kTl, kThr, kK>& va, SlabRegs<kTl, kThr, kK>& vb, int64_t f) {
         if (f < nfull) {
-            fetch_full<kTl, kThr, kK>(va, X, n, ldx, rA, f * kK, tid);
-            fetch_full<kTl, kThr, kK>(vb, X, n, ldx, rB, f * kK, tid);
+            full(va, vb, f);
         } else if (f < nslab) {
             fetch_tail<kTl, kThr, kK>(va, X, n, ldx, ntok, rA, f * kK, tid);
             fetch_tail<kTl, kThr, kK>(vb, X, n, ldx, ntok, rB, f * kK, tid);
@@ -270,8 +290,7 @@ __global__ __launch_bounds__(kThr, kThr == kThreads ? 2 : 1) void hessian_f16_ke
     if (nsteady > 0) {
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
-            fetch_full<kTl, kThr, kK>(ra[d], X, n, ldx, rA, (int64_t)d * kK, tid);
-            fetch_full<kTl, kThr, kK>(rb[d], X, n, ldx, rB, (int64_t)d * kK, tid);
+            full(ra[d], rb[d], d);
             __builtin_amdgcn_sched_barrier(0);  // issue the sets in slab order
         }
         for (; s0 < nsteady; s0 += kDepth) {
@@ -279,8 +298,7 @@ __global__ __launch_bounds__(kThr, kThr == kThreads ? 2 : 1) void hessian_f16_ke
             for (int d = 0; d < kDepth; ++d) {
                 const int64_t sl = s0 + d;
                 stash(ra[d], rb[d], sl);
-                fetch_full<kTl, kThr, kK>(ra[d], X, n, ldx, rA, (sl + kDepth) * kK, tid);
-                fetch_full<kTl, kThr, kK>(rb[d], X, n, ldx, rB, (sl + kDepth) * kK, tid);
+                full(ra[d], rb[d], sl + kDepth);
                 compute(sl);
             }
         }
@@ -333,7 +351,7 @@ static_assert(kWsPieces * kWsRowsPerPass == 2 * kWsTile && kWsPieces % 2 == 0, "
 __global__ __launch_bounds__(kWsThreads, 1) void hessian_f16_ws_kernel(float* __restrict__ H, int64_t n,
                                                                        const half_t* __restrict__ X, int64_t ldx,
                                                                        int64_t ntok, int64_t nfull, int T,
-                                                                       int per_xcd, int set) {
+                                                                       int per_xcd, int set, const XChunks xc, int spc) {
     __shared__ half_t As[2][kWsTile * kWsLd];
     __shared__ half_t Bs[2][kWsTile * kWsLd];
     const int t = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
@@ -373,7 +391,15 @@ __global__ __launch_bounds__(kWsThreads, 1) void hessian_f16_ws_kernel(float* __
         half8 v[kWsDepth][kWsPieces];
         // a full slab: one unconditional 16-byte load per piece
         auto fetch_full_ws = [&](half8(&x)[kWsPieces], int64_t f) {
-            const char* base = reinterpret_cast<const char*>(X + f * kWsK);
+            // slab f % spc of chunk f / spc (with several chunks)
+            const half_t* Xc = X;
+            int64_t lf = f;
+            if (spc) {
+                const int c = (int)f / spc;
+                Xc = xc.p[c];
+                lf = f - (int64_t)c * spc;
+            }
+            const char* base = reinterpret_cast<const char*>(Xc + lf * kWsK);
 #pragma unroll
             for (int i = 0; i < kWsPieces; ++i) x[i] = *reinterpret_cast<const half8*>(base + voff[i]);
         };
@@ -568,11 +594,47 @@ __global__ __launch_bounds__(256) void zero_lower_kernel(float* __restrict__ H, 
 
 }  // namespace
 
-hipError_t launch_hessian(float* H, int64_t n, const void* X, int x_is_f16, int64_t ntok, int64_t ldx, int set,
-                          hipStream_t s) {
+namespace {
+
+// One float16 launch over g chunks of ntok tokens each (g = 1: xc.p[0] with
+// any ntok; g > 1: every chunk aligned with ntok a multiple of 64).
+hipError_t launch_f16(float* H, int64_t n, const XChunks& xc, int g, int64_t ntok, int64_t ldx, bool vec, int set,
+                      hipStream_t s) {
+    TimedLaunch t(K_HESS_F16, s);
+    const half_t* X = xc.p[0];
+    const int64_t tot = ntok * g;
     const int64_t T = (n + kTile - 1) / kTile;
     const int64_t tiles = T * (T + 1) / 2;
-    if (tiles == 0) return hipSuccess;
+    // full slabs take 16-byte loads when every row start is 16-byte aligned
+    const int64_t nfull = vec ? tot / kKf16 : 0;
+    const int spc = g > 1 ? (int)(ntok / kKf16) : 0;
+    const int64_t Tw = (n + kWideTile - 1) / kWideTile;
+    const int64_t tw_all = Tw * (Tw + 1) / 2;
+    const int n_cu = device_cu_count();
+    if (Tw >= kWideMinT && n_cu > 0 && tw_all >= (int64_t)kWideMinRounds * n_cu) {
+        const int per_xcd = (int)((tw_all + kXcds - 1) / kXcds);
+        GPTQ_LAUNCH(t, (hessian_f16_kernel<kWideTile, kWideThreads, kKf16, kDepthf16>),
+                    dim3((unsigned)(per_xcd * kXcds)), dim3(kWideThreads), 0, s, H, n, X, ldx, tot, nfull, (int)Tw,
+                    per_xcd, set, xc, spc);
+    } else if (Tw >= kWideMinT && (n - 1) * ldx * 2 + 256 < ((int64_t)1 << 32)) {
+        // (the warp-specialised kernel addresses X by 32-bit byte offsets
+        // from each slab's first token)
+        const int64_t Tm = (n + kWsTile - 1) / kWsTile;
+        const int64_t nfull_ws = vec ? tot / kWsK : 0;
+        const int spc_ws = g > 1 ? (int)(ntok / kWsK) : 0;
+        const int per_xcd = (int)((Tm * (Tm + 1) / 2 + kXcds - 1) / kXcds);
+        GPTQ_LAUNCH(t, hessian_f16_ws_kernel, dim3((unsigned)(per_xcd * kXcds)), dim3(kWsThreads), 0, s, H, n, X,
+                    ldx, tot, nfull_ws, (int)Tm, per_xcd, set, xc, spc_ws);
+    } else {
+        const int per_xcd = (int)((tiles + kXcds - 1) / kXcds);
+        GPTQ_LAUNCH(t, (hessian_f16_kernel<kTile, kThreads, kKf16, kDepthf16>), dim3((unsigned)(per_xcd * kXcds)),
+                    dim3(kThreads), 0, s, H, n, X, ldx, tot, nfull, (int)T, per_xcd, set, xc, spc);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_one(float* H, int64_t n, const void* X, int x_is_f16, int64_t ntok, int64_t ldx, int set,
+                      hipStream_t s) {
     if (ntok == 0) {
         if (!set) return hipSuccess;
         // H = 2 X X^T with no tokens: the lower triangle becomes zero
@@ -582,43 +644,49 @@ hipError_t launch_hessian(float* H, int64_t n, const void* X, int x_is_f16, int6
     }
     const uintptr_t addr = reinterpret_cast<uintptr_t>(X);
     if (x_is_f16) {
-        TimedLaunch t(K_HESS_F16, s);
-        // full slabs take 16-byte loads when every row start is 16-byte aligned
-        const bool vec = (addr % 16 == 0) && (ldx % 8 == 0);
-        const int64_t nfull = vec ? ntok / kKf16 : 0;
-        const int64_t Tw = (n + kWideTile - 1) / kWideTile;
-        const int64_t tw_all = Tw * (Tw + 1) / 2;
-        const int n_cu = device_cu_count();
-        if (Tw >= kWideMinT && n_cu > 0 && tw_all >= (int64_t)kWideMinRounds * n_cu) {
-            const int per_xcd = (int)((tw_all + kXcds - 1) / kXcds);
-            GPTQ_LAUNCH(t, (hessian_f16_kernel<kWideTile, kWideThreads, kKf16, kDepthf16>),
-                               dim3((unsigned)(per_xcd * kXcds)), dim3(kWideThreads), 0, s, H, n,
-                               static_cast<const half_t*>(X), ldx, ntok, nfull, (int)Tw, per_xcd, set);
-        } else if (Tw >= kWideMinT && (n - 1) * ldx * 2 + 256 < ((int64_t)1 << 32)) {
-            // (the warp-specialised kernel addresses X by 32-bit byte offsets
-            // from each slab's first token)
-            const int64_t Tm = (n + kWsTile - 1) / kWsTile;
-            const int64_t nfull_ws = vec ? ntok / kWsK : 0;
-            const int per_xcd = (int)((Tm * (Tm + 1) / 2 + kXcds - 1) / kXcds);
-            GPTQ_LAUNCH(t, hessian_f16_ws_kernel, dim3((unsigned)(per_xcd * kXcds)), dim3(kWsThreads), 0, s, H, n,
-                               static_cast<const half_t*>(X), ldx, ntok, nfull_ws, (int)Tm, per_xcd, set);
-        } else {
-            const int per_xcd = (int)((tiles + kXcds - 1) / kXcds);
-            GPTQ_LAUNCH(t, (hessian_f16_kernel<kTile, kThreads, kKf16, kDepthf16>),
-                               dim3((unsigned)(per_xcd * kXcds)), dim3(kThreads), 0, s, H, n,
-                               static_cast<const half_t*>(X), ldx, ntok, nfull, (int)T, per_xcd, set);
-        }
-    } else {
-        TimedLaunch t(K_HESS_F32, s);
-        const bool vec = (addr % 16 == 0) && (ldx % 4 == 0);
-        if (vec)
-            GPTQ_LAUNCH(t, hessian_f32_kernel<true>, dim3((unsigned)tiles), dim3(kThreads), 0, s, H, n,
-                               static_cast<const float*>(X), ldx, ntok, set);
-        else
-            GPTQ_LAUNCH(t, hessian_f32_kernel<false>, dim3((unsigned)tiles), dim3(kThreads), 0, s, H, n,
-                               static_cast<const float*>(X), ldx, ntok, set);
+        XChunks xc{};
+        xc.p[0] = static_cast<const half_t*>(X);
+        return launch_f16(H, n, xc, 1, ntok, ldx, (addr % 16 == 0) && (ldx % 8 == 0), set, s);
     }
+    const int64_t T = (n + kTile - 1) / kTile;
+    const int64_t tiles = T * (T + 1) / 2;
+    TimedLaunch t(K_HESS_F32, s);
+    const bool vec = (addr % 16 == 0) && (ldx % 4 == 0);
+    if (vec)
+        GPTQ_LAUNCH(t, hessian_f32_kernel<true>, dim3((unsigned)tiles), dim3(kThreads), 0, s, H, n,
+                    static_cast<const float*>(X), ldx, ntok, set);
+    else
+        GPTQ_LAUNCH(t, hessian_f32_kernel<false>, dim3((unsigned)tiles), dim3(kThreads), 0, s, H, n,
+                    static_cast<const float*>(X), ldx, ntok, set);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_hessian(float* H, int64_t n, const void* const* Xs, int64_t nchunks, int x_is_f16, int64_t ntok,
+                          int64_t ldx, int set, hipStream_t s) {
+    if (n == 0 || nchunks <= 0) return hipSuccess;
+    // several float16 chunks, each 16-byte aligned with whole 64-token slabs:
+    // up to kMaxChunks of them summed in one launch, with one add into H
+    bool batch = nchunks > 1 && x_is_f16 && ntok > 0 && ntok % 64 == 0 && ldx % 8 == 0 &&
+                 ntok * kMaxChunks / kKf16 < ((int64_t)1 << 31);
+    for (int64_t c = 0; batch && c < nchunks; ++c) batch = reinterpret_cast<uintptr_t>(Xs[c]) % 16 == 0;
+    if (!batch) {
+        for (int64_t c = 0; c < nchunks; ++c) {
+            const hipError_t e = launch_one(H, n, Xs[c], x_is_f16, ntok, ldx, c == 0 ? set : 0, s);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    for (int64_t c0 = 0; c0 < nchunks; c0 += kMaxChunks) {
+        const int g = (int)std::min<int64_t>(kMaxChunks, nchunks - c0);
+        XChunks xc{};
+        for (int i = 0; i < g; ++i) xc.p[i] = static_cast<const half_t*>(Xs[c0 + i]);
+        const hipError_t e = g == 1 ? launch_one(H, n, xc.p[0], 1, ntok, ldx, c0 == 0 ? set : 0, s)
+                                    : launch_f16(H, n, xc, g, ntok, ldx, true, c0 == 0 ? set : 0, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace gptq

@@ -62,7 +62,9 @@ struct TimingOff {
 int device_cu_count();
 
 // ---- stage 1 ---------------------------------------------------------------
-hipError_t launch_hessian(float* H, int64_t n, const void* X, int x_is_f16, int64_t ntok,
+// nchunks token chunks Xs[0..nchunks) of ntok tokens each, one row stride;
+// set: the first chunk writes H instead of adding into it.
+hipError_t launch_hessian(float* H, int64_t n, const void* const* Xs, int64_t nchunks, int x_is_f16, int64_t ntok,
                           int64_t ldx, int set, hipStream_t s);
 
 // ---- stages 2 + 3 ----------------------------------------------------------

@@ -52,6 +52,15 @@ def hessian(X, chunk: Optional[int] = None, H=None, stream=None):
     if H is None:
         H = torch.zeros((d_in, d_in), dtype=torch.float32, device=X.device)
     step = chunk or max(n, 1)
+    full = [X[:, t0:t0 + step] for t0 in range(0, n - step + 1, step)]
+    if len(full) > 1:
+        # whole chunks in one call (summed before each add into H), then
+        # the ragged last chunk
+        _lib.hessian_chunks(H, full, set_first=True, stream=stream)
+        t0 = len(full) * step
+        if t0 < n:
+            _lib.hessian_accumulate(H, X[:, t0:], stream=stream)
+        return H
     _lib.hessian_set(H, X[:, 0:min(step, n)], stream=stream)
     for t0 in range(step, n, step):
         _lib.hessian_accumulate(H, X[:, t0:t0 + step], stream=stream)

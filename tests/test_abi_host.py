@@ -80,6 +80,21 @@ def test_hessian_set_argument_errors(clib):
     assert f(None, 4, None, 1, 0, 0, None) == 1          # no tokens still writes H: H null is an error
 
 
+def test_hessian_chunks_argument_errors(clib):
+    f = clib.gptq_hessian_accumulate_chunks
+    fake = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    one_null = (ctypes.c_void_p * 2)(256, None)
+    assert f(fake, 4, None, 2, 0, 8, 8, 0, None) == 1             # chunk table null
+    assert f(fake, 4, one_null, 2, 0, 8, 8, 0, None) == 1         # a chunk pointer null
+    assert f(fake, 4, None, -1, 0, 8, 8, 0, None) == 1            # n_chunks < 0
+    assert f(fake, 4, None, 2, 0, 8, 4, 0, None) == 1             # ldx < n_tokens
+    assert f(fake, 4, None, 2, 7, 8, 8, 0, None) == 1             # dtype
+    assert f(fake, 4, None, 0, 0, 8, 8, 2, None) == 1             # set not 0 or 1
+    assert f(None, 4, None, 0, 0, 8, 8, 1, None) == 1             # an empty sum still writes H
+    assert f(None, 4, None, 0, 0, 8, 8, 0, None) == 0             # nothing to add
+    assert f(None, 0, None, 3, 0, 8, 8, 1, None) == 0             # empty layer
+
+
 def test_prepare_argument_errors(clib):
     f = clib.gptq_prepare_hinv
     fake = ctypes.c_void_p(256)  # never dereferenced: validation fails first

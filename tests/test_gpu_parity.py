@@ -127,6 +127,67 @@ def test_hessian_large_row_stride(lib, ldx):
     del big, Xv
 
 
+@pytest.mark.parametrize("n,nc,ntok,set_first", [
+    (300, 4, 64, True),       # 128-wide tiles
+    (4096, 3, 128, True),     # 192-wide tiles
+    (4000, 5, 64, False),     # 192-wide tiles, ragged d_in, adding into H
+    (8000, 2, 64, True),      # 256-wide tiles
+    (300, 35, 64, False),     # two launches: 32 chunks, then 3
+])
+def test_hessian_chunks_match_contiguous(lib, n, nc, ntok, set_first):
+    """Chunks in separate buffers summed by one call give, bit for bit, the
+    H of single calls over the same tokens stored contiguously, one per group
+    of 32 chunks."""
+    import torch
+    say("hessian chunks", n, nc, ntok, set_first)
+    g = torch.Generator(device="cuda").manual_seed(n + nc)
+    Xs = [torch.randn((n, ntok), generator=g, device="cuda").to(torch.float16) for _ in range(nc)]
+    init = 0.0 if set_first else 0.5
+    H0 = torch.full((n, n), init, dtype=torch.float32, device="cuda")
+    H1 = torch.full((n, n), init, dtype=torch.float32, device="cuda")
+    _lib_mod().hessian_chunks(H1, Xs, set_first=set_first)
+    for c0 in range(0, nc, 32):
+        Xcat = torch.cat(Xs[c0:c0 + 32], dim=1).contiguous()
+        if set_first and c0 == 0:
+            _lib_mod().hessian_set(H0, Xcat)
+        else:
+            _lib_mod().hessian_accumulate(H0, Xcat)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.tril(H0), torch.tril(H1))
+    iu = torch.triu_indices(n, n, 1, device="cuda")
+    assert torch.all(H1[iu[0], iu[1]] == init)  # strictly upper triangle not written
+    if n <= 4096:
+        Xall = np.concatenate([host(X) for X in Xs], axis=1)
+        ref = oracle.hessian([Xall])
+        if not set_first:
+            ref = ref + np.tril(np.full((n, n), init))
+        parity.check_h(host(H1), ref)
+
+
+@pytest.mark.parametrize("n,nc,ntok,xdtype,offset", [
+    (300, 3, 100, "f16", 0),                 # ragged chunks: one call per chunk
+    (300, 3, 64, "f16", 1),                  # unaligned rows: one call per chunk
+    (200, 3, 50, "f32", 0),                  # float32 inputs: one call per chunk
+])
+def test_hessian_chunks_fallback(lib, n, nc, ntok, xdtype, offset):
+    """Chunks the batched launch does not take are added one call per chunk:
+    the H of gptq_hessian_set on the first and gptq_hessian_accumulate on
+    the others, bit for bit."""
+    import torch
+    say("hessian chunks fallback", n, nc, ntok, xdtype, offset)
+    dt = torch.float16 if xdtype == "f16" else torch.float32
+    g = torch.Generator(device="cuda").manual_seed(3 * n + nc)
+    Xs = [torch.randn((n, ntok + offset), generator=g, device="cuda").to(dt)[:, offset:] for _ in range(nc)]
+    H0 = torch.full((n, n), 9.0, dtype=torch.float32, device="cuda")
+    H1 = torch.full((n, n), 9.0, dtype=torch.float32, device="cuda")
+    _lib_mod().hessian_chunks(H1, Xs, set_first=True)
+    _lib_mod().hessian_set(H0, Xs[0])
+    for X in Xs[1:]:
+        _lib_mod().hessian_accumulate(H0, X)
+    torch.cuda.synchronize()
+    assert torch.equal(H0, H1)
+
+
 def test_hessian_set_empty_writes_zero(lib):
     import torch
     say("hessian set, no tokens")
