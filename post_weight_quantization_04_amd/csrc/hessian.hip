@@ -8,7 +8,8 @@
 // as 2x2 MFMA 32x32 accumulators.  Token slabs of X rows I
 // and J are staged through LDS; products run on MFMA with fp32 accumulation
 // (f16 inputs: 32x32x16 f16, exact products; f32 inputs: 32x32x2 f32).  Each
-// call adds its token range into H once at the end.
+// launch adds its token range (one chunk, or up to kMaxChunks chunks held in
+// separate buffers) into H once at the end.
 // The MFMA instruction sequence over the tokens is the same for every tile,
 // slab size and prefetch depth (zero-padded tails add exact zeros), so the
 // sums are the same bits whichever kernel a shape takes.
